@@ -1,0 +1,293 @@
+"""The five synthetic workloads of the RMA hot path.
+
+Each workload is named by what it is.  Sizes follow the EdgeRock-4B model as the
+pages describe it: 16 query heads over 4 KV groups, head width 256, a 1024-slot
+sliding window, a 1024-record anchor bank and a 256-record pending block per
+group, 8 SWA||RMA layers, hidden width 2560 feeding a 2560->256->4 scorer.
+
+* ``tiny_stream``       batch 1, one layer, 2048-token stream (8 commits), then
+                        8 decode steps at positions 2048..2055.
+* ``steady_b64``        batch 64, 8 layers, decode at position 32768 with full
+                        window, full bank and a full pending block.
+* ``headline_b512``     batch 512, 8 layers, decode at position 65536 (same
+                        per-sequence state as ``steady_b64``; 36 GiB total),
+                        norm gains N(1, 0.1).
+* ``commit_burst_b512`` batch 512, 8 layers: score 256 new tokens per sequence
+                        and merge them with a full bank, with about 5% exact
+                        score ties planted.
+* ``long_stream_b1``    batch 1, 8 layers, a stream to position 262143.
+
+Every large BF16 tensor is a counter-based stream (see ``synth.core``), so the
+host can regenerate any slice of what the device drew.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from .core import (
+    StreamKey,
+    distinct_ints_np,
+    normal_bf16_np,
+    normal_bf16_torch_,
+    normal_f32_np,
+    rng_np,
+    stream_key,
+)
+
+Q_HEADS = 16
+KV_GROUPS = 4
+HEAD_DIM = 256
+WINDOW = 1024
+BANK = 1024
+BLOCK = 256
+HIDDEN = 2560
+MID = 256
+LAYERS = 8
+
+# Standard deviation of a 2560->256->4 bias-free chain with N(0,1) inputs and
+# N(0, 0.02^2) weights: sqrt(256 * 2560 * 0.02^2 * 0.02^2) = 0.3238.
+SCORE_STD = float(np.sqrt(256 * 2560 * 0.02**2 * 0.02**2))
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    layers: int
+    position: int  # decode position (or stream length for the streams)
+    gains: str  # "ones" or "normal"
+    src_hi: int = 31744  # anchor source positions are drawn from [0, src_hi)
+    eps: float = 1e-6
+    rope_base: float = 1e7
+    extra: dict = field(default_factory=dict)
+
+
+TINY_STREAM = Workload("tiny_stream", batch=1, layers=1, position=2048, gains="normal",
+                       extra={"decode_steps": 8})
+STEADY_B64 = Workload("steady_b64", batch=64, layers=8, position=32768, gains="ones")
+HEADLINE_B512 = Workload("headline_b512", batch=512, layers=8, position=65536, gains="normal")
+COMMIT_BURST_B512 = Workload("commit_burst_b512", batch=512, layers=8, position=32767,
+                             gains="ones", src_hi=32512)
+LONG_STREAM_B1 = Workload("long_stream_b1", batch=1, layers=8, position=262144, gains="normal")
+
+WORKLOADS = {w.name: w for w in (TINY_STREAM, STEADY_B64, HEADLINE_B512, COMMIT_BURST_B512,
+                                 LONG_STREAM_B1)}
+
+
+def key(wl: Workload | str, *names) -> StreamKey:
+    return stream_key(wl if isinstance(wl, str) else wl.name, *names)
+
+
+# ------------------------------------------------------------------ small tensors
+def gains(wl: Workload, layer: int) -> dict:
+    """The four FP32 [256] norm gains of one layer: gq_win, gk_win, gq_rma, gk_rma."""
+    out = {}
+    for nm in ("gq_win", "gk_win", "gq_rma", "gk_rma"):
+        if wl.gains == "ones":
+            out[nm] = np.ones(HEAD_DIM, np.float32)
+        else:
+            out[nm] = normal_f32_np(key(wl, layer, nm), (HEAD_DIM,), 1.0, 0.1)
+    return out
+
+
+def scorer_weights(wl: Workload, layer: int):
+    """W1 FP32 [2560][256] and W2 FP32 [256][4], both N(0, 0.02^2)."""
+    w1 = normal_f32_np(key(wl, layer, "W1"), (HIDDEN, MID), 0.0, 0.02)
+    w2 = normal_f32_np(key(wl, layer, "W2"), (MID, KV_GROUPS), 0.0, 0.02)
+    return w1, w2
+
+
+# ------------------------------------------------------------------ decode state
+KV_NAMES = ("win_k", "win_v", "bank_k", "bank_v", "pend_k", "pend_v")
+
+
+def kv_slots(name: str) -> int:
+    return {"win": WINDOW, "bank": BANK, "pend": BLOCK}[name.split("_")[0]]
+
+
+def kv_np(wl: Workload, layer: int, name: str, b: int) -> np.ndarray:
+    """One sequence's slice ``[4][slots][256]`` (uint16 BF16 bits) of a K/V state tensor."""
+    per_seq = KV_GROUPS * kv_slots(name) * HEAD_DIM
+    x = normal_bf16_np(key(wl, layer, name), per_seq, start=b * per_seq)
+    return x.reshape(KV_GROUPS, kv_slots(name), HEAD_DIM)
+
+
+def kv_torch_(wl: Workload, layer: int, name: str, out) -> None:
+    """Fill the device tensor ``out`` ``[B][4][slots][256]`` with the same stream."""
+    assert out.shape[1:] == (KV_GROUPS, kv_slots(name), HEAD_DIM)
+    normal_bf16_torch_(out, key(wl, layer, name))
+
+
+def q_np(wl: Workload, layer: int, b: int, step: int = 0) -> np.ndarray:
+    """Raw query ``[16][256]`` (uint16 BF16 bits) of sequence b."""
+    per_seq = Q_HEADS * HEAD_DIM
+    return normal_bf16_np(key(wl, layer, "q", step), per_seq, start=b * per_seq).reshape(
+        Q_HEADS, HEAD_DIM)
+
+
+def q_torch_(wl: Workload, layer: int, out, step: int = 0) -> None:
+    normal_bf16_torch_(out, key(wl, layer, "q", step))
+
+
+def bank_src(wl: Workload, layer: int, b: int) -> np.ndarray:
+    """Source positions ``[4][1024]`` of a full bank: distinct per group, uniform in [0, src_hi)."""
+    return np.stack([distinct_ints_np(key(wl, layer, "bank_src", b, g), BANK, 0, wl.src_hi)
+                     for g in range(KV_GROUPS)])
+
+
+def bank_src_all(wl: Workload, layer: int) -> np.ndarray:
+    return np.stack([bank_src(wl, layer, b) for b in range(wl.batch)])
+
+
+def pend_src(wl: Workload) -> np.ndarray:
+    """Source positions ``[256]`` of a full pending block: the last 256 positions up to p."""
+    return np.arange(wl.position - BLOCK + 1, wl.position + 1, dtype=np.int32)
+
+
+def decode_meta(wl: Workload, layer: int) -> dict:
+    """Host-side metadata of a steady-state layer (all sequences)."""
+    B = wl.batch
+    return {
+        "bank_score": normal_f32_np(key(wl, layer, "bank_score"), (B, KV_GROUPS, BANK)),
+        "bank_src": bank_src_all(wl, layer),
+        "pend_score": normal_f32_np(key(wl, layer, "pend_score"), (B, BLOCK, KV_GROUPS)),
+        "pend_src": np.broadcast_to(pend_src(wl), (B, BLOCK)).copy(),
+        "n_bank": np.full(B, BANK, np.int32),
+        "n_pend": np.full(B, BLOCK, np.int32),
+        "pos": np.full(B, wl.position, np.int32),
+    }
+
+
+def decode_state_np(wl: Workload, layer: int, b: int) -> dict:
+    """Everything the decode step of sequence b in one layer reads (host copy)."""
+    st = {nm: kv_np(wl, layer, nm, b) for nm in KV_NAMES}
+    st["n_bank"], st["n_pend"], st["pos"] = BANK, BLOCK, wl.position
+    return st
+
+
+# ------------------------------------------------------------------ commit burst
+def burst_hidden_np(wl: Workload, layer: int, b: int, rows=None) -> np.ndarray:
+    """Hidden states ``[256][2560]`` (BF16 bits) of sequence b's new block, with duplicated rows."""
+    per_seq = BLOCK * HIDDEN
+    h = normal_bf16_np(key(wl, layer, "H"), per_seq, start=b * per_seq).reshape(BLOCK, HIDDEN)
+    for dst, src in burst_dup_rows(wl, layer)[b]:
+        h[dst] = h[src]
+    return h if rows is None else h[rows]
+
+
+def burst_hidden_torch_(wl: Workload, layer: int, out) -> None:
+    """Fill ``out`` ``[B][256][2560]`` on its device with the same hidden states."""
+    import torch
+
+    normal_bf16_torch_(out, key(wl, layer, "H"))
+    dups = burst_dup_rows(wl, layer)
+    bi = torch.tensor([b for b in range(wl.batch) for _ in dups[b]], dtype=torch.int64)
+    di = torch.tensor([d for b in range(wl.batch) for d, _ in dups[b]], dtype=torch.int64)
+    si = torch.tensor([s for b in range(wl.batch) for _, s in dups[b]], dtype=torch.int64)
+    bi, di, si = bi.to(out.device), di.to(out.device), si.to(out.device)
+    out[bi, di] = out[bi, si]
+
+
+def burst_dup_rows(wl: Workload, layer: int, frac: float = 0.025):
+    """Per sequence, (dst, src) row pairs: 2.5% of the block's rows copy another row."""
+    rng = rng_np(key(wl, layer, "dup_rows"))
+    n = int(frac * BLOCK)
+    out = []
+    for _ in range(wl.batch):
+        pick = rng.choice(BLOCK, size=2 * n, replace=False)
+        out.append([(int(d), int(s)) for d, s in zip(pick[:n], pick[n:])])
+    return out
+
+
+def burst_scores(wl: Workload, layer: int) -> dict:
+    """Commit inputs with planted exact ties (host; FP32).
+
+    Per (sequence, group) the 1280 candidate scores are drawn N(0, 0.3238^2),
+    sorted, and the eight values around the 1024th place are set equal so the
+    cut falls inside a run of ties; in every fourth segment the whole segment
+    is shifted so that run is exactly zero, with half of it written as -0.0.
+    The values are then shuffled into 1024 bank and 256 pending slots.  After
+    that, 2.5% of each sequence's pending rows copy another row (all groups),
+    and 2.5% of each segment's bank scores copy a pending score.
+    Returns bank_score [B][4][1024], pend_score [B][256][4] and the sources.
+    """
+    B, G = wl.batch, KV_GROUPS
+    rng = rng_np(key(wl, layer, "burst_scores"))
+    n = BANK + BLOCK
+    v = np.sort(rng.standard_normal((B, G, n)) * SCORE_STD, axis=-1)[..., ::-1].copy()
+    v[..., BANK - 4:BANK + 4] = v[..., BANK - 1:BANK]
+    zseg = (np.arange(B * G).reshape(B, G) % 4) == 3
+    v[zseg] -= v[zseg][:, BANK - 1:BANK]
+    v = v.astype(np.float32)
+    neg = v[zseg]
+    neg[:, BANK - 4:BANK] = -0.0
+    neg[:, BANK:BANK + 4] = 0.0
+    v[zseg] = neg
+    perm = np.argsort(rng.random((B, G, n)), axis=-1)
+    v = np.take_along_axis(v, perm, axis=-1)
+    bank_score = v[..., :BANK].copy()
+    pend_score = np.ascontiguousarray(v[..., BANK:].transpose(0, 2, 1))  # [B][256][4]
+    nd = int(0.025 * BLOCK)
+    for b in range(B):
+        pick = rng.choice(BLOCK, size=2 * nd, replace=False)
+        pend_score[b, pick[:nd]] = pend_score[b, pick[nd:]]
+    nb = int(round(0.025 * BANK))
+    for b in range(B):
+        for g in range(G):
+            dst = rng.choice(BANK, size=nb, replace=False)
+            src = rng.integers(0, BLOCK, size=nb)
+            bank_score[b, g, dst] = pend_score[b, src, g]
+    return {
+        "bank_score": bank_score,
+        "pend_score": pend_score,
+        "bank_src": bank_src_all(wl, layer),
+        "pend_src": np.broadcast_to(pend_src(wl), (B, BLOCK)).copy(),
+        "n_bank": np.full(B, BANK, np.int32),
+        "n_pend": np.full(B, BLOCK, np.int32),
+        "pos": np.full(B, wl.position, np.int32),
+    }
+
+
+# ------------------------------------------------------------------ token streams
+RECORD_NAMES = ("k_win", "v_win", "k_rma", "v_rma")
+
+
+def record_np(wl: Workload, layer: int, name: str, t0: int, t1: int) -> np.ndarray:
+    """Raw per-token records ``[t1-t0][4][256]`` (BF16 bits) of positions t0..t1-1 (batch 1)."""
+    per_tok = KV_GROUPS * HEAD_DIM
+    x = normal_bf16_np(key(wl, layer, "rec", name), (t1 - t0) * per_tok, start=t0 * per_tok)
+    return x.reshape(t1 - t0, KV_GROUPS, HEAD_DIM)
+
+
+def record_torch_(wl: Workload, layer: int, name: str, t0: int, out) -> None:
+    normal_bf16_torch_(out, key(wl, layer, "rec", name), start=t0 * KV_GROUPS * HEAD_DIM)
+
+
+def stream_q_np(wl: Workload, layer: int, t0: int, t1: int) -> np.ndarray:
+    """Raw queries ``[t1-t0][16][256]`` of positions t0..t1-1 (batch 1)."""
+    per_tok = Q_HEADS * HEAD_DIM
+    x = normal_bf16_np(key(wl, layer, "stream_q"), (t1 - t0) * per_tok, start=t0 * per_tok)
+    return x.reshape(t1 - t0, Q_HEADS, HEAD_DIM)
+
+
+def stream_q_torch_(wl: Workload, layer: int, t0: int, out) -> None:
+    normal_bf16_torch_(out, key(wl, layer, "stream_q"), start=t0 * Q_HEADS * HEAD_DIM)
+
+
+def stream_hidden_np(wl: Workload, layer: int, t0: int, t1: int) -> np.ndarray:
+    """Hidden states ``[t1-t0][2560]`` of positions t0..t1-1 (batch 1)."""
+    x = normal_bf16_np(key(wl, layer, "stream_H"), (t1 - t0) * HIDDEN, start=t0 * HIDDEN)
+    return x.reshape(t1 - t0, HIDDEN)
+
+
+def stream_hidden_torch_(wl: Workload, layer: int, t0: int, out) -> None:
+    normal_bf16_torch_(out, key(wl, layer, "stream_H"), start=t0 * HIDDEN)
+
+
+def stream_scores_np(wl: Workload, layer: int, block: int) -> np.ndarray:
+    """Generator-supplied candidate scores ``[256][4]`` (FP32) of one 256-token block."""
+    return normal_f32_np(key(wl, layer, "stream_score", block), (BLOCK, KV_GROUPS), 0.0,
+                         SCORE_STD)

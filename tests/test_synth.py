@@ -1,0 +1,64 @@
+"""The seeded generators: host and device implementations draw identical bytes."""
+
+import numpy as np
+import torch
+
+import synth
+from synth import workloads as W
+
+
+def test_counter_stream_host_equals_torch_slice():
+    k = synth.stream_key("t", 1, "x")
+    n = 100_003
+    ref = synth.normal_bf16_np(k, n, start=123)
+    out = torch.empty(n, dtype=torch.bfloat16)
+    synth.normal_bf16_torch_(out, k, start=123, chunk=4096)
+    assert np.array_equal(out.view(torch.int16).numpy().view(np.uint16), ref)
+    # a slice regenerated from its own offset matches the full draw
+    assert np.array_equal(synth.normal_bf16_np(k, 500, start=123 + 7000), ref[7000:7500])
+
+
+def test_counter_stream_near_top_of_index_space():
+    k = synth.stream_key("edge")
+    start = (1 << 32) - 1000
+    ref = synth.normal_bf16_np(k, 1000, start=start)
+    out = torch.empty(1000, dtype=torch.int16)
+    synth.normal_bf16_torch_(out, k, start=start)
+    assert np.array_equal(out.numpy().view(np.uint16), ref)
+
+
+def test_normal_table_moments():
+    x = synth.bf16_bits_to_f32_np(synth.normal_bf16_np(synth.stream_key("m"), 1 << 20))
+    assert abs(float(x.mean())) < 5e-3 and abs(float(x.std()) - 1.0) < 5e-3
+
+
+def test_workload_slices_consistent():
+    wl = W.STEADY_B64
+    full = torch.empty(3, 4, 256, 256, dtype=torch.bfloat16)
+    # a pending-block-sized tensor for the first three sequences
+    synth.normal_bf16_torch_(full, W.key(wl, 2, "pend_k"))
+    for b in range(3):
+        assert np.array_equal(full[b].view(torch.int16).numpy().view(np.uint16),
+                              W.kv_np(wl, 2, "pend_k", b))
+
+
+def test_burst_scores_plant_ties():
+    wl = W.Workload("burst_small", batch=4, layers=1, position=32767, gains="ones", src_hi=32512)
+    d = W.burst_scores(wl, 0)
+    bs, ps = d["bank_score"], d["pend_score"]
+    assert bs.shape == (4, 4, 1024) and ps.shape == (4, 256, 4)
+    allv = np.concatenate([bs, ps.transpose(0, 2, 1)], axis=-1)
+    # at least 5% of values take part in exact ties
+    ties = 0
+    for b in range(4):
+        for g in range(4):
+            _, cnt = np.unique(allv[b, g], return_counts=True)
+            ties += cnt[cnt > 1].sum()
+    assert ties / allv.size > 0.05
+    # some segments carry both signed zeros
+    sb = np.signbit(allv) & (allv == 0)
+    assert sb.any() and ((allv == 0) & ~np.signbit(allv)).any()
+    for b in range(4):
+        for g in range(4):
+            assert len(set(d["bank_src"][b, g])) == 1024
+            assert d["bank_src"][b, g].max() < 32512
