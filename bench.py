@@ -1,0 +1,260 @@
+"""Benchmark of the SWA||RMA decode step on one MI355X.
+
+One step is the decode-step attention of all 8 SWA||RMA layers for every
+sequence of the batch (8 dependent launches of ``swa_rma_decode_attn`` on one
+stream; in a model, layer l+1's query needs layer l's output, so layers are not
+fused).  The state is the synthetic steady state of the pages' 32K-in + 32K-out
+serving shape: full 1024-slot window, full 1024-record bank and a full 256-record
+pending block per KV group, BF16, drawn from seeded counter streams directly in
+HBM before timing starts.
+
+Prints one JSON line: sequence-steps/s (steps/s x batch), the per-launch
+roofline of the attention kernel (algorithmic bytes / measured launch time
+against 8 TB/s), and the float64 oracle timed on the host cores on a bounded
+sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+# per (sequence, layer): window + bank + pending K/V, BF16
+STATE_BYTES_PER_UNIT = 2 * 4 * (1024 + 1024 + 256) * 256 * 2
+# per (sequence, layer): one query read for both branches (they alias), two
+# outputs, two log-sum-exp rows
+IO_BYTES_PER_UNIT = 16 * 256 * 2 + 2 * 16 * 256 * 2 + 2 * 16 * 4
+METRIC = "SWA∥RMA decode steps/s ×batch and HBM GB/s (% peak) at batch 512"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attn_headline_b512_traffic.txt")
+KERNEL_SOURCES = ("swa_memory_anchor_amd/csrc/decode_attn.hip",
+                  "swa_memory_anchor_amd/csrc/rma_device.h")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(units_per_launch: int):
+    """HBM bytes per launch from the committed counter summary, if it is current."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    if int(kv.get("units_per_launch", -1)) != units_per_launch:
+        return None
+    return float(kv["hbm_bytes_per_launch"])
+
+
+def cpu_baseline(wl, budget_s: float, max_units: int):
+    """The oracle, untuned, on a bounded sample of (sequence, layer) units."""
+    import numpy as np
+
+    import oracle as O
+    from synth import workloads as W
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    rng = np.random.default_rng(7)
+    units = 0
+    spent = 0.0
+    gains = {}
+    while units < max_units and spent < budget_s:
+        b, layer = int(rng.integers(0, wl.batch)), int(rng.integers(0, wl.layers))
+        s = W.decode_state_np(wl, layer, b)
+        q = W.q_np(wl, layer, b)
+        g = gains.setdefault(layer, W.gains(wl, layer))
+        t0 = time.perf_counter()
+        O.decode_one(list(s["win_k"]), list(s["win_v"]), q, g["gq_win"], s["pos"], wl.eps,
+                     wl.rope_base)
+        keys = [np.concatenate([s["bank_k"][i], s["pend_k"][i]]) for i in range(4)]
+        vals = [np.concatenate([s["bank_v"][i], s["pend_v"][i]]) for i in range(4)]
+        O.decode_one(keys, vals, q, g["gq_rma"], s["pos"], wl.eps, wl.rope_base)
+        spent += time.perf_counter() - t0
+        units += 1
+    units_per_s = units / spent
+    return {
+        "value": units_per_s / wl.layers,
+        "unit": "seq-steps/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{units} random (sequence, layer) units of {wl.name} (both branches each), "
+                  f"{spent:.1f} s of oracle time; value = units/s / {wl.layers} layers",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="headline_b512",
+                    choices=["headline_b512", "steady_b64", "batch1"])
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
+    ap.add_argument("--cpu-max-units", type=int, default=2000)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the RMA hot path is data parallel over "
+              "sequences and needs no exchange, so every GPU would run this same kernel on "
+              "its own sequences; run it with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": 1 << 30, "launches": 3}))
+        return 0
+
+    import swa_memory_anchor_amd as R
+    from synth import workloads as W
+
+    if args.workload == "headline_b512":
+        wl = W.HEADLINE_B512
+    elif args.workload == "steady_b64":
+        wl = W.STEADY_B64
+    else:
+        wl = W.Workload("batch1", batch=1, layers=8, position=65536, gains="normal")
+    B, L = wl.batch, wl.layers
+    dev = "cuda"
+
+    states, qs, norms, outs = [], [], [], []
+    for layer in range(L):
+        st = R.alloc_layer_state(B, dev, zero_kv=False)
+        for nm in W.KV_NAMES:
+            W.kv_torch_(wl, layer, nm, getattr(st, nm))
+        for k, v in W.decode_meta(wl, layer).items():
+            getattr(st, k).copy_(torch.from_numpy(v).to(dev))
+        q = torch.empty(B, 16, 256, dtype=torch.bfloat16, device=dev)
+        W.q_torch_(wl, layer, q)
+        g = W.gains(wl, layer)
+        nm_ = R.Norm(*[torch.from_numpy(g[k]).to(dev) for k in ("gq_win", "gk_win", "gq_rma",
+                                                                "gk_rma")], wl.eps, wl.rope_base)
+        o = (torch.empty(B, 16, 256, dtype=torch.bfloat16, device=dev),
+             torch.empty(B, 16, dtype=torch.float32, device=dev),
+             torch.empty(B, 16, 256, dtype=torch.bfloat16, device=dev),
+             torch.empty(B, 16, dtype=torch.float32, device=dev))
+        states.append(st)
+        qs.append(q)
+        norms.append(nm_)
+        outs.append(o)
+    ws = R.decode_workspace(B, dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        for layer in range(L):
+            o = outs[layer]
+            if ev is not None:
+                ev[layer][0].record(stream)
+            R.swa_rma_decode_attn(states[layer], B, qs[layer], qs[layer], norms[layer], o[0],
+                                  o[1], o[2], o[3], ws, stream)
+            if ev is not None:
+                ev[layer][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps, bracketed by synchronisation
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record(stream)
+    for _ in range(args.steps):
+        step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_begin.elapsed_time(t_end)
+
+    # per-launch durations of the attention call (same stream, separate pass)
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in range(L)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    launch_ms = [e[0].elapsed_time(e[1]) for s in evs for e in s]
+    launch_ms.sort()
+    avg_launch_ms = sum(launch_ms) / len(launch_ms)
+
+    ms_per_step = total_ms / args.steps
+    value = B * args.steps / (total_ms / 1e3)
+    bytes_per_launch = B * (STATE_BYTES_PER_UNIT + IO_BYTES_PER_UNIT)
+    achieved = bytes_per_launch / (avg_launch_ms / 1e3) / 1e9
+    traffic = measured_traffic(B)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "seq-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "batch": B,
+            "layers": L,
+            "position": wl.position,
+            "state_bytes_per_step": B * L * STATE_BYTES_PER_UNIT,
+            "decode_splits": R.rma_decode_splits(B),
+            "hbm_gbps_step": round(B * L * (STATE_BYTES_PER_UNIT + IO_BYTES_PER_UNIT)
+                                   / (ms_per_step / 1e3) / 1e9, 1),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "kernel": "decode_attn_kernel",
+            "avg_launch_ms": round(avg_launch_ms, 4),
+            "median_launch_ms": round(launch_ms[len(launch_ms) // 2], 4),
+            "bytes_per_launch": bytes_per_launch,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget, args.cpu_max_units)
+    print(json.dumps(res))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

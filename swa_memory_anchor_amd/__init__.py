@@ -1,0 +1,228 @@
+"""Python binding of ``librma.so``: the Rock Memory Anchors (RMA) hot path on MI355X.
+
+Argument marshalling only.  Every step of the path runs in the HIP kernels behind
+the C ABI declared in ``include/rma.h``; this module converts torch tensors (used
+for device memory and streams) into pointers and calls the entry points of the
+same names.  If the library has not been built, importing the entry points
+raises: there is no fallback.
+
+Entry points: ``swa_rma_append``, ``swa_rma_decode_attn``, ``rma_score``,
+``rma_commit_topk``, plus the size helpers ``rma_layer_state_bytes``,
+``rma_layer_kv_bytes``, ``rma_decode_workspace_bytes``, ``rma_decode_splits`` and
+``rma_status_str``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, fields
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librma.so")
+
+Q_HEADS, KV_GROUPS, HEAD_DIM, ROPE_DIM = 16, 4, 256, 64
+WINDOW, BANK, BLOCK, HIDDEN, SCORER_MID = 1024, 1024, 256, 2560, 256
+
+EXPORTS = (
+    "rma_layer_state_bytes", "rma_layer_kv_bytes", "rma_decode_workspace_bytes",
+    "rma_decode_splits", "swa_rma_append", "swa_rma_decode_attn", "rma_score",
+    "rma_commit_topk", "rma_status_str",
+)
+
+_c_void_p = ctypes.c_void_p
+
+
+class RmaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {rma_status_str(status)} (status {status})")
+        self.status = status
+
+
+class _StateC(ctypes.Structure):
+    _fields_ = [(n, _c_void_p) for n in (
+        "win_k", "win_v", "bank_k", "bank_v", "bank_score", "bank_src", "pend_k", "pend_v",
+        "pend_score", "pend_src", "n_bank", "n_pend", "pos")]
+
+
+class _NormC(ctypes.Structure):
+    _fields_ = [("gq_win", _c_void_p), ("gk_win", _c_void_p), ("gq_rma", _c_void_p),
+                ("gk_rma", _c_void_p), ("eps", ctypes.c_float), ("rope_base", ctypes.c_float)]
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the built library (raises if it is missing)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m swa_memory_anchor_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, i64, sz, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, _c_void_p
+        sp = ctypes.POINTER(_StateC)
+        npp = ctypes.POINTER(_NormC)
+        for nm in ("rma_layer_state_bytes", "rma_layer_kv_bytes", "rma_decode_workspace_bytes"):
+            getattr(L, nm).argtypes, getattr(L, nm).restype = [i32], sz
+        L.rma_decode_splits.argtypes, L.rma_decode_splits.restype = [i32], i32
+        L.swa_rma_append.argtypes = [sp, i32, vp, vp, vp, vp, vp, npp, vp]
+        L.swa_rma_append.restype = ctypes.c_int
+        L.swa_rma_decode_attn.argtypes = [sp, i32, vp, vp, npp, vp, vp, vp, vp, vp, sz, vp]
+        L.swa_rma_decode_attn.restype = ctypes.c_int
+        L.rma_score.argtypes = [vp, i64, i64, vp, vp, vp, i64, vp]
+        L.rma_score.restype = ctypes.c_int
+        L.rma_commit_topk.argtypes = [sp, i32, vp, vp]
+        L.rma_commit_topk.restype = ctypes.c_int
+        L.rma_status_str.argtypes, L.rma_status_str.restype = [ctypes.c_int], ctypes.c_char_p
+        _LIB = L
+    return _LIB
+
+
+# ---------------------------------------------------------------- plumbing (torch memory)
+@dataclass
+class LayerState:
+    """Device tensors of one layer's state; shapes as in ``include/rma.h``."""
+
+    win_k: object
+    win_v: object
+    bank_k: object
+    bank_v: object
+    bank_score: object
+    bank_src: object
+    pend_k: object
+    pend_v: object
+    pend_score: object
+    pend_src: object
+    n_bank: object
+    n_pend: object
+    pos: object
+
+    @property
+    def batch(self) -> int:
+        return int(self.n_bank.shape[0])
+
+
+@dataclass
+class Norm:
+    gq_win: object
+    gk_win: object
+    gq_rma: object
+    gk_rma: object
+    eps: float = 1e-6
+    rope_base: float = 1e7
+
+
+def alloc_layer_state(batch: int, device="cuda", zero_kv: bool = True) -> LayerState:
+    """Allocate one layer's state with torch (empty: n_bank = n_pend = 0, pos = -1)."""
+    import torch
+
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    mk = torch.zeros if zero_kv else torch.empty
+    return LayerState(
+        win_k=mk(batch, KV_GROUPS, WINDOW, HEAD_DIM, dtype=bf, device=device),
+        win_v=mk(batch, KV_GROUPS, WINDOW, HEAD_DIM, dtype=bf, device=device),
+        bank_k=mk(batch, KV_GROUPS, BANK, HEAD_DIM, dtype=bf, device=device),
+        bank_v=mk(batch, KV_GROUPS, BANK, HEAD_DIM, dtype=bf, device=device),
+        bank_score=torch.zeros(batch, KV_GROUPS, BANK, dtype=f32, device=device),
+        bank_src=torch.zeros(batch, KV_GROUPS, BANK, dtype=i32, device=device),
+        pend_k=mk(batch, KV_GROUPS, BLOCK, HEAD_DIM, dtype=bf, device=device),
+        pend_v=mk(batch, KV_GROUPS, BLOCK, HEAD_DIM, dtype=bf, device=device),
+        pend_score=torch.zeros(batch, BLOCK, KV_GROUPS, dtype=f32, device=device),
+        pend_src=torch.zeros(batch, BLOCK, dtype=i32, device=device),
+        n_bank=torch.zeros(batch, dtype=i32, device=device),
+        n_pend=torch.zeros(batch, dtype=i32, device=device),
+        pos=torch.full((batch,), -1, dtype=i32, device=device),
+    )
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    assert t.is_contiguous(), "tensors passed to the library must be contiguous"
+    return t.data_ptr()
+
+
+def _state_c(st: LayerState) -> _StateC:
+    return _StateC(*[_ptr(getattr(st, f.name)) for f in fields(LayerState)])
+
+
+def _norm_c(nm: Norm) -> _NormC:
+    return _NormC(_ptr(nm.gq_win), _ptr(nm.gk_win), _ptr(nm.gq_rma), _ptr(nm.gk_rma),
+                  float(nm.eps), float(nm.rope_base))
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise RmaError(status, where)
+
+
+# ---------------------------------------------------------------- entry points
+def rma_status_str(status: int) -> str:
+    return lib().rma_status_str(int(status)).decode()
+
+
+def rma_layer_state_bytes(batch: int) -> int:
+    return int(lib().rma_layer_state_bytes(int(batch)))
+
+
+def rma_layer_kv_bytes(batch: int) -> int:
+    return int(lib().rma_layer_kv_bytes(int(batch)))
+
+
+def rma_decode_workspace_bytes(batch: int) -> int:
+    return int(lib().rma_decode_workspace_bytes(int(batch)))
+
+
+def rma_decode_splits(batch: int) -> int:
+    return int(lib().rma_decode_splits(int(batch)))
+
+
+def swa_rma_append(st: LayerState, batch: int, k_win, v_win, k_rma, v_rma, score, norm: Norm,
+                   stream=None) -> None:
+    s = lib().swa_rma_append(ctypes.byref(_state_c(st)), int(batch), _ptr(k_win), _ptr(v_win),
+                             _ptr(k_rma), _ptr(v_rma), _ptr(score), ctypes.byref(_norm_c(norm)),
+                             _stream(stream))
+    _check(s, "swa_rma_append")
+
+
+def swa_rma_decode_attn(st: LayerState, batch: int, q_win, q_rma, norm: Norm, o_win, lse_win,
+                        o_rma, lse_rma, workspace=None, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    s = lib().swa_rma_decode_attn(ctypes.byref(_state_c(st)), int(batch), _ptr(q_win),
+                                  _ptr(q_rma), ctypes.byref(_norm_c(norm)), _ptr(o_win),
+                                  _ptr(lse_win), _ptr(o_rma), _ptr(lse_rma), _ptr(workspace),
+                                  ws_bytes, _stream(stream))
+    _check(s, "swa_rma_decode_attn")
+
+
+def rma_score(hidden, n_rows: int, ld_hidden: int, w1, w2, scores, ld_scores: int,
+              stream=None) -> None:
+    s = lib().rma_score(_ptr(hidden), int(n_rows), int(ld_hidden), _ptr(w1), _ptr(w2),
+                        _ptr(scores), int(ld_scores), _stream(stream))
+    _check(s, "rma_score")
+
+
+def rma_commit_topk(st: LayerState, batch: int, keep_idx=None, stream=None) -> None:
+    s = lib().rma_commit_topk(ctypes.byref(_state_c(st)), int(batch), _ptr(keep_idx),
+                              _stream(stream))
+    _check(s, "rma_commit_topk")
+
+
+def decode_workspace(batch: int, device="cuda"):
+    """A workspace tensor of the size swa_rma_decode_attn needs at this batch (or None)."""
+    import torch
+
+    n = rma_decode_workspace_bytes(batch)
+    return None if n == 0 else torch.empty(n, dtype=torch.uint8, device=device)

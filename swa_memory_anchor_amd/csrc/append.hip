@@ -1,0 +1,101 @@
+// Append one token per sequence to the window ring and the pending block.
+//
+// neodrop.ai repost of the QbitAI article "内存还会跌吗？KV Cache砍掉99%…", section
+// "三段记忆，只记值得记的": the writer emits one candidate record per token.
+// fluxbbs.com "EdgeRock-4B 开源：72 MiB 固定 KV…", section "架构：递归、局部窗口与记忆锚点
+// 三件套": keys get learned RMS norm and rotary on dims 0..63 (base 1e7); values
+// are stored raw.  Keys are finalised here, once, at their own position.
+//
+// One workgroup per sequence, one wave per KV group, lane l owns dims 4l..4l+3.
+#include "rma_device.h"
+
+namespace rma {
+
+struct AppendParams {
+  uint16_t *win_k, *win_v, *pend_k, *pend_v;
+  float *pend_score;
+  int32_t *pend_src, *n_pend, *pos;
+  const uint16_t *k_win, *v_win, *k_rma, *v_rma;
+  const float *score;
+  const float *gk_win, *gk_rma;
+  float eps, rope_base;
+};
+
+__global__ __launch_bounds__(256) void append_kernel(AppendParams a) {
+  const int b = blockIdx.x;
+  const int g = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int p = a.pos[b] + 1;
+  const int t = a.n_pend[b];
+  if (t < 0 || t >= kBlock) return;  // full (or corrupt) pending block: leave untouched
+  const int slot = p & (kWindow - 1);
+  const size_t in = (static_cast<size_t>(b) * kGroups + g) * kDim + 4 * lane;
+  const size_t w_row = ((static_cast<size_t>(b) * kGroups + g) * kWindow + slot) * kDim + 4 * lane;
+  const size_t p_row = ((static_cast<size_t>(b) * kGroups + g) * kBlock + t) * kDim + 4 * lane;
+
+  const uint2 kw = *reinterpret_cast<const uint2 *>(a.k_win + in);
+  const uint2 kr = *reinterpret_cast<const uint2 *>(a.k_rma + in);
+  float xw[4] = {bf16_lo(kw.x), bf16_hi(kw.x), bf16_lo(kw.y), bf16_hi(kw.y)};
+  float xr[4] = {bf16_lo(kr.x), bf16_hi(kr.x), bf16_lo(kr.y), bf16_hi(kr.y)};
+  norm_rope_head(xw, a.gk_win, a.eps, p, a.rope_base, lane);
+  norm_rope_head(xr, a.gk_rma, a.eps, p, a.rope_base, lane);
+  *reinterpret_cast<uint2 *>(a.win_k + w_row) =
+      make_uint2(pack_bf16x2(xw[0], xw[1]), pack_bf16x2(xw[2], xw[3]));
+  *reinterpret_cast<uint2 *>(a.pend_k + p_row) =
+      make_uint2(pack_bf16x2(xr[0], xr[1]), pack_bf16x2(xr[2], xr[3]));
+  *reinterpret_cast<uint2 *>(a.win_v + w_row) = *reinterpret_cast<const uint2 *>(a.v_win + in);
+  *reinterpret_cast<uint2 *>(a.pend_v + p_row) = *reinterpret_cast<const uint2 *>(a.v_rma + in);
+  if (a.score && lane == 0)
+    a.pend_score[(static_cast<size_t>(b) * kBlock + t) * kGroups + g] = a.score[b * kGroups + g];
+  __syncthreads();  // every wave has read n_pend / pos
+  if (threadIdx.x == 0) {
+    a.pend_src[static_cast<size_t>(b) * kBlock + t] = p;
+    a.n_pend[b] = t + 1;
+    a.pos[b] = p;
+  }
+}
+
+}  // namespace rma
+
+using namespace rma;
+
+static bool aligned8(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
+static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+extern "C" rma_status swa_rma_append(const rma_layer_state *st, int32_t batch,
+                                     const uint16_t *k_win, const uint16_t *v_win,
+                                     const uint16_t *k_rma, const uint16_t *v_rma,
+                                     const float *score, const rma_norm *norm, void *stream) {
+  if (!st || !norm || !k_win || !v_win || !k_rma || !v_rma) return RMA_E_ARG;
+  if (batch <= 0 || batch > RMA_MAX_BATCH) return RMA_E_ARG;
+  if (!st->win_k || !st->win_v || !st->pend_k || !st->pend_v || !st->pend_src || !st->n_pend ||
+      !st->pos || !norm->gk_win || !norm->gk_rma || (score && !st->pend_score))
+    return RMA_E_ARG;
+  const void *a16[] = {st->win_k, st->win_v, st->pend_k, st->pend_v, norm->gk_win, norm->gk_rma};
+  for (const void *p : a16)
+    if (!aligned16(p)) return RMA_E_ALIGN;
+  const void *a8[] = {k_win, v_win, k_rma, v_rma};
+  for (const void *p : a8)
+    if (!aligned8(p)) return RMA_E_ALIGN;
+  AppendParams p;
+  p.win_k = st->win_k;
+  p.win_v = st->win_v;
+  p.pend_k = st->pend_k;
+  p.pend_v = st->pend_v;
+  p.pend_score = st->pend_score;
+  p.pend_src = st->pend_src;
+  p.n_pend = st->n_pend;
+  p.pos = st->pos;
+  p.k_win = k_win;
+  p.v_win = v_win;
+  p.k_rma = k_rma;
+  p.v_rma = v_rma;
+  p.score = score;
+  p.gk_win = norm->gk_win;
+  p.gk_rma = norm->gk_rma;
+  p.eps = norm->eps;
+  p.rope_base = norm->rope_base;
+  hipLaunchKernelGGL(append_kernel, dim3(batch), dim3(256), 0, static_cast<hipStream_t>(stream), p);
+  if (hipPeekAtLastError() != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
+  return RMA_OK;
+}

@@ -1,0 +1,417 @@
+// Decode-step attention of one SWA||RMA layer on gfx950.
+//
+// What it computes (fluxbbs.com "EdgeRock-4B 开源：72 MiB 固定 KV，AIME 82.9 分",
+// section "架构：递归、局部窗口与记忆锚点三件套"): 16 query heads over 4 KV groups
+// of width 256 read two branches in parallel -- the 1024-slot sliding window and
+// the anchor records (committed bank, then the pending block) -- with learned RMS
+// norm on the query, rotary on dims 0..63 (base 1e7) and softmax scale 1/16.
+// Each branch returns its output and natural-log log-sum-exp.
+//
+// Design.  The step reads 9 MiB of BF16 K/V per (sequence, layer) against
+// 4 flop/byte, so it is bound by HBM bandwidth; the kernel is built to stream
+// every K/V byte exactly once:
+//  * one workgroup (4 waves) per (branch, sequence, KV group, key-range split);
+//    the 4 query heads of a group share every K/V row they read.
+//  * each wave walks 16-key tiles; K rows go straight from HBM into the A
+//    operand of v_mfma_f32_16x16x32_bf16 (each lane loads 16 contiguous bytes;
+//    the head dim is the contraction, so no reshuffle is needed), giving the
+//    scores of 16 keys x 4 heads in one 4-register accumulator.
+//  * V rows are loaded with coalesced 16-byte loads, staged in the wave's own
+//    LDS rows and read back transposed as the A operand of
+//    v_mfma_f32_16x16x16bf16_1k (contraction over keys); P (BF16) is the B
+//    operand and comes straight from the score accumulator's registers.
+//  * online softmax per head in the log2 domain: the scaled query carries
+//    log2(e)/16, so probabilities are exp2(s - m).
+//  * K and V reach registers through buffer loads whose range is the valid rows
+//    of the segment, so rows past the end read as zero; as soon as a tile's K
+//    and V are consumed (V copied to LDS, scores formed) the next tile's loads
+//    are issued, and they fly while the softmax update and P x V run.
+//  * waves merge through LDS; with several splits a second kernel merges the
+//    splits' (m, l, acc) partials.
+#include "rma_device.h"
+
+namespace rma {
+
+constexpr int kTile = 16;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kVStride = kDim + 8;  // LDS row stride of a V tile, in elements (528 B)
+constexpr int kPartStride = 4 + kDim;
+constexpr int kMaxSplits = 20;
+constexpr float kQScale = 1.4426950408889634f / 16.0f;  // log2(e) / sqrt(256)
+constexpr float kLn2 = 0.69314718055994531f;
+
+struct DecodeParams {
+  const uint16_t *win_k, *win_v, *bank_k, *bank_v, *pend_k, *pend_v;
+  const int32_t *n_bank, *n_pend, *pos;
+  const uint16_t *q_win, *q_rma;
+  const float *gq_win, *gq_rma;
+  float eps, rope_base;
+  uint16_t *o_win, *o_rma;
+  float *lse_win, *lse_rma;
+  float *part;
+  int batch, splits;
+};
+
+// One contiguous run of valid key rows (the window, the bank, or the pending
+// block of one sequence and group), addressed through buffer resources whose
+// size is the valid byte count: rows past the end read as zero.
+struct Segment {
+  __amdgpu_buffer_rsrc_t k, v;
+  int n;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
+}
+
+template <typename T, typename F>
+__device__ __forceinline__ T bitcast(const F &f) {
+  return __builtin_bit_cast(T, f);
+}
+
+// Issue the loads of one 16-key tile starting at row key0 of a segment: K as MFMA
+// A operands (lane: row key0 + lane%16, dims 32s + 8(lane/16) .. +8), V as row
+// chunks (lane: row key0 + 2i + lane/32, dims 8(lane%32) .. +8).
+__device__ __forceinline__ void load_tile(const Segment &sg, int key0, int lane, uint4 (&K)[8],
+                                          uint4 (&V)[8]) {
+  const int hh = lane & 15, kg = lane >> 4;
+  const int koff = hh * (kDim * 2) + kg * 16;
+  const int voff = (lane >> 5) * (kDim * 2) + (lane & 31) * 16;
+  const int soff = key0 * (kDim * 2);
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+    K[s] = bitcast<uint4>(__builtin_amdgcn_raw_buffer_load_b128(sg.k, koff + 64 * s, soff, 0));
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    V[i] = bitcast<uint4>(
+        __builtin_amdgcn_raw_buffer_load_b128(sg.v, voff + 2 * kDim * 2 * i, soff, 0));
+}
+
+struct SoftmaxState {
+  float m, l;
+  f32x4 acc[16];
+};
+
+// Stage V in LDS and form the scores of one tile (consumes K and V).
+__device__ __forceinline__ f32x4 scores_tile(int nvalid, int lane, const uint4 (&K)[8],
+                                             const uint4 (&V)[8], const uint16_t *ql,
+                                             uint16_t *vl) {
+  const int hh = lane & 15, kg = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    *reinterpret_cast<uint4 *>(vl + (2 * i + (lane >> 5)) * kVStride + 8 * (lane & 31)) = V[i];
+  // D[key][head] = sum_d K[key][d] * qhat[head][d]; the B operand is the staged
+  // query block (head hh; rows >= 4 are zero).  Lane holds keys 4kg..4kg+3 of head hh.
+  f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+  const uint16_t *qrow = ql + hh * kDim + 8 * kg;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const bf16x8 qv = bitcast<bf16x8>(*reinterpret_cast<const uint4 *>(qrow + 32 * s));
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(K[s]), qv, sc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (4 * kg + i >= nvalid) sc[i] = -INFINITY;
+  return sc;
+}
+
+// Online-softmax update and P x V for one tile whose V rows are staged in LDS.
+__device__ __forceinline__ void accumulate_tile(f32x4 sc, int lane, const uint16_t *vl,
+                                                SoftmaxState &st) {
+  const int hh = lane & 15, kg = lane >> 4;
+  float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+  mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+  const float m_new = fmaxf(st.m, mt);
+  float alpha = 1.f;
+  uint32_t pw0 = 0, pw1 = 0;
+  float psum = 0.f;
+  if (m_new != -INFINITY) {
+    alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+    const uint32_t p0 = f32_to_bf16(__builtin_amdgcn_exp2f(sc[0] - m_new));
+    const uint32_t p1 = f32_to_bf16(__builtin_amdgcn_exp2f(sc[1] - m_new));
+    const uint32_t p2 = f32_to_bf16(__builtin_amdgcn_exp2f(sc[2] - m_new));
+    const uint32_t p3 = f32_to_bf16(__builtin_amdgcn_exp2f(sc[3] - m_new));
+    // the denominator uses the same rounded weights as the numerator
+    psum = (bf16_to_f32(p0) + bf16_to_f32(p1)) + (bf16_to_f32(p2) + bf16_to_f32(p3));
+    pw0 = p0 | (p1 << 16);
+    pw1 = p2 | (p3 << 16);
+  }
+  st.l = st.l * alpha + psum;
+  st.m = m_new;
+  const s16x4 pb = bitcast<s16x4>(make_uint2(pw0, pw1));
+  // D[dim][head] += sum_key V[key][dim] * P[head][key].  This wave's LDS reads
+  // follow its own writes in scores_tile (LDS runs a wave's operations in order).
+#pragma unroll
+  for (int db = 0; db < 16; ++db) {
+    const uint16_t *col = vl + db * 16 + hh + 4 * kg * kVStride;
+    const uint32_t w0 = col[0] | (static_cast<uint32_t>(col[kVStride]) << 16);
+    const uint32_t w1 = col[2 * kVStride] | (static_cast<uint32_t>(col[3 * kVStride]) << 16);
+    const s16x4 va = bitcast<s16x4>(make_uint2(w0, w1));
+    st.acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, st.acc[db] * alpha, 0, 0, 0);
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(DecodeParams a) {
+  __shared__ __align__(16) uint16_t v_lds[kWaves][kTile * kVStride];
+  __shared__ __align__(16) uint16_t q_lds[16][kDim];  // rows 4..15 stay zero
+  __shared__ float red_m[kWaves][kHeadsPerGroup], red_l[kWaves][kHeadsPerGroup];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int split = blockIdx.x % a.splits;
+  const int unit = blockIdx.x / a.splits;
+  const int per_branch = a.batch * kGroups;
+  const bool anchor = unit < per_branch;  // anchor units first: they are the longer ones
+  const int bg = anchor ? unit : unit - per_branch;
+  const int b = bg / kGroups, g = bg % kGroups;
+
+  const int p = a.pos[b];
+  Segment seg0, seg1;
+  const size_t sgi = static_cast<size_t>(b) * kGroups + g;
+  if (anchor) {
+    const int nb = min(max(a.n_bank[b], 0), kBank);
+    const int np = min(max(a.n_pend[b], 0), kBlock);
+    seg0.k = make_rsrc(a.bank_k + sgi * kBank * kDim, nb * kDim * 2);
+    seg0.v = make_rsrc(a.bank_v + sgi * kBank * kDim, nb * kDim * 2);
+    seg0.n = nb;
+    seg1.k = make_rsrc(a.pend_k + sgi * kBlock * kDim, np * kDim * 2);
+    seg1.v = make_rsrc(a.pend_v + sgi * kBlock * kDim, np * kDim * 2);
+    seg1.n = np;
+  } else {
+    const int nw = min(max(p + 1, 0), kWindow);
+    seg0.k = make_rsrc(a.win_k + sgi * kWindow * kDim, nw * kDim * 2);
+    seg0.v = make_rsrc(a.win_v + sgi * kWindow * kDim, nw * kDim * 2);
+    seg0.n = nw;
+    seg1 = seg0;
+    seg1.n = 0;
+  }
+  // Tiles of segment 0 come first, then those of segment 1; each tile lies in one
+  // segment.  This workgroup takes tiles [tb, te).
+  const int T0 = (seg0.n + kTile - 1) / kTile;
+  const int T = T0 + (seg1.n + kTile - 1) / kTile;
+  const int per = (T + a.splits - 1) / a.splits;
+  const int tb = split * per;
+  const int te = min(T, tb + per);
+
+  // Query prep: wave w normalises, rotates and scales head 4g + w.
+  {
+    const uint16_t *q = (anchor ? a.q_rma : a.q_win) +
+                        (static_cast<size_t>(b) * kHeads + g * kHeadsPerGroup + wave) * kDim;
+    const uint2 raw = *reinterpret_cast<const uint2 *>(q + 4 * lane);
+    float x[4] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y)};
+    norm_rope_head(x, anchor ? a.gq_rma : a.gq_win, a.eps, p, a.rope_base, lane);
+    uint2 o;
+    o.x = pack_bf16x2(x[0] * kQScale, x[1] * kQScale);
+    o.y = pack_bf16x2(x[2] * kQScale, x[3] * kQScale);
+    *reinterpret_cast<uint2 *>(&q_lds[wave][4 * lane]) = o;
+  }
+  for (int i = threadIdx.x; i < 12 * kDim / 4; i += kThreads)
+    reinterpret_cast<uint2 *>(&q_lds[kHeadsPerGroup][0])[i] = make_uint2(0, 0);
+  __syncthreads();
+
+  SoftmaxState st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int d = 0; d < 16; ++d) st.acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  uint16_t *vl = v_lds[wave];
+  uint4 K[8], V[8];
+  int t = tb + wave;
+  if (t < te) load_tile(t < T0 ? seg0 : seg1, (t < T0 ? t : t - T0) * kTile, lane, K, V);
+  for (; t < te; t += kWaves) {
+    const int key0 = (t < T0 ? t : t - T0) * kTile;
+    const int nvalid = (t < T0 ? seg0.n : seg1.n) - key0;
+    const f32x4 sc = scores_tile(nvalid, lane, K, V, &q_lds[0][0], vl);
+    // K and V are consumed: the next tile's loads fly while this one accumulates.
+    const int tn = t + kWaves;
+    if (tn < te) load_tile(tn < T0 ? seg0 : seg1, (tn < T0 ? tn : tn - T0) * kTile, lane, K, V);
+    accumulate_tile(sc, lane, vl, st);
+  }
+
+  // Sum the denominators of the four lanes that share a head.
+  float l_tot = st.l + __shfl_xor(st.l, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+
+  __syncthreads();  // every wave is done with its V rows; reuse them for the merge
+  float *macc = reinterpret_cast<float *>(&v_lds[0][0]);  // [wave][head][256]
+  {
+    const int hh = lane & 15, kg = lane >> 4;
+    if (hh < kHeadsPerGroup) {
+      float *dst = macc + (wave * kHeadsPerGroup + hh) * kDim + 4 * kg;
+#pragma unroll
+      for (int db = 0; db < 16; ++db)
+        *reinterpret_cast<float4 *>(dst + 16 * db) =
+            make_float4(st.acc[db][0], st.acc[db][1], st.acc[db][2], st.acc[db][3]);
+      if (kg == 0) {
+        red_m[wave][hh] = st.m;
+        red_l[wave][hh] = l_tot;
+      }
+    }
+  }
+  __syncthreads();
+
+  const int h = wave;  // this wave now owns head 4g + h, dims 4*lane..4*lane+3
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_m[w][h]);
+  float L = 0.f;
+  float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = red_m[w][h];
+      const float wt = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      L += red_l[w][h] * wt;
+      const float4 v = *reinterpret_cast<const float4 *>(macc + (w * kHeadsPerGroup + h) * kDim +
+                                                         4 * lane);
+      O.x += v.x * wt;
+      O.y += v.y * wt;
+      O.z += v.z * wt;
+      O.w += v.w * wt;
+    }
+  }
+  const int head = g * kHeadsPerGroup + h;
+  if (a.splits == 1) {
+    uint16_t *o = (anchor ? a.o_rma : a.o_win) + (static_cast<size_t>(b) * kHeads + head) * kDim;
+    float *lse = (anchor ? a.lse_rma : a.lse_win) + static_cast<size_t>(b) * kHeads + head;
+    uint2 ov = make_uint2(0, 0);
+    float lv = -INFINITY;
+    if (M != -INFINITY) {
+      const float inv = 1.f / L;
+      ov.x = pack_bf16x2(O.x * inv, O.y * inv);
+      ov.y = pack_bf16x2(O.z * inv, O.w * inv);
+      lv = (M + log2f(L)) * kLn2;
+    }
+    *reinterpret_cast<uint2 *>(o + 4 * lane) = ov;
+    if (lane == 0) *lse = lv;
+  } else {
+    float *pp = a.part + (static_cast<size_t>(unit * a.splits + split) * kHeadsPerGroup + h) *
+                             kPartStride;
+    if (lane == 0) {
+      pp[0] = M;
+      pp[1] = L;
+    }
+    *reinterpret_cast<float4 *>(pp + 4 + 4 * lane) = O;
+  }
+}
+
+// Merge the splits of one (branch, sequence, group): 4 waves, one per head.
+__global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeParams a) {
+  const int lane = threadIdx.x & 63;
+  const int h = threadIdx.x >> 6;
+  const int unit = blockIdx.x;
+  const int per_branch = a.batch * kGroups;
+  const bool anchor = unit < per_branch;
+  const int bg = anchor ? unit : unit - per_branch;
+  const int b = bg / kGroups, g = bg % kGroups;
+  const float *base = a.part + static_cast<size_t>(unit) * a.splits * kHeadsPerGroup * kPartStride +
+                      h * kPartStride;
+  float M = -INFINITY;
+  for (int s = 0; s < a.splits; ++s)
+    M = fmaxf(M, base[static_cast<size_t>(s) * kHeadsPerGroup * kPartStride]);
+  float L = 0.f;
+  float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (M != -INFINITY) {
+    for (int s = 0; s < a.splits; ++s) {
+      const float *pp = base + static_cast<size_t>(s) * kHeadsPerGroup * kPartStride;
+      const float ms = pp[0];
+      const float wt = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+      L += pp[1] * wt;
+      const float4 v = *reinterpret_cast<const float4 *>(pp + 4 + 4 * lane);
+      O.x += v.x * wt;
+      O.y += v.y * wt;
+      O.z += v.z * wt;
+      O.w += v.w * wt;
+    }
+  }
+  const int head = g * kHeadsPerGroup + h;
+  uint16_t *o = (anchor ? a.o_rma : a.o_win) + (static_cast<size_t>(b) * kHeads + head) * kDim;
+  float *lse = (anchor ? a.lse_rma : a.lse_win) + static_cast<size_t>(b) * kHeads + head;
+  uint2 ov = make_uint2(0, 0);
+  float lv = -INFINITY;
+  if (M != -INFINITY) {
+    const float inv = 1.f / L;
+    ov.x = pack_bf16x2(O.x * inv, O.y * inv);
+    ov.y = pack_bf16x2(O.z * inv, O.w * inv);
+    lv = (M + log2f(L)) * kLn2;
+  }
+  *reinterpret_cast<uint2 *>(o + 4 * lane) = ov;
+  if (lane == 0) *lse = lv;
+}
+
+}  // namespace rma
+
+using namespace rma;
+
+static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+extern "C" int32_t rma_decode_splits(int32_t batch) {
+  if (batch <= 0) return 1;
+  // Aim for at least 2048 workgroups (8 per CU) so the HBM pipes stay full.
+  const int units = batch * kGroups * 2;
+  int s = (2048 + units - 1) / units;
+  return s < 1 ? 1 : (s > kMaxSplits ? kMaxSplits : s);
+}
+
+extern "C" size_t rma_decode_workspace_bytes(int32_t batch) {
+  if (batch <= 0) return 0;
+  const int s = rma_decode_splits(batch);
+  if (s == 1) return 0;
+  return static_cast<size_t>(batch) * kGroups * 2 * s * kHeadsPerGroup * kPartStride * sizeof(float);
+}
+
+extern "C" rma_status swa_rma_decode_attn(const rma_layer_state *st, int32_t batch,
+                                          const uint16_t *q_win, const uint16_t *q_rma,
+                                          const rma_norm *norm, uint16_t *o_win, float *lse_win,
+                                          uint16_t *o_rma, float *lse_rma, void *workspace,
+                                          size_t workspace_bytes, void *stream) {
+  if (!st || !norm || !q_win || !q_rma || !o_win || !lse_win || !o_rma || !lse_rma)
+    return RMA_E_ARG;
+  if (batch <= 0 || batch > RMA_MAX_BATCH) return RMA_E_ARG;
+  if (!st->win_k || !st->win_v || !st->bank_k || !st->bank_v || !st->pend_k || !st->pend_v ||
+      !st->n_bank || !st->n_pend || !st->pos || !norm->gq_win || !norm->gq_rma)
+    return RMA_E_ARG;
+  const void *al[] = {st->win_k, st->win_v, st->bank_k, st->bank_v, st->pend_k, st->pend_v,
+                      q_win,     q_rma,     o_win,      o_rma,      norm->gq_win, norm->gq_rma};
+  for (const void *p : al)
+    if (!aligned16(p)) return RMA_E_ALIGN;
+  const size_t need = rma_decode_workspace_bytes(batch);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return RMA_E_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return RMA_E_ALIGN;
+
+  DecodeParams p;
+  p.win_k = st->win_k;
+  p.win_v = st->win_v;
+  p.bank_k = st->bank_k;
+  p.bank_v = st->bank_v;
+  p.pend_k = st->pend_k;
+  p.pend_v = st->pend_v;
+  p.n_bank = st->n_bank;
+  p.n_pend = st->n_pend;
+  p.pos = st->pos;
+  p.q_win = q_win;
+  p.q_rma = q_rma;
+  p.gq_win = norm->gq_win;
+  p.gq_rma = norm->gq_rma;
+  p.eps = norm->eps;
+  p.rope_base = norm->rope_base;
+  p.o_win = o_win;
+  p.o_rma = o_rma;
+  p.lse_win = lse_win;
+  p.lse_rma = lse_rma;
+  p.part = static_cast<float *>(workspace);
+  p.batch = batch;
+  p.splits = rma_decode_splits(batch);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const unsigned units = static_cast<unsigned>(batch) * kGroups * 2;
+  hipLaunchKernelGGL(decode_attn_kernel, dim3(units * p.splits), dim3(kThreads), 0, s, p);
+  if (hipPeekAtLastError() != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
+  if (p.splits > 1) {
+    hipLaunchKernelGGL(decode_merge_kernel, dim3(units), dim3(kThreads), 0, s, p);
+    if (hipPeekAtLastError() != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
+  }
+  return RMA_OK;
+}

@@ -1,0 +1,108 @@
+"""Helpers for the GPU parity tests: moving state between the oracle (NumPy) and the
+library (torch device tensors), and the comparison rules."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle as O
+import swa_memory_anchor_amd as R
+
+DEV = "cuda"
+ATTN_TOL = 2e-2  # row-relative, BF16 I/O with FP32 accumulation
+SCORE_TOL = 1e-5  # |s_gpu - s_ref| <= SCORE_TOL * max(1, |s_ref|)
+
+
+def bf16_dev(bits: np.ndarray) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
+    return t.to(DEV).view(torch.bfloat16)
+
+
+def bits_host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def f32_dev(x) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV)
+
+
+def i32_dev(x) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(DEV)
+
+
+KV = ("win_k", "win_v", "bank_k", "bank_v", "pend_k", "pend_v")
+META = ("bank_score", "bank_src", "pend_score", "pend_src", "n_bank", "n_pend", "pos")
+
+
+def upload(st: O.LayerState) -> R.LayerState:
+    d = {nm: bf16_dev(getattr(st, nm)) for nm in KV}
+    for nm in META:
+        a = getattr(st, nm)
+        d[nm] = f32_dev(a) if a.dtype == np.float32 else i32_dev(a)
+    return R.LayerState(**d)
+
+
+def download(st: R.LayerState) -> O.LayerState:
+    d = {nm: bits_host(getattr(st, nm)) for nm in KV}
+    for nm in META:
+        d[nm] = getattr(st, nm).cpu().numpy()
+    return O.LayerState(**d)
+
+
+def norm_dev(gains: dict, eps=1e-6, base=1e7) -> R.Norm:
+    return R.Norm(f32_dev(gains["gq_win"]), f32_dev(gains["gk_win"]), f32_dev(gains["gq_rma"]),
+                  f32_dev(gains["gk_rma"]), eps, base)
+
+
+def decode_gpu(st: R.LayerState, q_win: torch.Tensor, q_rma: torch.Tensor, norm: R.Norm):
+    B = st.batch
+    o_w = torch.empty(B, 16, 256, dtype=torch.bfloat16, device=DEV)
+    o_r = torch.empty_like(o_w)
+    l_w = torch.empty(B, 16, dtype=torch.float32, device=DEV)
+    l_r = torch.empty_like(l_w)
+    ws = R.decode_workspace(B)
+    R.swa_rma_decode_attn(st, B, q_win, q_rma, norm, o_w, l_w, o_r, l_r, ws)
+    return o_w, l_w, o_r, l_r
+
+
+def attn_errors(o_gpu_bits, lse_gpu, o_ref, lse_ref):
+    """Per-row relative output error and per-row LSE error (arrays over all rows)."""
+    og = O.bf16_to_f64(o_gpu_bits).reshape(-1, o_ref.shape[-1])
+    orf = np.asarray(o_ref, np.float64).reshape(-1, o_ref.shape[-1])
+    scale = np.abs(orf).max(axis=1)
+    err = np.abs(og - orf).max(axis=1)
+    rel = np.where(scale > 0, err / np.where(scale > 0, scale, 1.0), err)
+    lg = np.asarray(lse_gpu, np.float64).reshape(-1)
+    lr = np.asarray(lse_ref, np.float64).reshape(-1)
+    both_inf = np.isneginf(lg) & np.isneginf(lr)
+    with np.errstate(invalid="ignore"):
+        lerr = np.where(both_inf, 0.0, np.abs(lg - lr) / np.maximum(1.0, np.abs(lr)))
+    return rel, lerr
+
+
+def assert_attn_close(o_gpu_bits, lse_gpu, o_ref, lse_ref, tol=ATTN_TOL, what=""):
+    rel, lerr = attn_errors(o_gpu_bits, lse_gpu, o_ref, lse_ref)
+    msg = (f"{what}: rows={rel.size} out max={rel.max():.3e} median={np.median(rel):.3e}; "
+           f"lse max={lerr.max():.3e}")
+    print(msg)
+    assert np.all(np.isfinite(rel)) and rel.max() <= tol, msg
+    assert np.all(np.isfinite(lerr)) and lerr.max() <= tol, msg
+    return rel, lerr
+
+
+def assert_scores_close(s_gpu, s_ref, tol=SCORE_TOL, what=""):
+    s_gpu = np.asarray(s_gpu, np.float64)
+    s_ref = np.asarray(s_ref, np.float64)
+    bound = tol * np.maximum(1.0, np.abs(s_ref))
+    err = np.abs(s_gpu - s_ref)
+    print(f"{what}: scores n={err.size} max err={err.max():.3e} (bound {bound.min():.1e})")
+    assert np.all(err <= bound), f"{what}: {int((err > bound).sum())} scores out of tolerance"
+
+
+def bf16_ulp_diff(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
+    """|a - b| in BF16 units in the last place (same-sign finite values)."""
+    def ordinal(x):
+        x = x.astype(np.int32)
+        return np.where(x & 0x8000, -(x & 0x7FFF), x)
+    return np.abs(ordinal(a_bits) - ordinal(b_bits))

@@ -1,0 +1,88 @@
+"""The C ABI library: it loads, exports every declared entry point, and rejects bad
+arguments on the host (no GPU needed: validation happens before any launch)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import swa_memory_anchor_amd as R
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "rma.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", txt, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(R.LIB_PATH):
+        pytest.skip("librma.so not built")
+    return R.lib()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert set(names) == set(R.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_closed_form_sizes(lib):
+    MiB = 1 << 20
+    assert R.rma_layer_kv_bytes(1) == 9 * MiB
+    assert 8 * R.rma_layer_kv_bytes(1) == 72 * MiB
+    assert R.rma_layer_kv_bytes(512) * 8 == 36 * (1 << 30)
+    meta = 4 * 1024 * 8 + 256 * (4 * 4 + 4) + 12
+    assert R.rma_layer_state_bytes(3) == 3 * (9 * MiB + meta)
+    assert R.rma_layer_state_bytes(0) == 0 and R.rma_layer_kv_bytes(-1) == 0
+
+
+def test_split_policy_and_workspace(lib):
+    assert R.rma_decode_splits(512) == 1 and R.rma_decode_workspace_bytes(512) == 0
+    assert R.rma_decode_splits(64) == 4
+    assert R.rma_decode_splits(1) == 20
+    assert R.rma_decode_workspace_bytes(64) == 64 * 8 * 4 * 4 * 260 * 4
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert R.rma_status_str(s).startswith("RMA_")
+
+
+def _state(ptr=16):
+    return R._StateC(*([ptr] * 13))
+
+
+def _norm(ptr=16):
+    return R._NormC(ptr, ptr, ptr, ptr, 1e-6, 1e7)
+
+
+def test_host_validation_rejects_bad_arguments(lib):
+    st, nm = _state(), _norm()
+    by = ctypes.byref
+    # null state / batch out of range / null output
+    assert lib.swa_rma_decode_attn(None, 4, 16, 16, by(nm), 16, 16, 16, 16, None, 0, None) == 1
+    assert lib.swa_rma_decode_attn(by(st), 0, 16, 16, by(nm), 16, 16, 16, 16, None, 0, None) == 1
+    assert lib.swa_rma_decode_attn(by(st), 4, 16, 16, by(nm), None, 16, 16, 16, None, 0, None) == 1
+    # misaligned query
+    assert lib.swa_rma_decode_attn(by(st), 512, 18, 16, by(nm), 16, 16, 16, 16, None, 0, None) == 2
+    # workspace missing or too small at a split batch
+    assert lib.swa_rma_decode_attn(by(st), 4, 16, 16, by(nm), 16, 16, 16, 16, None, 0, None) == 3
+    assert lib.swa_rma_decode_attn(by(st), 4, 16, 16, by(nm), 16, 16, 16, 16, 16, 100, None) == 3
+    assert lib.swa_rma_append(by(st), 0, 16, 16, 16, 16, None, by(nm), None) == 1
+    assert lib.swa_rma_append(by(st), 2, 16, 16, 20, 16, None, by(nm), None) == 2
+    bad = _state()
+    bad.pend_k = None
+    assert lib.swa_rma_append(by(bad), 2, 16, 16, 16, 16, None, by(nm), None) == 1
+    assert lib.rma_commit_topk(by(bad), 2, None, None) == 1
+    assert lib.rma_commit_topk(by(st), -1, None, None) == 1
+    assert lib.rma_score(16, -1, 2560, 16, 16, 16, 4, None) == 1
+    assert lib.rma_score(16, 0, 2560, 16, 16, 16, 4, None) == 0  # empty is a no-op
+    assert lib.rma_score(16, 5, 2559, 16, 16, 16, 4, None) == 1
+    assert lib.rma_score(16, 5, 2564, 16, 16, 16, 4, None) == 2
+    assert lib.rma_score(24, 5, 2560, 16, 16, 16, 4, None) == 2

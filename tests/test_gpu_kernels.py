@@ -1,0 +1,248 @@
+"""GPU parity of each entry point against the oracle on small, ragged cases.
+
+Sizes span several 16-key tiles with ragged tails, every split path the batch
+selects, empty branches, partially filled window/bank/pending blocks, and the
+commit's degenerate cases (nothing pending, empty bank, all ties, signed zeros,
+NaN scores).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import swa_memory_anchor_amd as R
+import synth
+from synth import workloads as W
+
+from gpu_util import (DEV, assert_attn_close, assert_scores_close, bf16_dev, bf16_ulp_diff,
+                      bits_host, decode_gpu, download, f32_dev, norm_dev, upload)
+
+pytestmark = pytest.mark.gpu
+
+
+def _rand_state(tag, counts):
+    """Oracle state with N(0,1) BF16 contents and the given (n_bank, n_pend, pos) per row."""
+    B = len(counts)
+    st = O.new_layer_state(B)
+    for i, nm in enumerate(("win_k", "win_v", "bank_k", "bank_v", "pend_k", "pend_v")):
+        a = getattr(st, nm)
+        a[...] = synth.normal_bf16_np(synth.stream_key(tag, nm), a.size).reshape(a.shape)
+    for b, (nb, npd, pos) in enumerate(counts):
+        st.n_bank[b], st.n_pend[b], st.pos[b] = nb, npd, pos
+    return st
+
+
+def _gains(tag):
+    return {nm: synth.normal_f32_np(synth.stream_key(tag, nm), (256,), 1.0, 0.1)
+            for nm in ("gq_win", "gk_win", "gq_rma", "gk_rma")}
+
+
+COUNTS = [(1024, 256, 70000), (37, 5, 600), (0, 1, 0), (1000, 255, 1023), (16, 16, 15),
+          (1024, 0, 262143), (0, 0, -1), (513, 129, 1024)]
+
+
+@pytest.mark.parametrize("same_q", [True, False])
+def test_decode_ragged_multi_split(same_q):
+    print(f"case: decode ragged batch={len(COUNTS)} same_q={same_q}", flush=True)
+    st = _rand_state("dec_ragged", COUNTS)
+    B = len(COUNTS)
+    g = _gains("dec_ragged")
+    qw = synth.normal_bf16_np(synth.stream_key("dec_ragged", "qw"), B * 4096).reshape(B, 16, 256)
+    qr = qw if same_q else synth.normal_bf16_np(synth.stream_key("dec_ragged", "qr"),
+                                                B * 4096).reshape(B, 16, 256)
+    dst = upload(st)
+    nm = norm_dev(g)
+    qwd = bf16_dev(qw)
+    qrd = qwd if same_q else bf16_dev(qr)
+    assert R.rma_decode_splits(B) > 1
+    o_w, l_w, o_r, l_r = decode_gpu(dst, qwd, qrd, nm)
+    torch.cuda.synchronize()
+    ref = O.decode(st, qw, qr, g["gq_win"], g["gq_rma"], 1e-6, 1e7)
+    assert_attn_close(bits_host(o_w), l_w.cpu().numpy(), ref[0], ref[1], what="window")
+    assert_attn_close(bits_host(o_r), l_r.cpu().numpy(), ref[2], ref[3], what="anchor")
+    # empty branches: o = 0, lse = -inf
+    b_empty = COUNTS.index((0, 0, -1))
+    assert np.all(bits_host(o_r)[b_empty] == 0) and np.all(np.isneginf(l_r.cpu().numpy()[b_empty]))
+    assert np.all(np.isneginf(l_w.cpu().numpy()[b_empty]))
+    # the state is read-only for decode
+    after = download(dst)
+    for nmk in ("win_k", "bank_v", "pend_k"):
+        assert np.array_equal(getattr(after, nmk), getattr(st, nmk))
+
+
+def test_decode_is_deterministic():
+    st = upload(_rand_state("det", COUNTS[:4]))
+    q = bf16_dev(synth.normal_bf16_np(synth.stream_key("det", "q"), 4 * 4096).reshape(4, 16, 256))
+    nm = norm_dev(_gains("det"))
+    a = decode_gpu(st, q, q, nm)
+    b = decode_gpu(st, q, q, nm)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
+                           y.view(torch.int16) if y.dtype == torch.bfloat16 else y)
+
+
+def test_append_matches_oracle_within_one_ulp():
+    print("case: append", flush=True)
+    counts = [(0, 0, -1), (10, 255, 5000), (1024, 100, 1023), (3, 7, 262142)]
+    st = _rand_state("app", counts)
+    B = len(counts)
+    g = _gains("app")
+    recs = [synth.normal_bf16_np(synth.stream_key("app", nm), B * 1024).reshape(B, 4, 256) * 1
+            for nm in ("kw", "vw", "kr", "vr")]
+    score = synth.normal_f32_np(synth.stream_key("app", "score"), (B, 4))
+    dst = upload(st)
+    nm = norm_dev(g)
+    dev = [bf16_dev(r) for r in recs]
+    R.swa_rma_append(dst, B, *dev, f32_dev(score), nm)
+    torch.cuda.synchronize()
+    O.append(st, *recs, g["gk_win"], g["gk_rma"], 1e-6, 1e7, score=score)
+    got = download(dst)
+    for nmk in ("win_v", "pend_v", "pend_score", "pend_src", "n_pend", "pos", "bank_k"):
+        assert np.array_equal(getattr(got, nmk), getattr(st, nmk)), nmk
+    for nmk in ("win_k", "pend_k"):
+        d = bf16_ulp_diff(getattr(got, nmk), getattr(st, nmk))
+        print(f"{nmk}: {int((d == 1).sum())} elements differ by 1 ulp of {d.size}")
+        assert d.max() <= 1, nmk
+    # a full pending block is left untouched
+    st2 = _rand_state("app_full", [(1024, 256, 9000)])
+    d2 = upload(st2)
+    R.swa_rma_append(d2, 1, *[bf16_dev(r[:1]) for r in recs], None, nm)
+    torch.cuda.synchronize()
+    g2 = download(d2)
+    assert g2.n_pend[0] == 256 and g2.pos[0] == 9000
+    assert np.array_equal(g2.win_k, st2.win_k)
+
+
+def _score_case(rng, n):
+    h = synth.normal_bf16_np(synth.stream_key("score", n), n * 2560).reshape(n, 2560)
+    w1 = (0.02 * rng.standard_normal((2560, 256))).astype(np.float32)
+    w2 = (0.02 * rng.standard_normal((256, 4))).astype(np.float32)
+    return h, w1, w2
+
+
+@pytest.mark.parametrize("n", [1, 127, 300, 1024])
+def test_score_matches_oracle(n):
+    print(f"case: score n={n}", flush=True)
+    rng = np.random.default_rng(n)
+    h, w1, w2 = _score_case(rng, n)
+    out = torch.full((n, 4), float("nan"), device=DEV)
+    R.rma_score(bf16_dev(h), n, 2560, f32_dev(w1), f32_dev(w2), out, 4)
+    torch.cuda.synchronize()
+    assert_scores_close(out.cpu().numpy(), O.score(h, w1, w2), what=f"n={n}")
+
+
+def test_score_strided_output_and_input():
+    rng = np.random.default_rng(7)
+    h, w1, w2 = _score_case(rng, 200)
+    hp = np.zeros((200, 2568), np.uint16)
+    hp[:, :2560] = h
+    out = torch.full((200, 8), -7.0, device=DEV)
+    R.rma_score(bf16_dev(hp), 200, 2568, f32_dev(w1), f32_dev(w2), out, 8)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.all(o[:, 4:] == -7.0)
+    assert_scores_close(o[:, :4], O.score(h, w1, w2), what="strided")
+
+
+def test_score_exact_integer_case_bit_exact():
+    # small integers and dyadic weights: every partial sum is exact in FP32 in any
+    # order (checked below), so the GPU must reproduce the exact value bit for bit
+    rng = np.random.default_rng(8)
+    n = 260
+    h = rng.integers(-2, 3, size=(n, 2560)).astype(np.float64)
+    w1 = rng.integers(-16, 17, size=(2560, 256)) / 64.0
+    w2 = rng.integers(-4, 5, size=(256, 4)) / 64.0
+    z = h @ w1
+    assert (np.abs(h) @ np.abs(w1)).max() * 64 < 2**24
+    assert (np.abs(z) @ np.abs(w2)).max() * 4096 < 2**24
+    hb = O.f64_to_bf16(h)
+    exact = (z @ w2).astype(np.float32)
+    out = torch.empty(n, 4, device=DEV)
+    R.rma_score(bf16_dev(hb), n, 2560, f32_dev(w1), f32_dev(w2), out, 4)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), exact)
+    assert np.array_equal(O.score(hb, w1.astype(np.float32), w2.astype(np.float32)), exact)
+
+
+def test_score_duplicate_rows_bit_identical():
+    rng = np.random.default_rng(9)
+    h, w1, w2 = _score_case(rng, 700)
+    pairs = [(0, 699), (5, 133), (64, 65), (127, 128), (300, 31), (511, 512)]
+    for d, s in pairs:
+        h[d] = h[s]
+    out = torch.empty(700, 4, device=DEV)
+    R.rma_score(bf16_dev(h), 700, 2560, f32_dev(w1), f32_dev(w2), out, 4)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    for d, s in pairs:
+        assert np.array_equal(o[d], o[s]), (d, s)
+
+
+def _commit_state(tag, counts, special=True):
+    B = len(counts)
+    st = O.new_layer_state(B)
+    rng = synth.rng_np(synth.stream_key(tag, "commit"))
+    for nm in ("bank_k", "bank_v", "pend_k", "pend_v"):
+        a = getattr(st, nm)
+        a[...] = synth.normal_bf16_np(synth.stream_key(tag, nm), a.size).reshape(a.shape)
+    vals = np.array([-1.5, -0.0, 0.0, 0.25, 0.25, 1.0], np.float32)
+    for b, (nb, npd) in enumerate(counts):
+        st.n_bank[b], st.n_pend[b], st.pos[b] = nb, npd, 50000 + b
+        for g in range(4):
+            st.bank_src[b, g] = rng.permutation(40000)[:1024]
+            st.bank_score[b, g] = rng.standard_normal(1024).astype(np.float32) * 0.3
+        st.pend_src[b] = np.arange(40000, 40256) + rng.integers(0, 5)
+        st.pend_score[b] = rng.standard_normal((256, 4)).astype(np.float32) * 0.3
+        if special:
+            # ties, signed zeros and NaN scattered over both parts
+            m = rng.random((4, 1024)) < 0.2
+            st.bank_score[b][m] = rng.choice(vals, size=int(m.sum()))
+            m2 = rng.random((256, 4)) < 0.2
+            st.pend_score[b][m2] = rng.choice(vals, size=int(m2.sum()))
+            st.bank_score[b, 1, 7] = np.nan
+            st.pend_score[b, 3, 2] = np.nan
+    return st
+
+
+COMMIT_COUNTS = [(1024, 256), (1000, 200), (500, 256), (0, 256), (1024, 0), (3, 1), (768, 256),
+                 (0, 0), (1023, 1)]
+
+
+@pytest.mark.parametrize("special", [True, False])
+def test_commit_bit_exact(special):
+    print(f"case: commit special={special}", flush=True)
+    st = _commit_state(f"commit{special}", COMMIT_COUNTS, special)
+    dst = upload(st)
+    B = len(COMMIT_COUNTS)
+    keep = torch.full((B, 4, 1024), -9, dtype=torch.int32, device=DEV)
+    R.rma_commit_topk(dst, B, keep)
+    torch.cuda.synchronize()
+    ref_keep = O.commit(st)
+    got = download(dst)
+    assert np.array_equal(keep.cpu().numpy(), ref_keep)
+    for nmk in ("bank_k", "bank_v", "bank_src", "n_bank", "n_pend"):
+        assert np.array_equal(getattr(got, nmk), getattr(st, nmk)), nmk
+    assert np.array_equal(got.bank_score.view(np.uint32), st.bank_score.view(np.uint32))
+    # pending arrays are not modified
+    for nmk in ("pend_k", "pend_v", "pend_score", "pend_src"):
+        assert np.array_equal(getattr(got, nmk).view(np.uint8), getattr(st, nmk).view(np.uint8))
+
+
+def test_commit_all_equal_scores_keep_lowest_sources():
+    st = _commit_state("commit_eq", [(1024, 256), (700, 256)], special=False)
+    st.bank_score[...] = 0.5
+    st.pend_score[...] = 0.5
+    dst = upload(st)
+    R.rma_commit_topk(dst, 2, None)
+    torch.cuda.synchronize()
+    ref = st.copy()
+    O.commit(ref)
+    got = download(dst)
+    assert np.array_equal(got.bank_src, ref.bank_src)
+    for b, nb in enumerate((1024, 700)):
+        n = min(1024, nb + 256)
+        assert got.n_bank[b] == n
+        for g in range(4):
+            cand = np.concatenate([st.bank_src[b, g, :nb], st.pend_src[b]])
+            assert np.array_equal(np.sort(got.bank_src[b, g, :n]), np.sort(cand)[:n])
