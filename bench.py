@@ -110,8 +110,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="headline_b512",
                     choices=["headline_b512", "steady_b64", "batch1"])
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
-    ap.add_argument("--cpu-max-units", type=int, default=2000)
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
+    ap.add_argument("--cpu-max-units", type=int, default=6000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")

@@ -18,7 +18,8 @@ struct AppendParams {
   const uint16_t *k_win, *v_win, *k_rma, *v_rma;
   const float *score;
   const float *gk_win, *gk_rma;
-  float eps, rope_base;
+  float eps;
+  RopeTable rope;
 };
 
 __global__ __launch_bounds__(256) void append_kernel(AppendParams a) {
@@ -37,8 +38,10 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams a) {
   const uint2 kr = *reinterpret_cast<const uint2 *>(a.k_rma + in);
   float xw[4] = {bf16_lo(kw.x), bf16_hi(kw.x), bf16_lo(kw.y), bf16_hi(kw.y)};
   float xr[4] = {bf16_lo(kr.x), bf16_hi(kr.x), bf16_lo(kr.y), bf16_hi(kr.y)};
-  norm_rope_head(xw, a.gk_win, a.eps, p, a.rope_base, lane);
-  norm_rope_head(xr, a.gk_rma, a.eps, p, a.rope_base, lane);
+  float c, sn;
+  rope_cos_sin(a.rope, p, lane, c, sn);
+  norm_rope_head(xw, a.gk_win, a.eps, c, sn, lane);
+  norm_rope_head(xr, a.gk_rma, a.eps, c, sn, lane);
   *reinterpret_cast<uint2 *>(a.win_k + w_row) =
       make_uint2(pack_bf16x2(xw[0], xw[1]), pack_bf16x2(xw[2], xw[3]));
   *reinterpret_cast<uint2 *>(a.pend_k + p_row) =
@@ -94,7 +97,7 @@ extern "C" rma_status swa_rma_append(const rma_layer_state *st, int32_t batch,
   p.gk_win = norm->gk_win;
   p.gk_rma = norm->gk_rma;
   p.eps = norm->eps;
-  p.rope_base = norm->rope_base;
+  p.rope = make_rope_table(norm->rope_base);
   hipLaunchKernelGGL(append_kernel, dim3(batch), dim3(256), 0, static_cast<hipStream_t>(stream), p);
   if (hipPeekAtLastError() != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
   return RMA_OK;

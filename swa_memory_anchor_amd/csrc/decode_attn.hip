@@ -38,15 +38,26 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kVStride = kDim + 8;  // LDS row stride of a V tile, in elements (528 B)
 constexpr int kPartStride = 4 + kDim;
 constexpr int kMaxSplits = 20;
+#ifndef RMA_DECODE_MIN_WGS
+#define RMA_DECODE_MIN_WGS 512
+#endif
+// Split each branch only until a launch has two workgroups per CU (256 CUs):
+// more, smaller workgroups measured slower at batch 64 and 512 (per-workgroup
+// prologue, partial writes and the merge launch cost more than they balance).
+constexpr int kMinWorkgroups = RMA_DECODE_MIN_WGS;
 constexpr float kQScale = 1.4426950408889634f / 16.0f;  // log2(e) / sqrt(256)
 constexpr float kLn2 = 0.69314718055994531f;
+// Cache policy of the K/V loads: non-temporal (every byte is read exactly once per
+// step, so it should not displace anything in the caches).
+constexpr int kStream = 2;
 
 struct DecodeParams {
   const uint16_t *win_k, *win_v, *bank_k, *bank_v, *pend_k, *pend_v;
   const int32_t *n_bank, *n_pend, *pos;
   const uint16_t *q_win, *q_rma;
   const float *gq_win, *gq_rma;
-  float eps, rope_base;
+  float eps;
+  RopeTable rope;
   uint16_t *o_win, *o_rma;
   float *lse_win, *lse_rma;
   float *part;
@@ -81,11 +92,11 @@ __device__ __forceinline__ void load_tile(const Segment &sg, int key0, int lane,
   const int soff = key0 * (kDim * 2);
 #pragma unroll
   for (int s = 0; s < 8; ++s)
-    K[s] = bitcast<uint4>(__builtin_amdgcn_raw_buffer_load_b128(sg.k, koff + 64 * s, soff, 0));
+    K[s] = bitcast<uint4>(__builtin_amdgcn_raw_buffer_load_b128(sg.k, koff + 64 * s, soff, kStream));
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     V[i] = bitcast<uint4>(
-        __builtin_amdgcn_raw_buffer_load_b128(sg.v, voff + 2 * kDim * 2 * i, soff, 0));
+        __builtin_amdgcn_raw_buffer_load_b128(sg.v, voff + 2 * kDim * 2 * i, soff, kStream));
 }
 
 struct SoftmaxState {
@@ -195,22 +206,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(DecodeParams a
   const int tb = split * per;
   const int te = min(T, tb + per);
 
-  // Query prep: wave w normalises, rotates and scales head 4g + w.
-  {
-    const uint16_t *q = (anchor ? a.q_rma : a.q_win) +
-                        (static_cast<size_t>(b) * kHeads + g * kHeadsPerGroup + wave) * kDim;
-    const uint2 raw = *reinterpret_cast<const uint2 *>(q + 4 * lane);
-    float x[4] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y)};
-    norm_rope_head(x, anchor ? a.gq_rma : a.gq_win, a.eps, p, a.rope_base, lane);
-    uint2 o;
-    o.x = pack_bf16x2(x[0] * kQScale, x[1] * kQScale);
-    o.y = pack_bf16x2(x[2] * kQScale, x[3] * kQScale);
-    *reinterpret_cast<uint2 *>(&q_lds[wave][4 * lane]) = o;
-  }
-  for (int i = threadIdx.x; i < 12 * kDim / 4; i += kThreads)
-    reinterpret_cast<uint2 *>(&q_lds[kHeadsPerGroup][0])[i] = make_uint2(0, 0);
-  __syncthreads();
-
   SoftmaxState st;
   st.m = -INFINITY;
   st.l = 0.f;
@@ -220,7 +215,28 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(DecodeParams a
   uint16_t *vl = v_lds[wave];
   uint4 K[8], V[8];
   int t = tb + wave;
+  // The first tile's loads do not depend on the query: issue them before the
+  // query prologue so its latency overlaps the norm and rotary work.
   if (t < te) load_tile(t < T0 ? seg0 : seg1, (t < T0 ? t : t - T0) * kTile, lane, K, V);
+
+  // Query prep: wave w normalises, rotates and scales head 4g + w.
+  {
+    const uint16_t *q = (anchor ? a.q_rma : a.q_win) +
+                        (static_cast<size_t>(b) * kHeads + g * kHeadsPerGroup + wave) * kDim;
+    const uint2 raw = *reinterpret_cast<const uint2 *>(q + 4 * lane);
+    float x[4] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y)};
+    float c, sn;
+    rope_cos_sin(a.rope, p, lane, c, sn);
+    norm_rope_head(x, anchor ? a.gq_rma : a.gq_win, a.eps, c, sn, lane);
+    uint2 o;
+    o.x = pack_bf16x2(x[0] * kQScale, x[1] * kQScale);
+    o.y = pack_bf16x2(x[2] * kQScale, x[3] * kQScale);
+    *reinterpret_cast<uint2 *>(&q_lds[wave][4 * lane]) = o;
+  }
+  for (int i = threadIdx.x; i < 12 * kDim / 4; i += kThreads)
+    reinterpret_cast<uint2 *>(&q_lds[kHeadsPerGroup][0])[i] = make_uint2(0, 0);
+  __syncthreads();
+
   for (; t < te; t += kWaves) {
     const int key0 = (t < T0 ? t : t - T0) * kTile;
     const int nvalid = (t < T0 ? seg0.n : seg1.n) - key0;
@@ -350,9 +366,9 @@ static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 extern "C" int32_t rma_decode_splits(int32_t batch) {
   if (batch <= 0) return 1;
-  // Aim for at least 2048 workgroups (8 per CU) so the HBM pipes stay full.
+  // Split each branch's keys until the launch has kMinWorkgroups workgroups.
   const int units = batch * kGroups * 2;
-  int s = (2048 + units - 1) / units;
+  int s = (kMinWorkgroups + units - 1) / units;
   return s < 1 ? 1 : (s > kMaxSplits ? kMaxSplits : s);
 }
 
@@ -397,7 +413,7 @@ extern "C" rma_status swa_rma_decode_attn(const rma_layer_state *st, int32_t bat
   p.gq_win = norm->gq_win;
   p.gq_rma = norm->gq_rma;
   p.eps = norm->eps;
-  p.rope_base = norm->rope_base;
+  p.rope = make_rope_table(norm->rope_base);
   p.o_win = o_win;
   p.o_rma = o_rma;
   p.lse_win = lse_win;

@@ -48,23 +48,47 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Rotary angle of pair i at position p, computed in double so that positions
-// up to 2^18 keep full FP32 accuracy in cos/sin.
-__device__ __forceinline__ void rope_cos_sin(int i, int p, float base, float &c, float &s) {
-  double theta = pow(static_cast<double>(base), -2.0 * static_cast<double>(i) / kRope);
-  double phi = static_cast<double>(p) * theta;
-  double sd, cd;
-  sincos(phi, &sd, &cd);
-  c = static_cast<float>(cd);
-  s = static_cast<float>(sd);
+// Rotary frequencies theta_i = base^(-2i/64), i = 0..31, computed on the host in
+// double precision and passed by value.
+struct RopeTable {
+  double theta[kRope / 2];
+};
+
+inline RopeTable make_rope_table(float base) {
+  RopeTable t;
+  for (int i = 0; i < kRope / 2; ++i)
+    t.theta[i] = __builtin_pow(static_cast<double>(base), -2.0 * i / kRope);
+  return t;
+}
+
+// (cos, sin) of pair `lane` (lanes 0..31) at position p.  The angle p * theta is
+// formed and reduced modulo 2*pi in double (Cody-Waite, two-term 2*pi), so
+// positions up to 2^18 keep full accuracy.  The reduced angle r (|r| <= pi) is
+// split into rf = fp32(r) and the remainder d = r - rf; sin and cos of rf are
+// taken in FP32 and corrected to first order in d (|d| <= 2^-22, so the
+// second-order term is below FP32 resolution).
+__device__ __forceinline__ void rope_cos_sin(const RopeTable &rt, int p, int lane, float &c,
+                                             float &s) {
+  constexpr double kTwoPiHi = 6.283185307179586232;       // 2*pi rounded to double
+  constexpr double kTwoPiLo = 2.4492935982947064e-16;      // 2*pi - kTwoPiHi
+  constexpr double kInvTwoPi = 0.15915494309189534561;
+  const double phi = static_cast<double>(p) * rt.theta[lane & (kRope / 2 - 1)];
+  const double k = rint(phi * kInvTwoPi);
+  double r = fma(-k, kTwoPiHi, phi);
+  r = fma(-k, kTwoPiLo, r);
+  const float rf = static_cast<float>(r);
+  const float d = static_cast<float>(r - static_cast<double>(rf));
+  const float s0 = sinf(rf), c0 = cosf(rf);
+  s = fmaf(c0, d, s0);
+  c = fmaf(-s0, d, c0);
 }
 
 // RMS-normalise one 256-wide head held by a wave (lane l holds dims 4l..4l+3),
-// multiply by the gain, then rotate dims 0..63 at position p (pairs i, i+32).
-// x is updated in place.  Lanes 0..7 hold the first half of the rotated dims
-// and lanes 8..15 their partners.
-__device__ __forceinline__ void norm_rope_head(float x[4], const float *gamma, float eps, int p,
-                                               float base, int lane) {
+// multiply by the gain, then rotate dims 0..63 at the position whose per-pair
+// (cos, sin) lane i < 32 holds in (c, s) (pairs i, i+32).  Lanes 0..7 hold the
+// first half of the rotated dims and lanes 8..15 their partners.
+__device__ __forceinline__ void norm_rope_head(float x[4], const float *gamma, float eps, float c,
+                                               float s, int lane) {
   float ss = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
   ss = wave_sum(ss);
   const float inv = 1.0f / sqrtf(ss * (1.0f / kDim) + eps);
@@ -73,19 +97,20 @@ __device__ __forceinline__ void norm_rope_head(float x[4], const float *gamma, f
   x[1] = x[1] * inv * gm.y;
   x[2] = x[2] * inv * gm.z;
   x[3] = x[3] * inv * gm.w;
-  float partner[4];
+  float partner[4], ce[4], se[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) partner[e] = __shfl_xor(x[e], 8, 64);
+  for (int e = 0; e < 4; ++e) {
+    partner[e] = __shfl_xor(x[e], 8, 64);
+    ce[e] = __shfl(c, 4 * (lane & 7) + e, 64);
+    se[e] = __shfl(s, 4 * (lane & 7) + e, 64);
+  }
   if (lane < 16) {
     const bool first = lane < 8;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int i = 4 * (lane & 7) + e;
-      float c, s;
-      rope_cos_sin(i, p, base, c, s);
       // first half:  y_i      = x_i c - x_{i+32} s
       // second half: y_{i+32} = x_{i+32} c + x_i s
-      x[e] = first ? (x[e] * c - partner[e] * s) : (x[e] * c + partner[e] * s);
+      x[e] = first ? (x[e] * ce[e] - partner[e] * se[e]) : (x[e] * ce[e] + partner[e] * se[e]);
     }
   }
 }

@@ -100,6 +100,29 @@ def assert_scores_close(s_gpu, s_ref, tol=SCORE_TOL, what=""):
     assert np.all(err <= bound), f"{what}: {int((err > bound).sum())} scores out of tolerance"
 
 
+def assert_keys_close(got_bits, ref_bits, what=""):
+    """Stored keys (normalised, rotated, rounded to BF16) against the oracle's.
+
+    The GPU computes them in FP32 and the oracle in float64; both round once to
+    BF16.  An FP32 result differs from the exact one by a few units of 2^-24 of
+    the row's scale, which can move it across one BF16 rounding boundary: the
+    bound is one BF16 ulp of the reference element plus 2^-20 of the row's
+    largest magnitude (the FP32 error with margin, for components that nearly
+    cancel in the rotation).
+    """
+    g = O.bf16_to_f64(got_bits)
+    r = O.bf16_to_f64(ref_bits)
+    _, e = np.frexp(r)
+    ulp = np.where(r != 0, np.ldexp(1.0, e - 8), 0.0)
+    row = np.abs(r).max(axis=-1, keepdims=True)
+    err = np.abs(g - r)
+    bound = ulp + 2.0**-20 * row
+    ndiff = int((got_bits != ref_bits).sum())
+    print(f"{what}: {ndiff} of {g.size} elements differ; max err/bound "
+          f"{float((err / np.maximum(bound, 1e-300)).max()):.3f}")
+    assert np.all(err <= bound), f"{what}: {int((err > bound).sum())} elements out of bound"
+
+
 def bf16_ulp_diff(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
     """|a - b| in BF16 units in the last place (same-sign finite values)."""
     def ordinal(x):
