@@ -103,13 +103,229 @@ def cpu_baseline(wl, budget_s: float, max_units: int):
     }
 
 
+SCORER_FLOP_PER_ROW = 2 * 2560 * 256 + 2 * 256 * 4
+FP32_MATRIX_PEAK_TFLOPS = 157.3
+
+
+def _timed(fn, reps, stream):
+    """Average ms of fn() over reps calls, with a HIP event pair around each call."""
+    import torch
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    return sum(ms) / len(ms), ms[len(ms) // 2]
+
+
+def bench_commit_burst(args):
+    """Scorer and commit of one 256-token burst per sequence at batch 512, all 8 layers."""
+    import numpy as np
+    import torch
+
+    import swa_memory_anchor_amd as R
+    from synth import workloads as W
+
+    wl = W.COMMIT_BURST_B512
+    B, L, dev = wl.batch, wl.layers, "cuda"
+    stream = torch.cuda.current_stream()
+    rows = B * 256
+    H, w1s, w2s, outs, states, saved, keeps = [], [], [], [], [], [], []
+    for layer in range(L):
+        h = torch.empty(B, 256, 2560, dtype=torch.bfloat16, device=dev)
+        W.burst_hidden_torch_(wl, layer, h)
+        w1, w2 = W.scorer_weights(wl, layer)
+        H.append(h)
+        w1s.append(torch.from_numpy(w1).to(dev))
+        w2s.append(torch.from_numpy(w2).to(dev))
+        outs.append(torch.empty(rows, 4, device=dev))
+        st = R.alloc_layer_state(B, dev, zero_kv=False)
+        for nm in ("bank_k", "bank_v", "pend_k", "pend_v"):
+            W.kv_torch_(wl, layer, nm, getattr(st, nm))
+        sc = W.burst_scores(wl, layer)
+        for k in ("bank_score", "pend_score", "bank_src", "pend_src", "n_bank", "n_pend", "pos"):
+            getattr(st, k).copy_(torch.from_numpy(np.ascontiguousarray(sc[k])).to(dev))
+        states.append(st)
+        saved.append({k: getattr(st, k).clone() for k in ("bank_score", "bank_src", "n_bank",
+                                                          "n_pend")})
+        keeps.append(torch.empty(B, 4, 1024, dtype=torch.int32, device=dev))
+
+    def score_all():
+        for l in range(L):
+            R.rma_score(H[l], rows, 2560, w1s[l], w2s[l], outs[l], 4, stream)
+
+    for _ in range(args.warmup):
+        score_all()
+    s_avg, s_med = _timed(score_all, args.steps, stream)
+    flop = L * rows * SCORER_FLOP_PER_ROW
+    tflops = flop / (s_avg / 1e3) / 1e12
+
+    def restore(l):
+        for k, v in saved[l].items():
+            getattr(states[l], k).copy_(v)
+
+    c_ms = []
+    for rep in range(args.warmup + args.steps):
+        for l in range(L):
+            restore(l)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            R.rma_commit_topk(states[l], B, keeps[l], stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            if rep >= args.warmup:
+                c_ms.append(a.elapsed_time(b))
+    admitted = int(sum(int((k >= 1024).sum()) for k in keeps))
+    c_avg = sum(c_ms) / len(c_ms)
+    key_bytes = B * 4 * 1280 * 8  # score + source of every candidate
+    copy_bytes = admitted / L * 2 * 2 * 512  # K and V rows, read and written
+    out_bytes = B * 4 * 1024 * 4  # keep_idx
+    return {
+        "metric": "commit burst at batch 512: scorer TFLOP/s (FP32 MFMA) and commit time per layer",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(s_avg + c_avg * L, 4),
+        "higher_is_better": True,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "layers": L, "rows_per_layer": rows},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": FP32_MATRIX_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / FP32_MATRIX_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "score_kernel", "avg_launch_ms": round(s_avg / L, 4)},
+        "commit": {"avg_launch_us": round(c_avg * 1e3, 1),
+                   "admitted_rows_per_layer": admitted // L,
+                   "algorithmic_bytes_per_launch": int(key_bytes + copy_bytes + out_bytes),
+                   "gbps": round((key_bytes + copy_bytes + out_bytes) / (c_avg / 1e3) / 1e9, 1)},
+    }
+
+
+def bench_long_stream(args):
+    """Batch-1 stream: per token, append + decode in all 8 layers; every 256 tokens the
+    scorer and the commit in all 8 layers.  Times the second half of the stream."""
+    import numpy as np
+    import torch
+
+    import swa_memory_anchor_amd as R
+    from synth import workloads as W
+
+    wl = W.LONG_STREAM_B1
+    L, dev = wl.layers, "cuda"
+    n = args.stream_tokens
+    assert n % 512 == 0
+    stream = torch.cuda.current_stream()
+    states = [R.alloc_layer_state(1, dev) for _ in range(L)]
+    norms = []
+    for l in range(L):
+        g = W.gains(wl, l)
+        norms.append(R.Norm(*[torch.from_numpy(g[k]).to(dev) for k in
+                              ("gq_win", "gk_win", "gq_rma", "gk_rma")], wl.eps, wl.rope_base))
+    rec = {nm: torch.empty(L, n, 4, 256, dtype=torch.bfloat16, device=dev)
+           for nm in W.RECORD_NAMES}
+    q = torch.empty(L, n, 16, 256, dtype=torch.bfloat16, device=dev)
+    hid = torch.empty(L, n, 2560, dtype=torch.bfloat16, device=dev)
+    w = []
+    for l in range(L):
+        for nm in W.RECORD_NAMES:
+            W.record_torch_(wl, l, nm, 0, rec[nm][l])
+        W.stream_q_torch_(wl, l, 0, q[l])
+        W.stream_hidden_torch_(wl, l, 0, hid[l])
+        w1, w2 = W.scorer_weights(wl, l)
+        w.append((torch.from_numpy(w1).to(dev), torch.from_numpy(w2).to(dev)))
+    outs = [(torch.empty(1, 16, 256, dtype=torch.bfloat16, device=dev),
+             torch.empty(1, 16, device=dev), torch.empty(1, 16, 256, dtype=torch.bfloat16,
+                                                         device=dev),
+             torch.empty(1, 16, device=dev)) for _ in range(L)]
+    ws = R.decode_workspace(1, dev)
+    lib = R.lib()
+    import ctypes
+
+    st_c = [ctypes.byref(R._state_c(s)) for s in states]
+    nm_c = [ctypes.byref(R._norm_c(x)) for x in norms]
+    sp = stream.cuda_stream
+    rp = {nm: [rec[nm][l].data_ptr() for l in range(L)] for nm in W.RECORD_NAMES}
+    qp = [q[l].data_ptr() for l in range(L)]
+    op = [[o.data_ptr() for o in os_] for os_ in outs]
+    wsp, wsn = ws.data_ptr(), ws.numel()
+
+    def token(t):
+        for l in range(L):
+            r = [rp[nm][l] + t * 2048 for nm in W.RECORD_NAMES]
+            lib.swa_rma_append(st_c[l], 1, r[0], r[1], r[2], r[3], None, nm_c[l], sp)
+            qq = qp[l] + t * 8192
+            o = op[l]
+            lib.swa_rma_decode_attn(st_c[l], 1, qq, qq, nm_c[l], o[0], o[1], o[2], o[3], wsp,
+                                    wsn, sp)
+        if (t + 1) % 256 == 0:
+            for l in range(L):
+                R.rma_score(hid[l, t - 255:t + 1], 256, 2560, w[l][0], w[l][1],
+                            states[l].pend_score, 4, stream)
+                R.rma_commit_topk(states[l], 1, None, stream)
+
+    half = n // 2
+    tail = 256  # tokens timed one by one at the end (latency distribution)
+    for t in range(half):
+        token(t)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for t in range(half, n - tail):
+        token(t)
+    b.record(stream)
+    torch.cuda.synchronize()
+    total_ms = a.elapsed_time(b)
+    per_tok_us = total_ms * 1e3 / (n - tail - half)
+    lat = []
+    for t in range(n - tail, n):
+        a.record(stream)
+        token(t)
+        b.record(stream)
+        torch.cuda.synchronize()
+        lat.append(a.elapsed_time(b) * 1e3)
+    lat.sort()
+    state_bytes = sum(x.numel() * x.element_size() for x in states[0].__dict__.values())
+    return {
+        "metric": "batch-1 stream: microseconds per token (8 layers append + decode, "
+                  "scorer + commit every 256 tokens)",
+        "value": round(per_tok_us, 2),
+        "unit": "us/token",
+        "n_gpus": 1,
+        "steps": half,
+        "warmup": half,
+        "ms_per_step": round(per_tok_us / 1e3, 5),
+        "higher_is_better": False,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": 1, "layers": L, "positions_timed":
+                   [half, n - tail - 1], "state_bytes_per_layer": state_bytes,
+                   "tokens_per_s": round(1e6 / per_tok_us, 1)},
+        "latency_us": {"tokens": tail, "median": round(lat[tail // 2], 1),
+                       "p99": round(lat[int(0.99 * tail)], 1), "max": round(lat[-1], 1),
+                       "note": "each token synchronised on its own; the last token of the "
+                               "stream includes the scorer and commit of its block"},
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="headline_b512",
-                    choices=["headline_b512", "steady_b64", "batch1"])
+                    choices=["headline_b512", "steady_b64", "batch1", "commit_burst_b512",
+                             "long_stream_b1"])
+    ap.add_argument("--stream-tokens", type=int, default=16384,
+                    help="long_stream_b1: tokens streamed (the second half is timed)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
     ap.add_argument("--cpu-max-units", type=int, default=6000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -137,6 +353,12 @@ def main() -> int:
     import swa_memory_anchor_amd as R
     from synth import workloads as W
 
+    if args.workload == "commit_burst_b512":
+        print(json.dumps(bench_commit_burst(args)))
+        return 0
+    if args.workload == "long_stream_b1":
+        print(json.dumps(bench_long_stream(args)))
+        return 0
     if args.workload == "headline_b512":
         wl = W.HEADLINE_B512
     elif args.workload == "steady_b64":

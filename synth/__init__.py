@@ -31,6 +31,7 @@ from .core import (  # noqa: F401
     stream_key,
     normal_bf16_table,
     normal_bf16_np,
+    normal_bf16_at_np,
     normal_bf16_torch_,
     normal_f32_np,
     distinct_ints_np,

@@ -109,6 +109,14 @@ def normal_bf16_np(key: StreamKey, count: int, start: int = 0) -> np.ndarray:
     return normal_bf16_table()[(h >> np.uint64(16)).astype(np.int64)]
 
 
+def normal_bf16_at_np(key: StreamKey, idx: np.ndarray) -> np.ndarray:
+    """The stream's elements at arbitrary flat indices ``idx`` (uint16 BF16 bits)."""
+    idx = np.asarray(idx, dtype=np.uint64)
+    assert idx.size == 0 or int(idx.max()) < (1 << 32)
+    h = _hash_np(key, idx)
+    return normal_bf16_table()[(h >> np.uint64(16)).astype(np.int64)]
+
+
 def normal_bf16_torch_(out, key: StreamKey, start: int = 0, chunk: int = 1 << 26) -> None:
     """Fill the contiguous 16-bit tensor ``out`` with the same stream, on out's device.
 

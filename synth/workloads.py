@@ -30,6 +30,7 @@ import numpy as np
 from .core import (
     StreamKey,
     distinct_ints_np,
+    normal_bf16_at_np,
     normal_bf16_np,
     normal_bf16_torch_,
     normal_f32_np,
@@ -260,6 +261,15 @@ def record_np(wl: Workload, layer: int, name: str, t0: int, t1: int) -> np.ndarr
     per_tok = KV_GROUPS * HEAD_DIM
     x = normal_bf16_np(key(wl, layer, "rec", name), (t1 - t0) * per_tok, start=t0 * per_tok)
     return x.reshape(t1 - t0, KV_GROUPS, HEAD_DIM)
+
+
+def record_rows_np(wl: Workload, layer: int, name: str, positions) -> np.ndarray:
+    """Raw records ``[len(positions)][4][256]`` at arbitrary positions (batch 1)."""
+    per_tok = KV_GROUPS * HEAD_DIM
+    pos = np.asarray(positions, dtype=np.uint64)
+    idx = pos[:, None] * np.uint64(per_tok) + np.arange(per_tok, dtype=np.uint64)[None, :]
+    return normal_bf16_at_np(key(wl, layer, "rec", name), idx).reshape(len(pos), KV_GROUPS,
+                                                                       HEAD_DIM)
 
 
 def record_torch_(wl: Workload, layer: int, name: str, t0: int, out) -> None:

@@ -62,3 +62,13 @@ def test_burst_scores_plant_ties():
         for g in range(4):
             assert len(set(d["bank_src"][b, g])) == 1024
             assert d["bank_src"][b, g].max() < 32512
+
+
+def test_record_rows_at_positions():
+    wl = W.LONG_STREAM_B1
+    full = W.record_np(wl, 3, "k_rma", 100, 140)
+    rows = W.record_rows_np(wl, 3, "k_rma", [139, 100, 117])
+    assert np.array_equal(rows, full[[39, 0, 17]])
+    out = torch.empty(40, 4, 256, dtype=torch.bfloat16)
+    W.record_torch_(wl, 3, "k_rma", 100, out)
+    assert np.array_equal(out.view(torch.int16).numpy().view(np.uint16), full)
