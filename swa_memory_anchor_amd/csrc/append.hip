@@ -19,7 +19,7 @@ struct AppendParams {
   const float *score;
   const float *gk_win, *gk_rma;
   float eps;
-  RopeTable rope;
+  double rope_ratio;  // base^(-1/32)
 };
 
 __global__ __launch_bounds__(256) void append_kernel(AppendParams a) {
@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams a) {
   float xw[4] = {bf16_lo(kw.x), bf16_hi(kw.x), bf16_lo(kw.y), bf16_hi(kw.y)};
   float xr[4] = {bf16_lo(kr.x), bf16_hi(kr.x), bf16_lo(kr.y), bf16_hi(kr.y)};
   float c, sn;
-  rope_cos_sin(a.rope, p, lane, c, sn);
+  rope_cos_sin(a.rope_ratio, p, lane, c, sn);
   norm_rope_head(xw, a.gk_win, a.eps, c, sn, lane);
   norm_rope_head(xr, a.gk_rma, a.eps, c, sn, lane);
   *reinterpret_cast<uint2 *>(a.win_k + w_row) =
@@ -97,7 +97,7 @@ extern "C" rma_status swa_rma_append(const rma_layer_state *st, int32_t batch,
   p.gk_win = norm->gk_win;
   p.gk_rma = norm->gk_rma;
   p.eps = norm->eps;
-  p.rope = make_rope_table(norm->rope_base);
+  p.rope_ratio = rope_ratio(norm->rope_base);
   hipLaunchKernelGGL(append_kernel, dim3(batch), dim3(256), 0, static_cast<hipStream_t>(stream), p);
   if (hipPeekAtLastError() != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
   return RMA_OK;

@@ -33,8 +33,13 @@
 namespace rma {
 
 constexpr int kTile = 16;
-constexpr int kWaves = 4;
+#ifndef RMA_DECODE_WAVES
+#define RMA_DECODE_WAVES 4
+#endif
+constexpr int kWaves = RMA_DECODE_WAVES;  // waves per workgroup, all on one (branch, seq, group)
 constexpr int kThreads = 64 * kWaves;
+constexpr int kMergeThreads = 64 * kHeadsPerGroup;
+static_assert(kWaves >= kHeadsPerGroup, "one wave per head in the query prologue and epilogue");
 constexpr int kVStride = kDim + 8;  // LDS row stride of a V tile, in elements (528 B)
 constexpr int kPartStride = 4 + kDim;
 constexpr int kMaxSplits = 20;
@@ -57,7 +62,7 @@ struct DecodeParams {
   const uint16_t *q_win, *q_rma;
   const float *gq_win, *gq_rma;
   float eps;
-  RopeTable rope;
+  double rope_ratio;  // base^(-1/32)
   uint16_t *o_win, *o_rma;
   float *lse_win, *lse_rma;
   float *part;
@@ -219,14 +224,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(DecodeParams a
   // query prologue so its latency overlaps the norm and rotary work.
   if (t < te) load_tile(t < T0 ? seg0 : seg1, (t < T0 ? t : t - T0) * kTile, lane, K, V);
 
-  // Query prep: wave w normalises, rotates and scales head 4g + w.
-  {
+  // Query prep: wave w < 4 normalises, rotates and scales head 4g + w.
+  if (wave < kHeadsPerGroup) {
     const uint16_t *q = (anchor ? a.q_rma : a.q_win) +
                         (static_cast<size_t>(b) * kHeads + g * kHeadsPerGroup + wave) * kDim;
     const uint2 raw = *reinterpret_cast<const uint2 *>(q + 4 * lane);
     float x[4] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y)};
     float c, sn;
-    rope_cos_sin(a.rope, p, lane, c, sn);
+    rope_cos_sin(a.rope_ratio, p, lane, c, sn);
     norm_rope_head(x, anchor ? a.gq_rma : a.gq_win, a.eps, c, sn, lane);
     uint2 o;
     o.x = pack_bf16x2(x[0] * kQScale, x[1] * kQScale);
@@ -269,6 +274,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(DecodeParams a
   }
   __syncthreads();
 
+  if (wave >= kHeadsPerGroup) return;
   const int h = wave;  // this wave now owns head 4g + h, dims 4*lane..4*lane+3
   float M = -INFINITY;
 #pragma unroll
@@ -315,7 +321,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(DecodeParams a
 }
 
 // Merge the splits of one (branch, sequence, group): 4 waves, one per head.
-__global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeParams a) {
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParams a) {
   const int lane = threadIdx.x & 63;
   const int h = threadIdx.x >> 6;
   const int unit = blockIdx.x;
@@ -413,7 +419,7 @@ extern "C" rma_status swa_rma_decode_attn(const rma_layer_state *st, int32_t bat
   p.gq_win = norm->gq_win;
   p.gq_rma = norm->gq_rma;
   p.eps = norm->eps;
-  p.rope = make_rope_table(norm->rope_base);
+  p.rope_ratio = rope_ratio(norm->rope_base);
   p.o_win = o_win;
   p.o_rma = o_rma;
   p.lse_win = lse_win;
@@ -426,7 +432,7 @@ extern "C" rma_status swa_rma_decode_attn(const rma_layer_state *st, int32_t bat
   hipLaunchKernelGGL(decode_attn_kernel, dim3(units * p.splits), dim3(kThreads), 0, s, p);
   if (hipPeekAtLastError() != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
   if (p.splits > 1) {
-    hipLaunchKernelGGL(decode_merge_kernel, dim3(units), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(decode_merge_kernel, dim3(units), dim3(kMergeThreads), 0, s, p);
     if (hipPeekAtLastError() != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
   }
   return RMA_OK;

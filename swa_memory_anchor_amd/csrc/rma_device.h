@@ -48,31 +48,29 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Rotary frequencies theta_i = base^(-2i/64), i = 0..31, computed on the host in
-// double precision and passed by value.
-struct RopeTable {
-  double theta[kRope / 2];
-};
+// Rotary frequencies theta_i = base^(-2i/64) = r^i with r = base^(-1/32).  r is
+// computed on the host in double precision; each lane forms r^i by binary
+// powering in double (at most 9 multiplies, relative error below 1e-15).
+inline double rope_ratio(float base) { return __builtin_pow(static_cast<double>(base), -2.0 / kRope); }
 
-inline RopeTable make_rope_table(float base) {
-  RopeTable t;
-  for (int i = 0; i < kRope / 2; ++i)
-    t.theta[i] = __builtin_pow(static_cast<double>(base), -2.0 * i / kRope);
-  return t;
-}
-
-// (cos, sin) of pair `lane` (lanes 0..31) at position p.  The angle p * theta is
-// formed and reduced modulo 2*pi in double (Cody-Waite, two-term 2*pi), so
-// positions up to 2^18 keep full accuracy.  The reduced angle r (|r| <= pi) is
-// split into rf = fp32(r) and the remainder d = r - rf; sin and cos of rf are
-// taken in FP32 and corrected to first order in d (|d| <= 2^-22, so the
-// second-order term is below FP32 resolution).
-__device__ __forceinline__ void rope_cos_sin(const RopeTable &rt, int p, int lane, float &c,
-                                             float &s) {
+// (cos, sin) of pair i = lane % 32 at position p.  The angle p * theta_i is formed
+// and reduced modulo 2*pi in double (Cody-Waite, two-term 2*pi), so positions up
+// to 2^18 keep full accuracy.  The reduced angle r (|r| <= pi) is split into
+// rf = fp32(r) and the remainder d = r - rf; sin and cos of rf are taken in FP32
+// and corrected to first order in d (|d| <= 2^-22, so the second-order term is
+// below FP32 resolution).
+__device__ __forceinline__ void rope_cos_sin(double ratio, int p, int lane, float &c, float &s) {
   constexpr double kTwoPiHi = 6.283185307179586232;       // 2*pi rounded to double
   constexpr double kTwoPiLo = 2.4492935982947064e-16;      // 2*pi - kTwoPiHi
   constexpr double kInvTwoPi = 0.15915494309189534561;
-  const double phi = static_cast<double>(p) * rt.theta[lane & (kRope / 2 - 1)];
+  int i = lane & (kRope / 2 - 1);
+  double theta = 1.0, sq = ratio;
+  while (i) {
+    if (i & 1) theta *= sq;
+    sq *= sq;
+    i >>= 1;
+  }
+  const double phi = static_cast<double>(p) * theta;
   const double k = rint(phi * kInvTwoPi);
   double r = fma(-k, kTwoPiHi, phi);
   r = fma(-k, kTwoPiLo, r);
