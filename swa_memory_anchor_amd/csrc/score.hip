@@ -10,9 +10,11 @@
 // runs on v_mfma_f32_32x32x2f32:
 //  * one workgroup (4 waves) per 128-row tile and all 256 columns; each wave owns
 //    a 64 x 128 block = 2 x 4 accumulators of 32 x 32;
-//  * K is walked in stages of 32: BF16 rows are widened (exactly) to FP32 while
-//    being staged in LDS (k-major), W1 rows are staged as is; two LDS buffers, the
-//    next stage's global loads in flight while the current stage computes;
+//  * K is walked in slices of 32: BF16 rows are widened (exactly) to FP32 while
+//    being staged in LDS row-major (m-major), W1 is staged column-major (n-major);
+//    each lane's 16 operands of a slice are then contiguous, so a slice's operands
+//    come in with 24 16-byte LDS reads and its 128 MFMAs issue back to back; two
+//    LDS buffers, the next slice's global loads in flight meanwhile;
 //  * stage 2 (x W2, 256 -> 4) is fused: the 128 x 256 block of stage-1 results is
 //    passed through LDS in two column halves and every output row is summed over
 //    its 256 columns in the same fixed order, so identical input rows give
@@ -22,11 +24,12 @@
 namespace rma {
 
 constexpr int kRowsWG = 128;
-constexpr int kKt = 32;
-constexpr int kAStr = kRowsWG + 4;  // A stage: [k][row], floats
-constexpr int kBStr = kMid + 4;     // B stage: [k][col], floats
+constexpr int kKt = 32;             // contraction depth of one staged slice
+constexpr int kStr = kKt + 4;       // LDS row stride (floats) of the m-major / n-major slices
+constexpr int kAFloats = kRowsWG * kStr;
+constexpr int kBFloats = kMid * kStr;
+constexpr int kStageFloats = kAFloats + kBFloats;
 constexpr int kZStr = 129;          // stage-1 block: [row][col], floats (one column half)
-constexpr int kStageFloats = kKt * kAStr + kKt * kBStr;
 constexpr int kScoreThreads = 256;
 
 struct ScoreParams {
@@ -37,6 +40,11 @@ struct ScoreParams {
   int64_t ld_scores;
 };
 
+// v_mfma_f32_32x32x2f32: lane l supplies A[m = l%32][k = l/32] and B[k = l/32][n = l%32].
+// Within a slice of 32 contraction indices, lane half h = l/32 takes indices
+// 16h .. 16h+15 over the slice's 16 MFMA steps, so each lane's 16 operands are
+// contiguous in the m-major (A) and n-major (B) LDS layouts and load as four
+// 16-byte reads.  The same k order is used for A and B, so the products pair up.
 __global__ __launch_bounds__(kScoreThreads, 1) void score_kernel(ScoreParams a) {
   __shared__ __align__(16) float smem[2 * kStageFloats];
   __shared__ float w2s[kMid * kGroups];
@@ -44,19 +52,20 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score_kernel(ScoreParams a) 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wr = wave >> 1, wc = wave & 1;
+  const int wr = wave >> 1, wc = wave & 1;  // wave's 64-row half and 128-column half
   const int64_t row0 = static_cast<int64_t>(blockIdx.x) * kRowsWG;
 
   for (int i = tid; i < kMid * kGroups; i += kScoreThreads) w2s[i] = a.w2[i];
 
-  // staging roles
-  const int am = tid >> 1, ah = tid & 1;        // A: row am, k half ah (16 values)
-  const int bk = tid >> 3, bc = (tid & 7) * 32;  // B: k row bk, columns bc..bc+31
+  // staging roles: A (hidden) row am, k half ah (16 values, m-major); B (W1)
+  // column bn, all 32 k of the slice (n-major)
+  const int am = tid >> 1, ah = tid & 1;
   const bool arow_ok = row0 + am < a.n_rows;
   const uint16_t *arow = a.hidden + (arow_ok ? (row0 + am) : 0) * a.ld_hidden + 16 * ah;
+  const int bn = tid;  // one W1 column per thread, all 32 k of the slice
 
   uint4 ha[2];
-  float4 wb[8];
+  float wb[kKt];
   auto load_stage = [&](int kt) {
     if (arow_ok) {
       ha[0] = *reinterpret_cast<const uint4 *>(arow + kt * kKt);
@@ -65,21 +74,23 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score_kernel(ScoreParams a) 
       ha[0] = make_uint4(0, 0, 0, 0);
       ha[1] = ha[0];
     }
-    const float *wrow = a.w1 + static_cast<size_t>(kt * kKt + bk) * kMid + bc;
+    const float *wcol = a.w1 + static_cast<size_t>(kt * kKt) * kMid + bn;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) wb[j] = *reinterpret_cast<const float4 *>(wrow + 4 * j);
+    for (int k = 0; k < kKt; ++k) wb[k] = wcol[static_cast<size_t>(k) * kMid];
   };
   auto store_stage = [&](int buf) {
     float *As = smem + buf * kStageFloats;
-    float *Bs = As + kKt * kAStr;
+    float *Bs = As + kAFloats;
     const uint32_t w[8] = {ha[0].x, ha[0].y, ha[0].z, ha[0].w, ha[1].x, ha[1].y, ha[1].z, ha[1].w};
+    float4 *ad = reinterpret_cast<float4 *>(As + am * kStr + 16 * ah);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      As[(16 * ah + 2 * j) * kAStr + am] = bf16_lo(w[j]);
-      As[(16 * ah + 2 * j + 1) * kAStr + am] = bf16_hi(w[j]);
-    }
+    for (int j = 0; j < 4; ++j)
+      ad[j] = make_float4(bf16_lo(w[2 * j]), bf16_hi(w[2 * j]), bf16_lo(w[2 * j + 1]),
+                          bf16_hi(w[2 * j + 1]));
+    float4 *bd = reinterpret_cast<float4 *>(Bs + bn * kStr);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) *reinterpret_cast<float4 *>(Bs + bk * kBStr + bc + 4 * j) = wb[j];
+    for (int j = 0; j < kKt / 4; ++j)
+      bd[j] = make_float4(wb[4 * j], wb[4 * j + 1], wb[4 * j + 2], wb[4 * j + 3]);
   };
 
   f32x16 acc[2][4];
@@ -94,23 +105,31 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score_kernel(ScoreParams a) 
   load_stage(0);
   store_stage(0);
   __syncthreads();
-  const int kl = lane >> 5, ml = lane & 31;
+  const int kh = lane >> 5, ml = lane & 31;
   for (int kt = 0; kt < nkt; ++kt) {
     if (kt + 1 < nkt) load_stage(kt + 1);
     const float *As = smem + (kt & 1) * kStageFloats;
-    const float *Bs = As + kKt * kAStr;
-#pragma unroll 4
-    for (int kk = 0; kk < kKt / 2; ++kk) {
-      const int k = 2 * kk + kl;
-      const float a0 = As[k * kAStr + wr * 64 + ml];
-      const float a1 = As[k * kAStr + wr * 64 + 32 + ml];
-      float bv[4];
+    const float *Bs = As + kAFloats;
+    float4 av[2][4], bv[4][4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) bv[c] = Bs[k * kBStr + wc * 128 + 32 * c + ml];
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        av[r][j] = *reinterpret_cast<const float4 *>(As + (wr * 64 + 32 * r + ml) * kStr + 16 * kh + 4 * j);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bv[c][j] = *reinterpret_cast<const float4 *>(Bs + (wc * 128 + 32 * c + ml) * kStr + 16 * kh + 4 * j);
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      const int j = kk >> 2, e = kk & 3;
+      const float a0 = av[0][j][e], a1 = av[1][j][e];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        acc[0][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, bv[c], acc[0][c], 0, 0, 0);
-        acc[1][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, bv[c], acc[1][c], 0, 0, 0);
+        const float b = bv[c][j][e];
+        acc[0][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b, acc[0][c], 0, 0, 0);
+        acc[1][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b, acc[1][c], 0, 0, 0);
       }
     }
     if (kt + 1 < nkt) store_stage((kt + 1) & 1);
@@ -131,7 +150,7 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score_kernel(ScoreParams a) 
         for (int c = 0; c < 4; ++c)
 #pragma unroll
           for (int q = 0; q < 16; ++q) {
-            const int row = wr * 64 + r * 32 + 8 * (q >> 2) + 4 * kl + (q & 3);
+            const int row = wr * 64 + r * 32 + 8 * (q >> 2) + 4 * kh + (q & 3);
             Z[row * kZStr + 32 * c + ml] = acc[r][c][q];
           }
     }
