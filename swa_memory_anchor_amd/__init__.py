@@ -221,8 +221,8 @@ def rma_commit_topk(st: LayerState, batch: int, keep_idx=None, stream=None) -> N
 
 
 def decode_workspace(batch: int, device="cuda"):
-    """A workspace tensor of the size swa_rma_decode_attn needs at this batch (or None)."""
+    """A zero-filled workspace of the size swa_rma_decode_attn needs at this batch (or None)."""
     import torch
 
     n = rma_decode_workspace_bytes(batch)
-    return None if n == 0 else torch.empty(n, dtype=torch.uint8, device=device)
+    return None if n == 0 else torch.zeros(n, dtype=torch.uint8, device=device)

@@ -331,22 +331,32 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
   const int b = bg / kGroups, g = bg % kGroups;
   const float *base = a.part + static_cast<size_t>(unit) * a.splits * kHeadsPerGroup * kPartStride +
                       h * kPartStride;
+  // Two passes over the splits (maxima, then weighted sums).  Each pass is fully
+  // unrolled over the split capacity, so all of its loads are in flight at once
+  // instead of one dependent load per split.
+  float ms[kMaxSplits];
   float M = -INFINITY;
-  for (int s = 0; s < a.splits; ++s)
-    M = fmaxf(M, base[static_cast<size_t>(s) * kHeadsPerGroup * kPartStride]);
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp) {
+    ms[sp] = sp < a.splits ? base[static_cast<size_t>(sp) * kHeadsPerGroup * kPartStride]
+                           : -INFINITY;
+    M = fmaxf(M, ms[sp]);
+  }
   float L = 0.f;
   float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
   if (M != -INFINITY) {
-    for (int s = 0; s < a.splits; ++s) {
-      const float *pp = base + static_cast<size_t>(s) * kHeadsPerGroup * kPartStride;
-      const float ms = pp[0];
-      const float wt = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-      L += pp[1] * wt;
-      const float4 v = *reinterpret_cast<const float4 *>(pp + 4 + 4 * lane);
-      O.x += v.x * wt;
-      O.y += v.y * wt;
-      O.z += v.z * wt;
-      O.w += v.w * wt;
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplits; ++sp) {
+      if (sp < a.splits) {
+        const float *pp = base + static_cast<size_t>(sp) * kHeadsPerGroup * kPartStride;
+        const float wt = ms[sp] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms[sp] - M);
+        L += pp[1] * wt;
+        const float4 v = *reinterpret_cast<const float4 *>(pp + 4 + 4 * lane);
+        O.x += v.x * wt;
+        O.y += v.y * wt;
+        O.z += v.z * wt;
+        O.w += v.w * wt;
+      }
     }
   }
   const int head = g * kHeadsPerGroup + h;

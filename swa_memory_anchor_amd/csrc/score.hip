@@ -9,7 +9,8 @@
 // Design.  Stage 1 is a dense FP32 contraction (256 flop per input byte), so it
 // runs on v_mfma_f32_32x32x2f32:
 //  * one workgroup (4 waves) per 128-row tile and all 256 columns; each wave owns
-//    a 64 x 128 block = 2 x 4 accumulators of 32 x 32;
+//    a 64 x 128 block = 2 x 4 accumulators of 32 x 32 (32-row tiles for calls too
+//    small to give every CU a 128-row tile);
 //  * K is walked in slices of 32: BF16 rows are widened (exactly) to FP32 while
 //    being staged in LDS row-major (m-major), W1 is staged column-major (n-major);
 //    each lane's 16 operands of a slice are then contiguous, so a slice's operands
@@ -23,14 +24,12 @@
 
 namespace rma {
 
-constexpr int kRowsWG = 128;
 constexpr int kKt = 32;             // contraction depth of one staged slice
 constexpr int kStr = kKt + 4;       // LDS row stride (floats) of the m-major / n-major slices
-constexpr int kAFloats = kRowsWG * kStr;
-constexpr int kBFloats = kMid * kStr;
-constexpr int kStageFloats = kAFloats + kBFloats;
 constexpr int kZStr = 129;          // stage-1 block: [row][col], floats (one column half)
 constexpr int kScoreThreads = 256;
+constexpr int kMaxRowsWG = 128;
+constexpr int kStageFloats = kMaxRowsWG * kStr + kMid * kStr;
 
 struct ScoreParams {
   const uint16_t *hidden;
@@ -45,59 +44,81 @@ struct ScoreParams {
 // 16h .. 16h+15 over the slice's 16 MFMA steps, so each lane's 16 operands are
 // contiguous in the m-major (A) and n-major (B) LDS layouts and load as four
 // 16-byte reads.  The same k order is used for A and B, so the products pair up.
+//
+// Tile shapes: the 4 waves are arranged WR x (4/WR); each wave owns RB row blocks
+// and CB column blocks of 32 x 32.  Large calls use 128-row tiles (WR=2, RB=2,
+// CB=4); calls with fewer row tiles than CUs use 32-row tiles (WR=1, RB=1, CB=2)
+// to spread over 4x more workgroups.  Both run the same instruction sequence per
+// output element, so results do not depend on the tile shape.
+template <int WR, int RB, int CB>
 __global__ __launch_bounds__(kScoreThreads, 1) void score_kernel(ScoreParams a) {
+  constexpr int WC = 4 / WR;
+  constexpr int kRows = 32 * RB * WR;
+  constexpr int kColsW = 32 * CB;  // columns per wave
+  static_assert(kColsW * WC == kMid, "waves cover the 256 columns");
+  constexpr int kAFloats = kRows * kStr;
+  constexpr int kSF = kAFloats + kMid * kStr;
+  constexpr int kTpr = kScoreThreads / kRows;  // staging threads per hidden row
+  constexpr int kKpt = kKt / kTpr;             // k values each of them stages (16 or 4)
   __shared__ __align__(16) float smem[2 * kStageFloats];
   __shared__ float w2s[kMid * kGroups];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wr = wave >> 1, wc = wave & 1;  // wave's 64-row half and 128-column half
-  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * kRowsWG;
+  const int wr = wave / WC, wc = wave % WC;
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * kRows;
 
   for (int i = tid; i < kMid * kGroups; i += kScoreThreads) w2s[i] = a.w2[i];
 
-  // staging roles: A (hidden) row am, k half ah (16 values, m-major); B (W1)
+  // staging roles: A (hidden) row am, k chunk ah (kKpt values, m-major); B (W1)
   // column bn, all 32 k of the slice (n-major)
-  const int am = tid >> 1, ah = tid & 1;
+  const int am = tid / kTpr, ah = tid % kTpr;
   const bool arow_ok = row0 + am < a.n_rows;
-  const uint16_t *arow = a.hidden + (arow_ok ? (row0 + am) : 0) * a.ld_hidden + 16 * ah;
-  const int bn = tid;  // one W1 column per thread, all 32 k of the slice
+  const uint16_t *arow = a.hidden + (arow_ok ? (row0 + am) : 0) * a.ld_hidden + kKpt * ah;
+  const int bn = tid;
 
-  uint4 ha[2];
+  uint32_t ha[kKpt / 2];
   float wb[kKt];
   auto load_stage = [&](int kt) {
-    if (arow_ok) {
-      ha[0] = *reinterpret_cast<const uint4 *>(arow + kt * kKt);
-      ha[1] = *reinterpret_cast<const uint4 *>(arow + kt * kKt + 8);
+    if constexpr (kKpt == 16) {
+      uint4 u0 = make_uint4(0, 0, 0, 0), u1 = u0;
+      if (arow_ok) {
+        u0 = *reinterpret_cast<const uint4 *>(arow + kt * kKt);
+        u1 = *reinterpret_cast<const uint4 *>(arow + kt * kKt + 8);
+      }
+      ha[0] = u0.x; ha[1] = u0.y; ha[2] = u0.z; ha[3] = u0.w;
+      ha[4] = u1.x; ha[5] = u1.y; ha[6] = u1.z; ha[7] = u1.w;
     } else {
-      ha[0] = make_uint4(0, 0, 0, 0);
-      ha[1] = ha[0];
+      static_assert(kKpt == 4, "staging chunk");
+      uint2 u = make_uint2(0, 0);
+      if (arow_ok) u = *reinterpret_cast<const uint2 *>(arow + kt * kKt);
+      ha[0] = u.x;
+      ha[1] = u.y;
     }
     const float *wcol = a.w1 + static_cast<size_t>(kt * kKt) * kMid + bn;
 #pragma unroll
     for (int k = 0; k < kKt; ++k) wb[k] = wcol[static_cast<size_t>(k) * kMid];
   };
   auto store_stage = [&](int buf) {
-    float *As = smem + buf * kStageFloats;
+    float *As = smem + buf * kSF;
     float *Bs = As + kAFloats;
-    const uint32_t w[8] = {ha[0].x, ha[0].y, ha[0].z, ha[0].w, ha[1].x, ha[1].y, ha[1].z, ha[1].w};
-    float4 *ad = reinterpret_cast<float4 *>(As + am * kStr + 16 * ah);
+    float4 *ad = reinterpret_cast<float4 *>(As + am * kStr + kKpt * ah);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      ad[j] = make_float4(bf16_lo(w[2 * j]), bf16_hi(w[2 * j]), bf16_lo(w[2 * j + 1]),
-                          bf16_hi(w[2 * j + 1]));
+    for (int j = 0; j < kKpt / 4; ++j)
+      ad[j] = make_float4(bf16_lo(ha[2 * j]), bf16_hi(ha[2 * j]), bf16_lo(ha[2 * j + 1]),
+                          bf16_hi(ha[2 * j + 1]));
     float4 *bd = reinterpret_cast<float4 *>(Bs + bn * kStr);
 #pragma unroll
     for (int j = 0; j < kKt / 4; ++j)
       bd[j] = make_float4(wb[4 * j], wb[4 * j + 1], wb[4 * j + 2], wb[4 * j + 3]);
   };
 
-  f32x16 acc[2][4];
+  f32x16 acc[RB][CB];
 #pragma unroll
-  for (int r = 0; r < 2; ++r)
+  for (int r = 0; r < RB; ++r)
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < CB; ++c)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[r][c][q] = 0.f;
 
@@ -108,66 +129,77 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score_kernel(ScoreParams a) 
   const int kh = lane >> 5, ml = lane & 31;
   for (int kt = 0; kt < nkt; ++kt) {
     if (kt + 1 < nkt) load_stage(kt + 1);
-    const float *As = smem + (kt & 1) * kStageFloats;
+    const float *As = smem + (kt & 1) * kSF;
     const float *Bs = As + kAFloats;
-    float4 av[2][4], bv[4][4];
+    float4 av[RB][4], bv[CB][4];
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        av[r][j] = *reinterpret_cast<const float4 *>(As + (wr * 64 + 32 * r + ml) * kStr + 16 * kh + 4 * j);
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int r = 0; r < RB; ++r)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        bv[c][j] = *reinterpret_cast<const float4 *>(Bs + (wc * 128 + 32 * c + ml) * kStr + 16 * kh + 4 * j);
+        av[r][j] = *reinterpret_cast<const float4 *>(
+            As + (wr * 32 * RB + 32 * r + ml) * kStr + 16 * kh + 4 * j);
+#pragma unroll
+    for (int c = 0; c < CB; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bv[c][j] = *reinterpret_cast<const float4 *>(
+            Bs + (wc * kColsW + 32 * c + ml) * kStr + 16 * kh + 4 * j);
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) {
       const int j = kk >> 2, e = kk & 3;
-      const float a0 = av[0][j][e], a1 = av[1][j][e];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < CB; ++c) {
         const float b = bv[c][j][e];
-        acc[0][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b, acc[0][c], 0, 0, 0);
-        acc[1][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b, acc[1][c], 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+          acc[r][c] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[r][j][e], b, acc[r][c], 0, 0, 0);
       }
     }
     if (kt + 1 < nkt) store_stage((kt + 1) & 1);
     __syncthreads();
   }
 
-  // Stage 2: s[row][g] = sum_{n=0..255} Z[row][n] * W2[n][g], n ascending.
+  // Stage 2: s[row][g] = sum_{n=0..255} Z[row][n] * W2[n][g], n ascending, passed
+  // through LDS in two column halves.
   float *Z = smem;
-  const int srow = tid & (kRowsWG - 1);
-  const int sg = (tid >> 7) * 2;  // this thread's two groups
-  float s0 = 0.f, s1 = 0.f;
+  constexpr int kOuts = kRows * kGroups;  // outputs of the tile
+  constexpr int kPerThread = (kOuts + kScoreThreads - 1) / kScoreThreads;  // 2 or 1
+  const int srow = tid % kRows;
+  const int sg = (tid / kRows) * kPerThread;  // first group of this thread
+  const bool active = sg < kGroups;
+  float sacc[kPerThread];
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) sacc[i] = 0.f;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    if (wc == half) {
+    if (wc * kColsW / 128 == half) {
+      const int cofs = wc * kColsW - half * 128;
 #pragma unroll
-      for (int r = 0; r < 2; ++r)
+      for (int r = 0; r < RB; ++r)
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < CB; ++c)
 #pragma unroll
           for (int q = 0; q < 16; ++q) {
-            const int row = wr * 64 + r * 32 + 8 * (q >> 2) + 4 * kh + (q & 3);
-            Z[row * kZStr + 32 * c + ml] = acc[r][c][q];
+            const int row = wr * 32 * RB + r * 32 + 8 * (q >> 2) + 4 * kh + (q & 3);
+            Z[row * kZStr + cofs + 32 * c + ml] = acc[r][c][q];
           }
     }
     __syncthreads();
-    const float *zr = Z + srow * kZStr;
-    const float *w2h = w2s + half * 128 * kGroups;
-    for (int n = 0; n < 128; ++n) {
-      const float z = zr[n];
-      s0 = fmaf(z, w2h[n * kGroups + sg], s0);
-      s1 = fmaf(z, w2h[n * kGroups + sg + 1], s1);
+    if (active) {
+      const float *zr = Z + srow * kZStr;
+      const float *w2h = w2s + half * 128 * kGroups;
+      for (int n = 0; n < 128; ++n) {
+        const float z = zr[n];
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) sacc[i] = fmaf(z, w2h[n * kGroups + sg + i], sacc[i]);
+      }
     }
     __syncthreads();
   }
-  if (row0 + srow < a.n_rows) {
+  if (active && row0 + srow < a.n_rows) {
     float *out = a.scores + (row0 + srow) * a.ld_scores + sg;
-    out[0] = s0;
-    out[1] = s1;
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) out[i] = sacc[i];
   }
 }
 
@@ -186,11 +218,20 @@ extern "C" rma_status rma_score(const uint16_t *hidden, int64_t n_rows, int64_t 
   if ((reinterpret_cast<uintptr_t>(hidden) & 15u) || (reinterpret_cast<uintptr_t>(w1) & 15u) ||
       (reinterpret_cast<uintptr_t>(scores) & 15u))
     return RMA_E_ALIGN;
-  const int64_t blocks = (n_rows + kRowsWG - 1) / kRowsWG;
-  if (blocks > 0x7fffffff) return RMA_E_ARG;
   ScoreParams p{hidden, n_rows, ld_hidden, w1, w2, scores, ld_scores};
-  hipLaunchKernelGGL(score_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kScoreThreads), 0,
-                     static_cast<hipStream_t>(stream), p);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // 128-row tiles while they give at least one workgroup per CU (256 CUs); below
+  // that, 32-row tiles spread the same work over four times as many CUs.
+  const int64_t big = (n_rows + 127) / 128;
+  if (big >= 256) {
+    if (big > 0x7fffffff) return RMA_E_ARG;
+    hipLaunchKernelGGL((score_kernel<2, 2, 4>), dim3(static_cast<unsigned>(big)),
+                       dim3(kScoreThreads), 0, s, p);
+  } else {
+    const int64_t small = (n_rows + 31) / 32;
+    hipLaunchKernelGGL((score_kernel<1, 1, 2>), dim3(static_cast<unsigned>(small)),
+                       dim3(kScoreThreads), 0, s, p);
+  }
   if (hipPeekAtLastError() != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
   return RMA_OK;
 }

@@ -71,15 +71,26 @@ def test_decode_ragged_multi_split(same_q):
         assert np.array_equal(getattr(after, nmk), getattr(st, nmk))
 
 
-def test_decode_is_deterministic():
-    st = upload(_rand_state("det", COUNTS[:4]))
-    q = bf16_dev(synth.normal_bf16_np(synth.stream_key("det", "q"), 4 * 4096).reshape(4, 16, 256))
+def test_decode_is_deterministic_with_a_reused_workspace():
+    B = 4
+    st = upload(_rand_state("det", COUNTS[:B]))
+    q = bf16_dev(synth.normal_bf16_np(synth.stream_key("det", "q"), B * 4096).reshape(B, 16, 256))
     nm = norm_dev(_gains("det"))
-    a = decode_gpu(st, q, q, nm)
-    b = decode_gpu(st, q, q, nm)
-    for x, y in zip(a, b):
-        assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
-                           y.view(torch.int16) if y.dtype == torch.bfloat16 else y)
+    ws = R.decode_workspace(B)
+    assert R.rma_decode_splits(B) > 1 and ws is not None
+    outs = []
+    for _ in range(3):
+        o = [torch.full((B, 16, 256), 7.0, dtype=torch.bfloat16, device=DEV),
+             torch.full((B, 16), 7.0, device=DEV),
+             torch.full((B, 16, 256), 7.0, dtype=torch.bfloat16, device=DEV),
+             torch.full((B, 16), 7.0, device=DEV)]
+        R.swa_rma_decode_attn(st, B, q, q, nm, o[0], o[1], o[2], o[3], ws)
+        torch.cuda.synchronize()
+        outs.append(o)
+    for o in outs[1:]:
+        for x, y in zip(o, outs[0]):
+            assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
+                               y.view(torch.int16) if y.dtype == torch.bfloat16 else y)
 
 
 def test_append_matches_oracle_within_one_ulp():
@@ -244,3 +255,26 @@ def test_commit_all_equal_scores_keep_lowest_sources():
         for g in range(4):
             cand = np.concatenate([st.bank_src[b, g, :nb], st.pend_src[b]])
             assert np.array_equal(np.sort(got.bank_src[b, g, :n]), np.sort(cand)[:n])
+
+
+def test_score_large_ragged_uses_big_tiles_and_matches_small_tiles():
+    # 33000 rows: 258 tiles of 128 rows (the large-tile kernel) with a ragged tail
+    n = 33000
+    rng = np.random.default_rng(10)
+    h = synth.normal_bf16_np(synth.stream_key("score_big"), n * 2560).reshape(n, 2560)
+    w1 = (0.02 * rng.standard_normal((2560, 256))).astype(np.float32)
+    w2 = (0.02 * rng.standard_normal((256, 4))).astype(np.float32)
+    hd, w1d, w2d = bf16_dev(h), f32_dev(w1), f32_dev(w2)
+    out = torch.full((n, 4), float("nan"), device=DEV)
+    R.rma_score(hd, n, 2560, w1d, w2d, out, 4)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.all(np.isfinite(o))
+    rows = np.array([0, 1, 127, 128, 16383, 32767, 32768, 32895, 32999])
+    assert_scores_close(o[rows], O.score(h[rows], w1, w2), what="large ragged")
+    # the same rows through the small-tile kernel (a 300-row call) give the same bits
+    sub = np.concatenate([rows, np.arange(291) + 100])
+    out2 = torch.empty(len(sub), 4, device=DEV)
+    R.rma_score(bf16_dev(h[sub]), len(sub), 2560, w1d, w2d, out2, 4)
+    torch.cuda.synchronize()
+    assert np.array_equal(out2.cpu().numpy(), o[sub])
