@@ -316,6 +316,101 @@ def bench_long_stream(args):
     }
 
 
+BF16_MATRIX_PEAK_TFLOPS = 2500.0
+
+
+def bench_prefill(args):
+    """Chunked prefill of one 256-token block per sequence in all 8 layers (steady state:
+    full window and bank, empty pending block, chunk at positions 65536..65791)."""
+    import numpy as np
+    import torch
+
+    import swa_memory_anchor_amd as R
+    from synth import workloads as W
+    from synth.core import normal_bf16_torch_
+
+    B = 512 if args.workload == "prefill_b512" else 64
+    wl = W.Workload(args.workload, batch=B, layers=8, position=65535, gains="normal")
+    L, C, dev = wl.layers, 256, "cuda"
+    stream = torch.cuda.current_stream()
+    states, saved, norms, ins, outs = [], [], [], [], []
+    for layer in range(L):
+        st = R.alloc_layer_state(B, dev, zero_kv=False)
+        for nm in W.KV_NAMES:
+            W.kv_torch_(wl, layer, nm, getattr(st, nm))
+        meta = W.decode_meta(wl, layer)
+        meta["n_pend"][:] = 0
+        for k, v in meta.items():
+            getattr(st, k).copy_(torch.from_numpy(v).to(dev))
+        states.append(st)
+        saved.append((st.n_pend.clone(), st.pos.clone()))
+        g = W.gains(wl, layer)
+        norms.append(R.Norm(*[torch.from_numpy(g[k]).to(dev) for k in
+                              ("gq_win", "gk_win", "gq_rma", "gk_rma")], wl.eps, wl.rope_base))
+        rec = []
+        for nm in W.RECORD_NAMES:
+            t = torch.empty(B, C, 4, 256, dtype=torch.bfloat16, device=dev)
+            normal_bf16_torch_(t, W.key(wl, layer, "prefill", nm))
+            rec.append(t)
+        q = torch.empty(B, C, 16, 256, dtype=torch.bfloat16, device=dev)
+        normal_bf16_torch_(q, W.key(wl, layer, "prefill", "q"))
+        ins.append((rec, q))
+        outs.append((torch.empty(B, C, 16, 256, dtype=torch.bfloat16, device=dev),
+                     torch.empty(B, C, 16, device=dev),
+                     torch.empty(B, C, 16, 256, dtype=torch.bfloat16, device=dev),
+                     torch.empty(B, C, 16, device=dev)))
+    ws = R.prefill_workspace(B, C, dev)
+    torch.cuda.synchronize()
+
+    def reset():
+        for l in range(L):
+            states[l].n_pend.copy_(saved[l][0])
+            states[l].pos.copy_(saved[l][1])
+
+    def step():
+        for l in range(L):
+            rec, q = ins[l]
+            o = outs[l]
+            R.swa_rma_prefill(states[l], B, C, rec[0], rec[1], rec[2], rec[3], None, q, q,
+                              norms[l], o[0], o[1], o[2], o[3], ws, stream)
+
+    ms = []
+    for rep in range(args.warmup + args.steps):
+        reset()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        if rep >= args.warmup:
+            ms.append(a.elapsed_time(b))
+    step_ms = sum(ms) / len(ms)
+    # algorithmic flops: token i sees 1024 window keys and 1024 + i + 1 anchor keys;
+    # q.k and p.v are 2 * 256 flops each per (key, head)
+    keys = sum(2048 + i + 1 for i in range(C))
+    flop = B * L * keys * 16 * 256 * 4
+    tflops = flop / (step_ms / 1e3) / 1e12
+    return {
+        "metric": "chunked prefill: tokens/s (256-token chunk per sequence, 8 layers)",
+        "value": round(B * C / (step_ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": B, "layers": L, "chunk": C,
+                   "positions": [65536, 65536 + C - 1]},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
+                     "peak": BF16_MATRIX_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / BF16_MATRIX_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill (write + attention + ring)"},
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -323,7 +418,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="headline_b512",
                     choices=["headline_b512", "steady_b64", "batch1", "commit_burst_b512",
-                             "long_stream_b1"])
+                             "long_stream_b1", "prefill_b512", "prefill_b64"])
     ap.add_argument("--stream-tokens", type=int, default=16384,
                     help="long_stream_b1: tokens streamed (the second half is timed)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
@@ -358,6 +453,9 @@ def main() -> int:
         return 0
     if args.workload == "long_stream_b1":
         print(json.dumps(bench_long_stream(args)))
+        return 0
+    if args.workload.startswith("prefill"):
+        print(json.dumps(bench_prefill(args)))
         return 0
     if args.workload == "headline_b512":
         wl = W.HEADLINE_B512

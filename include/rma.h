@@ -38,8 +38,8 @@
  *     undersized workspace, or a launch error.  Nothing is launched when a
  *     check fails.
  *   - Device-side contract (not checked on the host): 0 <= n_bank <= 1024,
- *     0 <= n_pend <= 256, n_pend < 256 before an append, and distinct source
- *     positions within a group.  Kernels clamp counts to their capacities so
+ *     0 <= n_pend <= 256, n_pend < 256 before an append, and distinct,
+ *     non-negative source positions within a group.  Kernels clamp counts to their capacities so
  *     that no access leaves the arrays.
  */
 #ifndef RMA_H
@@ -186,6 +186,33 @@ rma_status rma_score(const uint16_t *hidden, int64_t n_rows, int64_t ld_hidden, 
  */
 rma_status rma_commit_topk(const rma_layer_state *st, int32_t batch, int32_t *keep_idx,
                            void *stream);
+
+/* Workspace that swa_rma_prefill needs for `n_tokens` tokens per sequence. */
+size_t rma_prefill_workspace_bytes(int32_t batch, int32_t n_tokens);
+
+/*
+ * swa_rma_prefill - chunked prefill of one layer: n_tokens (1..256) tokens per
+ * sequence in one call.  The result is that of n_tokens successive
+ * swa_rma_append + swa_rma_decode_attn steps ([FB] section "架构…", [QB] section
+ * above): token i of sequence b sits at position p = pos[b] + 1 + i and attends
+ * to window positions p-1023..p, to all committed anchors and to the pending
+ * records at positions <= p.
+ *   k_win, v_win, k_rma, v_rma  bf16 [B][n_tokens][4][256], raw.
+ *   score   f32 [B][n_tokens][4] into pend_score, or NULL.
+ *   q_win, q_rma  bf16 [B][n_tokens][16][256], raw; they may alias.
+ *   o_win, o_rma  bf16 [B][n_tokens][16][256] out; lse_win, lse_rma f32
+ *                 [B][n_tokens][16] out.
+ *   workspace  rma_prefill_workspace_bytes(batch, n_tokens) bytes, 16-byte aligned.
+ * The pending block must have room: n_pend[b] + n_tokens <= 256 (commit first);
+ * a sequence without room is left untouched and its outputs are o = 0,
+ * lse = -inf.  Afterwards n_pend[b] += n_tokens and pos[b] += n_tokens.
+ */
+rma_status swa_rma_prefill(const rma_layer_state *st, int32_t batch, int32_t n_tokens,
+                           const uint16_t *k_win, const uint16_t *v_win, const uint16_t *k_rma,
+                           const uint16_t *v_rma, const float *score, const uint16_t *q_win,
+                           const uint16_t *q_rma, const rma_norm *norm, uint16_t *o_win,
+                           float *lse_win, uint16_t *o_rma, float *lse_rma, void *workspace,
+                           size_t workspace_bytes, void *stream);
 
 /* Human-readable name of a status code (static string). */
 const char *rma_status_str(rma_status s);

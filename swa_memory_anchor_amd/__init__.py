@@ -7,9 +7,9 @@ same names.  If the library has not been built, importing the entry points
 raises: there is no fallback.
 
 Entry points: ``swa_rma_append``, ``swa_rma_decode_attn``, ``rma_score``,
-``rma_commit_topk``, plus the size helpers ``rma_layer_state_bytes``,
-``rma_layer_kv_bytes``, ``rma_decode_workspace_bytes``, ``rma_decode_splits`` and
-``rma_status_str``.
+``rma_commit_topk``, ``swa_rma_prefill``, plus the size helpers ``rma_layer_state_bytes``,
+``rma_layer_kv_bytes``, ``rma_decode_workspace_bytes``, ``rma_decode_splits``,
+``rma_prefill_workspace_bytes`` and ``rma_status_str``.
 """
 
 from __future__ import annotations
@@ -26,7 +26,7 @@ WINDOW, BANK, BLOCK, HIDDEN, SCORER_MID = 1024, 1024, 256, 2560, 256
 EXPORTS = (
     "rma_layer_state_bytes", "rma_layer_kv_bytes", "rma_decode_workspace_bytes",
     "rma_decode_splits", "swa_rma_append", "swa_rma_decode_attn", "rma_score",
-    "rma_commit_topk", "rma_status_str",
+    "rma_commit_topk", "rma_status_str", "rma_prefill_workspace_bytes", "swa_rma_prefill",
 )
 
 _c_void_p = ctypes.c_void_p
@@ -74,6 +74,11 @@ def lib() -> ctypes.CDLL:
         L.rma_commit_topk.argtypes = [sp, i32, vp, vp]
         L.rma_commit_topk.restype = ctypes.c_int
         L.rma_status_str.argtypes, L.rma_status_str.restype = [ctypes.c_int], ctypes.c_char_p
+        L.rma_prefill_workspace_bytes.argtypes = [i32, i32]
+        L.rma_prefill_workspace_bytes.restype = sz
+        L.swa_rma_prefill.argtypes = [sp, i32, i32, vp, vp, vp, vp, vp, vp, vp, npp, vp, vp, vp,
+                                      vp, vp, sz, vp]
+        L.swa_rma_prefill.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -226,3 +231,27 @@ def decode_workspace(batch: int, device="cuda"):
 
     n = rma_decode_workspace_bytes(batch)
     return None if n == 0 else torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def rma_prefill_workspace_bytes(batch: int, n_tokens: int) -> int:
+    return int(lib().rma_prefill_workspace_bytes(int(batch), int(n_tokens)))
+
+
+def prefill_workspace(batch: int, n_tokens: int, device="cuda"):
+    """A workspace tensor of the size swa_rma_prefill needs."""
+    import torch
+
+    return torch.empty(rma_prefill_workspace_bytes(batch, n_tokens), dtype=torch.uint8,
+                       device=device)
+
+
+def swa_rma_prefill(st: LayerState, batch: int, n_tokens: int, k_win, v_win, k_rma, v_rma, score,
+                    q_win, q_rma, norm: Norm, o_win, lse_win, o_rma, lse_rma, workspace,
+                    stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size()
+    s = lib().swa_rma_prefill(ctypes.byref(_state_c(st)), int(batch), int(n_tokens), _ptr(k_win),
+                              _ptr(v_win), _ptr(k_rma), _ptr(v_rma), _ptr(score), _ptr(q_win),
+                              _ptr(q_rma), ctypes.byref(_norm_c(norm)), _ptr(o_win),
+                              _ptr(lse_win), _ptr(o_rma), _ptr(lse_rma), _ptr(workspace),
+                              ws_bytes, _stream(stream))
+    _check(s, "swa_rma_prefill")

@@ -87,3 +87,12 @@ def test_host_validation_rejects_bad_arguments(lib):
     assert lib.rma_score(16, 5, 2559, 16, 16, 16, 4, None) == 1
     assert lib.rma_score(16, 5, 2564, 16, 16, 16, 4, None) == 2
     assert lib.rma_score(24, 5, 2560, 16, 16, 16, 4, None) == 2
+    pf = lambda st_, b, n, ws, wsb, q=16: lib.swa_rma_prefill(  # noqa: E731
+        st_, b, n, 16, 16, 16, 16, None, q, 16, by(nm), 16, 16, 16, 16, ws, wsb, None)
+    need = R.rma_prefill_workspace_bytes(2, 100)
+    assert need == 2 * 100 * 4 * 256 * 2
+    assert pf(by(st), 2, 0, 16, need) == 1      # no tokens
+    assert pf(by(st), 2, 257, 16, 1 << 30) == 1  # more than a pending block
+    assert pf(by(st), 2, 100, None, 0) == 3      # no workspace
+    assert pf(by(st), 2, 100, 16, need - 1) == 3
+    assert pf(by(st), 2, 100, 16, need, q=24) == 2
