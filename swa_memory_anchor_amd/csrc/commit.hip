@@ -19,8 +19,9 @@
 //   3. a bank record survives in place; free slots (evicted slots, then slots
 //      >= n_bank) are listed in ascending order by a prefix sum; admitted
 //      pending rows, in ascending row order, take the free slots in order;
-//   4. only admitted rows move: 512-byte K and V rows are copied with 16-byte
-//      loads (one wave per row), plus their score and source;
+//   4. only admitted rows move: 512-byte K and V rows are copied in 16-byte
+//      pieces (a wave covers one row per pass, 8 passes in flight), plus their
+//      score and source;
 //   5. n_bank = min(1024, n_bank + n_pend), n_pend = 0.
 #include "rma_device.h"
 
@@ -30,6 +31,7 @@ constexpr int kCand = kBank + kBlock;  // 1280
 constexpr int kSortN = 2048;
 constexpr int kGroupThreads = 256;
 constexpr int kCommitThreads = kGroupThreads * kGroups;
+constexpr int kCopyBatch = 8;  // 16-byte copies in flight per thread
 
 struct CommitParams {
   uint16_t *bank_k, *bank_v;
@@ -183,15 +185,32 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kernel(CommitParams a) 
 #pragma unroll
     for (int e = 0; e < 4; ++e) a.keep_idx[sg * kBank + 4 * t + e] = kidx[g][4 * t + e];
   }
-  for (int w = t; w < n_adm * 64; w += kGroupThreads) {
-    const int q = w >> 6, part = w & 63;
-    const int row = adm_rows[g][q];
-    const int s = adm_slot[g][row];
-    const bool isv = part >= 32;
-    const int c = (part & 31) * 8;
-    const uint16_t *src = (isv ? a.pend_v : a.pend_k) + (sg * kBlock + row) * kDim + c;
-    uint16_t *dst = (isv ? a.bank_v : a.bank_k) + (sg * kBank + s) * kDim + c;
-    *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
+  // 16-byte pieces: 64 per admitted row (32 of K, 32 of V).  Each thread issues
+  // kCopyBatch loads before its stores, so a group waits for at most
+  // 64 * 256 / (256 * kCopyBatch) round trips to memory instead of one per piece.
+  const int pieces = n_adm * 64;
+  for (int w0 = 0; w0 < pieces; w0 += kGroupThreads * kCopyBatch) {
+    u32x4 buf[kCopyBatch];
+#pragma unroll
+    for (int u = 0; u < kCopyBatch; ++u) {
+      // past the end, repeat the last piece: the same bytes go to the same place
+      const int w = min(w0 + t + u * kGroupThreads, pieces - 1);
+      const int row = adm_rows[g][w >> 6];
+      const int part = w & 63;
+      const uint16_t *src = (part >= 32 ? a.pend_v : a.pend_k) + (sg * kBlock + row) * kDim +
+                            (part & 31) * 8;
+      buf[u] = *reinterpret_cast<const u32x4 *>(src);
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyBatch; ++u) {
+      const int w = min(w0 + t + u * kGroupThreads, pieces - 1);
+      const int row = adm_rows[g][w >> 6];
+      const int part = w & 63;
+      const int sl = adm_slot[g][row];
+      uint16_t *dst = (part >= 32 ? a.bank_v : a.bank_k) + (sg * kBank + sl) * kDim +
+                      (part & 31) * 8;
+      *reinterpret_cast<u32x4 *>(dst) = buf[u];
+    }
   }
   if (t < n_adm) {
     const int row = adm_rows[g][t];

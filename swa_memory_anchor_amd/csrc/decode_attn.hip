@@ -331,32 +331,38 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
   const int b = bg / kGroups, g = bg % kGroups;
   const float *base = a.part + static_cast<size_t>(unit) * a.splits * kHeadsPerGroup * kPartStride +
                       h * kPartStride;
-  // Two passes over the splits (maxima, then weighted sums).  Each pass is fully
-  // unrolled over the split capacity, so all of its loads are in flight at once
-  // instead of one dependent load per split.
-  float ms[kMaxSplits];
-  float M = -INFINITY;
+  // Every split's (m, l) and accumulator slice are loaded before any of them is
+  // used (the loop is unrolled over the split capacity), so the kernel waits for
+  // one round trip to memory rather than one per split or per pass.
+  float ms[kMaxSplits], ls[kMaxSplits];
+  float4 os[kMaxSplits];
 #pragma unroll
   for (int sp = 0; sp < kMaxSplits; ++sp) {
-    ms[sp] = sp < a.splits ? base[static_cast<size_t>(sp) * kHeadsPerGroup * kPartStride]
-                           : -INFINITY;
-    M = fmaxf(M, ms[sp]);
+    ms[sp] = -INFINITY;
+    ls[sp] = 0.f;
+    os[sp] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (sp < a.splits) {
+      const float *pp = base + static_cast<size_t>(sp) * kHeadsPerGroup * kPartStride;
+      const float2 ml = *reinterpret_cast<const float2 *>(pp);
+      ms[sp] = ml.x;
+      ls[sp] = ml.y;
+      os[sp] = *reinterpret_cast<const float4 *>(pp + 4 + 4 * lane);
+    }
   }
+  float M = -INFINITY;
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp) M = fmaxf(M, ms[sp]);
   float L = 0.f;
   float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
   if (M != -INFINITY) {
 #pragma unroll
     for (int sp = 0; sp < kMaxSplits; ++sp) {
-      if (sp < a.splits) {
-        const float *pp = base + static_cast<size_t>(sp) * kHeadsPerGroup * kPartStride;
-        const float wt = ms[sp] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms[sp] - M);
-        L += pp[1] * wt;
-        const float4 v = *reinterpret_cast<const float4 *>(pp + 4 + 4 * lane);
-        O.x += v.x * wt;
-        O.y += v.y * wt;
-        O.z += v.z * wt;
-        O.w += v.w * wt;
-      }
+      const float wt = ms[sp] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms[sp] - M);
+      L += ls[sp] * wt;
+      O.x += os[sp].x * wt;
+      O.y += os[sp].y * wt;
+      O.z += os[sp].z * wt;
+      O.w += os[sp].w * wt;
     }
   }
   const int head = g * kHeadsPerGroup + h;
