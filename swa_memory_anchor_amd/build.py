@@ -34,6 +34,15 @@ FLAGS = [
 ]
 
 
+# Per-file flags.  The prefill attention kernel holds 128 FP32 accumulators per lane
+# and rescales them with VALU multiplies; with the VGPR form of the MFMA
+# instructions they stay in VGPRs instead of being copied between AGPRs and VGPRs
+# on every key tile.
+FILE_FLAGS = {
+    "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def _hipcc() -> str:
     for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -47,7 +56,8 @@ def sources():
 
 def _compile(src: str, extra) -> str:
     obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *FLAGS, *extra, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src,
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -15,28 +15,36 @@
 //     straight into pending rows n_pend .. n_pend + C - 1, the window keys into the
 //     workspace (the ring cannot be overwritten yet: earlier tokens of the chunk
 //     still read the positions the chunk will replace).
-//  2. prefill_attn: one workgroup per (branch, sequence, group, 16-token tile): 64
-//     query rows (16 tokens x 4 heads), 16 per wave.  Key tiles of 16 are staged
-//     once in LDS for the four waves -- K row-major, V transposed -- and every key
-//     is masked by its position.  S^T = K Q^T and O^T += V^T P^T on MFMA, as in the
-//     decode kernel; the tiles of one unit are numbered onto one XCD so they share
-//     its L2.
+//  2. prefill_attn: one workgroup per (branch, sequence, group, 32-token tile): 128
+//     query rows (32 tokens x 4 heads), 32 per wave, held in AGPRs in the operand
+//     layout of v_mfma_f32_32x32x16_bf16 after norm + rotary.  Key tiles of 32
+//     reach LDS through buffer loads straight into LDS, four stages deep (three
+//     tiles in flight while one is computed); rows are XOR-swizzled against bank
+//     conflicts.  S^T = K Q^T reads K rows; O^T += V^T P^T reads V^T with
+//     transposing LDS reads, in the key order of the score accumulator, so P goes
+//     from registers straight into the second product.  Keys are masked by
+//     position (ring age, causal order in the chunk).  The softmax reference
+//     maximum moves only when a row's maximum grows by more than 2^8, so the 128
+//     accumulators are rarely rescaled.  The tiles of one unit are numbered onto
+//     one XCD so they share its L2.
 //  3. prefill_ring: copy the chunk's window K/V into ring slots, then advance
 //     n_pend and pos.
 #include "rma_device.h"
 
 namespace rma {
 
-constexpr int kPTok = 16;                          // tokens per attention workgroup
-constexpr int kPRowsWave = 16;                     // query rows per wave (4 tokens x 4 heads)
-constexpr int kPWaves = kPTok * kHeadsPerGroup / kPRowsWave;  // 4
+constexpr int kPWaves = 4;                         // waves per attention workgroup
 constexpr int kPThreads = 64 * kPWaves;
-constexpr int kPKeys = 16;                         // keys per tile
-constexpr int kKStr = kDim + 8;                    // K tile row stride (elements)
-constexpr int kVtStr = kPKeys + 8;                 // V^T tile row stride (elements)
+constexpr int kPRowsWave = 32;                     // query rows per wave (8 tokens x 4 heads)
+constexpr int kPTok = kPWaves * kPRowsWave / kHeadsPerGroup;  // 64 tokens per workgroup
+constexpr int kPKeys = 32;                         // keys per tile
+constexpr int kStages = 4;                         // LDS tile buffers (3 tiles in flight)
+constexpr int kTileElems = kPKeys * kDim;          // one K or V tile, row-major, 16 KB
+constexpr int kDmaPerTile = 2 * kTileElems * 2 / (kPThreads * 16);  // per wave: 8
 constexpr int kMaxChunk = kBlock;
 constexpr float kPQScale = 1.4426950408889634f / 16.0f;
 constexpr float kPLn2 = 0.69314718055994531f;
+constexpr float kPTau = 8.0f;  // reference-maximum slack (log2 units): P <= 2^8
 constexpr int kXcds = 8;
 
 template <typename T, typename F>
@@ -98,23 +106,75 @@ __global__ __launch_bounds__(256) void prefill_write_kernel(PrefillParams a) {
 }
 
 // ---------------------------------------------------------------- 2. attention
-// A run of key rows and how each row's position is known.
+// A run of key rows and how each row's position is known.  K and V are read
+// through buffer resources whose range ends at the last row, so rows past the
+// end read as zero.
 struct PSeg {
-  const uint16_t *k, *v;  // row-major, 256 BF16 per row
-  int n;                  // rows
-  int kind;               // 0: always visible; 1: window ring slot; 2: chunk row
+  __amdgpu_buffer_rsrc_t k, v;
+  int n;       // rows
+  int stride;  // bytes between rows
+  int kind;    // 0: always visible; 1: window ring slot; 2: chunk row
 };
 
-__global__ __launch_bounds__(kPThreads, 2) void prefill_attn_kernel(PrefillParams a) {
-  __shared__ __align__(16) uint16_t q_lds[kPTok * kHeadsPerGroup][kDim];
-  __shared__ __align__(16) uint16_t k_lds[2][kPKeys * kKStr];
-  __shared__ __align__(16) uint16_t vt_lds[2][kDim * kVtStr];
+__device__ __forceinline__ PSeg make_pseg(const uint16_t *k, const uint16_t *v, int n,
+                                          int stride_elems, int kind) {
+  const int bytes = n > 0 ? (n - 1) * stride_elems * 2 + kDim * 2 : 0;
+  PSeg sg;
+  sg.k = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(k), 0, bytes, 0x00020000);
+  sg.v = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(v), 0, bytes, 0x00020000);
+  sg.n = n;
+  sg.stride = stride_elems * 2;
+  sg.kind = kind;
+  return sg;
+}
 
+__device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// LDS tiles are row-major (32 keys x 32 sixteen-byte chunks) with the chunk index
+// XOR-swizzled by the key, so that the MFMA operand reads below hit 8 (K) or 16
+// (V, transposed reads) distinct bank groups:
+//   K chunk c of key k sits at chunk position c ^ (k & 7)
+//   V chunk c of key k sits at chunk position c ^ (2 (k & 3))
+__device__ __forceinline__ int k_swz(int key) { return key & 7; }
+__device__ __forceinline__ int v_swz(int key) { return 2 * (key & 3); }
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+constexpr uint32_t kOnesBf16x2Bits = 0x3f803f80u;  // (1.0, 1.0) in BF16
+#define kOnesBf16x2 pbitcast<bf16x2_t>(kOnesBf16x2Bits)
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+
+// Wait until this wave has at most N vector-memory operations in flight, then
+// meet the other waves at the barrier.  (A plain __syncthreads() would also wait
+// for every outstanding load-to-LDS, i.e. for the tiles still meant to be in flight.)
+// One K and one V tile buffer per pipeline stage, as separate arrays so that the
+// compiler's wait for loads-to-LDS can tell the stage being read from the stages
+// still being filled.
+__shared__ __align__(16) uint16_t pf_k0[kTileElems];
+__shared__ __align__(16) uint16_t pf_k1[kTileElems];
+__shared__ __align__(16) uint16_t pf_k2[kTileElems];
+__shared__ __align__(16) uint16_t pf_k3[kTileElems];
+__shared__ __align__(16) uint16_t pf_v0[kTileElems];
+__shared__ __align__(16) uint16_t pf_v1[kTileElems];
+__shared__ __align__(16) uint16_t pf_v2[kTileElems];
+__shared__ __align__(16) uint16_t pf_v3[kTileElems];
+static_assert(kStages == 4, "the tile loop below is written out for four stages");
+
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+__global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(PrefillParams a) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int tid = threadIdx.x;
   const int ntile = (a.chunk + kPTok - 1) / kPTok;
-  // XCD-aware numbering: the tiles of one unit run on one XCD, one after another.
+  // XCD-aware numbering: the token tiles of one unit run on one XCD.
   const int bid = blockIdx.x;
   const int xcd = bid % kXcds, slot = bid / kXcds;
   const int unit = (slot / ntile) * kXcds + xcd;
@@ -133,201 +193,320 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_attn_kernel(PrefillParam
   const int np0 = fits ? a.n_pend[b] : 0;
 
   // segments of this branch (named, not indexed, so they stay in scalar registers)
+  const int nchunk = fits ? min(tok0 + kPTok, a.chunk) : 0;  // chunk keys any row here sees
   PSeg seg0, seg1, seg2;
   if (anchor) {
-    const int nb = min(max(a.n_bank[b], 0), kBank);
-    seg0 = {a.bank_k + sgi * kBank * kDim, a.bank_v + sgi * kBank * kDim, nb, 0};
-    seg1 = {a.pend_k + sgi * kBlock * kDim, a.pend_v + sgi * kBlock * kDim, np0, 0};
-    seg2 = {a.pend_k + (sgi * kBlock + np0) * kDim, a.pend_v + (sgi * kBlock + np0) * kDim,
-            tok0 + ntok, 2};
+    const int nb = fits ? min(max(a.n_bank[b], 0), kBank) : 0;
+    seg0 = make_pseg(a.bank_k + sgi * kBank * kDim, a.bank_v + sgi * kBank * kDim, nb, kDim, 0);
+    seg1 = make_pseg(a.pend_k + sgi * kBlock * kDim, a.pend_v + sgi * kBlock * kDim, np0, kDim, 0);
+    seg2 = make_pseg(a.pend_k + (sgi * kBlock + np0) * kDim,
+                     a.pend_v + (sgi * kBlock + np0) * kDim, nchunk, kDim, 2);
   } else {
-    const int nw = min(max(p0 + 1, 0), kWindow);
-    seg0 = {a.win_k + sgi * kWindow * kDim, a.win_v + sgi * kWindow * kDim, nw, 1};
-    seg1 = {nullptr, nullptr, 0, 0};
-    // chunk window rows: keys from the workspace, values straight from the input
-    seg2 = {a.wk + static_cast<size_t>(b) * a.chunk * kGroups * kDim + g * kDim,
-            a.v_win + static_cast<size_t>(b) * a.chunk * kGroups * kDim + g * kDim,
-            tok0 + ntok, 2};
+    const int nw = fits ? min(max(p0 + 1, 0), kWindow) : 0;
+    seg0 = make_pseg(a.win_k + sgi * kWindow * kDim, a.win_v + sgi * kWindow * kDim, nw, kDim, 1);
+    seg1 = seg0;
+    seg1.n = 0;
+    // chunk window rows: keys from the workspace, values straight from the input,
+    // both in the [C][4][256] layout (rows strided by the 4 groups)
+    seg2 = make_pseg(a.wk + static_cast<size_t>(b) * a.chunk * kGroups * kDim + g * kDim,
+                     a.v_win + static_cast<size_t>(b) * a.chunk * kGroups * kDim + g * kDim,
+                     nchunk, kGroups * kDim, 2);
   }
-  // (chunk rows are strided by the 4 groups of the [C][4][256] workspace/input layout)
 
-  // ---- query prep: wave w owns rows 16w .. 16w+15 = tokens 4w .. 4w+3, heads 0..3
-  for (int r = 0; r < kPRowsWave; ++r) {
-    const int row = wave * kPRowsWave + r;
-    const int tl = row / kHeadsPerGroup, h = row % kHeadsPerGroup;
-    uint2 o = make_uint2(0, 0);
-    if (tl < ntok && fits) {
-      const int tok = tok0 + tl;
-      const uint16_t *q = (anchor ? a.q_rma : a.q_win) +
-                          ((static_cast<size_t>(b) * a.chunk + tok) * kHeads + g * kHeadsPerGroup + h) * kDim;
-      const uint2 raw = *reinterpret_cast<const uint2 *>(q + 4 * lane);
-      float x[4] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y)};
-      float c, sn;
-      rope_cos_sin(a.rope_ratio, p0 + 1 + tok, lane, c, sn);
-      norm_rope_head(x, anchor ? a.gq_rma : a.gq_win, a.eps, c, sn, lane);
-      o.x = pack_bf16x2(x[0] * kPQScale, x[1] * kPQScale);
-      o.y = pack_bf16x2(x[2] * kPQScale, x[3] * kPQScale);
-    }
-    *reinterpret_cast<uint2 *>(&q_lds[row][4 * lane]) = o;
-  }
-  __syncthreads();
-  const int rl = lane & 15, kg = lane >> 4;  // lane's query row (within the wave) and key group
-  bf16x8 qb[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s)
-    qb[s] = pbitcast<bf16x8>(
-        *reinterpret_cast<const uint4 *>(&q_lds[wave * kPRowsWave + rl][32 * s + 8 * kg]));
-  // this lane's query token and its position
-  const int my_tl = (wave * kPRowsWave + rl) / kHeadsPerGroup;
-  const int my_tok = tok0 + my_tl;
-  const int my_pos = p0 + 1 + my_tok;
-  const bool my_row_ok = my_tl < ntok && fits;
-
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 acc[16];
-#pragma unroll
-  for (int d = 0; d < 16; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // staging role: key (tid / 16), dims 16 * (tid % 16) .. +16
-  const int sk = tid >> 4, sd = (tid & 15) * 16;
-
-  // tile list: segment s contributes ceil(n / 16) tiles; chunk tiles past this
-  // workgroup's last token are invisible to all its rows and are not in the list
+  // tile list: segment s contributes ceil(n / 32) tiles
   const int tl0 = (seg0.n + kPKeys - 1) / kPKeys;
   const int tl1 = (seg1.n + kPKeys - 1) / kPKeys;
   const int tl2 = (seg2.n + kPKeys - 1) / kPKeys;
   const int total = tl0 + tl1 + tl2;
-  const size_t stride2 = anchor ? kDim : static_cast<size_t>(kGroups) * kDim;
 
-  // Global -> registers for tile t (all values wave-uniform except the lane offset).
-  uint4 kr0, kr1, vr0, vr1;
-#define PREFILL_LOAD_TILE(t_)                                                                 \
-  {                                                                                           \
-    const int t__ = (t_);                                                                     \
-    const int si = t__ < tl0 ? 0 : (t__ < tl0 + tl1 ? 1 : 2);                                 \
-    const int key = (t__ - (si == 0 ? 0 : (si == 1 ? tl0 : tl0 + tl1))) * kPKeys + sk;        \
-    const uint16_t *kb = si == 0 ? seg0.k : (si == 1 ? seg1.k : seg2.k);                      \
-    const uint16_t *vb = si == 0 ? seg0.v : (si == 1 ? seg1.v : seg2.v);                      \
-    const int n = si == 0 ? seg0.n : (si == 1 ? seg1.n : seg2.n);                             \
-    const size_t st = si == 2 ? stride2 : static_cast<size_t>(kDim);                          \
-    kr0 = kr1 = vr0 = vr1 = make_uint4(0, 0, 0, 0);                                           \
-    if (key < n) {                                                                            \
-      const uint4 *kp = reinterpret_cast<const uint4 *>(kb + static_cast<size_t>(key) * st + sd); \
-      const uint4 *vp = reinterpret_cast<const uint4 *>(vb + static_cast<size_t>(key) * st + sd); \
-      kr0 = kp[0];                                                                            \
-      kr1 = kp[1];                                                                            \
-      vr0 = vp[0];                                                                            \
-      vr1 = vp[1];                                                                            \
-    }                                                                                         \
-  }
-  // Registers -> LDS buffer buf: K row-major, V transposed (V^T[dim][key]).
-#define PREFILL_STORE_TILE(buf_)                                                              \
-  {                                                                                           \
-    uint4 *kd = reinterpret_cast<uint4 *>(&k_lds[(buf_)][sk * kKStr + sd]);                   \
-    kd[0] = kr0;                                                                              \
-    kd[1] = kr1;                                                                              \
-    uint16_t *vt = &vt_lds[(buf_)][sd * kVtStr + sk];                                         \
-    const uint32_t w0 = vr0.x, w1 = vr0.y, w2 = vr0.z, w3 = vr0.w;                            \
-    const uint32_t w4 = vr1.x, w5 = vr1.y, w6 = vr1.z, w7 = vr1.w;                            \
-    vt[0 * kVtStr] = w0 & 0xffffu;  vt[1 * kVtStr] = w0 >> 16;                                \
-    vt[2 * kVtStr] = w1 & 0xffffu;  vt[3 * kVtStr] = w1 >> 16;                                \
-    vt[4 * kVtStr] = w2 & 0xffffu;  vt[5 * kVtStr] = w2 >> 16;                                \
-    vt[6 * kVtStr] = w3 & 0xffffu;  vt[7 * kVtStr] = w3 >> 16;                                \
-    vt[8 * kVtStr] = w4 & 0xffffu;  vt[9 * kVtStr] = w4 >> 16;                                \
-    vt[10 * kVtStr] = w5 & 0xffffu; vt[11 * kVtStr] = w5 >> 16;                               \
-    vt[12 * kVtStr] = w6 & 0xffffu; vt[13 * kVtStr] = w6 >> 16;                               \
-    vt[14 * kVtStr] = w7 & 0xffffu; vt[15 * kVtStr] = w7 >> 16;                               \
-  }
+#define PREFILL_TILE_SEG(t_, sg_, k0_)                                                       \
+  const int si_##sg_ = (t_) < tl0 ? 0 : ((t_) < tl0 + tl1 ? 1 : 2);                          \
+  const PSeg &sg_ = si_##sg_ == 0 ? seg0 : (si_##sg_ == 1 ? seg1 : seg2);                    \
+  const int k0_ = ((t_) - (si_##sg_ == 0 ? 0 : (si_##sg_ == 1 ? tl0 : tl0 + tl1))) * kPKeys;
 
-  if (total > 0) {
-    PREFILL_LOAD_TILE(0);
-    PREFILL_STORE_TILE(0);
+  // Load-to-LDS of tile t into stage st: each wave moves 4 KB of K and 4 KB of V,
+  // 1 KB (two rows) per instruction; lane L fills chunk position L % 32 of row
+  // 2i + L / 32, i.e. fetches the chunk that the swizzle puts there.  Rows past
+  // the segment's end read as zero.
+  const int dma_row_lo = lane >> 5, dma_pos = lane & 31;
+#define PREFILL_ISSUE_TILE(t_, kdst_, vdst_)                                                 \
+  {                                                                                          \
+    PREFILL_TILE_SEG(t_, isg, ik0)                                                           \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                          \
+      const int pr = 4 * wave + i;                                                           \
+      const int row = 2 * pr + dma_row_lo;                                                   \
+      const int roff = (ik0 + row) * isg.stride;                                             \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(                                              \
+          isg.k, (lds_void *)&kdst_[pr * 2 * kDim], 16,                                      \
+          roff + ((dma_pos ^ k_swz(row)) << 4), 0, 0, 0);                                    \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(                                              \
+          isg.v, (lds_void *)&vdst_[pr * 2 * kDim], 16,                                      \
+          roff + ((dma_pos ^ v_swz(row)) << 4), 0, 0, 0);                                    \
+    }                                                                                        \
   }
-  __syncthreads();
-  for (int t = 0; t < total; ++t) {
-    const int buf = t & 1;
-    const bool more = t + 1 < total;
-    if (more) PREFILL_LOAD_TILE(t + 1);
-    const int si = t < tl0 ? 0 : (t < tl0 + tl1 ? 1 : 2);
-    const int ck0 = (t - (si == 0 ? 0 : (si == 1 ? tl0 : tl0 + tl1))) * kPKeys;
-    const int cn = si == 0 ? seg0.n : (si == 1 ? seg1.n : seg2.n);
-    const int ckind = si == 0 ? seg0.kind : (si == 1 ? seg1.kind : seg2.kind);
-    // S^T = K Q^T: lane holds keys 4kg+i (i = 0..3) of row rl
-    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-    const uint16_t *krow = &k_lds[buf][rl * kKStr + 8 * kg];
+  // Start the first tiles' loads before the query prologue.
+  if (total > 0) PREFILL_ISSUE_TILE(0, pf_k0, pf_v0);
+  if (total > 1) PREFILL_ISSUE_TILE(1, pf_k1, pf_v1);
+  if (total > 2) PREFILL_ISSUE_TILE(2, pf_k2, pf_v2);
+
+  // ---- query: lane l holds row rl = l % 32 of this wave (token 8w + rl/4, head
+  // rl % 4), dims 16s + 8hh .. +7 for s = 0..15 -- the B operand layout of
+  // v_mfma_f32_32x32x16_bf16.  Normalised, rotated and scaled by log2(e)/16 here.
+  const int rl = lane & 31, hh = lane >> 5;
+  const int my_tl = wave * (kPRowsWave / kHeadsPerGroup) + rl / kHeadsPerGroup;
+  const int my_head = rl % kHeadsPerGroup;
+  const int my_tok = tok0 + my_tl;
+  const int my_pos = p0 + 1 + my_tok;
+  const bool my_row_ok = my_tl < ntok && fits;
+  bf16x8 qb[16];
+  {
+    const uint16_t *qrow =
+        (anchor ? a.q_rma : a.q_win) +
+        ((static_cast<size_t>(b) * a.chunk + min(my_tok, a.chunk - 1)) * kHeads +
+         g * kHeadsPerGroup + my_head) * kDim + 8 * hh;
+    const float *gam = (anchor ? a.gq_rma : a.gq_win) + 8 * hh;
+    u32x4 raw[16];
+    float ss = 0.f;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const bf16x8 kv = pbitcast<bf16x8>(*reinterpret_cast<const uint4 *>(krow + 32 * s));
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qb[s], sc, 0, 0, 0);
-    }
+    for (int s = 0; s < 16; ++s) {
+      raw[s] = *reinterpret_cast<const u32x4 *>(qrow + 16 * s);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = ck0 + 4 * kg + i;
-      bool vis = my_row_ok && key < cn;
-      if (ckind == 1) {
-        const int kp = p0 - ((p0 - key) & (kWindow - 1));
-        vis = vis && kp >= 0 && kp >= my_pos - (kWindow - 1);
-      } else if (ckind == 2) {
-        vis = vis && key <= my_tok;
+      for (int e = 0; e < 4; ++e) {
+        const float lo = bf16_lo(raw[s][e]), hi = bf16_hi(raw[s][e]);
+        ss += lo * lo + hi * hi;
       }
-      if (!vis) sc[i] = -INFINITY;
     }
-    float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float m_new = fmaxf(m_run, mt);
-    float alpha = 1.f;
-    uint32_t pw0 = 0, pw1 = 0;
-    float psum = 0.f;
-    if (m_new != -INFINITY) {
-      alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      const uint32_t q0 = f32_to_bf16(__builtin_amdgcn_exp2f(sc[0] - m_new));
-      const uint32_t q1 = f32_to_bf16(__builtin_amdgcn_exp2f(sc[1] - m_new));
-      const uint32_t q2 = f32_to_bf16(__builtin_amdgcn_exp2f(sc[2] - m_new));
-      const uint32_t q3 = f32_to_bf16(__builtin_amdgcn_exp2f(sc[3] - m_new));
-      psum = (bf16_to_f32(q0) + bf16_to_f32(q1)) + (bf16_to_f32(q2) + bf16_to_f32(q3));
-      pw0 = q0 | (q1 << 16);
-      pw1 = q2 | (q3 << 16);
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    const s16x4 pb = pbitcast<s16x4>(make_uint2(pw0, pw1));
-    // O^T += V^T P^T: lane holds dims 16db + 4kg + i of row rl
+    ss += __shfl_xor(ss, 32, 64);
+    const float inv = 1.0f / sqrtf(ss * (1.0f / kDim) + a.eps);
+    // dims past the rotary part: scale and pack in place
 #pragma unroll
-    for (int db = 0; db < 16; ++db) {
-      const uint2 w = *reinterpret_cast<const uint2 *>(&vt_lds[buf][(db * 16 + rl) * kVtStr + 4 * kg]);
-      acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pbitcast<s16x4>(w), pb, acc[db] * alpha,
-                                                          0, 0, 0);
+    for (int s = 4; s < 16; ++s) {
+      const float4 g0 = *reinterpret_cast<const float4 *>(gam + 16 * s);
+      const float4 g1 = *reinterpret_cast<const float4 *>(gam + 16 * s + 4);
+      const float gm[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = bf16_lo(raw[s][e]) * inv * gm[2 * e];
+        const float hi = bf16_hi(raw[s][e]) * inv * gm[2 * e + 1];
+        w[e] = my_row_ok ? pack_bf16x2(lo * kPQScale, hi * kPQScale) : 0u;
+      }
+      qb[s] = pbitcast<bf16x8>(w);
     }
-    if (more) PREFILL_STORE_TILE(buf ^ 1);
-    __syncthreads();
+    // rotary dims i = 16s + 8hh + e (s = 0, 1) pair with i + 32 (chunk s + 2, same
+    // lane); theta_i = r^i, formed from r^(16s + 8hh) by repeated multiplication
+    const double r8 = a.rope_ratio * a.rope_ratio * a.rope_ratio * a.rope_ratio *
+                      a.rope_ratio * a.rope_ratio * a.rope_ratio * a.rope_ratio;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const float4 ga0 = *reinterpret_cast<const float4 *>(gam + 16 * s);
+      const float4 ga1 = *reinterpret_cast<const float4 *>(gam + 16 * s + 4);
+      const float4 gb0 = *reinterpret_cast<const float4 *>(gam + 16 * (s + 2));
+      const float4 gb1 = *reinterpret_cast<const float4 *>(gam + 16 * (s + 2) + 4);
+      const float gma[8] = {ga0.x, ga0.y, ga0.z, ga0.w, ga1.x, ga1.y, ga1.z, ga1.w};
+      const float gmb[8] = {gb0.x, gb0.y, gb0.z, gb0.w, gb1.x, gb1.y, gb1.z, gb1.w};
+      double theta = (s ? r8 * r8 : 1.0) * (hh ? r8 : 1.0);
+      u32x4 wa, wb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float c, sn;
+        rope_cos_sin_theta(theta, my_pos, c, sn);
+        theta *= a.rope_ratio;
+        const uint32_t ra = raw[s][e >> 1], rb = raw[s + 2][e >> 1];
+        const float x1 = ((e & 1) ? bf16_hi(ra) : bf16_lo(ra)) * inv * gma[e];
+        const float x2 = ((e & 1) ? bf16_hi(rb) : bf16_lo(rb)) * inv * gmb[e];
+        const float y1 = (x1 * c - x2 * sn) * kPQScale;
+        const float y2 = (x2 * c + x1 * sn) * kPQScale;
+        const uint32_t b1 = my_row_ok ? f32_to_bf16(y1) : 0u;
+        const uint32_t b2 = my_row_ok ? f32_to_bf16(y2) : 0u;
+        if (e & 1) {
+          wa[e >> 1] |= b1 << 16;
+          wb[e >> 1] |= b2 << 16;
+        } else {
+          wa[e >> 1] = b1;
+          wb[e >> 1] = b2;
+        }
+      }
+      qb[s] = pbitcast<bf16x8>(wa);
+      qb[s + 2] = pbitcast<bf16x8>(wb);
+    }
   }
-#undef PREFILL_LOAD_TILE
-#undef PREFILL_STORE_TILE
+  // keep the query operands in AGPRs (read-only MFMA B operands), leaving the VGPRs
+  // to the accumulators and the LDS operand reads
+#pragma unroll
+  for (int s = 0; s < 16; ++s) asm volatile("" : "+a"(qb[s]));
 
-  // epilogue: row rl of this wave = token my_tok, head h
-  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
-  const int h = (wave * kPRowsWave + rl) % kHeadsPerGroup;
-  const int head = g * kHeadsPerGroup + h;
+  float m_ref = -INFINITY, l_run = 0.f;  // reference maximum (log2 units) and row sum
+  f32x16 acc[kDim / 32];
+#pragma unroll
+  for (int d = 0; d < kDim / 32; ++d)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[d][r] = 0.f;
+
+  // the tokens this wave's rows hold (rows past ntok compute but are not stored)
+  const int wave_first_tok = tok0 + wave * (kPRowsWave / kHeadsPerGroup);
+  const int wave_last_tok = wave_first_tok + kPRowsWave / kHeadsPerGroup - 1;
+  const bool wave_live = fits && wave * (kPRowsWave / kHeadsPerGroup) < ntok;
+  // window rows see ring slots whose age (p0 - slot) mod 1024 is at most age_max;
+  // wave_age_max is the smallest of those over the wave's rows
+  const int age_max = min(p0, kWindow - 2 - my_tok);
+  const int wave_age_max = min(p0, kWindow - 2 - wave_last_tok);
+
+  // LDS operand addresses (elements).  K (A of S^T = K Q^T): key rl, chunk 2s + hh.
+  // V^T (A of O^T = V^T P^T) by transposed reads: lane i of 16-lane group G points
+  // at key 16j + 8r + 4(G/2) + i/4, dims 32d + 16(G%2) + 4(i%4) .. +3; the read
+  // hands lane i dim 32d + 16(G%2) + i of the four keys 16j + 8r + 4(G/2) + 0..3.
+  // chunk 2s + hh of key rl sits at 8 (s / 4) + ((2 (s % 4) + hh) ^ (rl & 7))
+  int k_addr[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) k_addr[c] = rl * kDim + (((2 * c + hh) ^ k_swz(rl)) << 3);
+  const int vg = lane >> 4, vi = lane & 15;
+  const int v_key = 4 * (vg >> 1) + (vi >> 2);  // + 16j + 8r (keeps key & 3)
+  const int v_dim = 16 * (vg & 1) + 4 * (vi & 3);  // + 32d
+  const int v_sw = v_swz(v_key);
+  // chunk of dim 32d + v_dim is 4d + (v_dim >> 3); the swizzle flips bits 1-2
+  const int v_even = v_key * kDim + ((((v_dim >> 3)) ^ v_sw) << 3) + (v_dim & 7);
+  const int v_odd = v_key * kDim + (((4 + (v_dim >> 3)) ^ v_sw) << 3) + (v_dim & 7);
+
+  // One key tile on this wave's 32 rows.  S^T = K Q^T in two independent MFMA
+  // chains (even / odd dim steps); mask; online softmax against a reference
+  // maximum that moves only when a row's maximum grows by more than kPTau (so P
+  // <= 2^kPTau and the 128 accumulators are rarely rescaled); O^T += V^T P^T.
+#define PREFILL_COMPUTE_TILE(t, kt, vt)                                                      \
+  {                                                                                          \
+    PREFILL_TILE_SEG(t, csg, k0)                                                             \
+    const int kind = csg.kind;                                                               \
+    const int n = csg.n;                                                                     \
+    /* chunk tiles that start after this wave's last token are invisible to it */            \
+    if (wave_live && !(kind == 2 && k0 > wave_last_tok)) {                                   \
+      f32x16 sc, sc1;                                                                        \
+      _Pragma("unroll") for (int s = 0; s < 16; s += 2) {                                    \
+        const bf16x8 k0v = pbitcast<bf16x8>(                                                 \
+            *reinterpret_cast<const u32x4 *>(kt + k_addr[s & 3] + 64 * (s >> 2)));           \
+        const bf16x8 k1v = pbitcast<bf16x8>(                                                 \
+            *reinterpret_cast<const u32x4 *>(kt + k_addr[(s + 1) & 3] + 64 * (s >> 2)));     \
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0v, qb[s], s ? sc : f32x16{}, 0, 0, 0); \
+        sc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1v, qb[s + 1], s ? sc1 : f32x16{}, 0, \
+                                                      0, 0);                                 \
+      }                                                                                      \
+      _Pragma("unroll") for (int r = 0; r < 16; ++r) sc[r] += sc1[r];                        \
+      /* key of register r: kl + 8(r/4) + r%4 */                                             \
+      const int kl = k0 + 4 * hh;                                                            \
+      if (kind == 1) {                                                                       \
+        /* ring ages in this tile run down from A (no wrap when A >= 31); every row of */    \
+        /* the wave sees ages up to wave_age_max */                                          \
+        const int A = (p0 - k0) & (kWindow - 1);                                             \
+        if (A < kPKeys - 1 || A > wave_age_max) {                                            \
+          const int age0 = p0 - kl;                                                          \
+          _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                   \
+            const int age = (age0 - (8 * (r >> 2) + (r & 3))) & (kWindow - 1);              \
+            sc[r] = age <= age_max ? sc[r] : -INFINITY;                                      \
+          }                                                                                  \
+        }                                                                                    \
+      } else if (kind == 2) {                                                                \
+        if (k0 + kPKeys - 1 > wave_first_tok) {                                              \
+          _Pragma("unroll") for (int r = 0; r < 16; ++r) sc[r] =                             \
+              kl + 8 * (r >> 2) + (r & 3) <= my_tok ? sc[r] : -INFINITY;                     \
+        }                                                                                    \
+      } else if (k0 + kPKeys > n) {                                                          \
+        _Pragma("unroll") for (int r = 0; r < 16; ++r) sc[r] =                               \
+            kl + 8 * (r >> 2) + (r & 3) < n ? sc[r] : -INFINITY;                             \
+      }                                                                                      \
+      float mt = sc[0];                                                                      \
+      _Pragma("unroll") for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sc[r]);                  \
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));                                                \
+      /* move the reference only past kPTau (covers m_ref = -inf, mt finite) */             \
+      const bool move = mt > m_ref + kPTau;                                                  \
+      const float m_use = move ? mt : m_ref;                                                 \
+      /* rows with nothing accumulated yet need no rescale */                                \
+      const float alpha =                                                                    \
+          (move && m_ref != -INFINITY) ? __builtin_amdgcn_exp2f(m_ref - m_use) : 1.f;        \
+      if (__any(alpha != 1.f)) {                                                             \
+        _Pragma("unroll") for (int d = 0; d < kDim / 32; ++d)                                \
+            _Pragma("unroll") for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;               \
+        l_run *= alpha;                                                                      \
+      }                                                                                      \
+      m_ref = m_use;                                                                         \
+      /* masked scores are -inf: exp2 gives 0; a row with no reference yet has no */        \
+      /* visible key in this tile either */                                                  \
+      const float m_sub = m_use == -INFINITY ? 0.f : m_use;                                  \
+      u32x4 pw[2];                                                                           \
+      _Pragma("unroll") for (int r = 0; r < 16; r += 2) {                                    \
+        const uint32_t e = pack_bf16x2_hw(__builtin_amdgcn_exp2f(sc[r] - m_sub),             \
+                                          __builtin_amdgcn_exp2f(sc[r + 1] - m_sub));        \
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(pbitcast<bf16x2_t>(e), kOnesBf16x2, l_run,   \
+                                                false);                                      \
+        pw[r >> 3][(r & 7) >> 1] = e;                                                        \
+      }                                                                                      \
+      /* O^T += V^T P^T: lane holds dims 32d + 8(r/4) + 4hh + r%4 of row rl */               \
+      _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                        \
+        const bf16x8 pb = pbitcast<bf16x8>(pw[j]);                                           \
+        _Pragma("unroll") for (int d = 0; d < kDim / 32; ++d) {                              \
+          const int vb = ((d & 1) ? v_odd + 32 * (d - 1) : v_even + 32 * d) + 16 * j * kDim; \
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + vb)); \
+          const s16x4_t hi =                                                                 \
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + vb + 8 * kDim));    \
+          const s16x4_t lohi[2] = {lo, hi};                                                  \
+          acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pbitcast<bf16x8>(lohi), pb,       \
+                                                           acc[d], 0, 0, 0);                 \
+        }                                                                                    \
+      }                                                                                      \
+    }                                                                                        \
+  }
+
+  // One key tile: wait for its loads (this wave's, then everyone's via the
+  // barrier), start the tile three ahead into the stage tile t - 1 used, compute.
+#define PREFILL_STEP(t_, kt, vt, knext, vnext)                                               \
+  if ((t_) < total) {                                                                        \
+    const int t = (t_);                                                                      \
+    /* this wave's loads of tile t are done once at most the later tiles' remain */          \
+    const int later = min(total - 1 - t, kStages - 2);                                       \
+    if (later >= 2)                                                                          \
+      wait_vm_barrier<2 * kDmaPerTile>();                                                    \
+    else if (later == 1)                                                                     \
+      wait_vm_barrier<kDmaPerTile>();                                                        \
+    else                                                                                     \
+      wait_vm_barrier<0>();                                                                  \
+    if (t + kStages - 1 < total) PREFILL_ISSUE_TILE(t + kStages - 1, knext, vnext);          \
+    PREFILL_COMPUTE_TILE(t, kt, vt)                                                          \
+  }
+
+  for (int t0 = 0; t0 < total; t0 += kStages) {
+    PREFILL_STEP(t0, pf_k0, pf_v0, pf_k3, pf_v3)
+    PREFILL_STEP(t0 + 1, pf_k1, pf_v1, pf_k0, pf_v0)
+    PREFILL_STEP(t0 + 2, pf_k2, pf_v2, pf_k1, pf_v1)
+    PREFILL_STEP(t0 + 3, pf_k3, pf_v3, pf_k2, pf_v2)
+  }
+#undef PREFILL_STEP
+#undef PREFILL_COMPUTE_TILE
+#undef PREFILL_TILE_SEG
+#undef PREFILL_ISSUE_TILE
+
+  // epilogue: row rl = token my_tok, head my_head; lanes rl and rl + 32 hold the
+  // two halves of each 8-dim run
+  float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (my_tl < ntok) {
+    const int head = g * kHeadsPerGroup + my_head;
     uint16_t *o = (anchor ? a.o_rma : a.o_win) +
                   ((static_cast<size_t>(b) * a.chunk + my_tok) * kHeads + head) * kDim;
-    const bool empty = m_run == -INFINITY;
+    const bool empty = m_ref == -INFINITY;
     const float inv = empty ? 0.f : 1.f / l_tot;
 #pragma unroll
-    for (int db = 0; db < 16; ++db) {
-      uint2 ov = make_uint2(0, 0);
-      if (!empty) {
-        ov.x = pack_bf16x2(acc[db][0] * inv, acc[db][1] * inv);
-        ov.y = pack_bf16x2(acc[db][2] * inv, acc[db][3] * inv);
+    for (int d = 0; d < kDim / 32; ++d) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint2 ov = make_uint2(0u, 0u);
+        if (!empty) {
+          ov.x = pack_bf16x2_hw(acc[d][4 * q] * inv, acc[d][4 * q + 1] * inv);
+          ov.y = pack_bf16x2_hw(acc[d][4 * q + 2] * inv, acc[d][4 * q + 3] * inv);
+        }
+        *reinterpret_cast<uint2 *>(o + 32 * d + 8 * q + 4 * hh) = ov;
       }
-      *reinterpret_cast<uint2 *>(o + db * 16 + 4 * kg) = ov;
     }
-    if (kg == 0) {
+    if (hh == 0) {
       float *lse = (anchor ? a.lse_rma : a.lse_win) +
                    (static_cast<size_t>(b) * a.chunk + my_tok) * kHeads + head;
-      *lse = empty ? -INFINITY : (m_run + log2f(l_tot)) * kPLn2;
+      *lse = empty ? -INFINITY : (m_ref + log2f(l_tot)) * kPLn2;
     }
   }
 }

@@ -60,17 +60,10 @@ inline double rope_ratio(float base) { return __builtin_pow(static_cast<double>(
 // rf = fp32(r) and the remainder d = r - rf; sin and cos of rf are taken in FP32
 // and corrected to first order in d (|d| <= 2^-22, so the second-order term is
 // below FP32 resolution).
-__device__ __forceinline__ void rope_cos_sin(double ratio, int p, int lane, float &c, float &s) {
+__device__ __forceinline__ void rope_cos_sin_theta(double theta, int p, float &c, float &s) {
   constexpr double kTwoPiHi = 6.283185307179586232;       // 2*pi rounded to double
   constexpr double kTwoPiLo = 2.4492935982947064e-16;      // 2*pi - kTwoPiHi
   constexpr double kInvTwoPi = 0.15915494309189534561;
-  int i = lane & (kRope / 2 - 1);
-  double theta = 1.0, sq = ratio;
-  while (i) {
-    if (i & 1) theta *= sq;
-    sq *= sq;
-    i >>= 1;
-  }
   const double phi = static_cast<double>(p) * theta;
   const double k = rint(phi * kInvTwoPi);
   double r = fma(-k, kTwoPiHi, phi);
@@ -80,6 +73,17 @@ __device__ __forceinline__ void rope_cos_sin(double ratio, int p, int lane, floa
   const float s0 = sinf(rf), c0 = cosf(rf);
   s = fmaf(c0, d, s0);
   c = fmaf(-s0, d, c0);
+}
+
+__device__ __forceinline__ void rope_cos_sin(double ratio, int p, int lane, float &c, float &s) {
+  int i = lane & (kRope / 2 - 1);
+  double theta = 1.0, sq = ratio;
+  while (i) {
+    if (i & 1) theta *= sq;
+    sq *= sq;
+    i >>= 1;
+  }
+  rope_cos_sin_theta(theta, p, c, s);
 }
 
 // RMS-normalise one 256-wide head held by a wave (lane l holds dims 4l..4l+3),
