@@ -135,12 +135,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi) {
 }
 
 // LDS tiles are row-major (32 keys x 32 sixteen-byte chunks) with the chunk index
-// XOR-swizzled by the key, so that the MFMA operand reads below hit 8 (K) or 16
-// (V, transposed reads) distinct bank groups:
-//   K chunk c of key k sits at chunk position c ^ (k & 7)
-//   V chunk c of key k sits at chunk position c ^ (2 (k & 3))
-__device__ __forceinline__ int k_swz(int key) { return key & 7; }
-__device__ __forceinline__ int v_swz(int key) { return 2 * (key & 3); }
+// XOR-swizzled by the key, so that the MFMA operand reads below spread over all
+// banks (gfx950 LDS serves 256 bytes per clock: 16 lanes of a 16-byte read, 32
+// lanes of an 8-byte transposed read):
+//   K chunk c of key k sits at chunk position c ^ (k & 15)
+//   V chunk c of key k sits at chunk position c ^ (4 (k & 3))
+__device__ __forceinline__ int k_swz(int key) { return key & 15; }
+__device__ __forceinline__ int v_swz(int key) { return 4 * (key & 3); }
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -356,17 +357,19 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(PrefillParams a
   // V^T (A of O^T = V^T P^T) by transposed reads: lane i of 16-lane group G points
   // at key 16j + 8r + 4(G/2) + i/4, dims 32d + 16(G%2) + 4(i%4) .. +3; the read
   // hands lane i dim 32d + 16(G%2) + i of the four keys 16j + 8r + 4(G/2) + 0..3.
-  // chunk 2s + hh of key rl sits at 8 (s / 4) + ((2 (s % 4) + hh) ^ (rl & 7))
-  int k_addr[4];
+  // chunk 2s + hh of key rl sits at 16 (s / 8) + ((2 (s % 8) + hh) ^ (rl & 15))
+  int k_addr[8];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) k_addr[c] = rl * kDim + (((2 * c + hh) ^ k_swz(rl)) << 3);
+  for (int c = 0; c < 8; ++c) k_addr[c] = rl * kDim + (((2 * c + hh) ^ k_swz(rl)) << 3);
   const int vg = lane >> 4, vi = lane & 15;
   const int v_key = 4 * (vg >> 1) + (vi >> 2);  // + 16j + 8r (keeps key & 3)
   const int v_dim = 16 * (vg & 1) + 4 * (vi & 3);  // + 32d
-  const int v_sw = v_swz(v_key);
-  // chunk of dim 32d + v_dim is 4d + (v_dim >> 3); the swizzle flips bits 1-2
-  const int v_even = v_key * kDim + ((((v_dim >> 3)) ^ v_sw) << 3) + (v_dim & 7);
-  const int v_odd = v_key * kDim + (((4 + (v_dim >> 3)) ^ v_sw) << 3) + (v_dim & 7);
+  // chunk 4d + x (x = v_dim / 8) sits at 4 (d ^ q) + x with q = key & 3, i.e. at the
+  // lane's base for d % 4 plus 16 chunks (128 elements) per d / 4
+  int v_addr[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    v_addr[c] = v_key * kDim + ((4 * (c ^ (v_key & 3)) + (v_dim >> 3)) << 3) + (v_dim & 7);
 
   // One key tile on this wave's 32 rows.  S^T = K Q^T in two independent MFMA
   // chains (even / odd dim steps); mask; online softmax against a reference
@@ -379,15 +382,35 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(PrefillParams a
     const int n = csg.n;                                                                     \
     /* chunk tiles that start after this wave's last token are invisible to it */            \
     if (wave_live && !(kind == 2 && k0 > wave_last_tok)) {                                   \
+      /* K operands read eight dim steps ahead of their MFMAs (the scheduler would */       \
+      /* otherwise issue each read just before its use and wait on every one) */             \
+      u32x4 kf[8];                                                                           \
+      _Pragma("unroll") for (int s = 0; s < 8; ++s) kf[s] =                                  \
+          *reinterpret_cast<const u32x4 *>(kt + k_addr[s & 7] + 128 * (s >> 3));              \
+      __builtin_amdgcn_sched_barrier(0);                                                     \
       f32x16 sc, sc1;                                                                        \
-      _Pragma("unroll") for (int s = 0; s < 16; s += 2) {                                    \
-        const bf16x8 k0v = pbitcast<bf16x8>(                                                 \
-            *reinterpret_cast<const u32x4 *>(kt + k_addr[s & 3] + 64 * (s >> 2)));           \
-        const bf16x8 k1v = pbitcast<bf16x8>(                                                 \
-            *reinterpret_cast<const u32x4 *>(kt + k_addr[(s + 1) & 3] + 64 * (s >> 2)));     \
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0v, qb[s], s ? sc : f32x16{}, 0, 0, 0); \
-        sc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1v, qb[s + 1], s ? sc1 : f32x16{}, 0, \
-                                                      0, 0);                                 \
+      _Pragma("unroll") for (int s = 0; s < 8; s += 2) {                                     \
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pbitcast<bf16x8>(kf[s]), qb[s],         \
+                                                     s ? sc : f32x16{}, 0, 0, 0);            \
+        kf[s] = *reinterpret_cast<const u32x4 *>(kt + k_addr[s & 7] + 128 * ((s + 8) >> 3));  \
+        sc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pbitcast<bf16x8>(kf[s + 1]), qb[s + 1], \
+                                                      s ? sc1 : f32x16{}, 0, 0, 0);          \
+        kf[s + 1] = *reinterpret_cast<const u32x4 *>(kt + k_addr[(s + 1) & 7] +              \
+                                                     128 * ((s + 9) >> 3));                   \
+      }                                                                                      \
+      __builtin_amdgcn_sched_barrier(0);                                                     \
+      _Pragma("unroll") for (int s = 8; s < 16; s += 2) {                                    \
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pbitcast<bf16x8>(kf[s - 8]), qb[s], sc, \
+                                                     0, 0, 0);                               \
+        sc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pbitcast<bf16x8>(kf[s - 7]),           \
+                                                      qb[s + 1], sc1, 0, 0, 0);              \
+      }                                                                                      \
+      /* first half of the V^T operands: independent of the softmax, read now */            \
+      s16x4_t vf[2 * (kDim / 32)];                                                           \
+      _Pragma("unroll") for (int d = 0; d < kDim / 32; ++d) {                                \
+        const int vb = v_addr[d & 3] + 128 * (d >> 2);                     \
+        vf[2 * d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + vb));         \
+        vf[2 * d + 1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + vb + 8 * kDim)); \
       }                                                                                      \
       _Pragma("unroll") for (int r = 0; r < 16; ++r) sc[r] += sc1[r];                        \
       /* key of register r: kl + 8(r/4) + r%4 */                                             \
@@ -412,9 +435,16 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(PrefillParams a
         _Pragma("unroll") for (int r = 0; r < 16; ++r) sc[r] =                               \
             kl + 8 * (r >> 2) + (r & 3) < n ? sc[r] : -INFINITY;                             \
       }                                                                                      \
-      float mt = sc[0];                                                                      \
-      _Pragma("unroll") for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sc[r]);                  \
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));                                                \
+      /* row maximum: a tree over the lane's 16 keys, then across the lane pair */          \
+      float m8[8];                                                                           \
+      _Pragma("unroll") for (int r = 0; r < 8; ++r) m8[r] = fmaxf(sc[r], sc[r + 8]);          \
+      _Pragma("unroll") for (int r = 0; r < 4; ++r) m8[r] = fmaxf(m8[r], m8[r + 4]);          \
+      float mt = fmaxf(fmaxf(m8[0], m8[2]), fmaxf(m8[1], m8[3]));                            \
+      {                                                                                      \
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt),                 \
+                                                         __float_as_uint(mt), false, false); \
+        mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));                          \
+      }                                                                                      \
       /* move the reference only past kPTau (covers m_ref = -inf, mt finite) */             \
       const bool move = mt > m_ref + kPTau;                                                  \
       const float m_use = move ? mt : m_ref;                                                 \
@@ -431,26 +461,32 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(PrefillParams a
       /* visible key in this tile either */                                                  \
       const float m_sub = m_use == -INFINITY ? 0.f : m_use;                                  \
       u32x4 pw[2];                                                                           \
-      _Pragma("unroll") for (int r = 0; r < 16; r += 2) {                                    \
-        const uint32_t e = pack_bf16x2_hw(__builtin_amdgcn_exp2f(sc[r] - m_sub),             \
-                                          __builtin_amdgcn_exp2f(sc[r + 1] - m_sub));        \
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(pbitcast<bf16x2_t>(e), kOnesBf16x2, l_run,   \
-                                                false);                                      \
-        pw[r >> 3][(r & 7) >> 1] = e;                                                        \
-      }                                                                                      \
+      _Pragma("unroll") for (int r = 0; r < 16; r += 2) pw[r >> 3][(r & 7) >> 1] =           \
+          pack_bf16x2_hw(__builtin_amdgcn_exp2f(sc[r] - m_sub),                              \
+                         __builtin_amdgcn_exp2f(sc[r + 1] - m_sub));                         \
       /* O^T += V^T P^T: lane holds dims 32d + 8(r/4) + 4hh + r%4 of row rl */               \
       _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                        \
         const bf16x8 pb = pbitcast<bf16x8>(pw[j]);                                           \
+        if (j == 1) {                                                                        \
+          _Pragma("unroll") for (int d = 0; d < kDim / 32; ++d) {                            \
+            const int vb = v_addr[d & 3] + 128 * (d >> 2) + 16 * kDim;   \
+            vf[2 * d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + vb));     \
+            vf[2 * d + 1] =                                                                  \
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + vb + 8 * kDim));  \
+          }                                                                                  \
+        }                                                                                    \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
         _Pragma("unroll") for (int d = 0; d < kDim / 32; ++d) {                              \
-          const int vb = ((d & 1) ? v_odd + 32 * (d - 1) : v_even + 32 * d) + 16 * j * kDim; \
-          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + vb)); \
-          const s16x4_t hi =                                                                 \
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + vb + 8 * kDim));    \
-          const s16x4_t lohi[2] = {lo, hi};                                                  \
+          const s16x4_t lohi[2] = {vf[2 * d], vf[2 * d + 1]};                                \
           acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pbitcast<bf16x8>(lohi), pb,       \
                                                            acc[d], 0, 0, 0);                 \
         }                                                                                    \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
       }                                                                                      \
+      /* row sums (lane-partial) of the rounded probabilities, off the MFMA path */         \
+      _Pragma("unroll") for (int q = 0; q < 8; ++q)                                          \
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pbitcast<bf16x2_t>(pw[q >> 2][q & 3]),      \
+                                                  kOnesBf16x2, l_run, false);                \
     }                                                                                        \
   }
 
