@@ -29,11 +29,17 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 # per (sequence, layer): window + bank + pending K/V, BF16
 STATE_BYTES_PER_UNIT = 2 * 4 * (1024 + 1024 + 256) * 256 * 2
+# the same rows held as 256 E4M3 codes and one FP32 scale each
+STATE_BYTES_PER_UNIT_FP8 = 2 * 4 * (1024 + 1024 + 256) * (256 + 4)
 # per (sequence, layer): one query read for both branches (they alias), two
 # outputs, two log-sum-exp rows
 IO_BYTES_PER_UNIT = 16 * 256 * 2 + 2 * 16 * 256 * 2 + 2 * 16 * 4
 METRIC = "SWA∥RMA decode steps/s ×batch and HBM GB/s (% peak) at batch 512"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attn_headline_b512_traffic.txt")
+TRAFFIC_FILES = {
+    "headline_b512": os.path.join(ROOT, "profiles", "decode_attn_headline_b512_traffic.txt"),
+    "headline_b512_fp8": os.path.join(ROOT, "profiles",
+                                      "decode_attn_fp8_headline_b512_fp8_traffic.txt"),
+}
 KERNEL_SOURCES = ("swa_memory_anchor_amd/csrc/decode_attn.hip",
                   "swa_memory_anchor_amd/csrc/rma_device.h")
 
@@ -46,12 +52,13 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(units_per_launch: int):
+def measured_traffic(workload: str, units_per_launch: int):
     """HBM bytes per launch from the committed counter summary, if it is current."""
-    if not os.path.exists(TRAFFIC_FILE):
+    path = TRAFFIC_FILES.get(workload)
+    if path is None or not os.path.exists(path):
         return None
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if "=" in line and not line.lstrip().startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
@@ -67,7 +74,10 @@ def cpu_baseline(wl, budget_s: float, max_units: int):
     import numpy as np
 
     import oracle as O
+    from oracle import fp8_ref as F
     from synth import workloads as W
+
+    fp8 = wl.extra.get("kv") == "e4m3"
 
     try:
         from threadpoolctl import threadpool_info
@@ -88,15 +98,25 @@ def cpu_baseline(wl, budget_s: float, max_units: int):
             print(f"cpu_baseline: {units} units, {spent:.1f} s oracle time", file=sys.stderr,
                   flush=True)
         b, layer = int(rng.integers(0, wl.batch)), int(rng.integers(0, wl.layers))
-        s = W.decode_state_np(wl, layer, b)
         q = W.q_np(wl, layer, b)
         g = gains.setdefault(layer, W.gains(wl, layer))
-        t0 = time.perf_counter()
-        O.decode_one(list(s["win_k"]), list(s["win_v"]), q, g["gq_win"], s["pos"], wl.eps,
-                     wl.rope_base)
-        keys = [np.concatenate([s["bank_k"][i], s["pend_k"][i]]) for i in range(4)]
-        vals = [np.concatenate([s["bank_v"][i], s["pend_v"][i]]) for i in range(4)]
-        O.decode_one(keys, vals, q, g["gq_rma"], s["pos"], wl.eps, wl.rope_base)
+        if fp8:
+            s = {nm: W.kv_fp8_np(wl, layer, nm, b) for nm in W.KV_NAMES}
+            t0 = time.perf_counter()
+            rows = {nm: F.dequantize(*s[nm]) for nm in W.KV_NAMES}
+            F.decode_one(list(rows["win_k"]), list(rows["win_v"]), q, g["gq_win"], wl.position,
+                         wl.eps, wl.rope_base)
+            keys = [np.concatenate([rows["bank_k"][i], rows["pend_k"][i]]) for i in range(4)]
+            vals = [np.concatenate([rows["bank_v"][i], rows["pend_v"][i]]) for i in range(4)]
+            F.decode_one(keys, vals, q, g["gq_rma"], wl.position, wl.eps, wl.rope_base)
+        else:
+            s = W.decode_state_np(wl, layer, b)
+            t0 = time.perf_counter()
+            O.decode_one(list(s["win_k"]), list(s["win_v"]), q, g["gq_win"], s["pos"], wl.eps,
+                         wl.rope_base)
+            keys = [np.concatenate([s["bank_k"][i], s["pend_k"][i]]) for i in range(4)]
+            vals = [np.concatenate([s["bank_v"][i], s["pend_v"][i]]) for i in range(4)]
+            O.decode_one(keys, vals, q, g["gq_rma"], s["pos"], wl.eps, wl.rope_base)
         spent += time.perf_counter() - t0
         units += 1
     units_per_s = units / spent
@@ -472,8 +492,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="headline_b512",
-                    choices=["headline_b512", "steady_b64", "batch1", "commit_burst_b512",
-                             "long_stream_b1", "prefill_b512", "prefill_b64"])
+                    choices=["headline_b512", "headline_b512_fp8", "steady_b64", "batch1",
+                             "commit_burst_b512", "long_stream_b1", "prefill_b512",
+                             "prefill_b64"])
     ap.add_argument("--stream-tokens", type=int, default=16384,
                     help="long_stream_b1: tokens streamed (the second half is timed)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
@@ -514,6 +535,8 @@ def main() -> int:
         return 0
     if args.workload == "headline_b512":
         wl = W.HEADLINE_B512
+    elif args.workload == "headline_b512_fp8":
+        wl = W.HEADLINE_B512_FP8
     elif args.workload == "steady_b64":
         wl = W.STEADY_B64
     else:
@@ -521,11 +544,19 @@ def main() -> int:
     B, L = wl.batch, wl.layers
     dev = "cuda"
 
+    fp8 = wl.extra.get("kv") == "e4m3"
+    attn = R.swa_rma_decode_attn_fp8 if fp8 else R.swa_rma_decode_attn
+    state_bytes = STATE_BYTES_PER_UNIT_FP8 if fp8 else STATE_BYTES_PER_UNIT
     states, qs, norms, outs = [], [], [], []
     for layer in range(L):
-        st = R.alloc_layer_state(B, dev, zero_kv=False)
-        for nm in W.KV_NAMES:
-            W.kv_torch_(wl, layer, nm, getattr(st, nm))
+        if fp8:
+            st = R.alloc_layer_state_fp8(B, dev)
+            for nm in W.KV_NAMES:
+                W.kv_fp8_torch_(wl, layer, nm, getattr(st, nm), getattr(st, nm + "s"))
+        else:
+            st = R.alloc_layer_state(B, dev, zero_kv=False)
+            for nm in W.KV_NAMES:
+                W.kv_torch_(wl, layer, nm, getattr(st, nm))
         for k, v in W.decode_meta(wl, layer).items():
             getattr(st, k).copy_(torch.from_numpy(v).to(dev))
         q = torch.empty(B, 16, 256, dtype=torch.bfloat16, device=dev)
@@ -551,8 +582,8 @@ def main() -> int:
             o = outs[layer]
             if ev is not None:
                 ev[layer][0].record(stream)
-            R.swa_rma_decode_attn(states[layer], B, qs[layer], qs[layer], norms[layer], o[0],
-                                  o[1], o[2], o[3], ws, stream)
+            attn(states[layer], B, qs[layer], qs[layer], norms[layer], o[0], o[1], o[2], o[3],
+                 ws, stream)
             if ev is not None:
                 ev[layer][1].record(stream)
 
@@ -584,9 +615,9 @@ def main() -> int:
 
     ms_per_step = total_ms / args.steps
     value = B * args.steps / (total_ms / 1e3)
-    bytes_per_launch = B * (STATE_BYTES_PER_UNIT + IO_BYTES_PER_UNIT)
+    bytes_per_launch = B * (state_bytes + IO_BYTES_PER_UNIT)
     achieved = bytes_per_launch / (avg_launch_ms / 1e3) / 1e9
-    traffic = measured_traffic(B)
+    traffic = measured_traffic(wl.name, B)
 
     res = {
         "metric": METRIC,
@@ -599,16 +630,17 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8e4m3+bf16" if fp8 else "bf16",
         "data": "synthetic",
         "config": {
             "workload": wl.name,
             "batch": B,
             "layers": L,
             "position": wl.position,
-            "state_bytes_per_step": B * L * STATE_BYTES_PER_UNIT,
+            "kv_format": "e4m3 codes + fp32 row scale" if fp8 else "bf16",
+            "state_bytes_per_step": B * L * state_bytes,
             "decode_splits": R.rma_decode_splits(B),
-            "hbm_gbps_step": round(B * L * (STATE_BYTES_PER_UNIT + IO_BYTES_PER_UNIT)
+            "hbm_gbps_step": round(B * L * (state_bytes + IO_BYTES_PER_UNIT)
                                    / (ms_per_step / 1e3) / 1e9, 1),
         },
         "roofline": {
@@ -618,7 +650,7 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": "decode_attn_kernel",
+            "kernel": "decode_attn_kernel<true>" if fp8 else "decode_attn_kernel<false>",
             "avg_launch_ms": round(avg_launch_ms, 4),
             "median_launch_ms": round(launch_ms[len(launch_ms) // 2], 4),
             "bytes_per_launch": bytes_per_launch,

@@ -214,6 +214,63 @@ rma_status swa_rma_prefill(const rma_layer_state *st, int32_t batch, int32_t n_t
                            float *lse_win, uint16_t *o_rma, float *lse_rma, void *workspace,
                            size_t workspace_bytes, void *stream);
 
+/*
+ * FP8 state variant.  The pages list quantised releases of the model's weights
+ * ([FB] section "架构…"; [QB] section "开源到哪一步") but no format for the
+ * attention state; this variant is a reading of this library:
+ *   - every stored K and V row (256 values) is 256 OCP FP8 E4M3 codes plus one
+ *     FP32 scale = amax / 448 (amax = max |x| over the row, FP32; an all-zero
+ *     row has scale 0 and zero codes);
+ *   - code = E4M3(x * (448 / amax)), products and quotient in FP32, E4M3
+ *     rounding to nearest, ties to even; the row means code value * scale;
+ *   - keys are quantised from their FP32 normalised and rotated value, values
+ *     from their BF16 input.
+ * Layout: as rma_layer_state with 1-byte codes, plus one scale array per K/V
+ * array:
+ *   win_k, win_v   u8  [B][4][1024][256]   win_ks, win_vs   f32 [B][4][1024]
+ *   bank_k, bank_v u8  [B][4][1024][256]   bank_ks, bank_vs f32 [B][4][1024]
+ *   pend_k, pend_v u8  [B][4][256][256]    pend_ks, pend_vs f32 [B][4][256]
+ *   bank_score, bank_src, pend_score, pend_src, n_bank, n_pend, pos as above.
+ * Code arrays and scale arrays must be 16-byte aligned.  A decode step reads
+ * 4,792,320 B of K/V state per sequence and layer, against 9,437,184 in BF16.
+ */
+typedef struct rma_layer_state_fp8 {
+  uint8_t *win_k, *win_v;
+  uint8_t *bank_k, *bank_v;
+  uint8_t *pend_k, *pend_v;
+  float *win_ks, *win_vs;
+  float *bank_ks, *bank_vs;
+  float *pend_ks, *pend_vs;
+  float *bank_score;
+  int32_t *bank_src;
+  float *pend_score;
+  int32_t *pend_src;
+  int32_t *n_bank, *n_pend;
+  int32_t *pos;
+} rma_layer_state_fp8;
+
+/* Bytes of all arrays of one layer's FP8 state for `batch` sequences. */
+size_t rma_layer_state_fp8_bytes(int32_t batch);
+
+/* swa_rma_append for the FP8 state: the same rows, quantised as described above. */
+rma_status swa_rma_append_fp8(const rma_layer_state_fp8 *st, int32_t batch, const uint16_t *k_win,
+                              const uint16_t *v_win, const uint16_t *k_rma, const uint16_t *v_rma,
+                              const float *score, const rma_norm *norm, void *stream);
+
+/* swa_rma_decode_attn over the FP8 state: the attention of the dequantised rows
+ * (score of a key times its scale; values weighed by their scales).  Same
+ * outputs, workspace (rma_decode_workspace_bytes) and error behaviour. */
+rma_status swa_rma_decode_attn_fp8(const rma_layer_state_fp8 *st, int32_t batch,
+                                   const uint16_t *q_win, const uint16_t *q_rma,
+                                   const rma_norm *norm, uint16_t *o_win, float *lse_win,
+                                   uint16_t *o_rma, float *lse_rma, void *workspace,
+                                   size_t workspace_bytes, void *stream);
+
+/* rma_commit_topk for the FP8 state: the same selection and slot rule; an
+ * admitted row moves with its codes and its K and V scales. */
+rma_status rma_commit_topk_fp8(const rma_layer_state_fp8 *st, int32_t batch, int32_t *keep_idx,
+                               void *stream);
+
 /* Human-readable name of a status code (static string). */
 const char *rma_status_str(rma_status s);
 

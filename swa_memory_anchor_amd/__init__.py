@@ -7,9 +7,11 @@ same names.  If the library has not been built, importing the entry points
 raises: there is no fallback.
 
 Entry points: ``swa_rma_append``, ``swa_rma_decode_attn``, ``rma_score``,
-``rma_commit_topk``, ``swa_rma_prefill``, plus the size helpers ``rma_layer_state_bytes``,
-``rma_layer_kv_bytes``, ``rma_decode_workspace_bytes``, ``rma_decode_splits``,
-``rma_prefill_workspace_bytes`` and ``rma_status_str``.
+``rma_commit_topk``, ``swa_rma_prefill``, the FP8-state variants ``swa_rma_append_fp8``,
+``swa_rma_decode_attn_fp8`` and ``rma_commit_topk_fp8``, plus the size helpers
+``rma_layer_state_bytes``, ``rma_layer_state_fp8_bytes``, ``rma_layer_kv_bytes``,
+``rma_decode_workspace_bytes``, ``rma_decode_splits``, ``rma_prefill_workspace_bytes`` and
+``rma_status_str``.
 """
 
 from __future__ import annotations
@@ -27,6 +29,8 @@ EXPORTS = (
     "rma_layer_state_bytes", "rma_layer_kv_bytes", "rma_decode_workspace_bytes",
     "rma_decode_splits", "swa_rma_append", "swa_rma_decode_attn", "rma_score",
     "rma_commit_topk", "rma_status_str", "rma_prefill_workspace_bytes", "swa_rma_prefill",
+    "rma_layer_state_fp8_bytes", "swa_rma_append_fp8", "swa_rma_decode_attn_fp8",
+    "rma_commit_topk_fp8",
 )
 
 _c_void_p = ctypes.c_void_p
@@ -42,6 +46,13 @@ class _StateC(ctypes.Structure):
     _fields_ = [(n, _c_void_p) for n in (
         "win_k", "win_v", "bank_k", "bank_v", "bank_score", "bank_src", "pend_k", "pend_v",
         "pend_score", "pend_src", "n_bank", "n_pend", "pos")]
+
+
+class _StateFp8C(ctypes.Structure):
+    _fields_ = [(n, _c_void_p) for n in (
+        "win_k", "win_v", "bank_k", "bank_v", "pend_k", "pend_v", "win_ks", "win_vs", "bank_ks",
+        "bank_vs", "pend_ks", "pend_vs", "bank_score", "bank_src", "pend_score", "pend_src",
+        "n_bank", "n_pend", "pos")]
 
 
 class _NormC(ctypes.Structure):
@@ -79,6 +90,14 @@ def lib() -> ctypes.CDLL:
         L.swa_rma_prefill.argtypes = [sp, i32, i32, vp, vp, vp, vp, vp, vp, vp, npp, vp, vp, vp,
                                       vp, vp, sz, vp]
         L.swa_rma_prefill.restype = ctypes.c_int
+        s8 = ctypes.POINTER(_StateFp8C)
+        L.rma_layer_state_fp8_bytes.argtypes, L.rma_layer_state_fp8_bytes.restype = [i32], sz
+        L.swa_rma_append_fp8.argtypes = [s8, i32, vp, vp, vp, vp, vp, npp, vp]
+        L.swa_rma_append_fp8.restype = ctypes.c_int
+        L.swa_rma_decode_attn_fp8.argtypes = [s8, i32, vp, vp, npp, vp, vp, vp, vp, vp, sz, vp]
+        L.swa_rma_decode_attn_fp8.restype = ctypes.c_int
+        L.rma_commit_topk_fp8.argtypes = [s8, i32, vp, vp]
+        L.rma_commit_topk_fp8.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -96,6 +115,35 @@ class LayerState:
     bank_src: object
     pend_k: object
     pend_v: object
+    pend_score: object
+    pend_src: object
+    n_bank: object
+    n_pend: object
+    pos: object
+
+    @property
+    def batch(self) -> int:
+        return int(self.n_bank.shape[0])
+
+
+@dataclass
+class LayerStateFP8:
+    """Device tensors of one layer's FP8 state (E4M3 codes + one FP32 scale per row)."""
+
+    win_k: object
+    win_v: object
+    bank_k: object
+    bank_v: object
+    pend_k: object
+    pend_v: object
+    win_ks: object
+    win_vs: object
+    bank_ks: object
+    bank_vs: object
+    pend_ks: object
+    pend_vs: object
+    bank_score: object
+    bank_src: object
     pend_score: object
     pend_src: object
     n_bank: object
@@ -140,6 +188,27 @@ def alloc_layer_state(batch: int, device="cuda", zero_kv: bool = True) -> LayerS
     )
 
 
+def alloc_layer_state_fp8(batch: int, device="cuda") -> LayerStateFP8:
+    """Allocate one layer's FP8 state with torch (empty: n_bank = n_pend = 0, pos = -1)."""
+    import torch
+
+    u8, f32, i32 = torch.uint8, torch.float32, torch.int32
+    c = lambda n: torch.zeros(batch, KV_GROUPS, n, HEAD_DIM, dtype=u8, device=device)  # noqa: E731
+    s = lambda n: torch.zeros(batch, KV_GROUPS, n, dtype=f32, device=device)  # noqa: E731
+    return LayerStateFP8(
+        win_k=c(WINDOW), win_v=c(WINDOW), bank_k=c(BANK), bank_v=c(BANK), pend_k=c(BLOCK),
+        pend_v=c(BLOCK), win_ks=s(WINDOW), win_vs=s(WINDOW), bank_ks=s(BANK), bank_vs=s(BANK),
+        pend_ks=s(BLOCK), pend_vs=s(BLOCK),
+        bank_score=torch.zeros(batch, KV_GROUPS, BANK, dtype=f32, device=device),
+        bank_src=torch.zeros(batch, KV_GROUPS, BANK, dtype=i32, device=device),
+        pend_score=torch.zeros(batch, BLOCK, KV_GROUPS, dtype=f32, device=device),
+        pend_src=torch.zeros(batch, BLOCK, dtype=i32, device=device),
+        n_bank=torch.zeros(batch, dtype=i32, device=device),
+        n_pend=torch.zeros(batch, dtype=i32, device=device),
+        pos=torch.full((batch,), -1, dtype=i32, device=device),
+    )
+
+
 def _ptr(t) -> int | None:
     if t is None:
         return None
@@ -151,6 +220,10 @@ def _ptr(t) -> int | None:
 
 def _state_c(st: LayerState) -> _StateC:
     return _StateC(*[_ptr(getattr(st, f.name)) for f in fields(LayerState)])
+
+
+def _state_fp8_c(st: LayerStateFP8) -> _StateFp8C:
+    return _StateFp8C(*[_ptr(getattr(st, f.name)) for f in fields(LayerStateFP8)])
 
 
 def _norm_c(nm: Norm) -> _NormC:
@@ -255,3 +328,32 @@ def swa_rma_prefill(st: LayerState, batch: int, n_tokens: int, k_win, v_win, k_r
                               _ptr(lse_win), _ptr(o_rma), _ptr(lse_rma), _ptr(workspace),
                               ws_bytes, _stream(stream))
     _check(s, "swa_rma_prefill")
+
+
+# ---------------------------------------------------------------- FP8 state variant
+def rma_layer_state_fp8_bytes(batch: int) -> int:
+    return int(lib().rma_layer_state_fp8_bytes(int(batch)))
+
+
+def swa_rma_append_fp8(st: LayerStateFP8, batch: int, k_win, v_win, k_rma, v_rma, score,
+                       norm: Norm, stream=None) -> None:
+    s = lib().swa_rma_append_fp8(ctypes.byref(_state_fp8_c(st)), int(batch), _ptr(k_win),
+                                 _ptr(v_win), _ptr(k_rma), _ptr(v_rma), _ptr(score),
+                                 ctypes.byref(_norm_c(norm)), _stream(stream))
+    _check(s, "swa_rma_append_fp8")
+
+
+def swa_rma_decode_attn_fp8(st: LayerStateFP8, batch: int, q_win, q_rma, norm: Norm, o_win,
+                            lse_win, o_rma, lse_rma, workspace=None, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    s = lib().swa_rma_decode_attn_fp8(ctypes.byref(_state_fp8_c(st)), int(batch), _ptr(q_win),
+                                      _ptr(q_rma), ctypes.byref(_norm_c(norm)), _ptr(o_win),
+                                      _ptr(lse_win), _ptr(o_rma), _ptr(lse_rma), _ptr(workspace),
+                                      ws_bytes, _stream(stream))
+    _check(s, "swa_rma_decode_attn_fp8")
+
+
+def rma_commit_topk_fp8(st: LayerStateFP8, batch: int, keep_idx=None, stream=None) -> None:
+    s = lib().rma_commit_topk_fp8(ctypes.byref(_state_fp8_c(st)), int(batch), _ptr(keep_idx),
+                                  _stream(stream))
+    _check(s, "rma_commit_topk_fp8")

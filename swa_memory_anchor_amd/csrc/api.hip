@@ -22,6 +22,16 @@ extern "C" size_t rma_layer_state_bytes(int32_t batch) {
   return rma_layer_kv_bytes(batch) + static_cast<size_t>(batch) * per_seq_meta;
 }
 
+// FP8 variant: 1-byte codes plus one FP32 scale per K and V row.
+extern "C" size_t rma_layer_state_fp8_bytes(int32_t batch) {
+  if (batch <= 0) return 0;
+  const size_t rows = static_cast<size_t>(2) * kGroups * (kWindow + kBank + kBlock);
+  const size_t per_seq_meta = static_cast<size_t>(kGroups) * kBank * (sizeof(float) + sizeof(int32_t)) +
+                              static_cast<size_t>(kBlock) * (kGroups * sizeof(float) + sizeof(int32_t)) +
+                              3 * sizeof(int32_t);
+  return static_cast<size_t>(batch) * (rows * (kDim + sizeof(float)) + per_seq_meta);
+}
+
 extern "C" const char *rma_status_str(rma_status s) {
   switch (s) {
     case RMA_OK: return "RMA_OK";

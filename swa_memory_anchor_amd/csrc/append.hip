@@ -58,6 +58,91 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams a) {
   }
 }
 
+// ---------------------------------------------------------------- FP8 state variant
+// Each written row becomes 256 E4M3 codes and one FP32 scale: amax = max |x| over
+// the row (a wave reduction), code = E4M3(x * (448 / amax)) with round to nearest
+// even (v_cvt_pk_fp8_f32), scale = amax / 448; an all-zero row gets zero codes and
+// scale.  Keys are quantised from their FP32 normalised and rotated value.
+struct AppendFp8Params {
+  uint8_t *win_k, *win_v, *pend_k, *pend_v;
+  float *win_ks, *win_vs, *pend_ks, *pend_vs;
+  float *pend_score;
+  int32_t *pend_src, *n_pend, *pos;
+  const uint16_t *k_win, *v_win, *k_rma, *v_rma;
+  const float *score;
+  const float *gk_win, *gk_rma;
+  float eps;
+  double rope_ratio;  // base^(-1/32)
+};
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// Quantise one 256-wide row held by a wave (lane l: x[0..3] = dims 4l..4l+3): the
+// lane's four codes (one word, dim 4l in the low byte) and the row's scale.
+__device__ __forceinline__ uint32_t quantize_row_e4m3(const float x[4], float &scale) {
+  const float amax =
+      wave_max(fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))));
+  const float inv = amax > 0.f ? 448.0f / amax : 0.f;
+  scale = amax / 448.0f;
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] * inv, x[1] * inv, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] * inv, x[3] * inv, w, true);
+  // an all-zero row stores +0 codes, also where its elements are -0
+  return amax > 0.f ? static_cast<uint32_t>(w) : 0u;
+}
+
+__global__ __launch_bounds__(256) void append_fp8_kernel(AppendFp8Params a) {
+  const int b = blockIdx.x;
+  const int g = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int p = a.pos[b] + 1;
+  const int t = a.n_pend[b];
+  if (t < 0 || t >= kBlock) return;  // full (or corrupt) pending block: leave untouched
+  const int slot = p & (kWindow - 1);
+  const size_t in = (static_cast<size_t>(b) * kGroups + g) * kDim + 4 * lane;
+  const size_t w_row = (static_cast<size_t>(b) * kGroups + g) * kWindow + slot;
+  const size_t p_row = (static_cast<size_t>(b) * kGroups + g) * kBlock + t;
+
+  const uint2 kw = *reinterpret_cast<const uint2 *>(a.k_win + in);
+  const uint2 kr = *reinterpret_cast<const uint2 *>(a.k_rma + in);
+  const uint2 vw = *reinterpret_cast<const uint2 *>(a.v_win + in);
+  const uint2 vr = *reinterpret_cast<const uint2 *>(a.v_rma + in);
+  float xw[4] = {bf16_lo(kw.x), bf16_hi(kw.x), bf16_lo(kw.y), bf16_hi(kw.y)};
+  float xr[4] = {bf16_lo(kr.x), bf16_hi(kr.x), bf16_lo(kr.y), bf16_hi(kr.y)};
+  const float yw[4] = {bf16_lo(vw.x), bf16_hi(vw.x), bf16_lo(vw.y), bf16_hi(vw.y)};
+  const float yr[4] = {bf16_lo(vr.x), bf16_hi(vr.x), bf16_lo(vr.y), bf16_hi(vr.y)};
+  float c, sn;
+  rope_cos_sin(a.rope_ratio, p, lane, c, sn);
+  norm_rope_head(xw, a.gk_win, a.eps, c, sn, lane);
+  norm_rope_head(xr, a.gk_rma, a.eps, c, sn, lane);
+  float s0, s1, s2, s3;
+  const uint32_t c0 = quantize_row_e4m3(xw, s0);
+  const uint32_t c1 = quantize_row_e4m3(yw, s1);
+  const uint32_t c2 = quantize_row_e4m3(xr, s2);
+  const uint32_t c3 = quantize_row_e4m3(yr, s3);
+  *reinterpret_cast<uint32_t *>(a.win_k + w_row * kDim + 4 * lane) = c0;
+  *reinterpret_cast<uint32_t *>(a.win_v + w_row * kDim + 4 * lane) = c1;
+  *reinterpret_cast<uint32_t *>(a.pend_k + p_row * kDim + 4 * lane) = c2;
+  *reinterpret_cast<uint32_t *>(a.pend_v + p_row * kDim + 4 * lane) = c3;
+  if (lane == 0) {
+    a.win_ks[w_row] = s0;
+    a.win_vs[w_row] = s1;
+    a.pend_ks[p_row] = s2;
+    a.pend_vs[p_row] = s3;
+    if (a.score)
+      a.pend_score[(static_cast<size_t>(b) * kBlock + t) * kGroups + g] = a.score[b * kGroups + g];
+  }
+  __syncthreads();  // every wave has read n_pend / pos
+  if (threadIdx.x == 0) {
+    a.pend_src[static_cast<size_t>(b) * kBlock + t] = p;
+    a.n_pend[b] = t + 1;
+    a.pos[b] = p;
+  }
+}
+
 }  // namespace rma
 
 using namespace rma;
@@ -99,6 +184,51 @@ extern "C" rma_status swa_rma_append(const rma_layer_state *st, int32_t batch,
   p.eps = norm->eps;
   p.rope_ratio = rope_ratio(norm->rope_base);
   hipLaunchKernelGGL(append_kernel, dim3(batch), dim3(256), 0, static_cast<hipStream_t>(stream), p);
+  if (hipPeekAtLastError() != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
+  return RMA_OK;
+}
+
+extern "C" rma_status swa_rma_append_fp8(const rma_layer_state_fp8 *st, int32_t batch,
+                                         const uint16_t *k_win, const uint16_t *v_win,
+                                         const uint16_t *k_rma, const uint16_t *v_rma,
+                                         const float *score, const rma_norm *norm, void *stream) {
+  if (!st || !norm || !k_win || !v_win || !k_rma || !v_rma) return RMA_E_ARG;
+  if (batch <= 0 || batch > RMA_MAX_BATCH) return RMA_E_ARG;
+  if (!st->win_k || !st->win_v || !st->pend_k || !st->pend_v || !st->win_ks || !st->win_vs ||
+      !st->pend_ks || !st->pend_vs || !st->pend_src || !st->n_pend || !st->pos ||
+      !norm->gk_win || !norm->gk_rma || (score && !st->pend_score))
+    return RMA_E_ARG;
+  const void *a16[] = {st->win_k,  st->win_v,  st->pend_k,  st->pend_v,   st->win_ks,
+                       st->win_vs, st->pend_ks, st->pend_vs, norm->gk_win, norm->gk_rma};
+  for (const void *p : a16)
+    if (!aligned16(p)) return RMA_E_ALIGN;
+  const void *a8[] = {k_win, v_win, k_rma, v_rma};
+  for (const void *p : a8)
+    if (!aligned8(p)) return RMA_E_ALIGN;
+  AppendFp8Params p;
+  p.win_k = st->win_k;
+  p.win_v = st->win_v;
+  p.pend_k = st->pend_k;
+  p.pend_v = st->pend_v;
+  p.win_ks = st->win_ks;
+  p.win_vs = st->win_vs;
+  p.pend_ks = st->pend_ks;
+  p.pend_vs = st->pend_vs;
+  p.pend_score = st->pend_score;
+  p.pend_src = st->pend_src;
+  p.n_pend = st->n_pend;
+  p.pos = st->pos;
+  p.k_win = k_win;
+  p.v_win = v_win;
+  p.k_rma = k_rma;
+  p.v_rma = v_rma;
+  p.score = score;
+  p.gk_win = norm->gk_win;
+  p.gk_rma = norm->gk_rma;
+  p.eps = norm->eps;
+  p.rope_ratio = rope_ratio(norm->rope_base);
+  hipLaunchKernelGGL(append_fp8_kernel, dim3(batch), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), p);
   if (hipPeekAtLastError() != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
   return RMA_OK;
 }

@@ -19,9 +19,10 @@
 //   3. a bank record survives in place; free slots (evicted slots, then slots
 //      >= n_bank) are listed in ascending order by a prefix sum; admitted
 //      pending rows, in ascending row order, take the free slots in order;
-//   4. only admitted rows move: 512-byte K and V rows are copied in 16-byte
-//      pieces (a wave covers one row per pass, 8 passes in flight), plus their
-//      score and source;
+//   4. only admitted rows move: K and V rows (512 bytes in BF16, 256 bytes of
+//      E4M3 codes in the FP8 variant) are copied in 16-byte pieces (8 in flight
+//      per thread), plus their score, source and, in the FP8 variant, the two
+//      row scales;
 //   5. n_bank = min(1024, n_bank + n_pend), n_pend = 0.
 #include "rma_device.h"
 
@@ -33,11 +34,15 @@ constexpr int kGroupThreads = 256;
 constexpr int kCommitThreads = kGroupThreads * kGroups;
 constexpr int kCopyBatch = 8;  // 16-byte copies in flight per thread
 
+// K/V rows are BF16 (512 bytes) or, in the FP8 variant, E4M3 codes (256 bytes)
+// with one FP32 scale per row (*_ks, *_vs), which moves with the row.
 struct CommitParams {
-  uint16_t *bank_k, *bank_v;
+  uint8_t *bank_k, *bank_v;
+  float *bank_ks, *bank_vs;
   float *bank_score;
   int32_t *bank_src;
-  const uint16_t *pend_k, *pend_v;
+  const uint8_t *pend_k, *pend_v;
+  const float *pend_ks, *pend_vs;
   const float *pend_score;
   const int32_t *pend_src;
   int32_t *n_bank, *n_pend;
@@ -81,7 +86,10 @@ __device__ __forceinline__ int group_exclusive_scan(int v, int (*wave_tot)[4], i
   return base + x - v;
 }
 
+template <bool kFp8>
 __global__ __launch_bounds__(kCommitThreads) void commit_kernel(CommitParams a) {
+  constexpr int kRowBytes = kFp8 ? kDim : 2 * kDim;
+  constexpr int kPieces = kRowBytes / 16;  // 16-byte pieces per row
   __shared__ uint64_t keys[kGroups][kSortN];
   __shared__ uint8_t keep[kGroups][kCand];
   __shared__ int16_t free_list[kGroups][kBank];
@@ -185,30 +193,30 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kernel(CommitParams a) 
 #pragma unroll
     for (int e = 0; e < 4; ++e) a.keep_idx[sg * kBank + 4 * t + e] = kidx[g][4 * t + e];
   }
-  // 16-byte pieces: 64 per admitted row (32 of K, 32 of V).  Each thread issues
-  // kCopyBatch loads before its stores, so a group waits for at most
-  // 64 * 256 / (256 * kCopyBatch) round trips to memory instead of one per piece.
-  const int pieces = n_adm * 64;
+  // 16-byte pieces: 2 * kPieces per admitted row (K then V).  Each thread issues
+  // kCopyBatch loads before its stores, so a group waits for a handful of round
+  // trips to memory instead of one per piece.
+  const int pieces = n_adm * 2 * kPieces;
   for (int w0 = 0; w0 < pieces; w0 += kGroupThreads * kCopyBatch) {
     u32x4 buf[kCopyBatch];
 #pragma unroll
     for (int u = 0; u < kCopyBatch; ++u) {
       // past the end, repeat the last piece: the same bytes go to the same place
       const int w = min(w0 + t + u * kGroupThreads, pieces - 1);
-      const int row = adm_rows[g][w >> 6];
-      const int part = w & 63;
-      const uint16_t *src = (part >= 32 ? a.pend_v : a.pend_k) + (sg * kBlock + row) * kDim +
-                            (part & 31) * 8;
+      const int row = adm_rows[g][w / (2 * kPieces)];
+      const int part = w % (2 * kPieces);
+      const uint8_t *src = (part >= kPieces ? a.pend_v : a.pend_k) +
+                           (sg * kBlock + row) * kRowBytes + (part % kPieces) * 16;
       buf[u] = *reinterpret_cast<const u32x4 *>(src);
     }
 #pragma unroll
     for (int u = 0; u < kCopyBatch; ++u) {
       const int w = min(w0 + t + u * kGroupThreads, pieces - 1);
-      const int row = adm_rows[g][w >> 6];
-      const int part = w & 63;
+      const int row = adm_rows[g][w / (2 * kPieces)];
+      const int part = w % (2 * kPieces);
       const int sl = adm_slot[g][row];
-      uint16_t *dst = (part >= 32 ? a.bank_v : a.bank_k) + (sg * kBank + sl) * kDim +
-                      (part & 31) * 8;
+      uint8_t *dst = (part >= kPieces ? a.bank_v : a.bank_k) + (sg * kBank + sl) * kRowBytes +
+                     (part % kPieces) * 16;
       *reinterpret_cast<u32x4 *>(dst) = buf[u];
     }
   }
@@ -217,6 +225,10 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kernel(CommitParams a) 
     const int s = adm_slot[g][row];
     a.bank_score[sg * kBank + s] = a.pend_score[(static_cast<size_t>(b) * kBlock + row) * kGroups + g];
     a.bank_src[sg * kBank + s] = a.pend_src[static_cast<size_t>(b) * kBlock + row];
+    if constexpr (kFp8) {
+      a.bank_ks[sg * kBank + s] = a.pend_ks[sg * kBlock + row];
+      a.bank_vs[sg * kBank + s] = a.pend_vs[sg * kBlock + row];
+    }
   }
 
   // 5. counters, after every group has read them
@@ -233,29 +245,58 @@ using namespace rma;
 
 static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+template <bool kFp8>
+static rma_status launch_commit(const CommitParams &p, int32_t batch, void *stream) {
+  if (batch <= 0 || batch > RMA_MAX_BATCH) return RMA_E_ARG;
+  if (!p.bank_k || !p.bank_v || !p.bank_score || !p.bank_src || !p.pend_k || !p.pend_v ||
+      !p.pend_score || !p.pend_src || !p.n_bank || !p.n_pend)
+    return RMA_E_ARG;
+  if (kFp8 && (!p.bank_ks || !p.bank_vs || !p.pend_ks || !p.pend_vs)) return RMA_E_ARG;
+  const void *al[] = {p.bank_k, p.bank_v, p.pend_k, p.pend_v};
+  for (const void *ptr : al)
+    if (!aligned16(ptr)) return RMA_E_ALIGN;
+  hipLaunchKernelGGL(commit_kernel<kFp8>, dim3(batch), dim3(kCommitThreads), 0,
+                     static_cast<hipStream_t>(stream), p);
+  if (hipPeekAtLastError() != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
+  return RMA_OK;
+}
+
 extern "C" rma_status rma_commit_topk(const rma_layer_state *st, int32_t batch, int32_t *keep_idx,
                                       void *stream) {
-  if (!st || batch <= 0 || batch > RMA_MAX_BATCH) return RMA_E_ARG;
-  if (!st->bank_k || !st->bank_v || !st->bank_score || !st->bank_src || !st->pend_k ||
-      !st->pend_v || !st->pend_score || !st->pend_src || !st->n_bank || !st->n_pend)
-    return RMA_E_ARG;
-  const void *al[] = {st->bank_k, st->bank_v, st->pend_k, st->pend_v};
-  for (const void *p : al)
-    if (!aligned16(p)) return RMA_E_ALIGN;
-  CommitParams p;
-  p.bank_k = st->bank_k;
-  p.bank_v = st->bank_v;
+  if (!st) return RMA_E_ARG;
+  CommitParams p{};
+  p.bank_k = reinterpret_cast<uint8_t *>(st->bank_k);
+  p.bank_v = reinterpret_cast<uint8_t *>(st->bank_v);
   p.bank_score = st->bank_score;
   p.bank_src = st->bank_src;
-  p.pend_k = st->pend_k;
-  p.pend_v = st->pend_v;
+  p.pend_k = reinterpret_cast<const uint8_t *>(st->pend_k);
+  p.pend_v = reinterpret_cast<const uint8_t *>(st->pend_v);
   p.pend_score = st->pend_score;
   p.pend_src = st->pend_src;
   p.n_bank = st->n_bank;
   p.n_pend = st->n_pend;
   p.keep_idx = keep_idx;
-  hipLaunchKernelGGL(commit_kernel, dim3(batch), dim3(kCommitThreads), 0,
-                     static_cast<hipStream_t>(stream), p);
-  if (hipPeekAtLastError() != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
-  return RMA_OK;
+  return launch_commit<false>(p, batch, stream);
+}
+
+extern "C" rma_status rma_commit_topk_fp8(const rma_layer_state_fp8 *st, int32_t batch,
+                                          int32_t *keep_idx, void *stream) {
+  if (!st) return RMA_E_ARG;
+  CommitParams p{};
+  p.bank_k = st->bank_k;
+  p.bank_v = st->bank_v;
+  p.bank_ks = st->bank_ks;
+  p.bank_vs = st->bank_vs;
+  p.bank_score = st->bank_score;
+  p.bank_src = st->bank_src;
+  p.pend_k = st->pend_k;
+  p.pend_v = st->pend_v;
+  p.pend_ks = st->pend_ks;
+  p.pend_vs = st->pend_vs;
+  p.pend_score = st->pend_score;
+  p.pend_src = st->pend_src;
+  p.n_bank = st->n_bank;
+  p.n_pend = st->n_pend;
+  p.keep_idx = keep_idx;
+  return launch_commit<true>(p, batch, stream);
 }

@@ -56,8 +56,11 @@ constexpr float kLn2 = 0.69314718055994531f;
 // step, so it should not displace anything in the caches).
 constexpr int kStream = 2;
 
+// K/V rows are BF16 (512 bytes) or, in the FP8 variant, E4M3 codes (256 bytes) with
+// one FP32 scale per row in the *_ks / *_vs arrays.
 struct DecodeParams {
-  const uint16_t *win_k, *win_v, *bank_k, *bank_v, *pend_k, *pend_v;
+  const uint8_t *win_k, *win_v, *bank_k, *bank_v, *pend_k, *pend_v;
+  const float *win_ks, *win_vs, *bank_ks, *bank_vs, *pend_ks, *pend_vs;
   const int32_t *n_bank, *n_pend, *pos;
   const uint16_t *q_win, *q_rma;
   const float *gq_win, *gq_rma;
@@ -74,6 +77,7 @@ struct DecodeParams {
 // size is the valid byte count: rows past the end read as zero.
 struct Segment {
   __amdgpu_buffer_rsrc_t k, v;
+  __amdgpu_buffer_rsrc_t ks, vs;  // FP8 variant: per-row scales
   int n;
 };
 
@@ -86,22 +90,65 @@ __device__ __forceinline__ T bitcast(const F &f) {
   return __builtin_bit_cast(T, f);
 }
 
+// Bytes of one K/V row.
+template <bool kFp8>
+constexpr int kRowBytes = kFp8 ? kDim : 2 * kDim;
+
+// Bytes of the scales of n rows, rounded up to whole groups of four rows.
+__device__ __forceinline__ int scale_bytes(int n) { return ((n + 3) & ~3) * 4; }
+
 // Issue the loads of one 16-key tile starting at row key0 of a segment: K as MFMA
 // A operands (lane: row key0 + lane%16, dims 32s + 8(lane/16) .. +8), V as row
-// chunks (lane: row key0 + 2i + lane/32, dims 8(lane%32) .. +8).
+// chunks (lane: row key0 + 2i + lane/32, dims 8(lane%32) .. +8).  BF16 rows fill
+// all of each uint4; FP8 rows only .x and .y (8 codes).  The FP8 variant also
+// loads the scales of the lane's four score keys (key0 + 4(lane/16) + 0..3).
+template <bool kFp8>
 __device__ __forceinline__ void load_tile(const Segment &sg, int key0, int lane, uint4 (&K)[8],
-                                          uint4 (&V)[8]) {
+                                          uint4 (&V)[8], f32x4 &ks, f32x4 &vs) {
+  constexpr int RB = kRowBytes<kFp8>;
+  constexpr int EB = kFp8 ? 1 : 2;  // bytes per element
   const int hh = lane & 15, kg = lane >> 4;
-  const int koff = hh * (kDim * 2) + kg * 16;
-  const int voff = (lane >> 5) * (kDim * 2) + (lane & 31) * 16;
-  const int soff = key0 * (kDim * 2);
+  const int koff = hh * RB + kg * 8 * EB;
+  const int voff = (lane >> 5) * RB + (lane & 31) * 8 * EB;
+  const int soff = key0 * RB;
+  if constexpr (kFp8) {
 #pragma unroll
-  for (int s = 0; s < 8; ++s)
-    K[s] = bitcast<uint4>(__builtin_amdgcn_raw_buffer_load_b128(sg.k, koff + 64 * s, soff, kStream));
+    for (int s = 0; s < 8; ++s) {
+      const auto w = __builtin_amdgcn_raw_buffer_load_b64(sg.k, koff + 32 * s, soff, kStream);
+      K[s].x = w[0];
+      K[s].y = w[1];
+    }
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    V[i] = bitcast<uint4>(
-        __builtin_amdgcn_raw_buffer_load_b128(sg.v, voff + 2 * kDim * 2 * i, soff, kStream));
+    for (int i = 0; i < 8; ++i) {
+      const auto w = __builtin_amdgcn_raw_buffer_load_b64(sg.v, voff + 2 * RB * i, soff, kStream);
+      V[i].x = w[0];
+      V[i].y = w[1];
+    }
+    ks = bitcast<f32x4>(__builtin_amdgcn_raw_buffer_load_b128(sg.ks, 16 * kg, key0 * 4, kStream));
+    vs = bitcast<f32x4>(__builtin_amdgcn_raw_buffer_load_b128(sg.vs, 16 * kg, key0 * 4, kStream));
+  } else {
+    (void)ks;
+    (void)vs;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      K[s] = bitcast<uint4>(__builtin_amdgcn_raw_buffer_load_b128(sg.k, koff + 64 * s, soff, kStream));
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      V[i] = bitcast<uint4>(
+          __builtin_amdgcn_raw_buffer_load_b128(sg.v, voff + 2 * RB * i, soff, kStream));
+  }
+}
+
+// Eight E4M3 codes -> eight BF16 values (every E4M3 value is exact in BF16).
+__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
+  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
+  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+  const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+  auto hi16 = [](float x, float y) {
+    return (__float_as_uint(x) >> 16) | (__float_as_uint(y) & 0xffff0000u);
+  };
+  return make_uint4(hi16(a[0], a[1]), hi16(b[0], b[1]), hi16(c[0], c[1]), hi16(d[0], d[1]));
 }
 
 struct SoftmaxState {
@@ -109,14 +156,17 @@ struct SoftmaxState {
   f32x4 acc[16];
 };
 
-// Stage V in LDS and form the scores of one tile (consumes K and V).
+// Stage V in LDS and form the scores of one tile (consumes K and V).  FP8 rows are
+// widened to BF16 on the way; a key's score is multiplied by its K scale.
+template <bool kFp8>
 __device__ __forceinline__ f32x4 scores_tile(int nvalid, int lane, const uint4 (&K)[8],
-                                             const uint4 (&V)[8], const uint16_t *ql,
-                                             uint16_t *vl) {
+                                             const uint4 (&V)[8], const f32x4 &ks,
+                                             const uint16_t *ql, uint16_t *vl) {
   const int hh = lane & 15, kg = lane >> 4;
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    *reinterpret_cast<uint4 *>(vl + (2 * i + (lane >> 5)) * kVStride + 8 * (lane & 31)) = V[i];
+    *reinterpret_cast<uint4 *>(vl + (2 * i + (lane >> 5)) * kVStride + 8 * (lane & 31)) =
+        kFp8 ? fp8x8_to_bf16x8(V[i].x, V[i].y) : V[i];
   // D[key][head] = sum_d K[key][d] * qhat[head][d]; the B operand is the staged
   // query block (head hh; rows >= 4 are zero).  Lane holds keys 4kg..4kg+3 of head hh.
   f32x4 sc = {0.f, 0.f, 0.f, 0.f};
@@ -124,8 +174,10 @@ __device__ __forceinline__ f32x4 scores_tile(int nvalid, int lane, const uint4 (
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     const bf16x8 qv = bitcast<bf16x8>(*reinterpret_cast<const uint4 *>(qrow + 32 * s));
-    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(K[s]), qv, sc, 0, 0, 0);
+    const uint4 kv = kFp8 ? fp8x8_to_bf16x8(K[s].x, K[s].y) : K[s];
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(kv), qv, sc, 0, 0, 0);
   }
+  if constexpr (kFp8) sc *= ks;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     if (4 * kg + i >= nvalid) sc[i] = -INFINITY;
@@ -133,8 +185,11 @@ __device__ __forceinline__ f32x4 scores_tile(int nvalid, int lane, const uint4 (
 }
 
 // Online-softmax update and P x V for one tile whose V rows are staged in LDS.
+// The FP8 variant weighs each value row by its scale in the numerator (the
+// denominator sums the unscaled probabilities).
+template <bool kFp8>
 __device__ __forceinline__ void accumulate_tile(f32x4 sc, int lane, const uint16_t *vl,
-                                                SoftmaxState &st) {
+                                                const f32x4 &vsc, SoftmaxState &st) {
   const int hh = lane & 15, kg = lane >> 4;
   float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
   mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
@@ -145,14 +200,22 @@ __device__ __forceinline__ void accumulate_tile(f32x4 sc, int lane, const uint16
   float psum = 0.f;
   if (m_new != -INFINITY) {
     alpha = __builtin_amdgcn_exp2f(st.m - m_new);
-    const uint32_t p0 = f32_to_bf16(__builtin_amdgcn_exp2f(sc[0] - m_new));
-    const uint32_t p1 = f32_to_bf16(__builtin_amdgcn_exp2f(sc[1] - m_new));
-    const uint32_t p2 = f32_to_bf16(__builtin_amdgcn_exp2f(sc[2] - m_new));
-    const uint32_t p3 = f32_to_bf16(__builtin_amdgcn_exp2f(sc[3] - m_new));
+    const float e0 = __builtin_amdgcn_exp2f(sc[0] - m_new);
+    const float e1 = __builtin_amdgcn_exp2f(sc[1] - m_new);
+    const float e2 = __builtin_amdgcn_exp2f(sc[2] - m_new);
+    const float e3 = __builtin_amdgcn_exp2f(sc[3] - m_new);
+    const uint32_t p0 = f32_to_bf16(e0), p1 = f32_to_bf16(e1);
+    const uint32_t p2 = f32_to_bf16(e2), p3 = f32_to_bf16(e3);
     // the denominator uses the same rounded weights as the numerator
     psum = (bf16_to_f32(p0) + bf16_to_f32(p1)) + (bf16_to_f32(p2) + bf16_to_f32(p3));
-    pw0 = p0 | (p1 << 16);
-    pw1 = p2 | (p3 << 16);
+    if constexpr (kFp8) {
+      pw0 = f32_to_bf16(e0 * vsc[0]) | (f32_to_bf16(e1 * vsc[1]) << 16);
+      pw1 = f32_to_bf16(e2 * vsc[2]) | (f32_to_bf16(e3 * vsc[3]) << 16);
+    } else {
+      (void)vsc;
+      pw0 = p0 | (p1 << 16);
+      pw1 = p2 | (p3 << 16);
+    }
   }
   st.l = st.l * alpha + psum;
   st.m = m_new;
@@ -169,6 +232,7 @@ __device__ __forceinline__ void accumulate_tile(f32x4 sc, int lane, const uint16
   }
 }
 
+template <bool kFp8>
 __global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(DecodeParams a) {
   __shared__ __align__(16) uint16_t v_lds[kWaves][kTile * kVStride];
   __shared__ __align__(16) uint16_t q_lds[16][kDim];  // rows 4..15 stay zero
@@ -186,20 +250,33 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(DecodeParams a
   const int p = a.pos[b];
   Segment seg0, seg1;
   const size_t sgi = static_cast<size_t>(b) * kGroups + g;
+  constexpr int RB = kRowBytes<kFp8>;
   if (anchor) {
     const int nb = min(max(a.n_bank[b], 0), kBank);
     const int np = min(max(a.n_pend[b], 0), kBlock);
-    seg0.k = make_rsrc(a.bank_k + sgi * kBank * kDim, nb * kDim * 2);
-    seg0.v = make_rsrc(a.bank_v + sgi * kBank * kDim, nb * kDim * 2);
+    seg0.k = make_rsrc(a.bank_k + sgi * kBank * RB, nb * RB);
+    seg0.v = make_rsrc(a.bank_v + sgi * kBank * RB, nb * RB);
     seg0.n = nb;
-    seg1.k = make_rsrc(a.pend_k + sgi * kBlock * kDim, np * kDim * 2);
-    seg1.v = make_rsrc(a.pend_v + sgi * kBlock * kDim, np * kDim * 2);
+    seg1.k = make_rsrc(a.pend_k + sgi * kBlock * RB, np * RB);
+    seg1.v = make_rsrc(a.pend_v + sgi * kBlock * RB, np * RB);
     seg1.n = np;
+    if constexpr (kFp8) {
+      // scales are read four keys at a time: the range covers whole quads (the
+      // arrays hold a multiple of four rows), and keys past n are masked
+      seg0.ks = make_rsrc(a.bank_ks + sgi * kBank, scale_bytes(nb));
+      seg0.vs = make_rsrc(a.bank_vs + sgi * kBank, scale_bytes(nb));
+      seg1.ks = make_rsrc(a.pend_ks + sgi * kBlock, scale_bytes(np));
+      seg1.vs = make_rsrc(a.pend_vs + sgi * kBlock, scale_bytes(np));
+    }
   } else {
     const int nw = min(max(p + 1, 0), kWindow);
-    seg0.k = make_rsrc(a.win_k + sgi * kWindow * kDim, nw * kDim * 2);
-    seg0.v = make_rsrc(a.win_v + sgi * kWindow * kDim, nw * kDim * 2);
+    seg0.k = make_rsrc(a.win_k + sgi * kWindow * RB, nw * RB);
+    seg0.v = make_rsrc(a.win_v + sgi * kWindow * RB, nw * RB);
     seg0.n = nw;
+    if constexpr (kFp8) {
+      seg0.ks = make_rsrc(a.win_ks + sgi * kWindow, scale_bytes(nw));
+      seg0.vs = make_rsrc(a.win_vs + sgi * kWindow, scale_bytes(nw));
+    }
     seg1 = seg0;
     seg1.n = 0;
   }
@@ -219,10 +296,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(DecodeParams a
 
   uint16_t *vl = v_lds[wave];
   uint4 K[8], V[8];
+  f32x4 ks, vs;
   int t = tb + wave;
   // The first tile's loads do not depend on the query: issue them before the
   // query prologue so its latency overlaps the norm and rotary work.
-  if (t < te) load_tile(t < T0 ? seg0 : seg1, (t < T0 ? t : t - T0) * kTile, lane, K, V);
+  if (t < te)
+    load_tile<kFp8>(t < T0 ? seg0 : seg1, (t < T0 ? t : t - T0) * kTile, lane, K, V, ks, vs);
 
   // Query prep: wave w < 4 normalises, rotates and scales head 4g + w.
   if (wave < kHeadsPerGroup) {
@@ -245,11 +324,17 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(DecodeParams a
   for (; t < te; t += kWaves) {
     const int key0 = (t < T0 ? t : t - T0) * kTile;
     const int nvalid = (t < T0 ? seg0.n : seg1.n) - key0;
-    const f32x4 sc = scores_tile(nvalid, lane, K, V, &q_lds[0][0], vl);
+    const f32x4 sc = scores_tile<kFp8>(nvalid, lane, K, V, ks, &q_lds[0][0], vl);
+    // this tile's value scales, taken before the next tile's loads; a key past the
+    // end weighs 0 whatever its slot holds (its probability is 0, and 0 * inf is NaN)
+    f32x4 vsc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vsc[i] = 4 * (lane >> 4) + i < nvalid ? vs[i] : 0.f;
     // K and V are consumed: the next tile's loads fly while this one accumulates.
     const int tn = t + kWaves;
-    if (tn < te) load_tile(tn < T0 ? seg0 : seg1, (tn < T0 ? tn : tn - T0) * kTile, lane, K, V);
-    accumulate_tile(sc, lane, vl, st);
+    if (tn < te)
+      load_tile<kFp8>(tn < T0 ? seg0 : seg1, (tn < T0 ? tn : tn - T0) * kTile, lane, K, V, ks, vs);
+    accumulate_tile<kFp8>(sc, lane, vl, vsc, st);
   }
 
   // Sum the denominators of the four lanes that share a head.
@@ -401,35 +486,32 @@ extern "C" size_t rma_decode_workspace_bytes(int32_t batch) {
   return static_cast<size_t>(batch) * kGroups * 2 * s * kHeadsPerGroup * kPartStride * sizeof(float);
 }
 
-extern "C" rma_status swa_rma_decode_attn(const rma_layer_state *st, int32_t batch,
-                                          const uint16_t *q_win, const uint16_t *q_rma,
-                                          const rma_norm *norm, uint16_t *o_win, float *lse_win,
-                                          uint16_t *o_rma, float *lse_rma, void *workspace,
-                                          size_t workspace_bytes, void *stream) {
-  if (!st || !norm || !q_win || !q_rma || !o_win || !lse_win || !o_rma || !lse_rma)
-    return RMA_E_ARG;
+// Validate the shared arguments and launch the decode (and the split merge).
+template <bool kFp8>
+static rma_status launch_decode(DecodeParams &p, int32_t batch, const uint16_t *q_win,
+                                const uint16_t *q_rma, const rma_norm *norm, uint16_t *o_win,
+                                float *lse_win, uint16_t *o_rma, float *lse_rma, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+  if (!norm || !q_win || !q_rma || !o_win || !lse_win || !o_rma || !lse_rma) return RMA_E_ARG;
   if (batch <= 0 || batch > RMA_MAX_BATCH) return RMA_E_ARG;
-  if (!st->win_k || !st->win_v || !st->bank_k || !st->bank_v || !st->pend_k || !st->pend_v ||
-      !st->n_bank || !st->n_pend || !st->pos || !norm->gq_win || !norm->gq_rma)
+  if (!p.win_k || !p.win_v || !p.bank_k || !p.bank_v || !p.pend_k || !p.pend_v || !p.n_bank ||
+      !p.n_pend || !p.pos || !norm->gq_win || !norm->gq_rma)
     return RMA_E_ARG;
-  const void *al[] = {st->win_k, st->win_v, st->bank_k, st->bank_v, st->pend_k, st->pend_v,
-                      q_win,     q_rma,     o_win,      o_rma,      norm->gq_win, norm->gq_rma};
-  for (const void *p : al)
-    if (!aligned16(p)) return RMA_E_ALIGN;
+  if (kFp8 && (!p.win_ks || !p.win_vs || !p.bank_ks || !p.bank_vs || !p.pend_ks || !p.pend_vs))
+    return RMA_E_ARG;
+  const void *al[] = {p.win_k, p.win_v, p.bank_k, p.bank_v,     p.pend_k,     p.pend_v,
+                      q_win,   q_rma,   o_win,    o_rma,        norm->gq_win, norm->gq_rma};
+  for (const void *ptr : al)
+    if (!aligned16(ptr)) return RMA_E_ALIGN;
+  if (kFp8) {
+    const void *as[] = {p.win_ks, p.win_vs, p.bank_ks, p.bank_vs, p.pend_ks, p.pend_vs};
+    for (const void *ptr : as)
+      if (!aligned16(ptr)) return RMA_E_ALIGN;
+  }
   const size_t need = rma_decode_workspace_bytes(batch);
   if (need > 0 && (!workspace || workspace_bytes < need)) return RMA_E_WORKSPACE;
   if (need > 0 && !aligned16(workspace)) return RMA_E_ALIGN;
 
-  DecodeParams p;
-  p.win_k = st->win_k;
-  p.win_v = st->win_v;
-  p.bank_k = st->bank_k;
-  p.bank_v = st->bank_v;
-  p.pend_k = st->pend_k;
-  p.pend_v = st->pend_v;
-  p.n_bank = st->n_bank;
-  p.n_pend = st->n_pend;
-  p.pos = st->pos;
   p.q_win = q_win;
   p.q_rma = q_rma;
   p.gq_win = norm->gq_win;
@@ -445,11 +527,58 @@ extern "C" rma_status swa_rma_decode_attn(const rma_layer_state *st, int32_t bat
   p.splits = rma_decode_splits(batch);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const unsigned units = static_cast<unsigned>(batch) * kGroups * 2;
-  hipLaunchKernelGGL(decode_attn_kernel, dim3(units * p.splits), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(decode_attn_kernel<kFp8>, dim3(units * p.splits), dim3(kThreads), 0, s, p);
   if (hipPeekAtLastError() != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
   if (p.splits > 1) {
     hipLaunchKernelGGL(decode_merge_kernel, dim3(units), dim3(kMergeThreads), 0, s, p);
     if (hipPeekAtLastError() != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
   }
   return RMA_OK;
+}
+
+extern "C" rma_status swa_rma_decode_attn(const rma_layer_state *st, int32_t batch,
+                                          const uint16_t *q_win, const uint16_t *q_rma,
+                                          const rma_norm *norm, uint16_t *o_win, float *lse_win,
+                                          uint16_t *o_rma, float *lse_rma, void *workspace,
+                                          size_t workspace_bytes, void *stream) {
+  if (!st) return RMA_E_ARG;
+  DecodeParams p{};
+  p.win_k = reinterpret_cast<const uint8_t *>(st->win_k);
+  p.win_v = reinterpret_cast<const uint8_t *>(st->win_v);
+  p.bank_k = reinterpret_cast<const uint8_t *>(st->bank_k);
+  p.bank_v = reinterpret_cast<const uint8_t *>(st->bank_v);
+  p.pend_k = reinterpret_cast<const uint8_t *>(st->pend_k);
+  p.pend_v = reinterpret_cast<const uint8_t *>(st->pend_v);
+  p.n_bank = st->n_bank;
+  p.n_pend = st->n_pend;
+  p.pos = st->pos;
+  return launch_decode<false>(p, batch, q_win, q_rma, norm, o_win, lse_win, o_rma, lse_rma,
+                              workspace, workspace_bytes, stream);
+}
+
+extern "C" rma_status swa_rma_decode_attn_fp8(const rma_layer_state_fp8 *st, int32_t batch,
+                                              const uint16_t *q_win, const uint16_t *q_rma,
+                                              const rma_norm *norm, uint16_t *o_win,
+                                              float *lse_win, uint16_t *o_rma, float *lse_rma,
+                                              void *workspace, size_t workspace_bytes,
+                                              void *stream) {
+  if (!st) return RMA_E_ARG;
+  DecodeParams p{};
+  p.win_k = st->win_k;
+  p.win_v = st->win_v;
+  p.bank_k = st->bank_k;
+  p.bank_v = st->bank_v;
+  p.pend_k = st->pend_k;
+  p.pend_v = st->pend_v;
+  p.win_ks = st->win_ks;
+  p.win_vs = st->win_vs;
+  p.bank_ks = st->bank_ks;
+  p.bank_vs = st->bank_vs;
+  p.pend_ks = st->pend_ks;
+  p.pend_vs = st->pend_vs;
+  p.n_bank = st->n_bank;
+  p.n_pend = st->n_pend;
+  p.pos = st->pos;
+  return launch_decode<true>(p, batch, q_win, q_rma, norm, o_win, lse_win, o_rma, lse_rma,
+                             workspace, workspace_bytes, stream);
 }

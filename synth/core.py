@@ -153,3 +153,74 @@ def distinct_ints_np(key: StreamKey, count: int, lo: int, hi: int) -> np.ndarray
 def bf16_bits_to_f32_np(bits: np.ndarray) -> np.ndarray:
     """Widen BF16 bit patterns to float32 (used only to summarise drawn inputs)."""
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+# ---------------------------------------------------------------- FP8 (E4M3) codes
+_E4M3_TABLE: np.ndarray | None = None
+E4M3_SPREAD = 128.0  # a N(0,1) quantile q is stored as the code nearest to 128 * q
+
+
+def normal_e4m3_table() -> np.ndarray:
+    """OCP E4M3 codes of the 65536 standard-normal quantiles times 128, clipped to
+    the format's largest finite magnitude 448 (torch's float8_e4m3fn cast, nearest
+    even).  Stored with a row scale near 1/128, a code decodes to about N(0,1)."""
+    global _E4M3_TABLE
+    if _E4M3_TABLE is None:
+        import torch
+        from scipy.special import ndtri
+
+        j = np.arange(65536, dtype=np.float64)
+        q = np.clip(ndtri((j + 0.5) / 65536.0) * E4M3_SPREAD, -448.0, 448.0).astype(np.float32)
+        t = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+        assert not np.any((t & 0x7F) == 0x7F)  # no NaN code
+        _E4M3_TABLE = t
+        _E4M3_TABLE.setflags(write=False)
+    return _E4M3_TABLE
+
+
+def normal_e4m3_np(key: StreamKey, count: int, start: int = 0) -> np.ndarray:
+    """Elements ``start .. start+count-1`` of an E4M3 code stream (uint8)."""
+    assert 0 <= start and start + count <= (1 << 32)
+    idx = np.arange(start, start + count, dtype=np.uint64)
+    return normal_e4m3_table()[(_hash_np(key, idx) >> np.uint64(16)).astype(np.int64)]
+
+
+def normal_e4m3_torch_(out, key: StreamKey, start: int = 0, chunk: int = 1 << 26) -> None:
+    """Fill the contiguous 8-bit tensor ``out`` with the same code stream."""
+    import torch
+
+    n = out.numel()
+    assert out.is_contiguous() and out.element_size() == 1
+    assert 0 <= start and start + n <= (1 << 32)
+    flat = out.view(torch.uint8).view(-1)
+    table = torch.from_numpy(normal_e4m3_table().copy()).to(out.device)
+    for c0 in range(0, n, chunk):
+        c1 = min(n, c0 + chunk)
+        idx = torch.arange(start + c0, start + c1, dtype=torch.int64, device=out.device)
+        flat[c0:c1] = table[_hash_t(key, idx) >> 16]
+        del idx
+
+
+def row_scale_np(key: StreamKey, count: int, start: int = 0) -> np.ndarray:
+    """FP32 row scales in [3/512, 4/512): (3 + u) / 512 with u = (hash >> 10) / 2^22,
+    every operation exact in FP32 (so host and device streams agree bit for bit)."""
+    assert 0 <= start and start + count <= (1 << 32)
+    idx = np.arange(start, start + count, dtype=np.uint64)
+    u = (_hash_np(key, idx) >> np.uint64(10)).astype(np.float32) * np.float32(2.0 ** -22)
+    return ((np.float32(3.0) + u) * np.float32(1.0 / 512.0)).astype(np.float32)
+
+
+def row_scale_torch_(out, key: StreamKey, start: int = 0, chunk: int = 1 << 24) -> None:
+    """Fill the contiguous FP32 tensor ``out`` with the same scale stream."""
+    import torch
+
+    n = out.numel()
+    assert out.is_contiguous() and out.dtype == torch.float32
+    assert 0 <= start and start + n <= (1 << 32)
+    flat = out.view(-1)
+    for c0 in range(0, n, chunk):
+        c1 = min(n, c0 + chunk)
+        idx = torch.arange(start + c0, start + c1, dtype=torch.int64, device=out.device)
+        u = (_hash_t(key, idx) >> 10).to(torch.float32) * (2.0 ** -22)
+        flat[c0:c1] = (u + 3.0) * (1.0 / 512.0)
+        del idx, u

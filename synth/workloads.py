@@ -16,6 +16,10 @@ group, 8 SWA||RMA layers, hidden width 2560 feeding a 2560->256->4 scorer.
                         and merge them with a full bank, with about 5% exact
                         score ties planted.
 * ``long_stream_b1``    batch 1, 8 layers, a stream to position 262143.
+* ``headline_b512_fp8`` ``headline_b512`` with every stored K/V row held as 256
+                        E4M3 codes and one FP32 scale: codes of N(0,1) quantiles
+                        times 128 with scales in [3/512, 4/512), so a row decodes
+                        to about N(0, 1) as in the BF16 state.
 
 Every large BF16 tensor is a counter-based stream (see ``synth.core``), so the
 host can regenerate any slice of what the device drew.
@@ -33,8 +37,12 @@ from .core import (
     normal_bf16_at_np,
     normal_bf16_np,
     normal_bf16_torch_,
+    normal_e4m3_np,
+    normal_e4m3_torch_,
     normal_f32_np,
     rng_np,
+    row_scale_np,
+    row_scale_torch_,
     stream_key,
 )
 
@@ -73,9 +81,11 @@ HEADLINE_B512 = Workload("headline_b512", batch=512, layers=8, position=65536, g
 COMMIT_BURST_B512 = Workload("commit_burst_b512", batch=512, layers=8, position=32767,
                              gains="ones", src_hi=32512)
 LONG_STREAM_B1 = Workload("long_stream_b1", batch=1, layers=8, position=262144, gains="normal")
+HEADLINE_B512_FP8 = Workload("headline_b512_fp8", batch=512, layers=8, position=65536,
+                             gains="normal", extra={"kv": "e4m3"})
 
 WORKLOADS = {w.name: w for w in (TINY_STREAM, STEADY_B64, HEADLINE_B512, COMMIT_BURST_B512,
-                                 LONG_STREAM_B1)}
+                                 LONG_STREAM_B1, HEADLINE_B512_FP8)}
 
 
 def key(wl: Workload | str, *names) -> StreamKey:
@@ -120,6 +130,24 @@ def kv_torch_(wl: Workload, layer: int, name: str, out) -> None:
     """Fill the device tensor ``out`` ``[B][4][slots][256]`` with the same stream."""
     assert out.shape[1:] == (KV_GROUPS, kv_slots(name), HEAD_DIM)
     normal_bf16_torch_(out, key(wl, layer, name))
+
+
+def kv_fp8_np(wl: Workload, layer: int, name: str, b: int):
+    """One sequence's FP8 slice: codes ``[4][slots][256]`` (uint8) and scales ``[4][slots]``."""
+    slots = kv_slots(name)
+    per_seq = KV_GROUPS * slots
+    codes = normal_e4m3_np(key(wl, layer, name, "e4m3"), per_seq * HEAD_DIM,
+                           start=b * per_seq * HEAD_DIM)
+    scales = row_scale_np(key(wl, layer, name, "scale"), per_seq, start=b * per_seq)
+    return codes.reshape(KV_GROUPS, slots, HEAD_DIM), scales.reshape(KV_GROUPS, slots)
+
+
+def kv_fp8_torch_(wl: Workload, layer: int, name: str, codes, scales) -> None:
+    """Fill device tensors codes ``[B][4][slots][256]`` (uint8) and scales ``[B][4][slots]``."""
+    assert codes.shape[1:] == (KV_GROUPS, kv_slots(name), HEAD_DIM)
+    assert scales.shape == codes.shape[:3]
+    normal_e4m3_torch_(codes, key(wl, layer, name, "e4m3"))
+    row_scale_torch_(scales, key(wl, layer, name, "scale"))
 
 
 def q_np(wl: Workload, layer: int, b: int, step: int = 0) -> np.ndarray:

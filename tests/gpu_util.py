@@ -129,3 +129,66 @@ def bf16_ulp_diff(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
         x = x.astype(np.int32)
         return np.where(x & 0x8000, -(x & 0x7FFF), x)
     return np.abs(ordinal(a_bits) - ordinal(b_bits))
+
+
+# ---------------------------------------------------------------- FP8 state
+KV_SCALES = tuple(nm + "s" for nm in KV)
+
+
+def upload_fp8(st) -> R.LayerStateFP8:
+    """oracle.fp8_ref.LayerStateFP8 (host) -> device state."""
+    d = {nm: torch.from_numpy(np.ascontiguousarray(getattr(st, nm), dtype=np.uint8)).to(DEV)
+         for nm in KV}
+    for nm in KV_SCALES:
+        d[nm] = f32_dev(getattr(st, nm))
+    for nm in META:
+        a = getattr(st, nm)
+        d[nm] = f32_dev(a) if a.dtype == np.float32 else i32_dev(a)
+    return R.LayerStateFP8(**d)
+
+
+def download_fp8(st: R.LayerStateFP8):
+    from oracle import fp8_ref as F
+
+    d = {nm: getattr(st, nm).cpu().numpy() for nm in KV + KV_SCALES + META}
+    return F.LayerStateFP8(**d)
+
+
+def decode_gpu_fp8(st: R.LayerStateFP8, q_win, q_rma, norm: R.Norm):
+    B = st.pos.shape[0]
+    o_w = torch.empty(B, 16, 256, dtype=torch.bfloat16, device=DEV)
+    o_r = torch.empty_like(o_w)
+    l_w = torch.empty(B, 16, dtype=torch.float32, device=DEV)
+    l_r = torch.empty_like(l_w)
+    R.swa_rma_decode_attn_fp8(st, B, q_win, q_rma, norm, o_w, l_w, o_r, l_r,
+                              R.decode_workspace(B))
+    return o_w, l_w, o_r, l_r
+
+
+def assert_fp8_keys_close(got_codes, got_scale, ref_codes, ref_scale, what=""):
+    """Stored FP8 key rows against the oracle's.
+
+    The GPU forms the normalised, rotated key in FP32 and the oracle in float64
+    (then rounds to FP32), so the two FP32 rows differ by a few units of 2^-24 of
+    the row's largest magnitude.  The row maximum, and with it the scale, can move
+    by as much; a scaled element near a rounding midpoint of the E4M3 grid can
+    then take the neighbouring code.  The bound on each dequantised element is one
+    E4M3 step at the reference element plus 2^-16 of the row's largest dequantised
+    magnitude (the scale change acting on a code up to 448, with margin); the
+    scales must agree to 2^-18 relative.
+    """
+    from oracle import fp8_ref as F
+
+    gs = np.asarray(got_scale, np.float64)
+    rs = np.asarray(ref_scale, np.float64)
+    assert np.all(np.abs(gs - rs) <= 2.0 ** -18 * rs), f"{what}: scales differ"
+    g = F.dequantize(got_codes, got_scale)
+    r = F.dequantize(ref_codes, ref_scale)
+    step = F.e4m3_step(F.e4m3_decode(ref_codes)) * rs[..., None]
+    row = np.abs(r).max(axis=-1, keepdims=True)
+    err = np.abs(g - r)
+    bound = step + 2.0 ** -16 * row
+    ndiff = int((np.asarray(got_codes) != np.asarray(ref_codes)).sum())
+    print(f"{what}: {ndiff} of {g.size} codes differ; max err/bound "
+          f"{float((err / np.maximum(bound, 1e-300)).max()):.3f}")
+    assert np.all(err <= bound), f"{what}: {int((err > bound).sum())} elements out of bound"

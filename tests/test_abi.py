@@ -96,3 +96,29 @@ def test_host_validation_rejects_bad_arguments(lib):
     assert pf(by(st), 2, 100, None, 0) == 3      # no workspace
     assert pf(by(st), 2, 100, 16, need - 1) == 3
     assert pf(by(st), 2, 100, 16, need, q=24) == 2
+
+
+def test_fp8_state_size_and_host_validation(lib):
+    # codes (1 B) + one FP32 scale per K and V row, plus the same metadata
+    rows = 2 * 4 * (1024 + 1024 + 256)
+    meta = 4 * 1024 * 8 + 256 * (4 * 4 + 4) + 12
+    assert R.rma_layer_state_fp8_bytes(3) == 3 * (rows * 260 + meta)
+    assert R.rma_layer_state_fp8_bytes(0) == 0
+    st8 = R._StateFp8C(*([16] * 19))
+    nm = _norm()
+    by = ctypes.byref
+    assert lib.swa_rma_decode_attn_fp8(None, 4, 16, 16, by(nm), 16, 16, 16, 16, None, 0, None) == 1
+    bad = R._StateFp8C(*([16] * 19))
+    bad.pend_vs = None  # a missing scale array
+    assert lib.swa_rma_decode_attn_fp8(by(bad), 512, 16, 16, by(nm), 16, 16, 16, 16, None, 0,
+                                       None) == 1
+    mis = R._StateFp8C(*([16] * 19))
+    mis.bank_ks = 20  # misaligned scale array
+    assert lib.swa_rma_decode_attn_fp8(by(mis), 512, 16, 16, by(nm), 16, 16, 16, 16, None, 0,
+                                       None) == 2
+    assert lib.swa_rma_decode_attn_fp8(by(st8), 4, 16, 16, by(nm), 16, 16, 16, 16, None, 0,
+                                       None) == 3
+    assert lib.swa_rma_append_fp8(by(bad), 2, 16, 16, 16, 16, None, by(nm), None) == 1
+    assert lib.swa_rma_append_fp8(by(st8), 0, 16, 16, 16, 16, None, by(nm), None) == 1
+    assert lib.rma_commit_topk_fp8(by(bad), 2, None, None) == 1
+    assert lib.rma_commit_topk_fp8(None, 2, None, None) == 1

@@ -72,3 +72,28 @@ def test_record_rows_at_positions():
     out = torch.empty(40, 4, 256, dtype=torch.bfloat16)
     W.record_torch_(wl, 3, "k_rma", 100, out)
     assert np.array_equal(out.view(torch.int16).numpy().view(np.uint16), full)
+
+
+def test_e4m3_streams_host_equal_torch_and_have_no_nan_codes():
+    k = synth.stream_key("synth_test", "e4m3")
+    a = synth.core.normal_e4m3_np(k, 70001, start=12345)
+    t = torch.empty(70001, dtype=torch.uint8)
+    synth.core.normal_e4m3_torch_(t, k, start=12345)
+    assert np.array_equal(a, t.numpy())
+    assert not np.any((a & 0x7F) == 0x7F)
+    v = torch.from_numpy(a.copy()).view(torch.float8_e4m3fn).double().numpy() / 128.0
+    assert abs(v.mean()) < 0.02 and abs(v.std() - 1.0) < 0.02
+    s = synth.core.row_scale_np(k, 5000, start=99)
+    ts = torch.empty(5000)
+    synth.core.row_scale_torch_(ts, k, start=99)
+    assert np.array_equal(s.view(np.uint32), ts.numpy().view(np.uint32))
+    assert s.min() >= 3 / 512 and s.max() < 4 / 512
+
+
+def test_fp8_workload_slices_consistent():
+    wl = W.HEADLINE_B512_FP8
+    codes = torch.empty(3, 4, W.BLOCK, 256, dtype=torch.uint8)
+    scales = torch.empty(3, 4, W.BLOCK)
+    W.kv_fp8_torch_(wl, 1, "pend_v", codes, scales)
+    c, s = W.kv_fp8_np(wl, 1, "pend_v", 2)
+    assert np.array_equal(codes[2].numpy(), c) and np.array_equal(scales[2].numpy(), s)
