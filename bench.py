@@ -650,7 +650,7 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": "decode_attn_kernel<true>" if fp8 else "decode_attn_kernel<false>",
+            "kernel": "decode_attn_fp8_kernel" if fp8 else "decode_attn_kernel",
             "avg_launch_ms": round(avg_launch_ms, 4),
             "median_launch_ms": round(launch_ms[len(launch_ms) // 2], 4),
             "bytes_per_launch": bytes_per_launch,

@@ -17,7 +17,7 @@
 //    the head dim is the contraction, so no reshuffle is needed), giving the
 //    scores of 16 keys x 4 heads in one 4-register accumulator.
 //  * V rows are loaded with coalesced 16-byte loads, staged in the wave's own
-//    LDS rows and read back transposed as the A operand of
+//    LDS rows and read back with transposed 8-byte LDS reads as the A operand of
 //    v_mfma_f32_16x16x16bf16_1k (contraction over keys); P (BF16) is the B
 //    operand and comes straight from the score accumulator's registers.
 //  * online softmax per head in the log2 domain: the scaled query carries
@@ -28,6 +28,12 @@
 //    are issued, and they fly while the softmax update and P x V run.
 //  * waves merge through LDS; with several splits a second kernel merges the
 //    splits' (m, l, acc) partials.
+//
+// FP8 variant (rows of 256 E4M3 codes plus one FP32 scale): 32-key tiles keep
+// the same bytes in flight per wave; codes are widened to BF16 exactly with the
+// hardware conversion and fed to the same MFMAs (the 32 keys form one 32-long
+// contraction for P x V, read back with transposed LDS reads); the K scale
+// multiplies each score and the V scale each probability weight.
 #include "rma_device.h"
 
 namespace rma {
@@ -40,7 +46,9 @@ constexpr int kWaves = RMA_DECODE_WAVES;  // waves per workgroup, all on one (br
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMergeThreads = 64 * kHeadsPerGroup;
 static_assert(kWaves >= kHeadsPerGroup, "one wave per head in the query prologue and epilogue");
-constexpr int kVStride = kDim + 8;  // LDS row stride of a V tile, in elements (528 B)
+// LDS row stride of a staged V tile, in elements: 544 bytes, so rows start 8 banks
+// apart and a transposed read of 8 rows x 32 bytes hits 64 distinct banks.
+constexpr int kVStride = kDim + 16;
 constexpr int kPartStride = 4 + kDim;
 constexpr int kMaxSplits = 20;
 #ifndef RMA_DECODE_MIN_WGS
@@ -74,7 +82,8 @@ struct DecodeParams {
 
 // One contiguous run of valid key rows (the window, the bank, or the pending
 // block of one sequence and group), addressed through buffer resources whose
-// size is the valid byte count: rows past the end read as zero.
+// size is the valid byte count.  The hardware checks the range per dword with the
+// scalar offset included, so rows (and scales) past the end read as zero.
 struct Segment {
   __amdgpu_buffer_rsrc_t k, v;
   __amdgpu_buffer_rsrc_t ks, vs;  // FP8 variant: per-row scales
@@ -90,259 +99,86 @@ __device__ __forceinline__ T bitcast(const F &f) {
   return __builtin_bit_cast(T, f);
 }
 
-// Bytes of one K/V row.
-template <bool kFp8>
-constexpr int kRowBytes = kFp8 ? kDim : 2 * kDim;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// Bytes of the scales of n rows, rounded up to whole groups of four rows.
-__device__ __forceinline__ int scale_bytes(int n) { return ((n + 3) & ~3) * 4; }
-
-// Issue the loads of one 16-key tile starting at row key0 of a segment: K as MFMA
-// A operands (lane: row key0 + lane%16, dims 32s + 8(lane/16) .. +8), V as row
-// chunks (lane: row key0 + 2i + lane/32, dims 8(lane%32) .. +8).  BF16 rows fill
-// all of each uint4; FP8 rows only .x and .y (8 codes).  The FP8 variant also
-// loads the scales of the lane's four score keys (key0 + 4(lane/16) + 0..3).
-template <bool kFp8>
-__device__ __forceinline__ void load_tile(const Segment &sg, int key0, int lane, uint4 (&K)[8],
-                                          uint4 (&V)[8], f32x4 &ks, f32x4 &vs) {
-  constexpr int RB = kRowBytes<kFp8>;
-  constexpr int EB = kFp8 ? 1 : 2;  // bytes per element
-  const int hh = lane & 15, kg = lane >> 4;
-  const int koff = hh * RB + kg * 8 * EB;
-  const int voff = (lane >> 5) * RB + (lane & 31) * 8 * EB;
-  const int soff = key0 * RB;
-  if constexpr (kFp8) {
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const auto w = __builtin_amdgcn_raw_buffer_load_b64(sg.k, koff + 32 * s, soff, kStream);
-      K[s].x = w[0];
-      K[s].y = w[1];
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const auto w = __builtin_amdgcn_raw_buffer_load_b64(sg.v, voff + 2 * RB * i, soff, kStream);
-      V[i].x = w[0];
-      V[i].y = w[1];
-    }
-    ks = bitcast<f32x4>(__builtin_amdgcn_raw_buffer_load_b128(sg.ks, 16 * kg, key0 * 4, kStream));
-    vs = bitcast<f32x4>(__builtin_amdgcn_raw_buffer_load_b128(sg.vs, 16 * kg, key0 * 4, kStream));
-  } else {
-    (void)ks;
-    (void)vs;
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-      K[s] = bitcast<uint4>(__builtin_amdgcn_raw_buffer_load_b128(sg.k, koff + 64 * s, soff, kStream));
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      V[i] = bitcast<uint4>(
-          __builtin_amdgcn_raw_buffer_load_b128(sg.v, voff + 2 * RB * i, soff, kStream));
-  }
-}
-
-// Eight E4M3 codes -> eight BF16 values (every E4M3 value is exact in BF16).
-__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
-  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
-  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
-  const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
-  const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
-  auto hi16 = [](float x, float y) {
-    return (__float_as_uint(x) >> 16) | (__float_as_uint(y) & 0xffff0000u);
-  };
-  return make_uint4(hi16(a[0], a[1]), hi16(b[0], b[1]), hi16(c[0], c[1]), hi16(d[0], d[1]));
-}
+// The staged query block: rows 0..3 hold the group's four scaled queries, rows
+// 4..15 stay zero (the score MFMA is 16 wide).  Rows are padded to 528 bytes so
+// that the 16 lanes reading one 16-byte column from 16 rows hit 16 distinct
+// groups of four banks.
+constexpr int kQStride = kDim + 8;
 
 struct SoftmaxState {
   float m, l;
   f32x4 acc[16];
 };
 
-// Stage V in LDS and form the scores of one tile (consumes K and V).  FP8 rows are
-// widened to BF16 on the way; a key's score is multiplied by its K scale.
+// ---------------------------------------------------------------- setup and epilogue
+// The key segments of one (branch, sequence, group); rb = bytes per row.
 template <bool kFp8>
-__device__ __forceinline__ f32x4 scores_tile(int nvalid, int lane, const uint4 (&K)[8],
-                                             const uint4 (&V)[8], const f32x4 &ks,
-                                             const uint16_t *ql, uint16_t *vl) {
-  const int hh = lane & 15, kg = lane >> 4;
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    *reinterpret_cast<uint4 *>(vl + (2 * i + (lane >> 5)) * kVStride + 8 * (lane & 31)) =
-        kFp8 ? fp8x8_to_bf16x8(V[i].x, V[i].y) : V[i];
-  // D[key][head] = sum_d K[key][d] * qhat[head][d]; the B operand is the staged
-  // query block (head hh; rows >= 4 are zero).  Lane holds keys 4kg..4kg+3 of head hh.
-  f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-  const uint16_t *qrow = ql + hh * kDim + 8 * kg;
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const bf16x8 qv = bitcast<bf16x8>(*reinterpret_cast<const uint4 *>(qrow + 32 * s));
-    const uint4 kv = kFp8 ? fp8x8_to_bf16x8(K[s].x, K[s].y) : K[s];
-    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(kv), qv, sc, 0, 0, 0);
-  }
-  if constexpr (kFp8) sc *= ks;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if (4 * kg + i >= nvalid) sc[i] = -INFINITY;
-  return sc;
-}
-
-// Online-softmax update and P x V for one tile whose V rows are staged in LDS.
-// The FP8 variant weighs each value row by its scale in the numerator (the
-// denominator sums the unscaled probabilities).
-template <bool kFp8>
-__device__ __forceinline__ void accumulate_tile(f32x4 sc, int lane, const uint16_t *vl,
-                                                const f32x4 &vsc, SoftmaxState &st) {
-  const int hh = lane & 15, kg = lane >> 4;
-  float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-  mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-  const float m_new = fmaxf(st.m, mt);
-  float alpha = 1.f;
-  uint32_t pw0 = 0, pw1 = 0;
-  float psum = 0.f;
-  if (m_new != -INFINITY) {
-    alpha = __builtin_amdgcn_exp2f(st.m - m_new);
-    const float e0 = __builtin_amdgcn_exp2f(sc[0] - m_new);
-    const float e1 = __builtin_amdgcn_exp2f(sc[1] - m_new);
-    const float e2 = __builtin_amdgcn_exp2f(sc[2] - m_new);
-    const float e3 = __builtin_amdgcn_exp2f(sc[3] - m_new);
-    const uint32_t p0 = f32_to_bf16(e0), p1 = f32_to_bf16(e1);
-    const uint32_t p2 = f32_to_bf16(e2), p3 = f32_to_bf16(e3);
-    // the denominator uses the same rounded weights as the numerator
-    psum = (bf16_to_f32(p0) + bf16_to_f32(p1)) + (bf16_to_f32(p2) + bf16_to_f32(p3));
-    if constexpr (kFp8) {
-      pw0 = f32_to_bf16(e0 * vsc[0]) | (f32_to_bf16(e1 * vsc[1]) << 16);
-      pw1 = f32_to_bf16(e2 * vsc[2]) | (f32_to_bf16(e3 * vsc[3]) << 16);
-    } else {
-      (void)vsc;
-      pw0 = p0 | (p1 << 16);
-      pw1 = p2 | (p3 << 16);
-    }
-  }
-  st.l = st.l * alpha + psum;
-  st.m = m_new;
-  const s16x4 pb = bitcast<s16x4>(make_uint2(pw0, pw1));
-  // D[dim][head] += sum_key V[key][dim] * P[head][key].  This wave's LDS reads
-  // follow its own writes in scores_tile (LDS runs a wave's operations in order).
-#pragma unroll
-  for (int db = 0; db < 16; ++db) {
-    const uint16_t *col = vl + db * 16 + hh + 4 * kg * kVStride;
-    const uint32_t w0 = col[0] | (static_cast<uint32_t>(col[kVStride]) << 16);
-    const uint32_t w1 = col[2 * kVStride] | (static_cast<uint32_t>(col[3 * kVStride]) << 16);
-    const s16x4 va = bitcast<s16x4>(make_uint2(w0, w1));
-    st.acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, st.acc[db] * alpha, 0, 0, 0);
-  }
-}
-
-template <bool kFp8>
-__global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(DecodeParams a) {
-  __shared__ __align__(16) uint16_t v_lds[kWaves][kTile * kVStride];
-  __shared__ __align__(16) uint16_t q_lds[16][kDim];  // rows 4..15 stay zero
-  __shared__ float red_m[kWaves][kHeadsPerGroup], red_l[kWaves][kHeadsPerGroup];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int split = blockIdx.x % a.splits;
-  const int unit = blockIdx.x / a.splits;
-  const int per_branch = a.batch * kGroups;
-  const bool anchor = unit < per_branch;  // anchor units first: they are the longer ones
-  const int bg = anchor ? unit : unit - per_branch;
-  const int b = bg / kGroups, g = bg % kGroups;
-
-  const int p = a.pos[b];
-  Segment seg0, seg1;
+__device__ __forceinline__ void unit_segments(const DecodeParams &a, int b, int g, bool anchor,
+                                              Segment &seg0, Segment &seg1) {
+  constexpr int rb = kFp8 ? kDim : 2 * kDim;
   const size_t sgi = static_cast<size_t>(b) * kGroups + g;
-  constexpr int RB = kRowBytes<kFp8>;
   if (anchor) {
     const int nb = min(max(a.n_bank[b], 0), kBank);
     const int np = min(max(a.n_pend[b], 0), kBlock);
-    seg0.k = make_rsrc(a.bank_k + sgi * kBank * RB, nb * RB);
-    seg0.v = make_rsrc(a.bank_v + sgi * kBank * RB, nb * RB);
+    seg0.k = make_rsrc(a.bank_k + sgi * kBank * rb, nb * rb);
+    seg0.v = make_rsrc(a.bank_v + sgi * kBank * rb, nb * rb);
     seg0.n = nb;
-    seg1.k = make_rsrc(a.pend_k + sgi * kBlock * RB, np * RB);
-    seg1.v = make_rsrc(a.pend_v + sgi * kBlock * RB, np * RB);
+    seg1.k = make_rsrc(a.pend_k + sgi * kBlock * rb, np * rb);
+    seg1.v = make_rsrc(a.pend_v + sgi * kBlock * rb, np * rb);
     seg1.n = np;
     if constexpr (kFp8) {
-      // scales are read four keys at a time: the range covers whole quads (the
-      // arrays hold a multiple of four rows), and keys past n are masked
-      seg0.ks = make_rsrc(a.bank_ks + sgi * kBank, scale_bytes(nb));
-      seg0.vs = make_rsrc(a.bank_vs + sgi * kBank, scale_bytes(nb));
-      seg1.ks = make_rsrc(a.pend_ks + sgi * kBlock, scale_bytes(np));
-      seg1.vs = make_rsrc(a.pend_vs + sgi * kBlock, scale_bytes(np));
+      seg0.ks = make_rsrc(a.bank_ks + sgi * kBank, nb * 4);
+      seg0.vs = make_rsrc(a.bank_vs + sgi * kBank, nb * 4);
+      seg1.ks = make_rsrc(a.pend_ks + sgi * kBlock, np * 4);
+      seg1.vs = make_rsrc(a.pend_vs + sgi * kBlock, np * 4);
     }
   } else {
-    const int nw = min(max(p + 1, 0), kWindow);
-    seg0.k = make_rsrc(a.win_k + sgi * kWindow * RB, nw * RB);
-    seg0.v = make_rsrc(a.win_v + sgi * kWindow * RB, nw * RB);
+    const int nw = min(max(a.pos[b] + 1, 0), kWindow);
+    seg0.k = make_rsrc(a.win_k + sgi * kWindow * rb, nw * rb);
+    seg0.v = make_rsrc(a.win_v + sgi * kWindow * rb, nw * rb);
     seg0.n = nw;
     if constexpr (kFp8) {
-      seg0.ks = make_rsrc(a.win_ks + sgi * kWindow, scale_bytes(nw));
-      seg0.vs = make_rsrc(a.win_vs + sgi * kWindow, scale_bytes(nw));
+      seg0.ks = make_rsrc(a.win_ks + sgi * kWindow, nw * 4);
+      seg0.vs = make_rsrc(a.win_vs + sgi * kWindow, nw * 4);
     }
     seg1 = seg0;
     seg1.n = 0;
   }
-  // Tiles of segment 0 come first, then those of segment 1; each tile lies in one
-  // segment.  This workgroup takes tiles [tb, te).
-  const int T0 = (seg0.n + kTile - 1) / kTile;
-  const int T = T0 + (seg1.n + kTile - 1) / kTile;
-  const int per = (T + a.splits - 1) / a.splits;
-  const int tb = split * per;
-  const int te = min(T, tb + per);
+}
 
-  SoftmaxState st;
-  st.m = -INFINITY;
-  st.l = 0.f;
-#pragma unroll
-  for (int d = 0; d < 16; ++d) st.acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  uint16_t *vl = v_lds[wave];
-  uint4 K[8], V[8];
-  f32x4 ks, vs;
-  int t = tb + wave;
-  // The first tile's loads do not depend on the query: issue them before the
-  // query prologue so its latency overlaps the norm and rotary work.
-  if (t < te)
-    load_tile<kFp8>(t < T0 ? seg0 : seg1, (t < T0 ? t : t - T0) * kTile, lane, K, V, ks, vs);
-
-  // Query prep: wave w < 4 normalises, rotates and scales head 4g + w.
+// Query prep: wave w < 4 normalises, rotates and scales head 4g + w into q_lds
+// row w; the other rows are zeroed.  Ends with a workgroup barrier.
+__device__ __forceinline__ void stage_query(const DecodeParams &a, int b, int g, bool anchor,
+                                            int wave, int lane, uint16_t (*q_lds)[kQStride]) {
   if (wave < kHeadsPerGroup) {
     const uint16_t *q = (anchor ? a.q_rma : a.q_win) +
                         (static_cast<size_t>(b) * kHeads + g * kHeadsPerGroup + wave) * kDim;
     const uint2 raw = *reinterpret_cast<const uint2 *>(q + 4 * lane);
     float x[4] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y)};
     float c, sn;
-    rope_cos_sin(a.rope_ratio, p, lane, c, sn);
+    rope_cos_sin(a.rope_ratio, a.pos[b], lane, c, sn);
     norm_rope_head(x, anchor ? a.gq_rma : a.gq_win, a.eps, c, sn, lane);
     uint2 o;
     o.x = pack_bf16x2(x[0] * kQScale, x[1] * kQScale);
     o.y = pack_bf16x2(x[2] * kQScale, x[3] * kQScale);
     *reinterpret_cast<uint2 *>(&q_lds[wave][4 * lane]) = o;
   }
-  for (int i = threadIdx.x; i < 12 * kDim / 4; i += kThreads)
+  for (int i = threadIdx.x; i < 12 * kQStride / 4; i += kThreads)
     reinterpret_cast<uint2 *>(&q_lds[kHeadsPerGroup][0])[i] = make_uint2(0, 0);
   __syncthreads();
+}
 
-  for (; t < te; t += kWaves) {
-    const int key0 = (t < T0 ? t : t - T0) * kTile;
-    const int nvalid = (t < T0 ? seg0.n : seg1.n) - key0;
-    const f32x4 sc = scores_tile<kFp8>(nvalid, lane, K, V, ks, &q_lds[0][0], vl);
-    // this tile's value scales, taken before the next tile's loads; a key past the
-    // end weighs 0 whatever its slot holds (its probability is 0, and 0 * inf is NaN)
-    f32x4 vsc;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) vsc[i] = 4 * (lane >> 4) + i < nvalid ? vs[i] : 0.f;
-    // K and V are consumed: the next tile's loads fly while this one accumulates.
-    const int tn = t + kWaves;
-    if (tn < te)
-      load_tile<kFp8>(tn < T0 ? seg0 : seg1, (tn < T0 ? tn : tn - T0) * kTile, lane, K, V, ks, vs);
-    accumulate_tile<kFp8>(sc, lane, vl, vsc, st);
-  }
-
+// Merge the four waves' partial softmax states through LDS (macc: 16 KiB that no
+// wave reads any more) and write the output, or this split's partial.
+__device__ __forceinline__ void finish_unit(const DecodeParams &a, const SoftmaxState &st,
+                                            float *macc, float (*red_m)[kHeadsPerGroup],
+                                            float (*red_l)[kHeadsPerGroup], int wave, int lane,
+                                            int unit, int split, bool anchor, int b, int g) {
   // Sum the denominators of the four lanes that share a head.
   float l_tot = st.l + __shfl_xor(st.l, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
-
-  __syncthreads();  // every wave is done with its V rows; reuse them for the merge
-  float *macc = reinterpret_cast<float *>(&v_lds[0][0]);  // [wave][head][256]
   {
     const int hh = lane & 15, kg = lane >> 4;
     if (hh < kHeadsPerGroup) {
@@ -403,6 +239,342 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(DecodeParams a
     }
     *reinterpret_cast<float4 *>(pp + 4 + 4 * lane) = O;
   }
+}
+
+// ---------------------------------------------------------------- BF16 rows
+// Issue the loads of one 16-key tile starting at row key0 of a segment: K as MFMA
+// A operands (lane: row key0 + lane%16, dims 32s + 8(lane/16) .. +8), V as row
+// chunks (lane: row key0 + 2i + lane/32, dims 8(lane%32) .. +8).
+__device__ __forceinline__ void load_tile(const Segment &sg, int key0, int lane, uint4 (&K)[8],
+                                          uint4 (&V)[8]) {
+  const int hh = lane & 15, kg = lane >> 4;
+  const int koff = hh * (kDim * 2) + kg * 16;
+  const int voff = (lane >> 5) * (kDim * 2) + (lane & 31) * 16;
+  const int soff = key0 * (kDim * 2);
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+    K[s] = bitcast<uint4>(__builtin_amdgcn_raw_buffer_load_b128(sg.k, koff + 64 * s, soff, kStream));
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    V[i] = bitcast<uint4>(
+        __builtin_amdgcn_raw_buffer_load_b128(sg.v, voff + 2 * kDim * 2 * i, soff, kStream));
+}
+
+// Stage V in LDS and form the scores of one tile (consumes K and V).
+__device__ __forceinline__ f32x4 scores_tile(int nvalid, int lane, const uint4 (&K)[8],
+                                             const uint4 (&V)[8], const uint16_t *ql,
+                                             uint16_t *vl) {
+  const int hh = lane & 15, kg = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    *reinterpret_cast<uint4 *>(vl + (2 * i + (lane >> 5)) * kVStride + 8 * (lane & 31)) = V[i];
+  // D[key][head] = sum_d K[key][d] * qhat[head][d]; the B operand is the staged
+  // query block (head hh; rows >= 4 are zero).  Lane holds keys 4kg..4kg+3 of head hh.
+  f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+  const uint16_t *qrow = ql + hh * kQStride + 8 * kg;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const bf16x8 qv = bitcast<bf16x8>(*reinterpret_cast<const uint4 *>(qrow + 32 * s));
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(K[s]), qv, sc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (4 * kg + i >= nvalid) sc[i] = -INFINITY;
+  return sc;
+}
+
+// Online-softmax update and P x V for one tile whose V rows are staged in LDS.
+__device__ __forceinline__ void accumulate_tile(f32x4 sc, int lane, const uint16_t *vl,
+                                                SoftmaxState &st) {
+  const int kg = lane >> 4;
+  float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+  mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+  const float m_new = fmaxf(st.m, mt);
+  float alpha = 1.f;
+  uint32_t pw0 = 0, pw1 = 0;
+  float psum = 0.f;
+  if (m_new != -INFINITY) {
+    alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+    const uint32_t p0 = f32_to_bf16(__builtin_amdgcn_exp2f(sc[0] - m_new));
+    const uint32_t p1 = f32_to_bf16(__builtin_amdgcn_exp2f(sc[1] - m_new));
+    const uint32_t p2 = f32_to_bf16(__builtin_amdgcn_exp2f(sc[2] - m_new));
+    const uint32_t p3 = f32_to_bf16(__builtin_amdgcn_exp2f(sc[3] - m_new));
+    // the denominator uses the same rounded weights as the numerator
+    psum = (bf16_to_f32(p0) + bf16_to_f32(p1)) + (bf16_to_f32(p2) + bf16_to_f32(p3));
+    pw0 = p0 | (p1 << 16);
+    pw1 = p2 | (p3 << 16);
+  }
+  // rescale the accumulators only when some head's running maximum moved (alpha
+  // is exactly 1 otherwise)
+  if (__any(m_new != st.m)) {
+#pragma unroll
+    for (int db = 0; db < 16; ++db) st.acc[db] *= alpha;
+  }
+  st.l = st.l * alpha + psum;
+  st.m = m_new;
+  const s16x4 pb = bitcast<s16x4>(make_uint2(pw0, pw1));
+  // D[dim][head] += sum_key V[key][dim] * P[head][key].  This wave's LDS reads
+  // follow its own writes in scores_tile (LDS runs a wave's operations in order).
+  // Transposed read: lane r of group kg supplies row 4kg + r/4, dims 4(r%4) .. +4 of
+  // a 16-dim block and receives dim r of rows 4kg .. 4kg+3.
+  const int r = lane & 15;
+  const uint16_t *src = vl + (4 * kg + (r >> 2)) * kVStride + 4 * (r & 3);
+#pragma unroll
+  for (int db = 0; db < 16; ++db) {
+    const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src + 16 * db));
+    st.acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, st.acc[db], 0, 0, 0);
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(DecodeParams a) {
+  __shared__ __align__(16) uint16_t v_lds[kWaves][kTile * kVStride];
+  __shared__ __align__(16) uint16_t q_lds[16][kQStride];  // rows 4..15 stay zero
+  __shared__ float red_m[kWaves][kHeadsPerGroup], red_l[kWaves][kHeadsPerGroup];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int split = blockIdx.x % a.splits;
+  const int unit = blockIdx.x / a.splits;
+  const int per_branch = a.batch * kGroups;
+  const bool anchor = unit < per_branch;  // anchor units first: they are the longer ones
+  const int bg = anchor ? unit : unit - per_branch;
+  const int b = bg / kGroups, g = bg % kGroups;
+
+  Segment seg0, seg1;
+  unit_segments<false>(a, b, g, anchor, seg0, seg1);
+  // Tiles of segment 0 come first, then those of segment 1; each tile lies in one
+  // segment.  This workgroup takes tiles [tb, te).
+  const int T0 = (seg0.n + kTile - 1) / kTile;
+  const int T = T0 + (seg1.n + kTile - 1) / kTile;
+  const int per = (T + a.splits - 1) / a.splits;
+  const int tb = split * per;
+  const int te = min(T, tb + per);
+
+  SoftmaxState st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int d = 0; d < 16; ++d) st.acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  uint16_t *vl = v_lds[wave];
+  uint4 K[8], V[8];
+  int t = tb + wave;
+  // The first tile's loads do not depend on the query: issue them before the
+  // query prologue so its latency overlaps the norm and rotary work.
+  if (t < te) load_tile(t < T0 ? seg0 : seg1, (t < T0 ? t : t - T0) * kTile, lane, K, V);
+  stage_query(a, b, g, anchor, wave, lane, q_lds);
+
+  for (; t < te; t += kWaves) {
+    const int key0 = (t < T0 ? t : t - T0) * kTile;
+    const int nvalid = (t < T0 ? seg0.n : seg1.n) - key0;
+    const f32x4 sc = scores_tile(nvalid, lane, K, V, &q_lds[0][0], vl);
+    // K and V are consumed: the next tile's loads fly while this one accumulates.
+    const int tn = t + kWaves;
+    if (tn < te) load_tile(tn < T0 ? seg0 : seg1, (tn < T0 ? tn : tn - T0) * kTile, lane, K, V);
+    accumulate_tile(sc, lane, vl, st);
+  }
+
+  __syncthreads();  // every wave is done with its V rows; reuse them for the merge
+  finish_unit(a, st, reinterpret_cast<float *>(&v_lds[0][0]), red_m, red_l, wave, lane, unit,
+              split, anchor, b, g);
+}
+
+// ---------------------------------------------------------------- FP8 rows
+// A tile holds 32 keys, so a wave keeps 16 KiB of codes in flight, as a BF16 tile
+// of 16 keys does: half the bytes per key would otherwise halve the bytes in
+// flight, and with them the bandwidth a latency-bound stream reaches.  Codes are
+// widened to BF16 (exactly) for the same MFMAs; the K scale multiplies the score
+// and the V scale the probability weight of its key.
+constexpr int kTile8 = 32;
+// LDS row stride of a staged (widened) V tile, in elements: 544 bytes, so rows
+// start 8 banks apart and a transposed read of 8 rows x 32 bytes hits 64 banks.
+constexpr int kVStride8 = kDim + 16;
+
+// Eight E4M3 codes (two words) -> eight BF16 values.
+__device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  return make_uint4(bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false)),
+                    bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true)),
+                    bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false)),
+                    bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true)));
+}
+
+// Loads of one 32-key tile at row key0 of a segment (16-byte loads throughout):
+//  K[4u + s]: key key0 + 16u + lane%16, codes of dims 64s + 16(lane/16) .. +16;
+//  V[i]:      row key0 + 4i + lane/16, codes of dims 16(lane%16) .. +16;
+//  ks[u], vs[u]: scales of keys key0 + 16u + 4(lane/16) .. +4 (the lane's score keys).
+__device__ __forceinline__ void load_tile_fp8(const Segment &sg, int key0, int lane,
+                                              uint4 (&K)[8], uint4 (&V)[8], f32x4 (&ks)[2],
+                                              f32x4 (&vs)[2]) {
+  const int hh = lane & 15, kg = lane >> 4;
+  const int soff = key0 * kDim;
+  const int koff = hh * kDim + 16 * kg;
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      K[4 * u + s] = bitcast<uint4>(__builtin_amdgcn_raw_buffer_load_b128(
+          sg.k, koff + 16 * u * kDim + 64 * s, soff, kStream));
+  const int voff = (lane >> 4) * kDim + 16 * (lane & 15);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    V[i] = bitcast<uint4>(
+        __builtin_amdgcn_raw_buffer_load_b128(sg.v, voff + 4 * i * kDim, soff, kStream));
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    ks[u] = bitcast<f32x4>(
+        __builtin_amdgcn_raw_buffer_load_b128(sg.ks, 4 * (16 * u + 4 * kg), key0 * 4, kStream));
+    vs[u] = bitcast<f32x4>(
+        __builtin_amdgcn_raw_buffer_load_b128(sg.vs, 4 * (16 * u + 4 * kg), key0 * 4, kStream));
+  }
+}
+
+// Stage the widened V rows and form the scores of the tile's two 16-key halves.
+// The contraction over the head dimension runs in a permuted order that the K
+// loads and the query reads share: MFMA (s, h) covers, for lane group kg, dims
+// 64s + 16kg + 8h .. +8.  Lane holds, in sc[u], keys 16u + 4kg .. +4 of head hh.
+__device__ __forceinline__ void scores_tile_fp8(int nvalid, int lane, const uint4 (&K)[8],
+                                                const uint4 (&V)[8], const f32x4 (&ks)[2],
+                                                const uint16_t *ql, uint16_t *vl,
+                                                f32x4 (&sc)[2]) {
+  const int hh = lane & 15, kg = lane >> 4;
+  uint16_t *vrow = vl + (lane >> 4) * kVStride8 + 16 * (lane & 15);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    *reinterpret_cast<uint4 *>(vrow + 4 * i * kVStride8) = e4m3x8_to_bf16x8(V[i].x, V[i].y);
+    *reinterpret_cast<uint4 *>(vrow + 4 * i * kVStride8 + 8) = e4m3x8_to_bf16x8(V[i].z, V[i].w);
+  }
+  sc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+  sc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint16_t *qrow = ql + hh * kQStride + 16 * kg;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const bf16x8 qv = bitcast<bf16x8>(*reinterpret_cast<const uint4 *>(qrow + 64 * s + 8 * h));
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const uint4 &kw = K[4 * u + s];
+        const uint4 kb = h ? e4m3x8_to_bf16x8(kw.z, kw.w) : e4m3x8_to_bf16x8(kw.x, kw.y);
+        sc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(kb), qv, sc[u], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    sc[u] *= ks[u];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (16 * u + 4 * kg + i >= nvalid) sc[u][i] = -INFINITY;
+  }
+}
+
+// Online-softmax update over the tile's 32 keys and P x V with the keys as a
+// 32-long contraction in the order (4kg .. 4kg+3, 16 + 4kg .. 16 + 4kg+3) for
+// lane group kg: the P operand comes straight from the score registers and the V
+// operand from two transposed 8-byte LDS reads.  A key's numerator weight is its
+// rounded probability times its V scale; the denominator sums the rounded
+// probabilities.  A key past the end has probability 0 and scale 0.
+__device__ __forceinline__ void accumulate_tile_fp8(const f32x4 (&sc)[2], int lane,
+                                                    const uint16_t *vl, const f32x4 (&vsc)[2],
+                                                    SoftmaxState &st) {
+  const int kg = lane >> 4, r = lane & 15;
+  float mt = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                   fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+  mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+  const float m_new = fmaxf(st.m, mt);
+  float alpha = 1.f;
+  uint32_t pw[4] = {0, 0, 0, 0};
+  float psum = 0.f;
+  if (m_new != -INFINITY) {
+    alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float e[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        e[i] = __builtin_amdgcn_exp2f(sc[u][i] - m_new);
+        psum += bf16_to_f32(static_cast<uint16_t>(f32_to_bf16(e[i])));
+      }
+      pw[2 * u] = pack_bf16x2(e[0] * vsc[u][0], e[1] * vsc[u][1]);
+      pw[2 * u + 1] = pack_bf16x2(e[2] * vsc[u][2], e[3] * vsc[u][3]);
+    }
+  }
+  if (__any(m_new != st.m)) {
+#pragma unroll
+    for (int db = 0; db < 16; ++db) st.acc[db] *= alpha;
+  }
+  st.l = st.l * alpha + psum;
+  st.m = m_new;
+  const bf16x8 pb = bitcast<bf16x8>(make_uint4(pw[0], pw[1], pw[2], pw[3]));
+  // Transposed read: lane r of group kg supplies row 4kg + r/4, dims 4(r%4) .. +4 of
+  // a 16-dim block, and receives dim r of rows 4kg .. 4kg+3 (16 rows further on
+  // for the second half).
+  const uint16_t *src = vl + (4 * kg + (r >> 2)) * kVStride8 + 4 * (r & 3);
+#pragma unroll
+  for (int db = 0; db < 16; ++db) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src + 16 * db));
+    const s16x4 hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src + 16 * kVStride8 + 16 * db));
+    const bf16x8 va = bitcast<bf16x8>(make_uint4(bitcast<uint2>(lo).x, bitcast<uint2>(lo).y,
+                                                 bitcast<uint2>(hi).x, bitcast<uint2>(hi).y));
+    st.acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, st.acc[db], 0, 0, 0);
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 2) void decode_attn_fp8_kernel(DecodeParams a) {
+  __shared__ __align__(16) uint16_t v_lds[kWaves][kTile8 * kVStride8];
+  __shared__ __align__(16) uint16_t q_lds[16][kQStride];  // rows 4..15 stay zero
+  __shared__ float red_m[kWaves][kHeadsPerGroup], red_l[kWaves][kHeadsPerGroup];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int split = blockIdx.x % a.splits;
+  const int unit = blockIdx.x / a.splits;
+  const int per_branch = a.batch * kGroups;
+  const bool anchor = unit < per_branch;
+  const int bg = anchor ? unit : unit - per_branch;
+  const int b = bg / kGroups, g = bg % kGroups;
+
+  Segment seg0, seg1;
+  unit_segments<true>(a, b, g, anchor, seg0, seg1);
+  const int T0 = (seg0.n + kTile8 - 1) / kTile8;
+  const int T = T0 + (seg1.n + kTile8 - 1) / kTile8;
+  const int per = (T + a.splits - 1) / a.splits;
+  const int tb = split * per;
+  const int te = min(T, tb + per);
+
+  SoftmaxState st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int d = 0; d < 16; ++d) st.acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  uint16_t *vl = v_lds[wave];
+  uint4 K[8], V[8];
+  f32x4 ks[2], vs[2];
+  int t = tb + wave;
+  if (t < te)
+    load_tile_fp8(t < T0 ? seg0 : seg1, (t < T0 ? t : t - T0) * kTile8, lane, K, V, ks, vs);
+  stage_query(a, b, g, anchor, wave, lane, q_lds);
+
+  for (; t < te; t += kWaves) {
+    const int key0 = (t < T0 ? t : t - T0) * kTile8;
+    const int nvalid = (t < T0 ? seg0.n : seg1.n) - key0;
+    f32x4 sc[2];
+    scores_tile_fp8(nvalid, lane, K, V, ks, &q_lds[0][0], vl, sc);
+    const f32x4 vsc[2] = {vs[0], vs[1]};  // this tile's, before the next tile's loads
+    const int tn = t + kWaves;
+    if (tn < te)
+      load_tile_fp8(tn < T0 ? seg0 : seg1, (tn < T0 ? tn : tn - T0) * kTile8, lane, K, V, ks,
+                    vs);
+    accumulate_tile_fp8(sc, lane, vl, vsc, st);
+  }
+
+  __syncthreads();
+  finish_unit(a, st, reinterpret_cast<float *>(&v_lds[0][0]), red_m, red_l, wave, lane, unit,
+              split, anchor, b, g);
 }
 
 // Merge the splits of one (branch, sequence, group): 4 waves, one per head.
@@ -527,7 +699,10 @@ static rma_status launch_decode(DecodeParams &p, int32_t batch, const uint16_t *
   p.splits = rma_decode_splits(batch);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const unsigned units = static_cast<unsigned>(batch) * kGroups * 2;
-  hipLaunchKernelGGL(decode_attn_kernel<kFp8>, dim3(units * p.splits), dim3(kThreads), 0, s, p);
+  if constexpr (kFp8)
+    hipLaunchKernelGGL(decode_attn_fp8_kernel, dim3(units * p.splits), dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(decode_attn_kernel, dim3(units * p.splits), dim3(kThreads), 0, s, p);
   if (hipPeekAtLastError() != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
   if (p.splits > 1) {
     hipLaunchKernelGGL(decode_merge_kernel, dim3(units), dim3(kMergeThreads), 0, s, p);
