@@ -69,6 +69,16 @@ def measured_traffic(workload: str, units_per_launch: int):
     return float(kv["hbm_bytes_per_launch"])
 
 
+def _blas_threads() -> int:
+    """Threads the oracle's NumPy/BLAS calls may use on this host."""
+    try:
+        from threadpoolctl import threadpool_info
+
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
 def cpu_baseline(wl, budget_s: float, max_units: int):
     """The oracle, untuned, on a bounded sample of (sequence, layer) units."""
     import numpy as np
@@ -79,12 +89,7 @@ def cpu_baseline(wl, budget_s: float, max_units: int):
 
     fp8 = wl.extra.get("kv") == "e4m3"
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = 1
+    cores = _blas_threads()
     rng = np.random.default_rng(7)
     units = 0
     spent = 0.0
@@ -486,6 +491,125 @@ def bench_prefill(args):
     }
 
 
+def bench_gdn(args):
+    """One decode step of the 24 Gated DeltaNet layers for every sequence (24 dependent
+    launches of gdn_decode_step on one stream): FP16 matrices at batch 512, FP32 at
+    batch 1.  The state evolves from step to step, as in a stream."""
+    import numpy as np
+    import torch
+
+    import oracle.gdn_ref as G
+    import swa_memory_anchor_amd as R
+    from synth import workloads as W
+
+    wl = W.GDN_DECODE_B512 if args.workload == "gdn_decode_b512" else W.GDN_DECODE_B1
+    B, L, dev = wl.batch, wl.layers, "cuda"
+    f32 = wl.extra["state"] == "f32"
+    dt = torch.float32 if f32 else torch.float16
+    stream = torch.cuda.current_stream()
+    layers = []
+    for layer in range(L):
+        st = R.GdnState(torch.empty(B, 32, 128, 128, dtype=dt, device=dev),
+                        torch.empty(B, 4, 8192, dtype=torch.bfloat16, device=dev))
+        W.gdn_state_torch_(wl, layer, st.S)
+        W.gdn_conv_torch_(wl, layer, st.conv)
+        x = torch.empty(B, 8192, dtype=torch.bfloat16, device=dev)
+        W.gdn_x_torch_(wl, layer, x)
+        a, b = W.gdn_gate_inputs(wl, layer)
+        p = W.gdn_params(wl, layer)
+        prm = R.GdnParams(*[torch.from_numpy(p[k]).to(dev) for k in ("conv_w", "a_log",
+                                                                     "dt_bias")])
+        layers.append((st, x, torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev),
+                       torch.full((B,), wl.position, dtype=torch.int32, device=dev), prm,
+                       torch.empty(B, 32, 128, dtype=torch.bfloat16, device=dev)))
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        for l, (st, x, a, b, pos, prm, o) in enumerate(layers):
+            if ev is not None:
+                ev[l][0].record(stream)
+            R.gdn_decode_step(st, B, x, a, b, pos, prm, o, stream)
+            if ev is not None:
+                ev[l][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / args.steps
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in range(L)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    launch_ms = sorted(e[0].elapsed_time(e[1]) for s_ in evs for e in s_)
+    avg_launch = sum(launch_ms) / len(launch_ms)
+    unit = G.step_bytes_per_unit(4 if f32 else 2)
+    bytes_per_launch = B * unit
+    achieved = bytes_per_launch / (avg_launch / 1e3) / 1e9
+    res = {
+        "metric": "GDN decode steps/s ×batch and HBM GB/s (24 Gated DeltaNet layers)",
+        "value": round(B / (step_ms / 1e3), 1),
+        "unit": "seq-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if f32 else "f16 state, f32 math",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "layers": L, "position": wl.position,
+                   "state": wl.extra["state"], "bytes_per_unit": unit,
+                   "workgroups_per_launch": B * 32 * (1 if B >= 16 else 4)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "gdn_decode_kernel", "avg_launch_ms": round(avg_launch, 4),
+                     "median_launch_ms": round(launch_ms[len(launch_ms) // 2], 4),
+                     "bytes_per_launch": bytes_per_launch},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_gdn(wl, min(args.cpu_budget, 10.0))
+    return res
+
+
+def cpu_baseline_gdn(wl, budget_s: float):
+    """The GDN oracle, untuned, on random (sequence, layer) units (all 32 heads each)."""
+    import numpy as np
+
+    import oracle.gdn_ref as G
+    from synth import workloads as W
+
+    rng = np.random.default_rng(11)
+    units, spent = 0, 0.0
+    wall0 = time.perf_counter()
+    while spent < budget_s and time.perf_counter() - wall0 < 3 * budget_s:
+        b, layer = int(rng.integers(0, wl.batch)), int(rng.integers(0, wl.layers))
+        dt = np.float16 if wl.extra["state"] == "f16" else np.float32
+        st = G.GdnState(np.stack([W.gdn_state_np(wl, layer, b, h) for h in range(32)])[None]
+                        .astype(dt), W.gdn_conv_np(wl, layer, b)[None].copy())
+        a, bb = W.gdn_gate_inputs(wl, layer)
+        p = W.gdn_params(wl, layer)
+        x = W.gdn_x_np(wl, layer, b)[None]
+        t0 = time.perf_counter()
+        G.decode_step(st, x, a[b:b + 1], bb[b:b + 1], p["conv_w"], p["a_log"], p["dt_bias"],
+                      [wl.position])
+        spent += time.perf_counter() - t0
+        units += 1
+    return {"value": units / spent / wl.layers, "unit": "seq-steps/s", "cores": _blas_threads(),
+            "kind": "oracle",
+            "sample": f"{units} random (sequence, layer) units of {wl.name} (32 heads each), "
+                      f"{spent:.1f} s of oracle time; value = units/s / {wl.layers} layers"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -494,7 +618,7 @@ def main() -> int:
     ap.add_argument("--workload", default="headline_b512",
                     choices=["headline_b512", "headline_b512_fp8", "steady_b64", "batch1",
                              "commit_burst_b512", "long_stream_b1", "prefill_b512",
-                             "prefill_b64"])
+                             "prefill_b64", "gdn_decode_b512", "gdn_decode_b1"])
     ap.add_argument("--stream-tokens", type=int, default=16384,
                     help="long_stream_b1: tokens streamed (the second half is timed)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
@@ -532,6 +656,9 @@ def main() -> int:
         return 0
     if args.workload.startswith("prefill"):
         print(json.dumps(bench_prefill(args)))
+        return 0
+    if args.workload.startswith("gdn"):
+        print(json.dumps(bench_gdn(args)))
         return 0
     if args.workload == "headline_b512":
         wl = W.HEADLINE_B512

@@ -30,7 +30,7 @@ EXPORTS = (
     "rma_decode_splits", "swa_rma_append", "swa_rma_decode_attn", "rma_score",
     "rma_commit_topk", "rma_status_str", "rma_prefill_workspace_bytes", "swa_rma_prefill",
     "rma_layer_state_fp8_bytes", "swa_rma_append_fp8", "swa_rma_decode_attn_fp8",
-    "rma_commit_topk_fp8",
+    "rma_commit_topk_fp8", "gdn_layer_state_bytes", "gdn_decode_step",
 )
 
 _c_void_p = ctypes.c_void_p
@@ -58,6 +58,14 @@ class _StateFp8C(ctypes.Structure):
 class _NormC(ctypes.Structure):
     _fields_ = [("gq_win", _c_void_p), ("gk_win", _c_void_p), ("gq_rma", _c_void_p),
                 ("gk_rma", _c_void_p), ("eps", ctypes.c_float), ("rope_base", ctypes.c_float)]
+
+
+class _GdnStateC(ctypes.Structure):
+    _fields_ = [("S", _c_void_p), ("conv", _c_void_p)]
+
+
+class _GdnParamsC(ctypes.Structure):
+    _fields_ = [("conv_w", _c_void_p), ("a_log", _c_void_p), ("dt_bias", _c_void_p)]
 
 
 _LIB = None
@@ -98,6 +106,10 @@ def lib() -> ctypes.CDLL:
         L.swa_rma_decode_attn_fp8.restype = ctypes.c_int
         L.rma_commit_topk_fp8.argtypes = [s8, i32, vp, vp]
         L.rma_commit_topk_fp8.restype = ctypes.c_int
+        L.gdn_layer_state_bytes.argtypes, L.gdn_layer_state_bytes.restype = [i32, i32], sz
+        L.gdn_decode_step.argtypes = [ctypes.POINTER(_GdnStateC), i32, i32, vp, vp, vp, vp,
+                                      ctypes.POINTER(_GdnParamsC), vp, vp]
+        L.gdn_decode_step.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -357,3 +369,54 @@ def rma_commit_topk_fp8(st: LayerStateFP8, batch: int, keep_idx=None, stream=Non
     s = lib().rma_commit_topk_fp8(ctypes.byref(_state_fp8_c(st)), int(batch), _ptr(keep_idx),
                                   _stream(stream))
     _check(s, "rma_commit_topk_fp8")
+
+
+# ---------------------------------------------------------------- GDN decode step (gdn.h)
+GDN_K_HEADS, GDN_V_HEADS, GDN_HEAD_DIM, GDN_CONV, GDN_CONV_DIM = 16, 32, 128, 4, 8192
+GDN_STATE_F16, GDN_STATE_F32 = 0, 1
+
+
+@dataclass
+class GdnState:
+    """One GDN layer: S [B][32][128][128] (float16 or float32), conv bf16 [B][4][8192]."""
+
+    S: object
+    conv: object
+
+    @property
+    def dtype_code(self) -> int:
+        import torch
+
+        return GDN_STATE_F32 if self.S.dtype == torch.float32 else GDN_STATE_F16
+
+
+@dataclass
+class GdnParams:
+    """conv_w f32 [8192][4], a_log f32 [32], dt_bias f32 [32] (device)."""
+
+    conv_w: object
+    a_log: object
+    dt_bias: object
+
+
+def alloc_gdn_state(batch: int, dtype: str = "f16", device="cuda") -> GdnState:
+    """Zero state (the start of a stream)."""
+    import torch
+
+    dt = torch.float16 if dtype == "f16" else torch.float32
+    return GdnState(torch.zeros(batch, GDN_V_HEADS, GDN_HEAD_DIM, GDN_HEAD_DIM, dtype=dt,
+                                device=device),
+                    torch.zeros(batch, GDN_CONV, GDN_CONV_DIM, dtype=torch.bfloat16, device=device))
+
+
+def gdn_layer_state_bytes(batch: int, state_dtype: int) -> int:
+    return int(lib().gdn_layer_state_bytes(int(batch), int(state_dtype)))
+
+
+def gdn_decode_step(st: GdnState, batch: int, x, a, b, pos, prm: GdnParams, o,
+                    stream=None) -> None:
+    sc = _GdnStateC(_ptr(st.S), _ptr(st.conv))
+    pc = _GdnParamsC(_ptr(prm.conv_w), _ptr(prm.a_log), _ptr(prm.dt_bias))
+    s = lib().gdn_decode_step(ctypes.byref(sc), int(batch), st.dtype_code, _ptr(x), _ptr(a),
+                              _ptr(b), _ptr(pos), ctypes.byref(pc), _ptr(o), _stream(stream))
+    _check(s, "gdn_decode_step")

@@ -1,0 +1,287 @@
+// Decode step of the Gated DeltaNet (GDN) layers on gfx950.
+//
+// fluxbbs.com "EdgeRock-4B 开源：72 MiB 固定 KV，AIME 82.9 分": 24 GDN layers carry a
+// fixed-size recurrent matrix per value head (section "架构：递归、局部窗口与记忆锚点
+// 三件套": 16 key heads, 32 value heads, convolution width 4), held in FP16 when
+// batched and FP32 at batch 1 (section "72 MiB 是怎么算出来的").  The step is the
+// gated delta rule (see gdn.h for the conventions and the head-width reading).
+//
+// Bound: HBM.  Per (sequence, layer) the step reads and writes the 32 value heads'
+// 128 x 128 matrices (2 MiB in FP16) against about 6 flop per element, so the
+// kernel is built to move each matrix byte once:
+//  * one workgroup (4 waves) per (sequence, value head, column slice); a thread
+//    owns 8 consecutive value columns of a few key rows and loads them with
+//    16-byte non-temporal loads, issued before anything else;
+//  * meanwhile the workgroup forms the head's convolution outputs (q and k of
+//    its key head, v of its value head), their L2 norms, k.q and the two gates;
+//  * the new matrix follows from the old one in one pass: with S' = aS + k u^T
+//    and u = b (v - a S^T k), the output S'^T q = a S^T q + u (k.q) needs the
+//    same column sums S^T k and S^T q, reduced over the key rows (shuffles, then
+//    LDS across the waves); each thread then writes its elements of S' once;
+//  * a column slice narrower than the head spreads a small batch over more
+//    workgroups (the column sums do not cross columns).
+#include <hip/hip_runtime.h>
+
+#include "gdn.h"
+#include "rma_device.h"
+
+namespace gdn {
+
+constexpr int kKH = GDN_K_HEADS;
+constexpr int kVH = GDN_V_HEADS;
+constexpr int kD = GDN_HEAD_DIM;
+constexpr int kConv = GDN_CONV;
+constexpr int kCD = GDN_CONV_DIM;
+constexpr int kKeyDim = kKH * kD;  // channel offset of k
+constexpr int kValOff = 2 * kKeyDim;  // channel offset of v
+constexpr int kThreads = 256;
+constexpr float kL2Eps = 1e-6f;
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+struct Params {
+  void *S;
+  uint16_t *conv;
+  const uint16_t *x;
+  const float *a, *b;
+  const int32_t *pos;
+  const float *conv_w, *a_log, *dt_bias;
+  uint16_t *o;
+};
+
+__device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// SiLU of the width-4 causal convolution of channel ch at position p: the three
+// previous inputs come from the ring, the current one from x.
+__device__ __forceinline__ float conv_silu(const Params &pr, const uint16_t *ring,
+                                           const uint16_t *xb, int p, int ch) {
+  const float4 w = *reinterpret_cast<const float4 *>(pr.conv_w + 4 * ch);
+  float acc = w.x * bf16f(ring[((p - 3) & 3) * kCD + ch]);
+  acc = fmaf(w.y, bf16f(ring[((p - 2) & 3) * kCD + ch]), acc);
+  acc = fmaf(w.z, bf16f(ring[((p - 1) & 3) * kCD + ch]), acc);
+  acc = fmaf(w.w, bf16f(xb[ch]), acc);
+  return acc / (1.f + expf(-acc));
+}
+
+template <bool kF32, int kCW>
+__global__ __launch_bounds__(kThreads) void gdn_decode_kernel(Params pr) {
+  constexpr int kChunks = kCW / 8;         // 8-column chunks per slice
+  constexpr int kRG = kThreads / kChunks;  // row groups
+  constexpr int kRows = kD / kRG;          // key rows per thread
+  constexpr int kSlices = kD / kCW;
+  constexpr int kWaves = kThreads / 64;
+  __shared__ float q_s[kD], k_s[kD], v_s[kD];
+  __shared__ float red[kWaves][2][kCW];
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int slice = blockIdx.x % kSlices;
+  const int bh = blockIdx.x / kSlices;
+  const int b = bh / kVH, h = bh % kVH, kh = h / (kVH / kKH);
+  const int c = t % kChunks, rg = t / kChunks;
+  const int col = slice * kCW + 8 * c;  // first value column of this thread
+  const size_t head = static_cast<size_t>(bh) * kD * kD;
+
+  // 1. this thread's elements of the matrix: rows rg + kRG i, columns col .. col+7
+  constexpr int kVec = kF32 ? 2 : 1;  // 16-byte vectors per 8 elements
+  f32x4_t raw[kRows][kVec];
+#pragma unroll
+  for (int i = 0; i < kRows; ++i) {
+    const size_t e = head + static_cast<size_t>(rg + kRG * i) * kD + col;
+    if constexpr (kF32) {
+      const f32x4_t *src = reinterpret_cast<const f32x4_t *>(static_cast<const float *>(pr.S) + e);
+      raw[i][0] = __builtin_nontemporal_load(src);
+      raw[i][1] = __builtin_nontemporal_load(src + 1);
+    } else {
+      const f32x4_t *src =
+          reinterpret_cast<const f32x4_t *>(static_cast<const _Float16 *>(pr.S) + e);
+      raw[i][0] = __builtin_nontemporal_load(src);
+    }
+  }
+
+  // 2. convolution outputs of the channels this head reads; the ring keeps x
+  const int p = pr.pos[b];
+  const uint16_t *xb = pr.x + static_cast<size_t>(b) * kCD;
+  uint16_t *ring = pr.conv + static_cast<size_t>(b) * kConv * kCD;
+  uint16_t *slot = ring + (p & 3) * kCD;
+  if (t < kD) {
+    const int cq = kh * kD + t, cv = kValOff + h * kD + t;
+    q_s[t] = conv_silu(pr, ring, xb, p, cq);
+    v_s[t] = conv_silu(pr, ring, xb, p, cv);
+    if (slice == 0) {
+      slot[cv] = xb[cv];
+      if ((h & 1) == 0) slot[cq] = xb[cq];
+    }
+  } else {
+    const int ck = kKeyDim + kh * kD + (t - kD);
+    k_s[t - kD] = conv_silu(pr, ring, xb, p, ck);
+    if (slice == 0 && (h & 1) == 0) slot[ck] = xb[ck];
+  }
+  __syncthreads();
+
+  // L2 norms and k.q (every wave forms them for itself), gates
+  const float q0 = q_s[lane], q1 = q_s[lane + 64], k0 = k_s[lane], k1 = k_s[lane + 64];
+  const float sq = rma::wave_sum(q0 * q0 + q1 * q1);
+  const float sk = rma::wave_sum(k0 * k0 + k1 * k1);
+  const float sqk = rma::wave_sum(q0 * k0 + q1 * k1);
+  const float iq = (1.f / sqrtf(sq + kL2Eps)) * 0.08838834764831845f;  // 1/sqrt(128)
+  const float ik = 1.f / sqrtf(sk + kL2Eps);
+  const float kq = sqk * iq * ik;
+  const float za = pr.a[b * kVH + h] + pr.dt_bias[h];
+  const float softplus = fmaxf(za, 0.f) + log1pf(expf(-fabsf(za)));
+  const float alpha = expf(-expf(pr.a_log[h]) * softplus);
+  const float zb = pr.b[b * kVH + h];
+  const float eb = expf(-fabsf(zb));
+  const float beta = zb >= 0.f ? 1.f / (1.f + eb) : eb / (1.f + eb);
+
+  // 3. column sums S^T k and S^T q over this thread's rows, then over all rows
+  float s[kRows][8];
+#pragma unroll
+  for (int i = 0; i < kRows; ++i) {
+    if constexpr (kF32) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s[i][j] = raw[i][0][j];
+        s[i][4 + j] = raw[i][1][j];
+      }
+    } else {
+      const f16x8 hv = __builtin_bit_cast(f16x8, raw[i][0]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s[i][j] = static_cast<float>(hv[j]);
+    }
+  }
+  float pk[8], pq[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) pk[j] = pq[j] = 0.f;
+#pragma unroll
+  for (int i = 0; i < kRows; ++i) {
+    const int r = rg + kRG * i;
+    const float kr = k_s[r] * ik, qr = q_s[r] * iq;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      pk[j] = fmaf(s[i][j], kr, pk[j]);
+      pq[j] = fmaf(s[i][j], qr, pq[j]);
+    }
+  }
+  // lanes that share a column chunk differ by multiples of kChunks
+#pragma unroll
+  for (int off = kChunks; off < 64; off <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      pk[j] += __shfl_xor(pk[j], off, 64);
+      pq[j] += __shfl_xor(pq[j], off, 64);
+    }
+  }
+  if (lane < kChunks) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      red[wave][0][8 * c + j] = pk[j];
+      red[wave][1][8 * c + j] = pq[j];
+    }
+  }
+  __syncthreads();
+
+  // 4. u, the output, and the new matrix
+  float u[8], o[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float tk = 0.f, tq = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      tk += red[w][0][8 * c + j];
+      tq += red[w][1][8 * c + j];
+    }
+    u[j] = beta * (v_s[col + j] - alpha * tk);
+    o[j] = fmaf(alpha, tq, u[j] * kq);
+  }
+#pragma unroll
+  for (int i = 0; i < kRows; ++i) {
+    const int r = rg + kRG * i;
+    const float kr = k_s[r] * ik;
+    const size_t e = head + static_cast<size_t>(r) * kD + col;
+    if constexpr (kF32) {
+      f32x4_t lo, hi;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        lo[j] = fmaf(alpha, s[i][j], kr * u[j]);
+        hi[j] = fmaf(alpha, s[i][4 + j], kr * u[4 + j]);
+      }
+      f32x4_t *dst = reinterpret_cast<f32x4_t *>(static_cast<float *>(pr.S) + e);
+      __builtin_nontemporal_store(lo, dst);
+      __builtin_nontemporal_store(hi, dst + 1);
+    } else {
+      f16x8 hv;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) hv[j] = static_cast<_Float16>(fmaf(alpha, s[i][j], kr * u[j]));
+      __builtin_nontemporal_store(__builtin_bit_cast(f32x4_t, hv),
+                                  reinterpret_cast<f32x4_t *>(static_cast<_Float16 *>(pr.S) + e));
+    }
+  }
+  if (rg == 0) {
+    uint4 ov;
+    ov.x = rma::pack_bf16x2(o[0], o[1]);
+    ov.y = rma::pack_bf16x2(o[2], o[3]);
+    ov.z = rma::pack_bf16x2(o[4], o[5]);
+    ov.w = rma::pack_bf16x2(o[6], o[7]);
+    *reinterpret_cast<uint4 *>(pr.o + static_cast<size_t>(bh) * kD + col) = ov;
+  }
+}
+
+template <bool kF32, int kCW>
+static void launch(const Params &pr, int batch, hipStream_t s) {
+  hipLaunchKernelGGL((gdn_decode_kernel<kF32, kCW>), dim3(batch * kVH * (kD / kCW)),
+                     dim3(kThreads), 0, s, pr);
+}
+
+}  // namespace gdn
+
+static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+extern "C" size_t gdn_layer_state_bytes(int32_t batch, int32_t state_dtype) {
+  if (batch <= 0 || (state_dtype != GDN_STATE_F16 && state_dtype != GDN_STATE_F32)) return 0;
+  const size_t eb = state_dtype == GDN_STATE_F32 ? 4 : 2;
+  return static_cast<size_t>(batch) *
+         (static_cast<size_t>(GDN_V_HEADS) * GDN_HEAD_DIM * GDN_HEAD_DIM * eb +
+          static_cast<size_t>(GDN_CONV) * GDN_CONV_DIM * 2);
+}
+
+extern "C" rma_status gdn_decode_step(const gdn_layer_state *st, int32_t batch, int32_t state_dtype,
+                                      const uint16_t *x, const float *a, const float *b,
+                                      const int32_t *pos, const gdn_params *prm, uint16_t *o,
+                                      void *stream) {
+  if (!st || !prm || !x || !a || !b || !pos || !o) return RMA_E_ARG;
+  if (!st->S || !st->conv || !prm->conv_w || !prm->a_log || !prm->dt_bias) return RMA_E_ARG;
+  if (batch <= 0 || batch > RMA_MAX_BATCH) return RMA_E_ARG;
+  if (state_dtype != GDN_STATE_F16 && state_dtype != GDN_STATE_F32) return RMA_E_ARG;
+  const void *al[] = {st->S, st->conv, x, o, prm->conv_w};
+  for (const void *p : al)
+    if (!aligned16(p)) return RMA_E_ALIGN;
+  gdn::Params pr;
+  pr.S = st->S;
+  pr.conv = st->conv;
+  pr.x = x;
+  pr.a = a;
+  pr.b = b;
+  pr.pos = pos;
+  pr.conv_w = prm->conv_w;
+  pr.a_log = prm->a_log;
+  pr.dt_bias = prm->dt_bias;
+  pr.o = o;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // Below 16 sequences a head is split over 4 column slices of 32 so that the
+  // launch still has 128+ workgroups.
+  const bool wide = batch >= 16;
+  if (state_dtype == GDN_STATE_F32) {
+    if (wide)
+      gdn::launch<true, 128>(pr, batch, s);
+    else
+      gdn::launch<true, 32>(pr, batch, s);
+  } else {
+    if (wide)
+      gdn::launch<false, 128>(pr, batch, s);
+    else
+      gdn::launch<false, 32>(pr, batch, s);
+  }
+  if (hipPeekAtLastError() != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
+  return RMA_OK;
+}

@@ -224,3 +224,27 @@ def row_scale_torch_(out, key: StreamKey, start: int = 0, chunk: int = 1 << 24) 
         u = (_hash_t(key, idx) >> 10).to(torch.float32) * (2.0 ** -22)
         flat[c0:c1] = (u + 3.0) * (1.0 / 512.0)
         del idx, u
+
+
+# ---------------------------------------------------------------- FP16 / FP32 state streams
+def scaled_normal_np(key: StreamKey, count: int, start: int = 0, scale: float = 0.125,
+                     dtype=np.float16) -> np.ndarray:
+    """BF16 N(0,1) stream values times a power of two, stored as float16 (nearest
+    even) or float32 (exact)."""
+    x = bf16_bits_to_f32_np(normal_bf16_np(key, count, start)) * np.float32(scale)
+    return x.astype(dtype)
+
+
+def scaled_normal_torch_(out, key: StreamKey, scale: float = 0.125, chunk: int = 1 << 26) -> None:
+    """Fill the contiguous float16/float32 tensor ``out`` with the same values."""
+    import torch
+
+    n = out.numel()
+    assert out.is_contiguous() and out.dtype in (torch.float16, torch.float32)
+    flat = out.view(-1)
+    tmp = torch.empty(min(n, chunk), dtype=torch.bfloat16, device=out.device)
+    for c0 in range(0, n, chunk):
+        c1 = min(n, c0 + chunk)
+        t = tmp[:c1 - c0]
+        normal_bf16_torch_(t, key, start=c0)
+        flat[c0:c1] = (t.float() * scale).to(out.dtype)

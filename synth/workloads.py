@@ -16,6 +16,9 @@ group, 8 SWA||RMA layers, hidden width 2560 feeding a 2560->256->4 scorer.
                         and merge them with a full bank, with about 5% exact
                         score ties planted.
 * ``long_stream_b1``    batch 1, 8 layers, a stream to position 262143.
+* ``gdn_decode_b512``   batch 512, the 24 Gated DeltaNet layers, one decode step at
+                        position 65536 over FP16 recurrent matrices (12 GiB).
+* ``gdn_decode_b1``     batch 1, the 24 GDN layers, FP32 matrices.
 * ``headline_b512_fp8`` ``headline_b512`` with every stored K/V row held as 256
                         E4M3 codes and one FP32 scale: codes of N(0,1) quantiles
                         times 128 with scales in [3/512, 4/512), so a row decodes
@@ -43,6 +46,8 @@ from .core import (
     rng_np,
     row_scale_np,
     row_scale_torch_,
+    scaled_normal_np,
+    scaled_normal_torch_,
     stream_key,
 )
 
@@ -84,8 +89,14 @@ LONG_STREAM_B1 = Workload("long_stream_b1", batch=1, layers=8, position=262144, 
 HEADLINE_B512_FP8 = Workload("headline_b512_fp8", batch=512, layers=8, position=65536,
                              gains="normal", extra={"kv": "e4m3"})
 
+GDN_DECODE_B512 = Workload("gdn_decode_b512", batch=512, layers=24, position=65536, gains="ones",
+                           extra={"state": "f16"})
+GDN_DECODE_B1 = Workload("gdn_decode_b1", batch=1, layers=24, position=65536, gains="ones",
+                         extra={"state": "f32"})
+
 WORKLOADS = {w.name: w for w in (TINY_STREAM, STEADY_B64, HEADLINE_B512, COMMIT_BURST_B512,
-                                 LONG_STREAM_B1, HEADLINE_B512_FP8)}
+                                 LONG_STREAM_B1, HEADLINE_B512_FP8, GDN_DECODE_B512,
+                                 GDN_DECODE_B1)}
 
 
 def key(wl: Workload | str, *names) -> StreamKey:
@@ -329,3 +340,61 @@ def stream_scores_np(wl: Workload, layer: int, block: int) -> np.ndarray:
     """Generator-supplied candidate scores ``[256][4]`` (FP32) of one 256-token block."""
     return normal_f32_np(key(wl, layer, "stream_score", block), (BLOCK, KV_GROUPS), 0.0,
                          SCORE_STD)
+
+
+# ------------------------------------------------------------------ GDN decode step
+# The pages give no activations or weights for the recurrent layers; the draws are
+# unit-scale: projected inputs N(0,1) (BF16), gate inputs N(0,1), convolution taps
+# N(0, 0.5^2), A = exp(A_log) uniform in [1, 16), dt_bias N(0,1), and recurrent
+# matrices N(0, 1/64) -- the spread a unit-key delta rule reaches with values of
+# spread about 0.5 under moderate decay.
+GDN_V_HEADS, GDN_K_HEADS, GDN_DIM, GDN_CONV, GDN_CONV_DIM = 32, 16, 128, 4, 8192
+GDN_S_SCALE = 0.125  # a power of two: the FP16 and FP32 draws are exact scalings
+
+
+def gdn_state_np(wl: Workload, layer: int, b: int, h: int) -> np.ndarray:
+    """Recurrent matrix ``[128][128]`` of sequence b, value head h (float16 or float32)."""
+    per = GDN_DIM * GDN_DIM
+    dt = np.float16 if wl.extra["state"] == "f16" else np.float32
+    return scaled_normal_np(key(wl, layer, "S"), per, start=(b * GDN_V_HEADS + h) * per,
+                            scale=GDN_S_SCALE, dtype=dt).reshape(GDN_DIM, GDN_DIM)
+
+
+def gdn_state_torch_(wl: Workload, layer: int, out) -> None:
+    scaled_normal_torch_(out, key(wl, layer, "S"), scale=GDN_S_SCALE)
+
+
+def gdn_conv_np(wl: Workload, layer: int, b: int) -> np.ndarray:
+    """Convolution ring ``[4][8192]`` (BF16 bits) of sequence b."""
+    per = GDN_CONV * GDN_CONV_DIM
+    return normal_bf16_np(key(wl, layer, "conv"), per, start=b * per).reshape(GDN_CONV,
+                                                                              GDN_CONV_DIM)
+
+
+def gdn_conv_torch_(wl: Workload, layer: int, out) -> None:
+    normal_bf16_torch_(out, key(wl, layer, "conv"))
+
+
+def gdn_x_np(wl: Workload, layer: int, b: int, step: int = 0) -> np.ndarray:
+    """Projected input ``[8192]`` (BF16 bits) of sequence b."""
+    return normal_bf16_np(key(wl, layer, "x", step), GDN_CONV_DIM, start=b * GDN_CONV_DIM)
+
+
+def gdn_x_torch_(wl: Workload, layer: int, out, step: int = 0) -> None:
+    normal_bf16_torch_(out, key(wl, layer, "x", step))
+
+
+def gdn_gate_inputs(wl: Workload, layer: int, step: int = 0):
+    """a, b ``[B][32]`` FP32 (host)."""
+    return (normal_f32_np(key(wl, layer, "a", step), (wl.batch, GDN_V_HEADS)),
+            normal_f32_np(key(wl, layer, "b", step), (wl.batch, GDN_V_HEADS)))
+
+
+def gdn_params(wl: Workload, layer: int) -> dict:
+    """conv_w ``[8192][4]``, a_log ``[32]``, dt_bias ``[32]`` (FP32, host)."""
+    u = rng_np(key(wl, layer, "A")).uniform(1.0, 16.0, GDN_V_HEADS)
+    return {
+        "conv_w": normal_f32_np(key(wl, layer, "conv_w"), (GDN_CONV_DIM, GDN_CONV), 0.0, 0.5),
+        "a_log": np.log(u).astype(np.float32),
+        "dt_bias": normal_f32_np(key(wl, layer, "dt_bias"), (GDN_V_HEADS,)),
+    }

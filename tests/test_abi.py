@@ -13,7 +13,9 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared():
-    txt = open(os.path.join(ROOT, "include", "rma.h")).read()
+    inc = os.path.join(ROOT, "include")
+    txt = "\n".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc))
+                    if f.endswith(".h"))
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", txt, flags=re.M)))
 
@@ -122,3 +124,25 @@ def test_fp8_state_size_and_host_validation(lib):
     assert lib.swa_rma_append_fp8(by(st8), 0, 16, 16, 16, 16, None, by(nm), None) == 1
     assert lib.rma_commit_topk_fp8(by(bad), 2, None, None) == 1
     assert lib.rma_commit_topk_fp8(None, 2, None, None) == 1
+
+
+def test_gdn_state_size_and_host_validation(lib):
+    # 32 heads x 128 x 128 matrix entries + 4 convolution inputs of 8192 BF16 channels
+    assert R.gdn_layer_state_bytes(3, 0) == 3 * (32 * 128 * 128 * 2 + 4 * 8192 * 2)
+    assert R.gdn_layer_state_bytes(1, 1) == 32 * 128 * 128 * 4 + 4 * 8192 * 2
+    assert 24 * R.gdn_layer_state_bytes(1, 0) == int(25.5 * (1 << 20))
+    assert R.gdn_layer_state_bytes(0, 0) == 0 and R.gdn_layer_state_bytes(2, 7) == 0
+    by = ctypes.byref
+    st = R._GdnStateC(16, 16)
+    pr = R._GdnParamsC(16, 16, 16)
+    step = lib.gdn_decode_step
+    assert step(None, 4, 0, 16, 16, 16, 16, by(pr), 16, None) == 1
+    assert step(by(st), 4, 0, 16, 16, 16, 16, None, 16, None) == 1
+    assert step(by(st), 4, 2, 16, 16, 16, 16, by(pr), 16, None) == 1  # unknown dtype
+    assert step(by(st), 0, 0, 16, 16, 16, 16, by(pr), 16, None) == 1
+    assert step(by(st), 4, 0, None, 16, 16, 16, by(pr), 16, None) == 1
+    assert step(by(st), 4, 0, 16, 16, 16, None, by(pr), 16, None) == 1  # no positions
+    assert step(by(R._GdnStateC(16, None)), 4, 0, 16, 16, 16, 16, by(pr), 16, None) == 1
+    assert step(by(R._GdnStateC(24, 16)), 4, 0, 16, 16, 16, 16, by(pr), 16, None) == 2
+    assert step(by(st), 4, 1, 16, 16, 16, 16, by(R._GdnParamsC(20, 16, 16)), 16, None) == 2
+    assert step(by(st), 4, 0, 16, 16, 16, 16, by(pr), 40, None) == 2
