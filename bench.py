@@ -39,14 +39,16 @@ TRAFFIC_FILES = {
     "headline_b512": os.path.join(ROOT, "profiles", "decode_attn_headline_b512_traffic.txt"),
     "headline_b512_fp8": os.path.join(ROOT, "profiles",
                                       "decode_attn_fp8_headline_b512_fp8_traffic.txt"),
+    "gdn_decode_b512": os.path.join(ROOT, "profiles", "gdn_decode_gdn_decode_b512_traffic.txt"),
 }
 KERNEL_SOURCES = ("swa_memory_anchor_amd/csrc/decode_attn.hip",
                   "swa_memory_anchor_amd/csrc/rma_device.h")
+GDN_SOURCES = ("swa_memory_anchor_amd/csrc/gdn.hip", "swa_memory_anchor_amd/csrc/rma_device.h")
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -62,7 +64,8 @@ def measured_traffic(workload: str, units_per_launch: int):
         if "=" in line and not line.lstrip().startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256") != kernel_source_hash():
+    sources = GDN_SOURCES if workload.startswith("gdn") else KERNEL_SOURCES
+    if kv.get("kernel_source_sha256") != kernel_source_hash(sources):
         return None
     if int(kv.get("units_per_launch", -1)) != units_per_launch:
         return None
@@ -570,7 +573,8 @@ def bench_gdn(args):
                    "state": wl.extra["state"], "bytes_per_unit": unit,
                    "workgroups_per_launch": B * 32 * (1 if B >= 16 else 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(wl.name, B),
                      "kernel": "gdn_decode_kernel", "avg_launch_ms": round(avg_launch, 4),
                      "median_launch_ms": round(launch_ms[len(launch_ms) // 2], 4),
                      "bytes_per_launch": bytes_per_launch},

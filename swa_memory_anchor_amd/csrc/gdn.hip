@@ -36,6 +36,11 @@ constexpr int kKeyDim = kKH * kD;  // channel offset of k
 constexpr int kValOff = 2 * kKeyDim;  // channel offset of v
 constexpr int kThreads = 256;
 constexpr float kL2Eps = 1e-6f;
+// Value columns per workgroup for batches of 16 and more (128: one workgroup per
+// head).
+#ifndef RMA_GDN_WIDE_COLS
+#define RMA_GDN_WIDE_COLS 128
+#endif
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -52,16 +57,55 @@ struct Params {
 
 __device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
-// SiLU of the width-4 causal convolution of channel ch at position p: the three
-// previous inputs come from the ring, the current one from x.
-__device__ __forceinline__ float conv_silu(const Params &pr, const uint16_t *ring,
-                                           const uint16_t *xb, int p, int ch) {
-  const float4 w = *reinterpret_cast<const float4 *>(pr.conv_w + 4 * ch);
-  float acc = w.x * bf16f(ring[((p - 3) & 3) * kCD + ch]);
-  acc = fmaf(w.y, bf16f(ring[((p - 2) & 3) * kCD + ch]), acc);
-  acc = fmaf(w.z, bf16f(ring[((p - 1) & 3) * kCD + ch]), acc);
-  acc = fmaf(w.w, bf16f(xb[ch]), acc);
+// The inputs of one channel: all four ring slots (loaded without waiting for the
+// position, which only selects among them), the current input and the taps.
+struct ConvIn {
+  uint16_t r[kConv];
+  uint16_t x;
+  float4 w;
+};
+
+__device__ __forceinline__ ConvIn conv_load(const Params &pr, const uint16_t *ring,
+                                            const uint16_t *xb, int ch) {
+  ConvIn c;
+#pragma unroll
+  for (int j = 0; j < kConv; ++j) c.r[j] = ring[j * kCD + ch];
+  c.x = xb[ch];
+  c.w = *reinterpret_cast<const float4 *>(pr.conv_w + 4 * ch);
+  return c;
+}
+
+// Ring slot i (0..3) by selects, so the four values stay in registers.
+__device__ __forceinline__ float ring_at(const ConvIn &c, int i) {
+  const uint16_t lo = (i & 1) ? c.r[1] : c.r[0];
+  const uint16_t hi = (i & 1) ? c.r[3] : c.r[2];
+  return bf16f((i & 2) ? hi : lo);
+}
+
+// SiLU of the width-4 causal convolution at position p: taps 0..2 take the inputs
+// of positions p-3..p-1 (ring slots (p-3..p-1) mod 4), tap 3 the current input.
+__device__ __forceinline__ float conv_silu(const ConvIn &c, int p) {
+  float acc = c.w.x * ring_at(c, (p - 3) & 3);
+  acc = fmaf(c.w.y, ring_at(c, (p - 2) & 3), acc);
+  acc = fmaf(c.w.z, ring_at(c, (p - 1) & 3), acc);
+  acc = fmaf(c.w.w, bf16f(c.x), acc);
   return acc / (1.f + expf(-acc));
+}
+
+// Eight loaded matrix elements (one 16-byte vector of FP16, two of FP32) as floats.
+template <int kVec>
+__device__ __forceinline__ void widen(const f32x4_t (&v)[kVec], float (&e)[8]) {
+  if constexpr (kVec == 2) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      e[j] = v[0][j];
+      e[4 + j] = v[1][j];
+    }
+  } else {
+    const f16x8 hv = __builtin_bit_cast(f16x8, v[0]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = static_cast<float>(hv[j]);
+  }
 }
 
 template <bool kF32, int kCW>
@@ -99,24 +143,29 @@ __global__ __launch_bounds__(kThreads) void gdn_decode_kernel(Params pr) {
     }
   }
 
-  // 2. convolution outputs of the channels this head reads; the ring keeps x
-  const int p = pr.pos[b];
+  // 2. convolution outputs of the channels this head reads; the ring keeps x.  All
+  // of the step's small loads are issued together, before any of them is used.
   const uint16_t *xb = pr.x + static_cast<size_t>(b) * kCD;
   uint16_t *ring = pr.conv + static_cast<size_t>(b) * kConv * kCD;
+  const int ch0 = t < kD ? kh * kD + t : kKeyDim + kh * kD + (t - kD);  // q, then k
+  const int cv = kValOff + h * kD + (t & (kD - 1));
+  const ConvIn in0 = conv_load(pr, ring, xb, ch0);
+  ConvIn in1;
+  if (t < kD) in1 = conv_load(pr, ring, xb, cv);
+  const int p = pr.pos[b];
+  const float za = pr.a[b * kVH + h] + pr.dt_bias[h];
+  const float zb = pr.b[b * kVH + h];
+  const float a_log = pr.a_log[h];
   uint16_t *slot = ring + (p & 3) * kCD;
+  const float y0 = conv_silu(in0, p);
   if (t < kD) {
-    const int cq = kh * kD + t, cv = kValOff + h * kD + t;
-    q_s[t] = conv_silu(pr, ring, xb, p, cq);
-    v_s[t] = conv_silu(pr, ring, xb, p, cv);
-    if (slice == 0) {
-      slot[cv] = xb[cv];
-      if ((h & 1) == 0) slot[cq] = xb[cq];
-    }
+    q_s[t] = y0;
+    v_s[t] = conv_silu(in1, p);
+    if (slice == 0) slot[cv] = in1.x;
   } else {
-    const int ck = kKeyDim + kh * kD + (t - kD);
-    k_s[t - kD] = conv_silu(pr, ring, xb, p, ck);
-    if (slice == 0 && (h & 1) == 0) slot[ck] = xb[ck];
+    k_s[t - kD] = y0;
   }
+  if (slice == 0 && (h & 1) == 0) slot[ch0] = in0.x;
   __syncthreads();
 
   // L2 norms and k.q (every wave forms them for itself), gates
@@ -127,29 +176,15 @@ __global__ __launch_bounds__(kThreads) void gdn_decode_kernel(Params pr) {
   const float iq = (1.f / sqrtf(sq + kL2Eps)) * 0.08838834764831845f;  // 1/sqrt(128)
   const float ik = 1.f / sqrtf(sk + kL2Eps);
   const float kq = sqk * iq * ik;
-  const float za = pr.a[b * kVH + h] + pr.dt_bias[h];
   const float softplus = fmaxf(za, 0.f) + log1pf(expf(-fabsf(za)));
-  const float alpha = expf(-expf(pr.a_log[h]) * softplus);
-  const float zb = pr.b[b * kVH + h];
+  const float alpha = expf(-expf(a_log) * softplus);
   const float eb = expf(-fabsf(zb));
   const float beta = zb >= 0.f ? 1.f / (1.f + eb) : eb / (1.f + eb);
 
-  // 3. column sums S^T k and S^T q over this thread's rows, then over all rows
-  float s[kRows][8];
-#pragma unroll
-  for (int i = 0; i < kRows; ++i) {
-    if constexpr (kF32) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        s[i][j] = raw[i][0][j];
-        s[i][4 + j] = raw[i][1][j];
-      }
-    } else {
-      const f16x8 hv = __builtin_bit_cast(f16x8, raw[i][0]);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) s[i][j] = static_cast<float>(hv[j]);
-    }
-  }
+  // 3. column sums S^T k and S^T q over this thread's rows, then over all rows.  The
+  // elements stay in their loaded (packed) form and are widened again for the
+  // update, which keeps the register count, and with it the workgroups per CU
+  // that hide the memory latency, up.
   float pk[8], pq[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) pk[j] = pq[j] = 0.f;
@@ -157,10 +192,12 @@ __global__ __launch_bounds__(kThreads) void gdn_decode_kernel(Params pr) {
   for (int i = 0; i < kRows; ++i) {
     const int r = rg + kRG * i;
     const float kr = k_s[r] * ik, qr = q_s[r] * iq;
+    float e[8];
+    widen(raw[i], e);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      pk[j] = fmaf(s[i][j], kr, pk[j]);
-      pq[j] = fmaf(s[i][j], qr, pq[j]);
+      pk[j] = fmaf(e[j], kr, pk[j]);
+      pq[j] = fmaf(e[j], qr, pq[j]);
     }
   }
   // lanes that share a column chunk differ by multiples of kChunks
@@ -199,12 +236,14 @@ __global__ __launch_bounds__(kThreads) void gdn_decode_kernel(Params pr) {
     const int r = rg + kRG * i;
     const float kr = k_s[r] * ik;
     const size_t e = head + static_cast<size_t>(r) * kD + col;
+    float sv[8];
+    widen(raw[i], sv);
     if constexpr (kF32) {
       f32x4_t lo, hi;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        lo[j] = fmaf(alpha, s[i][j], kr * u[j]);
-        hi[j] = fmaf(alpha, s[i][4 + j], kr * u[4 + j]);
+        lo[j] = fmaf(alpha, sv[j], kr * u[j]);
+        hi[j] = fmaf(alpha, sv[4 + j], kr * u[4 + j]);
       }
       f32x4_t *dst = reinterpret_cast<f32x4_t *>(static_cast<float *>(pr.S) + e);
       __builtin_nontemporal_store(lo, dst);
@@ -212,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void gdn_decode_kernel(Params pr) {
     } else {
       f16x8 hv;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) hv[j] = static_cast<_Float16>(fmaf(alpha, s[i][j], kr * u[j]));
+      for (int j = 0; j < 8; ++j) hv[j] = static_cast<_Float16>(fmaf(alpha, sv[j], kr * u[j]));
       __builtin_nontemporal_store(__builtin_bit_cast(f32x4_t, hv),
                                   reinterpret_cast<f32x4_t *>(static_cast<_Float16 *>(pr.S) + e));
     }
@@ -273,12 +312,12 @@ extern "C" rma_status gdn_decode_step(const gdn_layer_state *st, int32_t batch, 
   const bool wide = batch >= 16;
   if (state_dtype == GDN_STATE_F32) {
     if (wide)
-      gdn::launch<true, 128>(pr, batch, s);
+      gdn::launch<true, RMA_GDN_WIDE_COLS>(pr, batch, s);
     else
       gdn::launch<true, 32>(pr, batch, s);
   } else {
     if (wide)
-      gdn::launch<false, 128>(pr, batch, s);
+      gdn::launch<false, RMA_GDN_WIDE_COLS>(pr, batch, s);
     else
       gdn::launch<false, 32>(pr, batch, s);
   }
