@@ -229,20 +229,29 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(PrefillParams a
   // 1 KB (two rows) per instruction; lane L fills chunk position L % 32 of row
   // 2i + L / 32, i.e. fetches the chunk that the swizzle puts there.  Rows past
   // the segment's end read as zero.
+  // The tile's first row and the wave's row pair go into the scalar offset; the
+  // lane's part (odd row of the pair, swizzled chunk) is fixed per load and is
+  // formed once here.
   const int dma_row_lo = lane >> 5, dma_pos = lane & 31;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  int dma_kc[4], dma_vc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 2 * (4 * wave_s + i) + dma_row_lo;
+    dma_kc[i] = (dma_pos ^ k_swz(row)) << 4;
+    dma_vc[i] = (dma_pos ^ v_swz(row)) << 4;
+  }
 #define PREFILL_ISSUE_TILE(t_, kdst_, vdst_)                                                 \
   {                                                                                          \
     PREFILL_TILE_SEG(t_, isg, ik0)                                                           \
+    const int lo_off = dma_row_lo * isg.stride;                                              \
     _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                          \
-      const int pr = 4 * wave + i;                                                           \
-      const int row = 2 * pr + dma_row_lo;                                                   \
-      const int roff = (ik0 + row) * isg.stride;                                             \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(                                              \
-          isg.k, (lds_void *)&kdst_[pr * 2 * kDim], 16,                                      \
-          roff + ((dma_pos ^ k_swz(row)) << 4), 0, 0, 0);                                    \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(                                              \
-          isg.v, (lds_void *)&vdst_[pr * 2 * kDim], 16,                                      \
-          roff + ((dma_pos ^ v_swz(row)) << 4), 0, 0, 0);                                    \
+      const int pr = 4 * wave_s + i;                                                         \
+      const int soff = (ik0 + 2 * pr) * isg.stride;                                          \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isg.k, (lds_void *)&kdst_[pr * 2 * kDim], 16, \
+                                               lo_off + dma_kc[i], soff, 0, 0);              \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isg.v, (lds_void *)&vdst_[pr * 2 * kDim], 16, \
+                                               lo_off + dma_vc[i], soff, 0, 0);              \
     }                                                                                        \
   }
   // Start the first tiles' loads before the query prologue.
