@@ -333,7 +333,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(DecodeParams a
   __shared__ float red_m[kWaves][kHeadsPerGroup], red_l[kWaves][kHeadsPerGroup];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps tile selection scalar
   const int split = blockIdx.x % a.splits;
   const int unit = blockIdx.x / a.splits;
   const int per_branch = a.batch * kGroups;
@@ -403,9 +403,10 @@ __device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 //  K[4u + s]: key key0 + 16u + lane%16, codes of dims 64s + 16(lane/16) .. +16;
 //  V[i]:      row key0 + 4i + lane/16, codes of dims 16(lane%16) .. +16;
 //  ks[u], vs[u]: scales of keys key0 + 16u + 4(lane/16) .. +4 (the lane's score keys).
-__device__ __forceinline__ void load_tile_fp8(const Segment &sg, int key0, int lane,
-                                              uint4 (&K)[8], uint4 (&V)[8], f32x4 (&ks)[2],
-                                              f32x4 (&vs)[2]) {
+// The K and V halves are issued separately: each half's next loads go out as soon
+// as its registers are consumed.
+__device__ __forceinline__ void load_k_fp8(const Segment &sg, int key0, int lane, uint4 (&K)[8],
+                                           f32x4 (&ks)[2]) {
   const int hh = lane & 15, kg = lane >> 4;
   const int soff = key0 * kDim;
   const int koff = hh * kDim + 16 * kg;
@@ -415,35 +416,45 @@ __device__ __forceinline__ void load_tile_fp8(const Segment &sg, int key0, int l
     for (int s = 0; s < 4; ++s)
       K[4 * u + s] = bitcast<uint4>(__builtin_amdgcn_raw_buffer_load_b128(
           sg.k, koff + 16 * u * kDim + 64 * s, soff, kStream));
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    ks[u] = bitcast<f32x4>(
+        __builtin_amdgcn_raw_buffer_load_b128(sg.ks, 4 * (16 * u + 4 * kg), key0 * 4, kStream));
+}
+
+__device__ __forceinline__ void load_v_fp8(const Segment &sg, int key0, int lane, uint4 (&V)[8],
+                                           f32x4 (&vs)[2]) {
+  const int kg = lane >> 4;
+  const int soff = key0 * kDim;
   const int voff = (lane >> 4) * kDim + 16 * (lane & 15);
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     V[i] = bitcast<uint4>(
         __builtin_amdgcn_raw_buffer_load_b128(sg.v, voff + 4 * i * kDim, soff, kStream));
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    ks[u] = bitcast<f32x4>(
-        __builtin_amdgcn_raw_buffer_load_b128(sg.ks, 4 * (16 * u + 4 * kg), key0 * 4, kStream));
+  for (int u = 0; u < 2; ++u)
     vs[u] = bitcast<f32x4>(
         __builtin_amdgcn_raw_buffer_load_b128(sg.vs, 4 * (16 * u + 4 * kg), key0 * 4, kStream));
-  }
 }
 
-// Stage the widened V rows and form the scores of the tile's two 16-key halves.
-// The contraction over the head dimension runs in a permuted order that the K
-// loads and the query reads share: MFMA (s, h) covers, for lane group kg, dims
-// 64s + 16kg + 8h .. +8.  Lane holds, in sc[u], keys 16u + 4kg .. +4 of head hh.
-__device__ __forceinline__ void scores_tile_fp8(int nvalid, int lane, const uint4 (&K)[8],
-                                                const uint4 (&V)[8], const f32x4 (&ks)[2],
-                                                const uint16_t *ql, uint16_t *vl,
-                                                f32x4 (&sc)[2]) {
-  const int hh = lane & 15, kg = lane >> 4;
+// Stage the widened V rows of a tile in the wave's LDS rows (consumes V).
+__device__ __forceinline__ void stage_v_fp8(int lane, const uint4 (&V)[8], uint16_t *vl) {
   uint16_t *vrow = vl + (lane >> 4) * kVStride8 + 16 * (lane & 15);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     *reinterpret_cast<uint4 *>(vrow + 4 * i * kVStride8) = e4m3x8_to_bf16x8(V[i].x, V[i].y);
     *reinterpret_cast<uint4 *>(vrow + 4 * i * kVStride8 + 8) = e4m3x8_to_bf16x8(V[i].z, V[i].w);
   }
+}
+
+// Scores of the tile's two 16-key halves (consumes K).  The contraction over the
+// head dimension runs in a permuted order that the K loads and the query reads
+// share: MFMA (s, h) covers, for lane group kg, dims 64s + 16kg + 8h .. +8.  Lane
+// holds, in sc[u], keys 16u + 4kg .. +4 of head hh.
+__device__ __forceinline__ void scores_tile_fp8(int nvalid, int lane, const uint4 (&K)[8],
+                                                const f32x4 (&ks)[2], const uint16_t *ql,
+                                                f32x4 (&sc)[2]) {
+  const int hh = lane & 15, kg = lane >> 4;
   sc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
   sc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
   const uint16_t *qrow = ql + hh * kQStride + 16 * kg;
@@ -529,7 +540,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_fp8_kernel(DecodePara
   __shared__ float red_m[kWaves][kHeadsPerGroup], red_l[kWaves][kHeadsPerGroup];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps tile selection scalar
   const int split = blockIdx.x % a.splits;
   const int unit = blockIdx.x / a.splits;
   const int per_branch = a.batch * kGroups;
@@ -555,20 +566,26 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_fp8_kernel(DecodePara
   uint4 K[8], V[8];
   f32x4 ks[2], vs[2];
   int t = tb + wave;
-  if (t < te)
-    load_tile_fp8(t < T0 ? seg0 : seg1, (t < T0 ? t : t - T0) * kTile8, lane, K, V, ks, vs);
+  if (t < te) {
+    const Segment &sg = t < T0 ? seg0 : seg1;
+    const int key0 = (t < T0 ? t : t - T0) * kTile8;
+    load_v_fp8(sg, key0, lane, V, vs);
+    load_k_fp8(sg, key0, lane, K, ks);
+  }
   stage_query(a, b, g, anchor, wave, lane, q_lds);
 
   for (; t < te; t += kWaves) {
     const int key0 = (t < T0 ? t : t - T0) * kTile8;
     const int nvalid = (t < T0 ? seg0.n : seg1.n) - key0;
-    f32x4 sc[2];
-    scores_tile_fp8(nvalid, lane, K, V, ks, &q_lds[0][0], vl, sc);
-    const f32x4 vsc[2] = {vs[0], vs[1]};  // this tile's, before the next tile's loads
     const int tn = t + kWaves;
-    if (tn < te)
-      load_tile_fp8(tn < T0 ? seg0 : seg1, (tn < T0 ? tn : tn - T0) * kTile8, lane, K, V, ks,
-                    vs);
+    const Segment &nsg = tn < T0 ? seg0 : seg1;
+    const int nkey0 = (tn < T0 ? tn : tn - T0) * kTile8;
+    stage_v_fp8(lane, V, vl);
+    const f32x4 vsc[2] = {vs[0], vs[1]};  // this tile's, before the next tile's loads
+    if (tn < te) load_v_fp8(nsg, nkey0, lane, V, vs);
+    f32x4 sc[2];
+    scores_tile_fp8(nvalid, lane, K, ks, &q_lds[0][0], sc);
+    if (tn < te) load_k_fp8(nsg, nkey0, lane, K, ks);
     accumulate_tile_fp8(sc, lane, vl, vsc, st);
   }
 
