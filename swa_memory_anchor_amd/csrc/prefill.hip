@@ -173,7 +173,7 @@ __device__ __forceinline__ void wait_vm_barrier() {
 
 __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(PrefillParams a) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps per-wave tests scalar
   const int ntile = (a.chunk + kPTok - 1) / kPTok;
   // XCD-aware numbering: the token tiles of one unit run on one XCD.
   const int bid = blockIdx.x;
