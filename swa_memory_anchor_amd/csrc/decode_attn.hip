@@ -262,21 +262,18 @@ __device__ __forceinline__ void load_tile(const Segment &sg, int key0, int lane,
 
 // Stage V in LDS and form the scores of one tile (consumes K and V).
 __device__ __forceinline__ f32x4 scores_tile(int nvalid, int lane, const uint4 (&K)[8],
-                                             const uint4 (&V)[8], const uint16_t *ql,
+                                             const uint4 (&V)[8], const bf16x8 (&qv)[8],
                                              uint16_t *vl) {
-  const int hh = lane & 15, kg = lane >> 4;
+  const int kg = lane >> 4;
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     *reinterpret_cast<uint4 *>(vl + (2 * i + (lane >> 5)) * kVStride + 8 * (lane & 31)) = V[i];
   // D[key][head] = sum_d K[key][d] * qhat[head][d]; the B operand is the staged
   // query block (head hh; rows >= 4 are zero).  Lane holds keys 4kg..4kg+3 of head hh.
   f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-  const uint16_t *qrow = ql + hh * kQStride + 8 * kg;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const bf16x8 qv = bitcast<bf16x8>(*reinterpret_cast<const uint4 *>(qrow + 32 * s));
-    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(K[s]), qv, sc, 0, 0, 0);
-  }
+  for (int s = 0; s < 8; ++s)
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(K[s]), qv[s], sc, 0, 0, 0);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     if (4 * kg + i >= nvalid) sc[i] = -INFINITY;
@@ -364,11 +361,19 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(DecodeParams a
   // query prologue so its latency overlaps the norm and rotary work.
   if (t < te) load_tile(t < T0 ? seg0 : seg1, (t < T0 ? t : t - T0) * kTile, lane, K, V);
   stage_query(a, b, g, anchor, wave, lane, q_lds);
+  // The query operands stay in registers for the whole key loop: lane (hh, kg) holds
+  // dims 32s + 8kg .. +8 of head hh (rows >= 4 are zero).
+  bf16x8 qv[8];
+  {
+    const uint16_t *qrow = &q_lds[0][0] + (lane & 15) * kQStride + 8 * (lane >> 4);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qv[s] = bitcast<bf16x8>(*reinterpret_cast<const uint4 *>(qrow + 32 * s));
+  }
 
   for (; t < te; t += kWaves) {
     const int key0 = (t < T0 ? t : t - T0) * kTile;
     const int nvalid = (t < T0 ? seg0.n : seg1.n) - key0;
-    const f32x4 sc = scores_tile(nvalid, lane, K, V, &q_lds[0][0], vl);
+    const f32x4 sc = scores_tile(nvalid, lane, K, V, qv, vl);
     // K and V are consumed: the next tile's loads fly while this one accumulates.
     const int tn = t + kWaves;
     if (tn < te) load_tile(tn < T0 ? seg0 : seg1, (tn < T0 ? tn : tn - T0) * kTile, lane, K, V);
@@ -452,22 +457,21 @@ __device__ __forceinline__ void stage_v_fp8(int lane, const uint4 (&V)[8], uint1
 // share: MFMA (s, h) covers, for lane group kg, dims 64s + 16kg + 8h .. +8.  Lane
 // holds, in sc[u], keys 16u + 4kg .. +4 of head hh.
 __device__ __forceinline__ void scores_tile_fp8(int nvalid, int lane, const uint4 (&K)[8],
-                                                const f32x4 (&ks)[2], const uint16_t *ql,
+                                                const f32x4 (&ks)[2], const bf16x8 (&qv)[8],
                                                 f32x4 (&sc)[2]) {
-  const int hh = lane & 15, kg = lane >> 4;
+  const int kg = lane >> 4;
   sc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
   sc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const uint16_t *qrow = ql + hh * kQStride + 16 * kg;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const bf16x8 qv = bitcast<bf16x8>(*reinterpret_cast<const uint4 *>(qrow + 64 * s + 8 * h));
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const uint4 &kw = K[4 * u + s];
         const uint4 kb = h ? e4m3x8_to_bf16x8(kw.z, kw.w) : e4m3x8_to_bf16x8(kw.x, kw.y);
-        sc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(kb), qv, sc[u], 0, 0, 0);
+        sc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(kb), qv[2 * s + h], sc[u],
+                                                        0, 0, 0);
       }
     }
   }
@@ -573,6 +577,17 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_fp8_kernel(DecodePara
     load_k_fp8(sg, key0, lane, K, ks);
   }
   stage_query(a, b, g, anchor, wave, lane, q_lds);
+  // Query operands in registers: qv[2s + h] holds, for lane (hh, kg), dims
+  // 64s + 16kg + 8h .. +8 of head hh (the permuted contraction order).
+  bf16x8 qv[8];
+  {
+    const uint16_t *qrow = &q_lds[0][0] + (lane & 15) * kQStride + 16 * (lane >> 4);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        qv[2 * s + h] = bitcast<bf16x8>(*reinterpret_cast<const uint4 *>(qrow + 64 * s + 8 * h));
+  }
 
   for (; t < te; t += kWaves) {
     const int key0 = (t < T0 ? t : t - T0) * kTile8;
@@ -584,7 +599,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_fp8_kernel(DecodePara
     const f32x4 vsc[2] = {vs[0], vs[1]};  // this tile's, before the next tile's loads
     if (tn < te) load_v_fp8(nsg, nkey0, lane, V, vs);
     f32x4 sc[2];
-    scores_tile_fp8(nvalid, lane, K, ks, &q_lds[0][0], sc);
+    scores_tile_fp8(nvalid, lane, K, ks, qv, sc);
     if (tn < te) load_k_fp8(nsg, nkey0, lane, K, ks);
     accumulate_tile_fp8(sc, lane, vl, vsc, st);
   }
