@@ -157,6 +157,28 @@ rma_status swa_rma_decode_attn(const rma_layer_state *st, int32_t batch, const u
                                float *lse_win, uint16_t *o_rma, float *lse_rma, void *workspace,
                                size_t workspace_bytes, void *stream);
 
+/* Workspace that swa_rma_step needs at this batch: the decode's split partials,
+ * then one 32-bit counter per sequence at a 256-byte aligned offset. */
+size_t rma_step_workspace_bytes(int32_t batch);
+
+/*
+ * swa_rma_step - one token per sequence, appended and attended in one launch
+ * (and the split merge where the decode splits): the same state and outputs as
+ * swa_rma_append(st, k_win, v_win, k_rma, v_rma, score) followed by
+ * swa_rma_decode_attn(st, q_win, q_rma), bit for bit.  Arguments as in those two.
+ * The new token's key and value are attended to by its own query.  A sequence
+ * whose pending block is full takes no token and attends to the state as it is.
+ * `workspace` must hold rma_step_workspace_bytes(batch) bytes, 16-byte aligned,
+ * all zero before its first use; every completed call leaves its counters at
+ * zero again, so the same workspace serves later calls (and decodes) as it is.
+ * Calls that share a workspace must not overlap.
+ */
+rma_status swa_rma_step(const rma_layer_state *st, int32_t batch, const uint16_t *k_win,
+                        const uint16_t *v_win, const uint16_t *k_rma, const uint16_t *v_rma,
+                        const float *score, const uint16_t *q_win, const uint16_t *q_rma,
+                        const rma_norm *norm, uint16_t *o_win, float *lse_win, uint16_t *o_rma,
+                        float *lse_rma, void *workspace, size_t workspace_bytes, void *stream);
+
 /*
  * rma_score - retention priorities ([FB] section "架构…": bias-free FP32 chain
  * 2560 -> 256 -> 4, one priority per KV group).

@@ -31,6 +31,7 @@ EXPORTS = (
     "rma_commit_topk", "rma_status_str", "rma_prefill_workspace_bytes", "swa_rma_prefill",
     "rma_layer_state_fp8_bytes", "swa_rma_append_fp8", "swa_rma_decode_attn_fp8",
     "rma_commit_topk_fp8", "gdn_layer_state_bytes", "gdn_decode_step",
+    "rma_step_workspace_bytes", "swa_rma_step",
 )
 
 _c_void_p = ctypes.c_void_p
@@ -81,13 +82,17 @@ def lib() -> ctypes.CDLL:
         i32, i64, sz, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, _c_void_p
         sp = ctypes.POINTER(_StateC)
         npp = ctypes.POINTER(_NormC)
-        for nm in ("rma_layer_state_bytes", "rma_layer_kv_bytes", "rma_decode_workspace_bytes"):
+        for nm in ("rma_layer_state_bytes", "rma_layer_kv_bytes", "rma_decode_workspace_bytes",
+                   "rma_step_workspace_bytes"):
             getattr(L, nm).argtypes, getattr(L, nm).restype = [i32], sz
         L.rma_decode_splits.argtypes, L.rma_decode_splits.restype = [i32], i32
         L.swa_rma_append.argtypes = [sp, i32, vp, vp, vp, vp, vp, npp, vp]
         L.swa_rma_append.restype = ctypes.c_int
         L.swa_rma_decode_attn.argtypes = [sp, i32, vp, vp, npp, vp, vp, vp, vp, vp, sz, vp]
         L.swa_rma_decode_attn.restype = ctypes.c_int
+        L.swa_rma_step.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, vp, npp, vp, vp, vp, vp, vp,
+                                   sz, vp]
+        L.swa_rma_step.restype = ctypes.c_int
         L.rma_score.argtypes = [vp, i64, i64, vp, vp, vp, i64, vp]
         L.rma_score.restype = ctypes.c_int
         L.rma_commit_topk.argtypes = [sp, i32, vp, vp]
@@ -297,6 +302,20 @@ def swa_rma_decode_attn(st: LayerState, batch: int, q_win, q_rma, norm: Norm, o_
     _check(s, "swa_rma_decode_attn")
 
 
+def rma_step_workspace_bytes(batch: int) -> int:
+    return int(lib().rma_step_workspace_bytes(int(batch)))
+
+
+def swa_rma_step(st: LayerState, batch: int, k_win, v_win, k_rma, v_rma, score, q_win, q_rma,
+                 norm: Norm, o_win, lse_win, o_rma, lse_rma, workspace, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    s = lib().swa_rma_step(ctypes.byref(_state_c(st)), int(batch), _ptr(k_win), _ptr(v_win),
+                           _ptr(k_rma), _ptr(v_rma), _ptr(score), _ptr(q_win), _ptr(q_rma),
+                           ctypes.byref(_norm_c(norm)), _ptr(o_win), _ptr(lse_win), _ptr(o_rma),
+                           _ptr(lse_rma), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(s, "swa_rma_step")
+
+
 def rma_score(hidden, n_rows: int, ld_hidden: int, w1, w2, scores, ld_scores: int,
               stream=None) -> None:
     s = lib().rma_score(_ptr(hidden), int(n_rows), int(ld_hidden), _ptr(w1), _ptr(w2),
@@ -316,6 +335,13 @@ def decode_workspace(batch: int, device="cuda"):
 
     n = rma_decode_workspace_bytes(batch)
     return None if n == 0 else torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def step_workspace(batch: int, device="cuda"):
+    """A zero-filled workspace for swa_rma_step at this batch; it stays valid across calls."""
+    import torch
+
+    return torch.zeros(rma_step_workspace_bytes(batch), dtype=torch.uint8, device=device)
 
 
 def rma_prefill_workspace_bytes(batch: int, n_tokens: int) -> int:

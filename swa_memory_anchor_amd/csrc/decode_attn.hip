@@ -113,15 +113,17 @@ struct SoftmaxState {
 };
 
 // ---------------------------------------------------------------- setup and epilogue
-// The key segments of one (branch, sequence, group); rb = bytes per row.
+// The key segments of one (branch, sequence, group) for position p and the given
+// bank and pending counts; rb = bytes per row.
 template <bool kFp8>
-__device__ __forceinline__ void unit_segments(const DecodeParams &a, int b, int g, bool anchor,
-                                              Segment &seg0, Segment &seg1) {
+__device__ __forceinline__ void unit_segments_at(const DecodeParams &a, int b, int g, bool anchor,
+                                                 int p, int n_bank, int n_pend, Segment &seg0,
+                                                 Segment &seg1) {
   constexpr int rb = kFp8 ? kDim : 2 * kDim;
   const size_t sgi = static_cast<size_t>(b) * kGroups + g;
   if (anchor) {
-    const int nb = min(max(a.n_bank[b], 0), kBank);
-    const int np = min(max(a.n_pend[b], 0), kBlock);
+    const int nb = min(max(n_bank, 0), kBank);
+    const int np = min(max(n_pend, 0), kBlock);
     seg0.k = make_rsrc(a.bank_k + sgi * kBank * rb, nb * rb);
     seg0.v = make_rsrc(a.bank_v + sgi * kBank * rb, nb * rb);
     seg0.n = nb;
@@ -135,7 +137,7 @@ __device__ __forceinline__ void unit_segments(const DecodeParams &a, int b, int 
       seg1.vs = make_rsrc(a.pend_vs + sgi * kBlock, np * 4);
     }
   } else {
-    const int nw = min(max(a.pos[b] + 1, 0), kWindow);
+    const int nw = min(max(p + 1, 0), kWindow);
     seg0.k = make_rsrc(a.win_k + sgi * kWindow * rb, nw * rb);
     seg0.v = make_rsrc(a.win_v + sgi * kWindow * rb, nw * rb);
     seg0.n = nw;
@@ -148,17 +150,28 @@ __device__ __forceinline__ void unit_segments(const DecodeParams &a, int b, int 
   }
 }
 
-// Query prep: wave w < 4 normalises, rotates and scales head 4g + w into q_lds
-// row w; the other rows are zeroed.  Ends with a workgroup barrier.
+// The key segments as the state holds them.
+template <bool kFp8>
+__device__ __forceinline__ void unit_segments(const DecodeParams &a, int b, int g, bool anchor,
+                                              Segment &seg0, Segment &seg1) {
+  if (anchor)
+    unit_segments_at<kFp8>(a, b, g, true, 0, a.n_bank[b], a.n_pend[b], seg0, seg1);
+  else
+    unit_segments_at<kFp8>(a, b, g, false, a.pos[b], 0, 0, seg0, seg1);
+}
+
+// Query prep at position p: wave w < 4 normalises, rotates and scales head 4g + w
+// into q_lds row w; the other rows are zeroed.  Ends with a workgroup barrier.
 __device__ __forceinline__ void stage_query(const DecodeParams &a, int b, int g, bool anchor,
-                                            int wave, int lane, uint16_t (*q_lds)[kQStride]) {
+                                            int p, int wave, int lane,
+                                            uint16_t (*q_lds)[kQStride]) {
   if (wave < kHeadsPerGroup) {
     const uint16_t *q = (anchor ? a.q_rma : a.q_win) +
                         (static_cast<size_t>(b) * kHeads + g * kHeadsPerGroup + wave) * kDim;
     const uint2 raw = *reinterpret_cast<const uint2 *>(q + 4 * lane);
     float x[4] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y)};
     float c, sn;
-    rope_cos_sin(a.rope_ratio, a.pos[b], lane, c, sn);
+    rope_cos_sin(a.rope_ratio, p, lane, c, sn);
     norm_rope_head(x, anchor ? a.gq_rma : a.gq_win, a.eps, c, sn, lane);
     uint2 o;
     o.x = pack_bf16x2(x[0] * kQScale, x[1] * kQScale);
@@ -360,7 +373,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(DecodeParams a
   // The first tile's loads do not depend on the query: issue them before the
   // query prologue so its latency overlaps the norm and rotary work.
   if (t < te) load_tile(t < T0 ? seg0 : seg1, (t < T0 ? t : t - T0) * kTile, lane, K, V);
-  stage_query(a, b, g, anchor, wave, lane, q_lds);
+  stage_query(a, b, g, anchor, a.pos[b], wave, lane, q_lds);
   // The query operands stay in registers for the whole key loop: lane (hh, kg) holds
   // dims 32s + 8kg .. +8 of head hh (rows >= 4 are zero).
   bf16x8 qv[8];
@@ -383,6 +396,151 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(DecodeParams a
   __syncthreads();  // every wave is done with its V rows; reuse them for the merge
   finish_unit(a, st, reinterpret_cast<float *>(&v_lds[0][0]), red_m, red_l, wave, lane, unit,
               split, anchor, b, g);
+}
+
+// ---------------------------------------------------------------- fused step
+// One token per sequence, appended and attended in one launch: the same result as
+// swa_rma_append followed by swa_rma_decode_attn (fluxbbs.com page, section
+// "架构：递归、局部窗口与记忆锚点三件套": keys normed and rotated at their own
+// position, values raw; neodrop.ai repost, section "三段记忆，只记值得记的": one
+// candidate per token into the pending block).
+//  * every workgroup reads pos and n_pend as they were and counts the new token in
+//    its segments (window slot p mod 1024, pending row n_pend);
+//  * the workgroup whose tiles hold a branch's new row forms that row (norm +
+//    rotary of the key, the value as given), writes it to the state and puts it in
+//    its tile registers in place of what the loads read from that row;
+//  * the last workgroup of a sequence to finish (a counter per sequence in the
+//    workspace) advances pos and n_pend and records the source position and
+//    score, after every workgroup of the sequence has read them.  No data passes
+//    between workgroups of the launch, so no cross-workgroup fence is needed.
+struct StepParams {
+  DecodeParams d;
+  uint16_t *win_k, *win_v, *pend_k, *pend_v;
+  float *pend_score;
+  int32_t *pend_src, *n_pend, *pos;
+  const uint16_t *k_win, *v_win, *k_rma, *v_rma;  // [B][4][256], raw
+  const float *score;                             // [B][4] or null
+  const float *gk_win, *gk_rma;
+  uint32_t *done;                                 // [B], zero between launches
+};
+
+__global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepParams sp) {
+  const DecodeParams &a = sp.d;
+  __shared__ __align__(16) uint16_t v_lds[kWaves][kTile * kVStride];
+  __shared__ __align__(16) uint16_t q_lds[16][kQStride];
+  __shared__ __align__(16) uint16_t patch[2][kDim];  // the new K and V rows
+  __shared__ float red_m[kWaves][kHeadsPerGroup], red_l[kWaves][kHeadsPerGroup];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int split = blockIdx.x % a.splits;
+  const int unit = blockIdx.x / a.splits;
+  const int per_branch = a.batch * kGroups;
+  const bool anchor = unit < per_branch;
+  const int bg = anchor ? unit : unit - per_branch;
+  const int b = bg / kGroups, g = bg % kGroups;
+
+  // the state before the token; a full pending block takes no token (as in append)
+  const int p_old = a.pos[b];
+  const int np_old = a.n_pend[b];
+  const bool app = np_old >= 0 && np_old < kBlock;
+  const int p = app ? p_old + 1 : p_old;
+  const int nb = anchor ? min(max(a.n_bank[b], 0), kBank) : 0;
+
+  Segment seg0, seg1;
+  unit_segments_at<false>(a, b, g, anchor, p, nb, app ? np_old + 1 : np_old, seg0, seg1);
+  const int T0 = (seg0.n + kTile - 1) / kTile;
+  const int T = T0 + (seg1.n + kTile - 1) / kTile;
+  const int per = (T + a.splits - 1) / a.splits;
+  const int tb = split * per;
+  const int te = min(T, tb + per);
+  // the tile and row of this branch's new key
+  const int new_key = anchor ? np_old : (p & (kWindow - 1));
+  const int new_tile = app ? (anchor ? T0 : 0) + new_key / kTile : -1;
+  const int new_off = new_key % kTile;
+  const bool owner = new_tile >= tb && new_tile < te;
+
+  SoftmaxState st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int d = 0; d < 16; ++d) st.acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  uint16_t *vl = v_lds[wave];
+  uint4 K[8], V[8];
+  int t = tb + wave;
+  if (t < te) load_tile(t < T0 ? seg0 : seg1, (t < T0 ? t : t - T0) * kTile, lane, K, V);
+  // the owner's wave 0 forms the new rows; stage_query's barrier publishes the patch
+  if (owner && wave == 0) {
+    const size_t in = (static_cast<size_t>(b) * kGroups + g) * kDim + 4 * lane;
+    const uint16_t *krec = anchor ? sp.k_rma : sp.k_win;
+    const uint16_t *vrec = anchor ? sp.v_rma : sp.v_win;
+    const uint2 kr = *reinterpret_cast<const uint2 *>(krec + in);
+    const uint2 vr = *reinterpret_cast<const uint2 *>(vrec + in);
+    float x[4] = {bf16_lo(kr.x), bf16_hi(kr.x), bf16_lo(kr.y), bf16_hi(kr.y)};
+    float c, sn;
+    rope_cos_sin(a.rope_ratio, p, lane, c, sn);
+    norm_rope_head(x, anchor ? sp.gk_rma : sp.gk_win, a.eps, c, sn, lane);
+    const uint2 kw = make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
+    *reinterpret_cast<uint2 *>(&patch[0][4 * lane]) = kw;
+    *reinterpret_cast<uint2 *>(&patch[1][4 * lane]) = vr;
+    const size_t sgi = static_cast<size_t>(b) * kGroups + g;
+    const size_t row = anchor ? (sgi * kBlock + np_old) * kDim : (sgi * kWindow + new_key) * kDim;
+    *reinterpret_cast<uint2 *>((anchor ? sp.pend_k : sp.win_k) + row + 4 * lane) = kw;
+    *reinterpret_cast<uint2 *>((anchor ? sp.pend_v : sp.win_v) + row + 4 * lane) = vr;
+  }
+  stage_query(a, b, g, anchor, p, wave, lane, q_lds);
+  bf16x8 qv[8];
+  {
+    const uint16_t *qrow = &q_lds[0][0] + (lane & 15) * kQStride + 8 * (lane >> 4);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qv[s] = bitcast<bf16x8>(*reinterpret_cast<const uint4 *>(qrow + 32 * s));
+  }
+
+  for (; t < te; t += kWaves) {
+    const int key0 = (t < T0 ? t : t - T0) * kTile;
+    const int nvalid = (t < T0 ? seg0.n : seg1.n) - key0;
+    if (t == new_tile) {
+      // the new row replaces whatever the loads read from it (lane: key lane % 16
+      // for K, rows 2i + lane / 32 for V)
+      if ((lane & 15) == new_off) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          K[s] = *reinterpret_cast<const uint4 *>(&patch[0][32 * s + 8 * (lane >> 4)]);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (2 * i + (lane >> 5) == new_off)
+          V[i] = *reinterpret_cast<const uint4 *>(&patch[1][8 * (lane & 31)]);
+    }
+    const f32x4 sc = scores_tile(nvalid, lane, K, V, qv, vl);
+    const int tn = t + kWaves;
+    if (tn < te) load_tile(tn < T0 ? seg0 : seg1, (tn < T0 ? tn : tn - T0) * kTile, lane, K, V);
+    accumulate_tile(sc, lane, vl, st);
+  }
+
+  __syncthreads();
+  finish_unit(a, st, reinterpret_cast<float *>(&v_lds[0][0]), red_m, red_l, wave, lane, unit,
+              split, anchor, b, g);
+  // every workgroup of the sequence has read pos / n_pend once its count is in
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t nwg = 2u * kGroups * static_cast<uint32_t>(a.splits);
+    if (atomicAdd(&sp.done[b], 1u) == nwg - 1) {
+      sp.done[b] = 0u;
+      if (app) {
+        sp.pend_src[static_cast<size_t>(b) * kBlock + np_old] = p;
+        if (sp.score) {
+#pragma unroll
+          for (int gg = 0; gg < kGroups; ++gg)
+            sp.pend_score[(static_cast<size_t>(b) * kBlock + np_old) * kGroups + gg] =
+                sp.score[b * kGroups + gg];
+        }
+        sp.n_pend[b] = np_old + 1;
+        sp.pos[b] = p;
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------- FP8 rows
@@ -576,7 +734,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_fp8_kernel(DecodePara
     load_v_fp8(sg, key0, lane, V, vs);
     load_k_fp8(sg, key0, lane, K, ks);
   }
-  stage_query(a, b, g, anchor, wave, lane, q_lds);
+  stage_query(a, b, g, anchor, a.pos[b], wave, lane, q_lds);
   // Query operands in registers: qv[2s + h] holds, for lane (hh, kg), dims
   // 64s + 16kg + 8h .. +8 of head hh (the permuted contraction order).
   bf16x8 qv[8];
@@ -674,6 +832,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
 using namespace rma;
 
 static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+static bool aligned8(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
 
 extern "C" int32_t rma_decode_splits(int32_t batch) {
   if (batch <= 0) return 1;
@@ -690,12 +849,12 @@ extern "C" size_t rma_decode_workspace_bytes(int32_t batch) {
   return static_cast<size_t>(batch) * kGroups * 2 * s * kHeadsPerGroup * kPartStride * sizeof(float);
 }
 
-// Validate the shared arguments and launch the decode (and the split merge).
+// Validate the shared arguments and fill the rest of the decode parameters.
 template <bool kFp8>
-static rma_status launch_decode(DecodeParams &p, int32_t batch, const uint16_t *q_win,
-                                const uint16_t *q_rma, const rma_norm *norm, uint16_t *o_win,
-                                float *lse_win, uint16_t *o_rma, float *lse_rma, void *workspace,
-                                size_t workspace_bytes, void *stream) {
+static rma_status prepare_decode(DecodeParams &p, int32_t batch, const uint16_t *q_win,
+                                 const uint16_t *q_rma, const rma_norm *norm, uint16_t *o_win,
+                                 float *lse_win, uint16_t *o_rma, float *lse_rma, void *workspace,
+                                 size_t workspace_bytes) {
   if (!norm || !q_win || !q_rma || !o_win || !lse_win || !o_rma || !lse_rma) return RMA_E_ARG;
   if (batch <= 0 || batch > RMA_MAX_BATCH) return RMA_E_ARG;
   if (!p.win_k || !p.win_v || !p.bank_k || !p.bank_v || !p.pend_k || !p.pend_v || !p.n_bank ||
@@ -729,6 +888,27 @@ static rma_status launch_decode(DecodeParams &p, int32_t batch, const uint16_t *
   p.part = static_cast<float *>(workspace);
   p.batch = batch;
   p.splits = rma_decode_splits(batch);
+  return RMA_OK;
+}
+
+static rma_status launch_merge(const DecodeParams &p, hipStream_t s) {
+  if (p.splits > 1) {
+    const unsigned units = static_cast<unsigned>(p.batch) * kGroups * 2;
+    hipLaunchKernelGGL(decode_merge_kernel, dim3(units), dim3(kMergeThreads), 0, s, p);
+    if (hipPeekAtLastError() != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
+  }
+  return RMA_OK;
+}
+
+// Validate, then launch the decode and the split merge.
+template <bool kFp8>
+static rma_status launch_decode(DecodeParams &p, int32_t batch, const uint16_t *q_win,
+                                const uint16_t *q_rma, const rma_norm *norm, uint16_t *o_win,
+                                float *lse_win, uint16_t *o_rma, float *lse_rma, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+  const rma_status rc = prepare_decode<kFp8>(p, batch, q_win, q_rma, norm, o_win, lse_win, o_rma,
+                                             lse_rma, workspace, workspace_bytes);
+  if (rc != RMA_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const unsigned units = static_cast<unsigned>(batch) * kGroups * 2;
   if constexpr (kFp8)
@@ -736,11 +916,7 @@ static rma_status launch_decode(DecodeParams &p, int32_t batch, const uint16_t *
   else
     hipLaunchKernelGGL(decode_attn_kernel, dim3(units * p.splits), dim3(kThreads), 0, s, p);
   if (hipPeekAtLastError() != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
-  if (p.splits > 1) {
-    hipLaunchKernelGGL(decode_merge_kernel, dim3(units), dim3(kMergeThreads), 0, s, p);
-    if (hipPeekAtLastError() != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
-  }
-  return RMA_OK;
+  return launch_merge(p, s);
 }
 
 extern "C" rma_status swa_rma_decode_attn(const rma_layer_state *st, int32_t batch,
@@ -788,4 +964,69 @@ extern "C" rma_status swa_rma_decode_attn_fp8(const rma_layer_state_fp8 *st, int
   p.pos = st->pos;
   return launch_decode<true>(p, batch, q_win, q_rma, norm, o_win, lse_win, o_rma, lse_rma,
                              workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------- fused step host
+static size_t step_counter_offset(int32_t batch) {
+  return (rma_decode_workspace_bytes(batch) + 255) & ~static_cast<size_t>(255);
+}
+
+extern "C" size_t rma_step_workspace_bytes(int32_t batch) {
+  if (batch <= 0) return 0;
+  return step_counter_offset(batch) + static_cast<size_t>(batch) * sizeof(uint32_t);
+}
+
+extern "C" rma_status swa_rma_step(const rma_layer_state *st, int32_t batch, const uint16_t *k_win,
+                                   const uint16_t *v_win, const uint16_t *k_rma,
+                                   const uint16_t *v_rma, const float *score,
+                                   const uint16_t *q_win, const uint16_t *q_rma,
+                                   const rma_norm *norm, uint16_t *o_win, float *lse_win,
+                                   uint16_t *o_rma, float *lse_rma, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+  if (!st || !norm || !k_win || !v_win || !k_rma || !v_rma) return RMA_E_ARG;
+  if (batch <= 0 || batch > RMA_MAX_BATCH) return RMA_E_ARG;
+  if (!st->pend_src || !norm->gk_win || !norm->gk_rma || (score && !st->pend_score))
+    return RMA_E_ARG;
+  if (!aligned16(norm->gk_win) || !aligned16(norm->gk_rma)) return RMA_E_ALIGN;
+  const void *a8[] = {k_win, v_win, k_rma, v_rma};
+  for (const void *ptr : a8)
+    if (!aligned8(ptr)) return RMA_E_ALIGN;
+  if (!workspace || workspace_bytes < rma_step_workspace_bytes(batch)) return RMA_E_WORKSPACE;
+  if (!aligned16(workspace)) return RMA_E_ALIGN;
+
+  StepParams sp{};
+  DecodeParams &p = sp.d;
+  p.win_k = reinterpret_cast<const uint8_t *>(st->win_k);
+  p.win_v = reinterpret_cast<const uint8_t *>(st->win_v);
+  p.bank_k = reinterpret_cast<const uint8_t *>(st->bank_k);
+  p.bank_v = reinterpret_cast<const uint8_t *>(st->bank_v);
+  p.pend_k = reinterpret_cast<const uint8_t *>(st->pend_k);
+  p.pend_v = reinterpret_cast<const uint8_t *>(st->pend_v);
+  p.n_bank = st->n_bank;
+  p.n_pend = st->n_pend;
+  p.pos = st->pos;
+  const rma_status rc = prepare_decode<false>(p, batch, q_win, q_rma, norm, o_win, lse_win, o_rma,
+                                              lse_rma, workspace, workspace_bytes);
+  if (rc != RMA_OK) return rc;
+  sp.win_k = st->win_k;
+  sp.win_v = st->win_v;
+  sp.pend_k = st->pend_k;
+  sp.pend_v = st->pend_v;
+  sp.pend_score = st->pend_score;
+  sp.pend_src = st->pend_src;
+  sp.n_pend = st->n_pend;
+  sp.pos = st->pos;
+  sp.k_win = k_win;
+  sp.v_win = v_win;
+  sp.k_rma = k_rma;
+  sp.v_rma = v_rma;
+  sp.score = score;
+  sp.gk_win = norm->gk_win;
+  sp.gk_rma = norm->gk_rma;
+  sp.done = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) + step_counter_offset(batch));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const unsigned units = static_cast<unsigned>(batch) * kGroups * 2;
+  hipLaunchKernelGGL(decode_step_kernel, dim3(units * p.splits), dim3(kThreads), 0, s, sp);
+  if (hipPeekAtLastError() != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
+  return launch_merge(p, s);
 }

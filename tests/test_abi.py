@@ -100,6 +100,35 @@ def test_host_validation_rejects_bad_arguments(lib):
     assert pf(by(st), 2, 100, 16, need, q=24) == 2
 
 
+def test_step_workspace_and_host_validation(lib):
+    # the decode's partials, then one counter per sequence at a 256-byte offset
+    assert R.rma_step_workspace_bytes(512) == 512 * 4
+    assert R.rma_step_workspace_bytes(16) == 16 * 8 * 4 * 4 * 260 * 4 + 16 * 4
+    d1 = R.rma_decode_workspace_bytes(1)
+    assert R.rma_step_workspace_bytes(1) == (d1 + 255) // 256 * 256 + 4
+    assert R.rma_step_workspace_bytes(0) == 0
+    st, nm = _state(), _norm()
+    by = ctypes.byref
+    need = R.rma_step_workspace_bytes(4)
+    step = lambda st_, b, ws, wsb, k=16, q=16, score=None: lib.swa_rma_step(  # noqa: E731
+        st_, b, k, 16, 16, 16, score, q, 16, by(nm), 16, 16, 16, 16, ws, wsb, None)
+    assert step(None, 4, 16, need) == 1
+    assert step(by(st), 0, 16, need) == 1
+    assert step(by(st), 4, 16, need, k=None) == 1
+    assert step(by(st), 4, 16, need, k=20) == 2      # raw key rows are read 8 bytes at a time
+    assert step(by(st), 4, 16, need, q=24) == 2
+    assert step(by(st), 4, None, 0) == 3             # the counters are always needed
+    assert step(by(st), 512, 16, 512 * 4 - 1) == 3
+    assert step(by(st), 4, 16, need - 1) == 3
+    assert step(by(st), 4, 24, need) == 2
+    bad = _state()
+    bad.pend_score = None
+    assert step(by(bad), 4, 16, need, score=16) == 1  # a score needs somewhere to go
+    bad = _state()
+    bad.pend_src = None
+    assert step(by(bad), 4, 16, need) == 1
+
+
 def test_fp8_state_size_and_host_validation(lib):
     # codes (1 B) + one FP32 scale per K and V row, plus the same metadata
     rows = 2 * 4 * (1024 + 1024 + 256)
