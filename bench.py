@@ -247,15 +247,17 @@ def bench_commit_burst(args):
 
 
 def bench_long_stream(args):
-    """Batch-1 stream: per token, append + decode in all 8 layers; every 256 tokens the
-    scorer and the commit in all 8 layers.
+    """Batch-1 stream: per token, one step (append + attention + split merge) in all 8
+    layers; every 256 tokens the scorer and the commit in all 8 layers.
 
     The first quarter of the stream runs eagerly (warm-up), the second quarter is timed
-    eagerly (one library call per launch), the second half is timed as replays of a
+    eagerly (one fused-step call per layer), the second half is timed as replays of a
     HIP graph holding one whole 256-token block (inputs copied into the graph's static
-    buffers before each replay, outside the timed events).  The last 256 tokens time
-    single tokens: a one-token graph per token, the block's score + commit after the
-    last one."""
+    buffers before each replay, outside the timed events): blocks alternate between the
+    fused-step graph (the reported value) and the graph of separate append, decode and
+    merge launches (reported beside it).  Both give the same bits, so the stream is one
+    stream whichever graph advances it.  The last 256 tokens time single tokens: a
+    one-token fused graph per token, the block's score + commit after the last one."""
     import torch
 
     import swa_memory_anchor_amd as R
@@ -289,7 +291,7 @@ def bench_long_stream(args):
              torch.empty(1, 16, device=dev), torch.empty(1, 16, 256, dtype=torch.bfloat16,
                                                          device=dev),
              torch.empty(1, 16, device=dev)) for _ in range(L)]
-    ws = R.decode_workspace(1, dev)
+    ws = R.step_workspace(1, dev)
     lib = R.lib()
     import ctypes
 
@@ -310,11 +312,10 @@ def bench_long_stream(args):
     def token(t):
         for l in range(L):
             r = [rp[nm][l] + t * 2048 for nm in W.RECORD_NAMES]
-            lib.swa_rma_append(st_c[l], 1, r[0], r[1], r[2], r[3], None, nm_c[l], sp)
             qq = qp[l] + t * 8192
             o = op[l]
-            lib.swa_rma_decode_attn(st_c[l], 1, qq, qq, nm_c[l], o[0], o[1], o[2], o[3], wsp,
-                                    wsn, sp)
+            lib.swa_rma_step(st_c[l], 1, r[0], r[1], r[2], r[3], None, qq, qq, nm_c[l], o[0],
+                             o[1], o[2], o[3], wsp, wsn, sp)
         if (t + 1) % 256 == 0:
             commit_block(t)
 
@@ -331,27 +332,40 @@ def bench_long_stream(args):
     torch.cuda.synchronize()
     eager_us = a.elapsed_time(b) * 1e3 / (half - quarter)
 
-    # whole blocks as graph replays
-    blk = StreamBlockGraph(states, norms, w, 1).capture()
+    # whole blocks as graph replays, alternating the fused and the separate-launch graph
+    # (the separate path's kernels run once eagerly first, so their code is loaded)
+    qq, o = qp[0] + (half - 1) * 8192, op[0]
+    scratch = R.alloc_layer_state(1, dev)
+    sc_c = ctypes.byref(R._state_c(scratch))
+    dws = R.decode_workspace(1, dev)
+    lib.swa_rma_append(sc_c, 1, *[rp[nm][0] for nm in W.RECORD_NAMES], None, nm_c[0], sp)
+    lib.swa_rma_decode_attn(sc_c, 1, qq, qq, nm_c[0], o[0], o[1], o[2], o[3], dws.data_ptr(),
+                            dws.numel(), sp)
+    blocks = {True: StreamBlockGraph(states, norms, w, 1, fused=True).capture(),
+              False: StreamBlockGraph(states, norms, w, 1, fused=False).capture()}
 
-    def load_block(t0):
+    def load_block(blk, t0):
         for nm, src in zip(RECORD_NAMES, W.RECORD_NAMES):
             blk.rec[nm].copy_(rec[src][:, t0:t0 + 256].unsqueeze(2))
         blk.q_win.copy_(q[:, t0:t0 + 256].unsqueeze(2))
         blk.q_rma.copy_(blk.q_win)
         blk.hidden.copy_(hid[:, t0:t0 + 256].unsqueeze(1))
 
-    graph_ms = 0.0
-    ntok_graph = 0
-    for t0 in range(half, n - tail, 256):
-        load_block(t0)
+    graph_ms = {True: 0.0, False: 0.0}
+    ntok = {True: 0, False: 0}
+    for i, t0 in enumerate(range(half, n - tail, 256)):
+        fused = i % 2 == 0
+        blk = blocks[fused]
+        load_block(blk, t0)
         a.record(stream)
         blk.replay()
         b.record(stream)
         torch.cuda.synchronize()
-        graph_ms += a.elapsed_time(b)
-        ntok_graph += 256
-    graph_us = graph_ms * 1e3 / ntok_graph
+        graph_ms[fused] += a.elapsed_time(b)
+        ntok[fused] += 256
+    graph_us = graph_ms[True] * 1e3 / ntok[True]
+    separate_us = graph_ms[False] * 1e3 / ntok[False]
+    ntok_graph = ntok[True]
 
     # single tokens: one-token graph (all layers' append + decode) per token
     one = StreamBlockGraph(states, norms, w, 1, tokens=1, commit=False).capture()
@@ -388,8 +402,10 @@ def bench_long_stream(args):
                    "positions_timed_eager": [quarter, half - 1],
                    "state_bytes_per_layer": state_bytes,
                    "tokens_per_s": round(1e6 / graph_us, 1),
-                   "launch": "one HIP graph per 256-token block (all layers)"},
+                   "launch": "one HIP graph per 256-token block (all layers), one fused "
+                             "step launch per layer and token"},
         "eager_us_per_token": round(eager_us, 2),
+        "separate_launches_us_per_token": round(separate_us, 2),
         "latency_us": {"tokens": tail, "median": round(lat_sorted[tail // 2], 1),
                        "p99": round(lat_sorted[int(0.99 * tail)], 1),
                        "max": round(lat_sorted[-1], 1),

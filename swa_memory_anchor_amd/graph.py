@@ -7,9 +7,11 @@ these launches is short, so host-side launch cost matters as much as the kernels
 the pages' single-request decoding rates (fluxbbs.com page, section "吞吐：一张
 80GB 卡跑 512 路长推理") come from a backend that replays captured graphs
 (agentlenshq.com "rockmatrix-ai/EdgeRock", section "如何尝试").  ``StreamBlockGraph``
-records one whole 256-token block for every layer (256 x L x (append, decode),
-then L x (score, commit)) into a single HIP graph through torch's graph capture,
-and replays it per block.
+records one whole 256-token block for every layer (256 x L steps, then
+L x (score, commit)) into a single HIP graph through torch's graph capture, and
+replays it per block.  A step is one ``swa_rma_step`` launch (append and
+attention fused; the split merge follows where the key range is split) or, with
+``fused=False``, the separate append and decode launches.
 
 The graph reads its inputs from static buffers owned by this object (fill them
 before each replay: ``rec``, ``q_win``, ``q_rma``, ``hidden``) and writes every
@@ -25,7 +27,7 @@ from __future__ import annotations
 import ctypes
 
 from . import (BLOCK, HEAD_DIM, HIDDEN, KV_GROUPS, Q_HEADS, LayerState, Norm, _norm_c, _ptr,
-               _state_c, decode_workspace, lib)
+               _state_c, decode_workspace, lib, step_workspace)
 
 RECORD_NAMES = ("k_win", "v_win", "k_rma", "v_rma")
 
@@ -44,7 +46,7 @@ class StreamBlockGraph:
     """
 
     def __init__(self, states: list[LayerState], norms: list[Norm], scorer, batch: int,
-                 tokens: int = BLOCK, commit: bool = True, device="cuda"):
+                 tokens: int = BLOCK, commit: bool = True, fused: bool = True, device="cuda"):
         import torch
 
         if commit and tokens != BLOCK:
@@ -62,7 +64,10 @@ class StreamBlockGraph:
         self.o_rma = torch.zeros_like(self.o_win)
         self.lse_win = torch.zeros(L, tokens, batch, Q_HEADS, device=device)
         self.lse_rma = torch.zeros_like(self.lse_win)
-        self.workspace = decode_workspace(batch, device)
+        self.fused = fused
+        # the fused step's workspace holds counters that start at zero and are back
+        # at zero after every step, so one zero fill serves every replay
+        self.workspace = step_workspace(batch, device) if fused else decode_workspace(batch, device)
         self._states, self._norms, self._scorer = states, norms, scorer
         # the ctypes structs must outlive the graph: kernels read them at launch only,
         # but keep them with the object for the record
@@ -85,6 +90,15 @@ class StreamBlockGraph:
                 r = [rp[nm] + off * rb for nm in RECORD_NAMES]
                 st = ctypes.byref(self._st_c[l])
                 nm = ctypes.byref(self._nm_c[l])
+                if self.fused:
+                    s = lb.swa_rma_step(
+                        st, B, r[0], r[1], r[2], r[3], None, self.q_win.data_ptr() + off * qb,
+                        self.q_rma.data_ptr() + off * qb, nm, self.o_win.data_ptr() + off * qb,
+                        self.lse_win.data_ptr() + off * lb_, self.o_rma.data_ptr() + off * qb,
+                        self.lse_rma.data_ptr() + off * lb_, ws, wsn, stream)
+                    if s != 0:
+                        raise RuntimeError(f"swa_rma_step failed during capture (status {s})")
+                    continue
                 s = lb.swa_rma_append(st, B, r[0], r[1], r[2], r[3], None, nm, stream)
                 if s != 0:
                     raise RuntimeError(f"swa_rma_append failed during capture (status {s})")

@@ -62,8 +62,12 @@ def _eager(states, norms, scorer, g: StreamBlockGraph):
     return outs
 
 
+@pytest.mark.parametrize("fused", [True, False])
 @pytest.mark.parametrize("B", [1, 3])
-def test_block_graph_replays_match_eager(B):
+def test_block_graph_replays_match_eager(B, fused):
+    """The eager reference is always the separate append + decode; the fused step's
+    graph must match it bit for bit too."""
+    print(f"case: block graph B={B} fused={fused}", flush=True)
     tag = f"graph_b{B}"
     L = 2
     counts = [(1024, 65535), (300, 767), (0, -1)][:B]
@@ -84,13 +88,18 @@ def test_block_graph_replays_match_eager(B):
 
     live = [_clone(s) for s in init]
     eager_states = [_clone(s) for s in init]
-    g = StreamBlockGraph(live, norms, scorer, B)
+    g = StreamBlockGraph(live, norms, scorer, B, fused=fused)
     for nm in RECORD_NAMES:
         normal_bf16_torch_(g.rec[nm], synth.stream_key(tag, "rec", nm))
     normal_bf16_torch_(g.q_win, synth.stream_key(tag, "qw"))
     normal_bf16_torch_(g.q_rma, synth.stream_key(tag, "qr"))
     normal_bf16_torch_(g.hidden, synth.stream_key(tag, "hid"))
     ref = _eager(eager_states, norms, scorer, g)  # also loads every kernel before capture
+    if fused:  # load the fused step's kernel too, on a throwaway copy of the state
+        scratch = _clone(init[0])
+        o = [torch.empty_like(x[0, 0]) for x in (g.o_win, g.lse_win, g.o_rma, g.lse_rma)]
+        R.swa_rma_step(scratch, B, *[g.rec[nm][0, 0] for nm in RECORD_NAMES], None,
+                       g.q_win[0, 0], g.q_rma[0, 0], norms[0], *o, R.step_workspace(B))
     torch.cuda.synchronize()
     g.capture()
     ref_bits = [bits_host(ref[0]), ref[1].cpu().numpy(), bits_host(ref[2]), ref[3].cpu().numpy()]

@@ -1,7 +1,8 @@
 """GPU parity of the fused step (swa_rma_step): one launch that appends the token
-and attends with it must leave the same state and produce the same outputs, bit
-for bit, as the append followed by the decode; and both match the oracle's
-append followed by its decode within the decode's bars.
+and attends with it (then the split merge, as in the decode) must leave the same
+state and produce the same outputs, bit for bit, as the append followed by the
+decode; and both match the oracle's append followed by its decode within the
+decode's bars.
 
 Cases: ragged states at a batch that splits the key range and at one that does
 not, the window ring wrapping (pos + 1 a multiple of 1024), an empty state, a
@@ -115,7 +116,8 @@ def _run_both(tag, counts, steps, with_score, reps=1):
         _assert_states_equal(fused, split, f"{tag} t={t}")
         for x, y, nmo in zip(o_f, o_s, ("o_win", "lse_win", "o_rma", "lse_rma")):
             assert _same(x, y), f"{tag} t={t}: {nmo}"
-        assert not ws[R.rma_step_workspace_bytes(B) - 4 * B:].any(), "counters not reset"
+        off = (R.rma_decode_workspace_bytes(B) + 255) // 256 * 256
+        assert not ws[off:].any(), "counters not reset"
         # the oracle: append, then decode
         _oracle_append(st, recs, g, score if with_score else None)
         ref = O.decode(st, q[0], q[1], g["gq_win"], g["gq_rma"], 1e-6, 1e7)
