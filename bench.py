@@ -220,6 +220,7 @@ def bench_commit_burst(args):
                 c_ms.append(a.elapsed_time(b))
     admitted = int(sum(int((k >= 1024).sum()) for k in keeps))
     c_avg = sum(c_ms) / len(c_ms)
+    cpu = None if args.no_cpu_baseline else cpu_baseline_commit_burst(wl, min(args.cpu_budget, 20.0))
     key_bytes = B * 4 * 1280 * 8  # score + source of every candidate
     copy_bytes = admitted / L * 2 * 2 * 512  # K and V rows, read and written
     out_bytes = B * 4 * 1024 * 4  # keep_idx
@@ -243,6 +244,7 @@ def bench_commit_burst(args):
                    "admitted_rows_per_layer": admitted // L,
                    "algorithmic_bytes_per_launch": int(key_bytes + copy_bytes + out_bytes),
                    "gbps": round((key_bytes + copy_bytes + out_bytes) / (c_avg / 1e3) / 1e9, 1)},
+        "cpu_baseline": cpu,
     }
 
 
@@ -384,6 +386,7 @@ def bench_long_stream(args):
         torch.cuda.synchronize()
         lat.append(a.elapsed_time(b) * 1e3)
     lat_sorted = sorted(lat)
+    cpu = None if args.no_cpu_baseline else cpu_baseline_long_stream(wl, min(args.cpu_budget, 20.0))
     state_bytes = sum(x.numel() * x.element_size() for x in states[0].__dict__.values())
     return {
         "metric": "batch-1 stream: microseconds per token (8 layers append + decode, "
@@ -412,6 +415,7 @@ def bench_long_stream(args):
                        "block_end_token": round(lat[-1], 1),
                        "note": "one-token graph per token, synchronised on its own; the "
                                "block's last token adds the scorer and commit (eager)"},
+        "cpu_baseline": cpu,
     }
 
 
@@ -599,6 +603,105 @@ def bench_gdn(args):
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_gdn(wl, min(args.cpu_budget, 10.0))
     return res
+
+
+def cpu_baseline_commit_burst(wl, budget_s: float):
+    """The oracle's scorer and commit, untuned, on a bounded sample of one burst.
+
+    Scorer: the float64 chain on the 256 hidden rows of random (sequence, layer)
+    pairs, scaled to every row of the burst.  Commit: the selection of random
+    (sequence, layer, group) segments on the burst's own scores, plus the copies of
+    the admitted K/V rows (into scratch rows of the real size: the copy's cost does
+    not depend on the values), scaled to every segment."""
+    import numpy as np
+
+    import oracle as O
+    from synth import workloads as W
+
+    rng = np.random.default_rng(13)
+    B, L = wl.batch, wl.layers
+    w = {}
+    rows, s_spent = 0, 0.0
+    while s_spent < budget_s / 2:
+        b, layer = int(rng.integers(0, B)), int(rng.integers(0, L))
+        w1, w2 = w.setdefault(layer, W.scorer_weights(wl, layer))
+        h = W.burst_hidden_np(wl, layer, b)
+        t0 = time.perf_counter()
+        O.score(h, w1, w2)
+        s_spent += time.perf_counter() - t0
+        rows += h.shape[0]
+    sc = {0: W.burst_scores(wl, 0)}
+    k_src, v_src = np.zeros((2, 256, 256), np.uint16)
+    k_dst, v_dst = np.zeros((2, 1024, 256), np.uint16)
+    segs, c_spent = 0, 0.0
+    while c_spent < budget_s / 2:
+        layer = int(rng.integers(0, 2))  # the scores of two layers are enough to sample from
+        if layer not in sc:
+            sc[layer] = W.burst_scores(wl, layer)
+        d = sc[layer]
+        b, g = int(rng.integers(0, B)), int(rng.integers(0, 4))
+        t0 = time.perf_counter()
+        _, moves = O.commit_segment(d["bank_score"][b, g], d["bank_src"][b, g],
+                                    int(d["n_bank"][b]), d["pend_score"][b, :, g],
+                                    d["pend_src"][b], int(d["n_pend"][b]), 1024)
+        for t, slot in moves:
+            k_dst[slot] = k_src[t]
+            v_dst[slot] = v_src[t]
+        c_spent += time.perf_counter() - t0
+        segs += 1
+    score_s = s_spent / rows * B * 256 * L
+    commit_s = c_spent / segs * B * 4 * L
+    return {"value": round(score_s + commit_s, 2), "unit": "s/burst", "cores": _blas_threads(),
+            "kind": "oracle",
+            "score_s_per_burst": round(score_s, 2), "commit_s_per_burst": round(commit_s, 2),
+            "sample": f"scorer: {rows} rows ({rows // 256} random (sequence, layer) pairs) in "
+                      f"{s_spent:.1f} s, scaled to {B * 256 * L} rows; commit: {segs} random "
+                      f"segments in {c_spent:.1f} s, scaled to {B * 4 * L} segments"}
+
+
+def cpu_baseline_long_stream(wl, budget_s: float):
+    """The oracle, untuned, on the batch-1 stream: per token append + decode of one
+    layer on a steady-state state (full bank, window wrapped), then one block's
+    scorer + commit; scaled to 8 layers and amortised over the 256-token block."""
+    import numpy as np
+
+    import oracle as O
+    import synth
+    from synth import workloads as W
+
+    layer, p0 = 0, 8191
+    st = O.new_layer_state(1)
+    for nm in ("win_k", "win_v", "bank_k", "bank_v", "pend_k", "pend_v"):
+        a = getattr(st, nm)
+        a[...] = synth.normal_bf16_np(W.key(wl, "cpu", nm), a.size).reshape(a.shape)
+    st.n_bank[0], st.n_pend[0], st.pos[0] = 1024, 0, p0
+    st.bank_score[...] = synth.normal_f32_np(W.key(wl, "cpu", "bank_score"), st.bank_score.shape,
+                                             0.0, 0.3)
+    st.bank_src[...] = np.arange(1024, dtype=np.int32)[None, None, :] * 7
+    g = W.gains(wl, layer)
+    recs = {nm: W.record_np(wl, layer, nm, p0 + 1, p0 + 257) for nm in W.RECORD_NAMES}
+    q = W.stream_q_np(wl, layer, p0 + 1, p0 + 257)
+    tok, spent = 0, 0.0
+    while tok < 256 and spent < budget_s:
+        r = [recs[nm][tok:tok + 1] for nm in W.RECORD_NAMES]
+        t0 = time.perf_counter()
+        O.append(st, *r, g["gk_win"], g["gk_rma"], wl.eps, wl.rope_base)
+        O.decode(st, q[tok:tok + 1], q[tok:tok + 1], g["gq_win"], g["gq_rma"], wl.eps,
+                 wl.rope_base)
+        spent += time.perf_counter() - t0
+        tok += 1
+    st.n_pend[0] = 256  # the block as it stands at its end
+    w1, w2 = W.scorer_weights(wl, layer)
+    h = W.stream_hidden_np(wl, layer, p0 + 1, p0 + 257)
+    t0 = time.perf_counter()
+    st.pend_score[0] = O.score(h, w1, w2)
+    O.commit(st)
+    block_s = time.perf_counter() - t0
+    ms = wl.layers * (spent / tok + block_s / 256) * 1e3
+    return {"value": round(ms, 3), "unit": "ms/token", "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"{tok} tokens of one layer at positions {p0 + 1}.. in {spent:.1f} s plus "
+                      f"one block's scorer + commit ({block_s:.2f} s), x {wl.layers} layers, "
+                      f"the block part amortised over 256 tokens"}
 
 
 def cpu_baseline_gdn(wl, budget_s: float):
