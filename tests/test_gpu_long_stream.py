@@ -1,8 +1,9 @@
 """GPU parity on the batch-1 long stream: 262144 positions through all 8 layers.
 
-Per token and layer the stream appends (window + pending) and decodes; every
-256 tokens each layer commits.  Candidate scores come from the input generator
-(passed through swa_rma_append), so the commit chain of the GPU and of the
+Per token and layer the stream runs one fused step (swa_rma_step: append to
+window + pending, then decode, as the benchmark's stream does); every 256 tokens
+each layer commits.  Candidate scores come from the input generator (passed
+through the step), so the commit chain of the GPU and of the
 oracle see identical scores and must agree bit for bit; the scorer itself is
 checked separately on sampled blocks of the stream's hidden states.
 
@@ -97,7 +98,7 @@ def test_long_stream_b1():
              torch.empty(1, 16, 256, dtype=torch.bfloat16, device=DEV),
              torch.empty(1, 16, dtype=torch.float32, device=DEV)) for _ in range(L)]
     out_p = [[o.data_ptr() for o in os_] for os_ in outs]
-    ws = R.decode_workspace(1)
+    ws = R.step_workspace(1)
     ws_p, ws_n = ws.data_ptr(), ws.numel()
     keeps = torch.empty(NBLK, L, 4, O.BANK, dtype=torch.int32, device=DEV)
     captured = {}
@@ -119,13 +120,10 @@ def test_long_stream_b1():
             p = c0 + t
             for l in range(L):
                 r = [base[nm][l] + t * rec_stride for nm in W.RECORD_NAMES]
-                s = lib.swa_rma_append(st_c[l], 1, r[0], r[1], r[2], r[3], sbase[l] + t * 16,
-                                       nm_c[l], stream)
-                assert s == 0
                 q = qbase[l] + t * q_stride
                 o = out_p[l]
-                s = lib.swa_rma_decode_attn(st_c[l], 1, q, q, nm_c[l], o[0], o[1], o[2], o[3],
-                                            ws_p, ws_n, stream)
+                s = lib.swa_rma_step(st_c[l], 1, r[0], r[1], r[2], r[3], sbase[l] + t * 16, q, q,
+                                     nm_c[l], o[0], o[1], o[2], o[3], ws_p, ws_n, stream)
                 assert s == 0
                 if p in samples and l in CHECK_LAYERS:
                     captured[(p, l)] = [x.clone() for x in outs[l]]
