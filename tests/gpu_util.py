@@ -8,6 +8,7 @@ import torch
 
 import oracle as O
 import swa_memory_anchor_amd as R
+from attn_check import attn_errors  # noqa: F401  (re-exported)
 
 DEV = "cuda"
 ATTN_TOL = 2e-2  # row-relative, BF16 I/O with FP32 accumulation
@@ -64,21 +65,6 @@ def decode_gpu(st: R.LayerState, q_win: torch.Tensor, q_rma: torch.Tensor, norm:
     ws = R.decode_workspace(B)
     R.swa_rma_decode_attn(st, B, q_win, q_rma, norm, o_w, l_w, o_r, l_r, ws)
     return o_w, l_w, o_r, l_r
-
-
-def attn_errors(o_gpu_bits, lse_gpu, o_ref, lse_ref):
-    """Per-row relative output error and per-row LSE error (arrays over all rows)."""
-    og = O.bf16_to_f64(o_gpu_bits).reshape(-1, o_ref.shape[-1])
-    orf = np.asarray(o_ref, np.float64).reshape(-1, o_ref.shape[-1])
-    scale = np.abs(orf).max(axis=1)
-    err = np.abs(og - orf).max(axis=1)
-    rel = np.where(scale > 0, err / np.where(scale > 0, scale, 1.0), err)
-    lg = np.asarray(lse_gpu, np.float64).reshape(-1)
-    lr = np.asarray(lse_ref, np.float64).reshape(-1)
-    both_inf = np.isneginf(lg) & np.isneginf(lr)
-    with np.errstate(invalid="ignore"):
-        lerr = np.where(both_inf, 0.0, np.abs(lg - lr) / np.maximum(1.0, np.abs(lr)))
-    return rel, lerr
 
 
 def assert_attn_close(o_gpu_bits, lse_gpu, o_ref, lse_ref, tol=ATTN_TOL, what=""):

@@ -3,12 +3,15 @@
 * tiny_stream: the whole 2048-token stream (appends, 8 score bursts, 8 commits)
   and 8 decode steps, every output against the oracle's own run.
 * steady_b64 / headline_b512: one decode step over all 8 layers in the launch
-  configuration the benchmark times; sampled (sequence, layer) units against the
-  oracle, which regenerates their state from the seeds.
+  configuration the benchmark times; every (sequence, layer) unit (512 and 4096)
+  against the oracle, which regenerates each unit's state from the seeds in
+  worker processes.
 * commit_burst_b512: the scorer over all 131072 rows of a layer (sampled rows
   against the oracle, duplicated rows bit-identical) and the commit of all 512
   sequences with generator-supplied scores carrying planted exact ties.
 """
+
+import time
 
 import numpy as np
 import pytest
@@ -18,7 +21,8 @@ import oracle as O
 import swa_memory_anchor_amd as R
 from synth import workloads as W
 
-from gpu_util import (DEV, SCORE_TOL, assert_attn_close, assert_scores_close, bf16_dev,
+import oracle_pool
+from gpu_util import (ATTN_TOL, DEV, SCORE_TOL, assert_attn_close, assert_scores_close, bf16_dev,
                       assert_keys_close, bits_host, decode_gpu, download, f32_dev, i32_dev,
                       norm_dev)
 
@@ -125,7 +129,11 @@ def _fill_decode_layer(wl, layer, st: R.LayerState):
 
 
 def _decode_workload(wl, samples):
-    """Fill all layers, run one step (all layers), compare sampled units with the oracle."""
+    """Fill all layers, run one step (all layers), compare every unit with the oracle.
+
+    The oracle runs in worker processes (oracle_pool), each regenerating its units'
+    inputs on the host; the device copies of the sampled units' queries are also
+    checked against the host generator bit for bit."""
     B, L = wl.batch, wl.layers
     print(f"case: {wl.name} B={B} L={L} splits={R.rma_decode_splits(B)}", flush=True)
     states, qs, norms, gains = [], [], [], []
@@ -142,34 +150,29 @@ def _decode_workload(wl, samples):
     torch.cuda.synchronize()
     outs = [decode_gpu(states[l], qs[l], qs[l], norms[l]) for l in range(L)]
     torch.cuda.synchronize()
-    print("decode done; checking samples", flush=True)
-    rels = []
+    print("decode done; checking every unit", flush=True)
     for (b, layer) in samples:
-        s = W.decode_state_np(wl, layer, b)
-        q = W.q_np(wl, layer, b)
         # the device copy was drawn from the same counter streams
-        assert np.array_equal(bits_host(qs[layer][b]), q)
-        kv = {k: s[k] for k in W.KV_NAMES}
-        g = gains[layer]
-        ow, lw = O.decode_one(list(kv["win_k"]), list(kv["win_v"]), q, g["gq_win"], s["pos"],
-                              wl.eps, wl.rope_base)
-        keys = [np.concatenate([kv["bank_k"][gg], kv["pend_k"][gg]]) for gg in range(4)]
-        vals = [np.concatenate([kv["bank_v"][gg], kv["pend_v"][gg]]) for gg in range(4)]
-        orr, lr = O.decode_one(keys, vals, q, g["gq_rma"], s["pos"], wl.eps, wl.rope_base)
-        o_w, l_w, o_r, l_r = outs[layer]
-        r1, _ = assert_attn_close(bits_host(o_w[b]), l_w[b].cpu().numpy(), ow, lw,
-                                  what=f"b={b} layer={layer} win")
-        r2, _ = assert_attn_close(bits_host(o_r[b]), l_r[b].cpu().numpy(), orr, lr,
-                                  what=f"b={b} layer={layer} rma")
-        rels += [r1.max(), r2.max()]
-    # properties at every row: finite outputs and log-sum-exps in the range the
-    # state allows (ln of the key count plus the score range)
-    for o_w, l_w, o_r, l_r in outs:
-        for lse in (l_w, l_r):
-            assert torch.isfinite(lse).all()
-        for o in (o_w, o_r):
-            assert torch.isfinite(o.float()).all()
-    print(f"{wl.name}: {len(samples)} units, worst row-relative error {max(rels):.3e}")
+        assert np.array_equal(bits_host(qs[layer][b]), W.q_np(wl, layer, b))
+    host = [(bits_host(o_w), l_w.cpu().numpy(), bits_host(o_r), l_r.cpu().numpy())
+            for o_w, l_w, o_r, l_r in outs]
+    del states, outs
+    tasks = [(wl.name, layer, b, host[layer][0][b], host[layer][1][b], host[layer][2][b],
+              host[layer][3][b]) for layer in range(L) for b in range(B)]
+    t0 = time.perf_counter()
+    res = oracle_pool.all_unit_errors(tasks)
+    worst = max(res, key=lambda r: max(r[2], r[4]))
+    print(f"{wl.name}: all {len(res)} units against the oracle in {time.perf_counter() - t0:.1f} s "
+          f"({oracle_pool.workers()} workers); worst row-relative error {max(worst[2], worst[4]):.3e} "
+          f"(b={worst[0]} layer={worst[1]}), worst lse error "
+          f"{max(max(r[3], r[5]) for r in res):.3e}", flush=True)
+    bad = [r for r in res if not (max(r[2], r[4]) <= ATTN_TOL and max(r[3], r[5]) <= ATTN_TOL)]
+    assert not bad, f"{len(bad)} units out of bound, e.g. {bad[:4]}"
+    # properties at every row: finite outputs and log-sum-exps
+    for ow_bits, lw, or_bits, lr in host:
+        assert np.all(np.isfinite(lw)) and np.all(np.isfinite(lr))
+        for o in (ow_bits, or_bits):
+            assert np.all(np.isfinite(O.bf16_to_f64(o)))
 
 
 def test_steady_b64_decode():
