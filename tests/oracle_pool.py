@@ -3,7 +3,8 @@ over worker processes.
 
 Each worker regenerates the unit's inputs on the host from the seeded generators
 (state, query, gains: the same counter streams the device copies were drawn from),
-runs the float64 oracle for both branches, and compares with the GPU's outputs for
+runs the float64 oracle for both branches (the FP8 oracle on the dequantised rows
+for an E4M3 state), and compares with the GPU's outputs for
 that unit, which the parent passes in.  Workers import NumPy, the oracle and the
 generators only: no torch, no GPU.  They are started with "spawn" (never forked
 from a process that holds a GPU context).
@@ -39,13 +40,20 @@ def unit_errors(task):
     g = _GAINS.get((name, layer))
     if g is None:
         g = _GAINS[(name, layer)] = W.gains(wl, layer)
-    s = W.decode_state_np(wl, layer, b)
     q = W.q_np(wl, layer, b)
-    ow, lwr = O.decode_one(list(s["win_k"]), list(s["win_v"]), q, g["gq_win"], s["pos"], wl.eps,
-                           wl.rope_base)
-    keys = [np.concatenate([s["bank_k"][gg], s["pend_k"][gg]]) for gg in range(4)]
-    vals = [np.concatenate([s["bank_v"][gg], s["pend_v"][gg]]) for gg in range(4)]
-    orr, lrr = O.decode_one(keys, vals, q, g["gq_rma"], s["pos"], wl.eps, wl.rope_base)
+    if wl.extra.get("kv") == "e4m3":  # codes + row scales, dequantised by the FP8 oracle
+        from oracle import fp8_ref as F
+
+        rows = {nm: F.dequantize(*W.kv_fp8_np(wl, layer, nm, b)) for nm in W.KV_NAMES}
+        dec, pos = F.decode_one, wl.position
+    else:
+        rows = W.decode_state_np(wl, layer, b)
+        dec, pos = O.decode_one, rows["pos"]
+    ow, lwr = dec(list(rows["win_k"]), list(rows["win_v"]), q, g["gq_win"], pos, wl.eps,
+                  wl.rope_base)
+    keys = [np.concatenate([rows["bank_k"][gg], rows["pend_k"][gg]]) for gg in range(4)]
+    vals = [np.concatenate([rows["bank_v"][gg], rows["pend_v"][gg]]) for gg in range(4)]
+    orr, lrr = dec(keys, vals, q, g["gq_rma"], pos, wl.eps, wl.rope_base)
     r1, e1 = attn_errors(ow_bits, lw, ow, lwr)
     r2, e2 = attn_errors(or_bits, lr, orr, lrr)
     return (b, layer, float(np.max(r1)), float(np.max(e1)), float(np.max(r2)), float(np.max(e2)))
@@ -68,3 +76,40 @@ def all_unit_errors(tasks, procs=None):
     ctx = mp.get_context("spawn")
     with ctx.Pool(procs, initializer=_init_worker) as pool:
         return pool.map(unit_errors, tasks, chunksize=max(1, len(tasks) // (8 * procs)))
+
+
+_GDN = {}
+
+
+def gdn_unit_errors(task):
+    """task = (workload name, layer, b, new matrices [32][128][128], output bits
+    [32][128], convolution ring bits [4][8192]) from the GPU -> (b, layer, largest
+    state error / bound, largest output row error, ring bit-exact)."""
+    import synth
+    from gdn_check import out_rel, state_err_ratio
+    from oracle import gdn_ref as G
+    from synth import workloads as W
+
+    name, layer, b, s_gpu, o_bits, ring_gpu = task
+    wl = W.WORKLOADS[name]
+    prm = _GDN.get((name, layer))
+    if prm is None:
+        prm = _GDN[(name, layer)] = (W.gdn_params(wl, layer), W.gdn_gate_inputs(wl, layer))
+    p, (a, bb) = prm
+    sdt = np.float16 if wl.extra["state"] == "f16" else np.float32
+    st = G.GdnState(np.stack([W.gdn_state_np(wl, layer, b, h) for h in range(32)])[None]
+                    .astype(sdt), W.gdn_conv_np(wl, layer, b)[None].copy())
+    ref_o = G.decode_step(st, W.gdn_x_np(wl, layer, b)[None], a[b:b + 1], bb[b:b + 1],
+                          p["conv_w"], p["a_log"], p["dt_bias"], [wl.position])
+    return (b, layer, state_err_ratio(s_gpu, st.S[0]),
+            float(out_rel(synth.bf16_bits_to_f32_np(o_bits), ref_o[0]).max()),
+            bool(np.array_equal(ring_gpu, st.conv[0])))
+
+
+def all_gdn_unit_errors(tasks, procs=None):
+    import multiprocessing as mp
+
+    procs = procs or workers()
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(procs, initializer=_init_worker) as pool:
+        return pool.map(gdn_unit_errors, tasks, chunksize=max(1, len(tasks) // (8 * procs)))

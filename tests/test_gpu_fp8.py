@@ -17,8 +17,9 @@ import synth
 from synth import core as C
 from synth import workloads as W
 
-from gpu_util import (DEV, KV, KV_SCALES, assert_attn_close, assert_fp8_keys_close, bf16_dev,
-                      bits_host, decode_gpu_fp8, download_fp8, f32_dev, norm_dev, upload_fp8)
+import oracle_pool
+from gpu_util import (ATTN_TOL, DEV, KV, KV_SCALES, assert_attn_close, assert_fp8_keys_close,
+                      bf16_dev, bits_host, decode_gpu_fp8, download_fp8, f32_dev, norm_dev, upload_fp8)
 
 pytestmark = pytest.mark.gpu
 
@@ -217,7 +218,7 @@ def test_fp8_short_stream_append_commit_decode():
 
 def test_headline_b512_fp8_decode():
     """The full-size FP8 workload in the launch configuration the benchmark times,
-    checked on sampled (sequence, layer) units."""
+    every (sequence, layer) unit checked against the FP8 oracle (worker processes)."""
     wl = W.HEADLINE_B512_FP8
     B, L = wl.batch, wl.layers
     print(f"case: {wl.name} B={B} L={L} splits={R.rma_decode_splits(B)}", flush=True)
@@ -238,26 +239,25 @@ def test_headline_b512_fp8_decode():
     torch.cuda.synchronize()
     outs = [decode_gpu_fp8(states[l], qs[l], qs[l], norms[l]) for l in range(L)]
     torch.cuda.synchronize()
-    print("decode done; checking samples", flush=True)
+    print("decode done; checking every unit", flush=True)
     rng = np.random.default_rng(5128)
-    samples = [(int(b), int(l)) for b, l in zip(rng.integers(0, B, 16), rng.integers(0, L, 16))]
-    samples += [(0, 0), (B - 1, L - 1)]
-    for b, layer in samples:
-        s = {nmk: W.kv_fp8_np(wl, layer, nmk, b) for nmk in W.KV_NAMES}
-        assert np.array_equal(states[layer].bank_k[b].cpu().numpy(), s["bank_k"][0])
-        rows = {nmk: F.dequantize(*s[nmk]) for nmk in W.KV_NAMES}
-        q = W.q_np(wl, layer, b)
-        gl = gains[layer]
-        ow, lw = F.decode_one(list(rows["win_k"]), list(rows["win_v"]), q, gl["gq_win"],
-                              wl.position, wl.eps, wl.rope_base)
-        keys = [np.concatenate([rows["bank_k"][i], rows["pend_k"][i]]) for i in range(4)]
-        vals = [np.concatenate([rows["bank_v"][i], rows["pend_v"][i]]) for i in range(4)]
-        orr, lr = F.decode_one(keys, vals, q, gl["gq_rma"], wl.position, wl.eps, wl.rope_base)
-        o_w, l_w, o_r, l_r = outs[layer]
-        assert_attn_close(bits_host(o_w[b]), l_w[b].cpu().numpy(), ow, lw,
-                          what=f"b={b} layer={layer} win")
-        assert_attn_close(bits_host(o_r[b]), l_r[b].cpu().numpy(), orr, lr,
-                          what=f"b={b} layer={layer} rma")
+    samples = [(int(b), int(l)) for b, l in zip(rng.integers(0, B, 8), rng.integers(0, L, 8))]
+    for b, layer in samples + [(0, 0), (B - 1, L - 1)]:
+        # the device copies were drawn from the same counter streams
+        codes, scales = W.kv_fp8_np(wl, layer, "bank_k", b)
+        assert np.array_equal(states[layer].bank_k[b].cpu().numpy(), codes)
+        assert np.array_equal(states[layer].bank_ks[b].cpu().numpy(), scales)
+    host = [(bits_host(o_w), l_w.cpu().numpy(), bits_host(o_r), l_r.cpu().numpy())
+            for o_w, l_w, o_r, l_r in outs]
+    tasks = [(wl.name, layer, b, host[layer][0][b], host[layer][1][b], host[layer][2][b],
+              host[layer][3][b]) for layer in range(L) for b in range(B)]
+    res = oracle_pool.all_unit_errors(tasks)
+    worst = max(res, key=lambda r: max(r[2], r[4]))
+    print(f"{wl.name}: all {len(res)} units against the FP8 oracle; worst row-relative error "
+          f"{max(worst[2], worst[4]):.3e} (b={worst[0]} layer={worst[1]}), worst lse error "
+          f"{max(max(r[3], r[5]) for r in res):.3e}", flush=True)
+    bad = [r for r in res if not (max(r[2], r[4]) <= ATTN_TOL and max(r[3], r[5]) <= ATTN_TOL)]
+    assert not bad, f"{len(bad)} units out of bound, e.g. {bad[:4]}"
     for o_w, l_w, o_r, l_r in outs:
         assert torch.isfinite(l_w).all() and torch.isfinite(l_r).all()
         assert torch.isfinite(o_w.float()).all() and torch.isfinite(o_r.float()).all()

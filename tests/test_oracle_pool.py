@@ -39,3 +39,28 @@ def test_pool_passes_the_oracles_own_outputs_and_reports_a_planted_error():
     assert (b0, l0, b1, l1) == (0, 0, 63, 7)
     assert max(r1, r2) <= 2.0 ** -8 and max(e1, e2) <= 1e-6
     assert 0.04 <= s1 <= 0.06 and s2 <= 2.0 ** -8 and max(f1, f2) <= 1e-6
+
+
+def test_gdn_pool_passes_the_oracles_own_step_and_reports_a_planted_error():
+    from oracle import gdn_ref as G
+
+    wl = W.GDN_DECODE_B512
+    layer = 1
+    p = W.gdn_params(wl, layer)
+    a, bb = W.gdn_gate_inputs(wl, layer)
+    tasks = []
+    for b in (0, 300):
+        st = G.GdnState(np.stack([W.gdn_state_np(wl, layer, b, h) for h in range(32)])[None],
+                        W.gdn_conv_np(wl, layer, b)[None].copy())
+        o = G.decode_step(st, W.gdn_x_np(wl, layer, b)[None], a[b:b + 1], bb[b:b + 1],
+                          p["conv_w"], p["a_log"], p["dt_bias"], [wl.position])
+        S = st.S[0].copy()
+        ring = st.conv[0].copy()
+        if b == 300:  # one matrix element off by 1% and one ring entry changed
+            S[3, 5, 7] = np.float16(float(S[3, 5, 7]) * 1.01 + 0.01)
+            ring[2, 100] ^= 1
+        tasks.append((wl.name, layer, b, S, O.f64_to_bf16(o[0]), ring))
+    (b0, _, s0, o0, r0), (b1, _, s1, o1, r1) = oracle_pool.all_gdn_unit_errors(tasks, procs=2)
+    assert (b0, b1) == (0, 300)
+    assert s0 == 0.0 and o0 <= 2.0 ** -8 and r0
+    assert s1 > 10.0 and o1 <= 2.0 ** -8 and not r1
