@@ -113,3 +113,32 @@ def all_gdn_unit_errors(tasks, procs=None):
     ctx = mp.get_context("spawn")
     with ctx.Pool(procs, initializer=_init_worker) as pool:
         return pool.map(gdn_unit_errors, tasks, chunksize=max(1, len(tasks) // (8 * procs)))
+
+
+_SCORER = {}
+
+
+def score_unit_errors(task):
+    """task = (workload name, layer, b, GPU scores [256][4] of sequence b's burst) ->
+    (b, largest |s_gpu - s_ref| / max(1, |s_ref|)), the oracle's scorer in float64
+    on the host-regenerated hidden rows."""
+    import oracle as O
+    from synth import workloads as W
+
+    name, layer, b, s_gpu = task
+    wl = W.WORKLOADS[name]
+    w = _SCORER.get((name, layer))
+    if w is None:
+        w = _SCORER[(name, layer)] = W.scorer_weights(wl, layer)
+    ref = O.score(W.burst_hidden_np(wl, layer, b), *w).astype(np.float64)
+    err = np.abs(np.asarray(s_gpu, np.float64) - ref) / np.maximum(1.0, np.abs(ref))
+    return (b, float(err.max()))
+
+
+def all_score_unit_errors(tasks, procs=None):
+    import multiprocessing as mp
+
+    procs = procs or workers()
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(procs, initializer=_init_worker) as pool:
+        return pool.map(score_unit_errors, tasks, chunksize=max(1, len(tasks) // (8 * procs)))

@@ -64,3 +64,14 @@ def test_gdn_pool_passes_the_oracles_own_step_and_reports_a_planted_error():
     assert (b0, b1) == (0, 300)
     assert s0 == 0.0 and o0 <= 2.0 ** -8 and r0
     assert s1 > 10.0 and o1 <= 2.0 ** -8 and not r1
+
+
+def test_scorer_pool_passes_the_oracles_scores_and_reports_a_planted_error():
+    wl = W.COMMIT_BURST_B512
+    w1, w2 = W.scorer_weights(wl, 5)
+    good = O.score(W.burst_hidden_np(wl, 5, 3), w1, w2)
+    bad = good.copy()
+    bad[17, 2] = bad[17, 2] * (1 + 3e-5) + 3e-5
+    res = oracle_pool.all_score_unit_errors([(wl.name, 5, 3, good), (wl.name, 5, 3, bad)], procs=2)
+    assert res[0] == (3, 0.0)
+    assert 2e-5 < res[1][1] < 1e-4
