@@ -430,11 +430,9 @@ def bench_prefill(args):
 
     import swa_memory_anchor_amd as R
     from synth import workloads as W
-    from synth.core import normal_bf16_torch_
 
-    B = 512 if args.workload == "prefill_b512" else 64
-    wl = W.Workload(args.workload, batch=B, layers=8, position=65535, gains="normal")
-    L, C, dev = wl.layers, 256, "cuda"
+    wl = W.WORKLOADS[args.workload]
+    B, L, C, dev = wl.batch, wl.layers, 256, "cuda"
     stream = torch.cuda.current_stream()
     states, saved, norms, ins, outs = [], [], [], [], []
     for layer in range(L):
@@ -453,10 +451,10 @@ def bench_prefill(args):
         rec = []
         for nm in W.RECORD_NAMES:
             t = torch.empty(B, C, 4, 256, dtype=torch.bfloat16, device=dev)
-            normal_bf16_torch_(t, W.key(wl, layer, "prefill", nm))
+            W.prefill_record_torch_(wl, layer, nm, t)
             rec.append(t)
         q = torch.empty(B, C, 16, 256, dtype=torch.bfloat16, device=dev)
-        normal_bf16_torch_(q, W.key(wl, layer, "prefill", "q"))
+        W.prefill_q_torch_(wl, layer, q)
         ins.append((rec, q))
         outs.append((torch.empty(B, C, 16, 256, dtype=torch.bfloat16, device=dev),
                      torch.empty(B, C, 16, device=dev),

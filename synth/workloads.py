@@ -94,9 +94,14 @@ GDN_DECODE_B512 = Workload("gdn_decode_b512", batch=512, layers=24, position=655
 GDN_DECODE_B1 = Workload("gdn_decode_b1", batch=1, layers=24, position=65536, gains="ones",
                          extra={"state": "f32"})
 
+# Chunked prefill: one 256-token chunk per sequence at positions 65536..65791 on a
+# steady-state layer (full window and bank, empty pending block).
+PREFILL_B512 = Workload("prefill_b512", batch=512, layers=8, position=65535, gains="normal")
+PREFILL_B64 = Workload("prefill_b64", batch=64, layers=8, position=65535, gains="normal")
+
 WORKLOADS = {w.name: w for w in (TINY_STREAM, STEADY_B64, HEADLINE_B512, COMMIT_BURST_B512,
                                  LONG_STREAM_B1, HEADLINE_B512_FP8, GDN_DECODE_B512,
-                                 GDN_DECODE_B1)}
+                                 GDN_DECODE_B1, PREFILL_B512, PREFILL_B64)}
 
 
 def key(wl: Workload | str, *names) -> StreamKey:
@@ -340,6 +345,29 @@ def stream_scores_np(wl: Workload, layer: int, block: int) -> np.ndarray:
     """Generator-supplied candidate scores ``[256][4]`` (FP32) of one 256-token block."""
     return normal_f32_np(key(wl, layer, "stream_score", block), (BLOCK, KV_GROUPS), 0.0,
                          SCORE_STD)
+
+
+def prefill_record_np(wl: Workload, layer: int, name: str, b: int, chunk: int) -> np.ndarray:
+    """Raw chunk records ``[chunk][4][256]`` (BF16 bits) of sequence b."""
+    per = chunk * KV_GROUPS * HEAD_DIM
+    return normal_bf16_np(key(wl, layer, "prefill", name), per, start=b * per).reshape(
+        chunk, KV_GROUPS, HEAD_DIM)
+
+
+def prefill_record_torch_(wl: Workload, layer: int, name: str, out) -> None:
+    """All sequences' chunk records ``[B][chunk][4][256]``."""
+    normal_bf16_torch_(out, key(wl, layer, "prefill", name))
+
+
+def prefill_q_np(wl: Workload, layer: int, b: int, chunk: int) -> np.ndarray:
+    """Raw chunk queries ``[chunk][16][256]`` (BF16 bits) of sequence b."""
+    per = chunk * Q_HEADS * HEAD_DIM
+    return normal_bf16_np(key(wl, layer, "prefill", "q"), per, start=b * per).reshape(
+        chunk, Q_HEADS, HEAD_DIM)
+
+
+def prefill_q_torch_(wl: Workload, layer: int, out) -> None:
+    normal_bf16_torch_(out, key(wl, layer, "prefill", "q"))
 
 
 # ------------------------------------------------------------------ GDN decode step

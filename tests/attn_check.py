@@ -1,5 +1,5 @@
-"""Comparison rule for attention outputs (NumPy only, so worker processes can use it
-without torch)."""
+"""Comparison rules for attention outputs and stored keys (NumPy only, so worker
+processes can use them without torch)."""
 
 from __future__ import annotations
 
@@ -21,3 +21,23 @@ def attn_errors(o_gpu_bits, lse_gpu, o_ref, lse_ref):
     with np.errstate(invalid="ignore"):
         lerr = np.where(both_inf, 0.0, np.abs(lg - lr) / np.maximum(1.0, np.abs(lr)))
     return rel, lerr
+
+
+def key_err_ratio(got_bits, ref_bits):
+    """Largest |got - ref| / bound of stored keys (normalised, rotated, rounded to BF16).
+
+    The GPU computes them in FP32 and the oracle in float64; both round once to
+    BF16.  An FP32 result differs from the exact one by a few units of 2^-24 of
+    the row's scale, which can move it across one BF16 rounding boundary: the
+    bound is one BF16 ulp of the reference element plus 2^-20 of the row's
+    largest magnitude (the FP32 error with margin, for components that nearly
+    cancel in the rotation).
+    """
+    g = O.bf16_to_f64(got_bits)
+    r = O.bf16_to_f64(ref_bits)
+    _, e = np.frexp(r)
+    ulp = np.where(r != 0, np.ldexp(1.0, e - 8), 0.0)
+    row = np.abs(r).max(axis=-1, keepdims=True)
+    err = np.abs(g - r)
+    bound = ulp + 2.0**-20 * row
+    return float((err / np.maximum(bound, 1e-300)).max()) if err.size else 0.0

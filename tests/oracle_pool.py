@@ -142,3 +142,54 @@ def all_score_unit_errors(tasks, procs=None):
     ctx = mp.get_context("spawn")
     with ctx.Pool(procs, initializer=_init_worker) as pool:
         return pool.map(score_unit_errors, tasks, chunksize=max(1, len(tasks) // (8 * procs)))
+
+
+def prefill_unit_errors(task):
+    """task = (workload name, layer, b, chunk, GPU results of sequence b: o_win bits
+    [C][16][256], lse_win [C][16], o_rma bits, lse_rma, pending K and V rows [4][C][256]
+    bits, window K and V rows at the chunk's ring slots [4][C][256] bits, n_pend, pos).
+
+    The oracle runs the chunk as C successive (append, decode) steps on the sequence's
+    steady-state layer (regenerated from the seeds: full window and bank, empty
+    pending block) -> (b, layer, worst output error, worst LSE error, worst key error
+    / bound, values and counters exact)."""
+    import oracle as O
+    from attn_check import attn_errors, key_err_ratio
+    from synth import workloads as W
+
+    name, layer, b, C, ow_b, lw, or_b, lr, pk, pv, wk, wv, n_pend, pos = task
+    wl = W.WORKLOADS[name]
+    g = _GAINS.get((name, layer))
+    if g is None:
+        g = _GAINS[(name, layer)] = W.gains(wl, layer)
+    s = W.decode_state_np(wl, layer, b)
+    one = O.new_layer_state(1)
+    for nm in W.KV_NAMES:
+        getattr(one, nm)[0] = s[nm]
+    one.n_bank[0], one.n_pend[0], one.pos[0] = O.BANK, 0, wl.position
+    recs = [W.prefill_record_np(wl, layer, nm, b, C) for nm in W.RECORD_NAMES]
+    q = W.prefill_q_np(wl, layer, b, C)
+    ref = [[], [], [], []]
+    for i in range(C):
+        O.append(one, *[r[i][None] for r in recs], g["gk_win"], g["gk_rma"], wl.eps,
+                 wl.rope_base)
+        d = O.decode(one, q[i][None], q[i][None], g["gq_win"], g["gq_rma"], wl.eps, wl.rope_base)
+        for j in range(4):
+            ref[j].append(d[j][0])
+    r1, e1 = attn_errors(ow_b, lw, np.stack(ref[0]), np.stack(ref[1]))
+    r2, e2 = attn_errors(or_b, lr, np.stack(ref[2]), np.stack(ref[3]))
+    slots = (wl.position + 1 + np.arange(C)) % O.WINDOW
+    kerr = max(key_err_ratio(pk, one.pend_k[0][:, :C]), key_err_ratio(wk, one.win_k[0][:, slots]))
+    exact = (np.array_equal(pv, one.pend_v[0][:, :C]) and
+             np.array_equal(wv, one.win_v[0][:, slots]) and
+             int(n_pend) == int(one.n_pend[0]) and int(pos) == int(one.pos[0]))
+    return (b, layer, float(max(r1.max(), r2.max())), float(max(e1.max(), e2.max())), kerr, exact)
+
+
+def all_prefill_unit_errors(tasks, procs=None):
+    import multiprocessing as mp
+
+    procs = procs or workers()
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(procs, initializer=_init_worker) as pool:
+        return pool.map(prefill_unit_errors, tasks, chunksize=1)

@@ -141,3 +141,61 @@ def test_prefill_then_decode_continues_the_stream():
     d = O.decode(ref, q[:, C], q[:, C], g["gq_win"], g["gq_rma"], 1e-6, 1e7)
     assert_attn_close(bits_host(o[0]), o[1].cpu().numpy(), d[0], d[1], what="next win")
     assert_attn_close(bits_host(o[2]), o[3].cpu().numpy(), d[2], d[3], what="next rma")
+
+
+def test_prefill_b512_full_size_sampled_sequences():
+    """The full-size prefill_b512 call (512 sequences x 256 tokens, steady-state layer)
+    in the benchmark's launch configuration: sampled sequences replayed token by token
+    by the oracle in worker processes (all 256 output rows of both branches, the
+    chunk's stored keys and values, the counters); every output row finite."""
+    import oracle_pool
+
+    wl = W.PREFILL_B512
+    B, C = wl.batch, 256
+    out = {}
+    for layer in (0, 5):
+        print(f"case: {wl.name} layer={layer} B={B} C={C}", flush=True)
+        st = R.alloc_layer_state(B, DEV, zero_kv=False)
+        for nm in W.KV_NAMES:
+            W.kv_torch_(wl, layer, nm, getattr(st, nm))
+        meta = W.decode_meta(wl, layer)
+        meta["n_pend"][:] = 0
+        for k, v in meta.items():
+            getattr(st, k).copy_(torch.from_numpy(v).to(DEV))
+        nm_ = norm_dev(W.gains(wl, layer), wl.eps, wl.rope_base)
+        recs = []
+        for nm in W.RECORD_NAMES:
+            t = torch.empty(B, C, 4, 256, dtype=torch.bfloat16, device=DEV)
+            W.prefill_record_torch_(wl, layer, nm, t)
+            recs.append(t)
+        q = torch.empty(B, C, 16, 256, dtype=torch.bfloat16, device=DEV)
+        W.prefill_q_torch_(wl, layer, q)
+        o_w = torch.empty(B, C, 16, 256, dtype=torch.bfloat16, device=DEV)
+        o_r = torch.empty_like(o_w)
+        l_w = torch.empty(B, C, 16, device=DEV)
+        l_r = torch.empty_like(l_w)
+        R.swa_rma_prefill(st, B, C, *recs, None, q, q, nm_, o_w, l_w, o_r, l_r,
+                          R.prefill_workspace(B, C))
+        torch.cuda.synchronize()
+        for x in (o_w, o_r, l_w, l_r):
+            assert torch.isfinite(x.float()).all()
+        rng = np.random.default_rng(256 + layer)
+        picks = sorted(set(int(x) for x in rng.integers(0, B, 12)) | {0, B - 1})
+        slots = torch.from_numpy((wl.position + 1 + np.arange(C)) % O.WINDOW).to(DEV)
+        for b in picks:
+            out[(layer, b)] = (bits_host(o_w[b]), l_w[b].cpu().numpy(), bits_host(o_r[b]),
+                               l_r[b].cpu().numpy(), bits_host(st.pend_k[b, :, :C]),
+                               bits_host(st.pend_v[b, :, :C]),
+                               bits_host(st.win_k[b].index_select(1, slots)),
+                               bits_host(st.win_v[b].index_select(1, slots)),
+                               int(st.n_pend[b]), int(st.pos[b]))
+        del st, recs, q, o_w, o_r, l_w, l_r
+    tasks = [(wl.name, layer, b, C, *v) for (layer, b), v in out.items()]
+    print(f"checking {len(tasks)} sequences x {C} tokens against the oracle", flush=True)
+    res = oracle_pool.all_prefill_unit_errors(tasks)
+    for b, layer, o_err, l_err, k_err, exact in res:
+        print(f"layer {layer} b={b}: out {o_err:.3e} lse {l_err:.3e} keys {k_err:.3f} "
+              f"exact={exact}")
+    assert all(r[5] for r in res), "stored values or counters differ"
+    assert max(r[2] for r in res) <= 2e-2 and max(r[3] for r in res) <= 2e-2
+    assert max(r[4] for r in res) <= 1.0

@@ -75,3 +75,38 @@ def test_scorer_pool_passes_the_oracles_scores_and_reports_a_planted_error():
     res = oracle_pool.all_score_unit_errors([(wl.name, 5, 3, good), (wl.name, 5, 3, bad)], procs=2)
     assert res[0] == (3, 0.0)
     assert 2e-5 < res[1][1] < 1e-4
+
+
+def test_prefill_pool_replays_the_chunk_and_reports_a_planted_error():
+    """A 3-token chunk on a prefill_b512 sequence: the oracle's own results pass; a
+    changed pending value is reported."""
+    wl = W.PREFILL_B512
+    layer, b, C = 0, 7, 3
+    s = W.decode_state_np(wl, layer, b)
+    g = W.gains(wl, layer)
+    one = O.new_layer_state(1)
+    for nm in W.KV_NAMES:
+        getattr(one, nm)[0] = s[nm]
+    one.n_bank[0], one.n_pend[0], one.pos[0] = O.BANK, 0, wl.position
+    recs = [W.prefill_record_np(wl, layer, nm, b, C) for nm in W.RECORD_NAMES]
+    q = W.prefill_q_np(wl, layer, b, C)
+    outs = [[], [], [], []]
+    for i in range(C):
+        O.append(one, *[r[i][None] for r in recs], g["gk_win"], g["gk_rma"], wl.eps, wl.rope_base)
+        d = O.decode(one, q[i][None], q[i][None], g["gq_win"], g["gq_rma"], wl.eps, wl.rope_base)
+        for j in range(4):
+            outs[j].append(d[j][0])
+    slots = (wl.position + 1 + np.arange(C)) % O.WINDOW
+    res_args = [O.f64_to_bf16(np.stack(outs[0])), np.stack(outs[1]).astype(np.float32),
+                O.f64_to_bf16(np.stack(outs[2])), np.stack(outs[3]).astype(np.float32),
+                one.pend_k[0][:, :C].copy(), one.pend_v[0][:, :C].copy(),
+                one.win_k[0][:, slots].copy(), one.win_v[0][:, slots].copy(), C,
+                wl.position + C]
+    bad = list(res_args)
+    bad[5] = bad[5].copy()
+    bad[5][1, 2, 3] ^= 0x40
+    res = oracle_pool.all_prefill_unit_errors(
+        [(wl.name, layer, b, C, *res_args), (wl.name, layer, b, C, *bad)], procs=2)
+    (_, _, o0, l0, k0, x0), (_, _, o1, l1, k1, x1) = res
+    assert o0 <= 2.0 ** -8 and l0 <= 1e-6 and k0 == 0.0 and x0
+    assert o1 <= 2.0 ** -8 and not x1

@@ -97,3 +97,19 @@ def test_fp8_workload_slices_consistent():
     W.kv_fp8_torch_(wl, 1, "pend_v", codes, scales)
     c, s = W.kv_fp8_np(wl, 1, "pend_v", 2)
     assert np.array_equal(codes[2].numpy(), c) and np.array_equal(scales[2].numpy(), s)
+
+
+def test_prefill_chunk_slices_equal_the_device_fill():
+    """A sequence's chunk records and queries drawn on the host are the same bits as
+    that sequence's slice of the all-sequence fill (torch, here on the CPU)."""
+    wl = W.Workload("prefill_b512", batch=3, layers=8, position=65535, gains="normal")
+    C = 5
+    rec = torch.empty(3, C, 4, 256, dtype=torch.bfloat16)
+    W.prefill_record_torch_(wl, 2, "v_rma", rec)
+    q = torch.empty(3, C, 16, 256, dtype=torch.bfloat16)
+    W.prefill_q_torch_(wl, 2, q)
+    for b in range(3):
+        assert np.array_equal(rec[b].view(torch.int16).numpy().view(np.uint16),
+                              W.prefill_record_np(wl, 2, "v_rma", b, C))
+        assert np.array_equal(q[b].view(torch.int16).numpy().view(np.uint16),
+                              W.prefill_q_np(wl, 2, b, C))
