@@ -13,9 +13,11 @@
 // source position in the low word), so "better" is "larger key" and the order is
 // total whenever sources are distinct within a group.
 //
-// One workgroup (1024 threads) per sequence; 256 threads per KV group:
-//   1. build 1280 keys (2048 with zero padding, below every real key) in LDS;
-//   2. bitonic sort, descending; the 1024th key is the admission threshold;
+// One workgroup (256 threads) per (sequence, KV group), so that a CU holds several
+// and one's sort overlaps another's copies:
+//   1. build the 1280 candidate keys, five per thread, in registers;
+//   2. the admission threshold is the min(1024, n_bank + n_pend)-th largest key,
+//      found by radix selection (byte by byte from the top, LDS histograms);
 //   3. a bank record survives in place; free slots (evicted slots, then slots
 //      >= n_bank) are listed in ascending order by a prefix sum; admitted
 //      pending rows, in ascending row order, take the free slots in order;
@@ -23,15 +25,14 @@
 //      E4M3 codes in the FP8 variant) are copied in 16-byte pieces (8 in flight
 //      per thread), plus their score, source and, in the FP8 variant, the two
 //      row scales;
-//   5. n_bank = min(1024, n_bank + n_pend), n_pend = 0.
+//   5. a second launch sets n_bank = min(1024, n_bank + n_pend), n_pend = 0, once
+//      every group's workgroup has read them.
 #include "rma_device.h"
 
 namespace rma {
 
 constexpr int kCand = kBank + kBlock;  // 1280
-constexpr int kSortN = 2048;
-constexpr int kGroupThreads = 256;
-constexpr int kCommitThreads = kGroupThreads * kGroups;
+constexpr int kCommitThreads = 256;
 constexpr int kCopyBatch = 8;  // 16-byte copies in flight per thread
 
 // K/V rows are BF16 (512 bytes) or, in the FP8 variant, E4M3 codes (256 bytes)
@@ -62,24 +63,24 @@ __device__ __forceinline__ uint64_t cand_key(float score, int32_t src) {
   return (static_cast<uint64_t>(score_order(score)) << 32) | static_cast<uint32_t>(~src);
 }
 
-// Exclusive prefix sum over the 256 threads of one group; every thread of the
-// workgroup must call it (it contains workgroup barriers).
-__device__ __forceinline__ int group_exclusive_scan(int v, int (*wave_tot)[4], int g, int gw,
-                                                    int lane, int &total) {
+// Exclusive prefix sum over the workgroup's 256 threads; every thread must call it
+// (it contains workgroup barriers).
+__device__ __forceinline__ int exclusive_scan(int v, int *wave_tot, int wave, int lane,
+                                              int &total) {
   int x = v;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const int y = __shfl_up(x, off, 64);
     if (lane >= off) x += y;
   }
-  if (lane == 63) wave_tot[g][gw] = x;
+  if (lane == 63) wave_tot[wave] = x;
   __syncthreads();
   int base = 0;
   total = 0;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    const int c = wave_tot[g][w];
-    base += w < gw ? c : 0;
+    const int c = wave_tot[w];
+    base += w < wave ? c : 0;
     total += c;
   }
   __syncthreads();
@@ -90,69 +91,94 @@ template <bool kFp8>
 __global__ __launch_bounds__(kCommitThreads) void commit_kernel(CommitParams a) {
   constexpr int kRowBytes = kFp8 ? kDim : 2 * kDim;
   constexpr int kPieces = kRowBytes / 16;  // 16-byte pieces per row
-  __shared__ uint64_t keys[kGroups][kSortN];
-  __shared__ uint8_t keep[kGroups][kCand];
-  __shared__ int16_t free_list[kGroups][kBank];
-  __shared__ int16_t kidx[kGroups][kBank];
-  __shared__ int16_t adm_slot[kGroups][kBlock];
-  __shared__ int16_t adm_rows[kGroups][kBlock];
-  __shared__ int wave_tot[kGroups][4];
+  __shared__ uint32_t hist[256];
+  __shared__ uint64_t sel_key;
+  __shared__ int sel_digit, sel_rank, sel_count;
+  __shared__ uint8_t keep[kCand];
+  __shared__ int16_t free_list[kBank];
+  __shared__ int16_t kidx[kBank];
+  __shared__ int16_t adm_slot[kBlock];
+  __shared__ int16_t adm_rows[kBlock];
+  __shared__ int wave_tot[4];
 
-  const int b = blockIdx.x;
-  const int g = threadIdx.x / kGroupThreads;
-  const int t = threadIdx.x % kGroupThreads;
-  const int gw = t >> 6;
-  const int lane = threadIdx.x & 63;
+  const int b = blockIdx.x / kGroups;
+  const int g = blockIdx.x % kGroups;
+  const int t = threadIdx.x;
+  const int wave = t >> 6;
+  const int lane = t & 63;
   const int nb = min(max(a.n_bank[b], 0), kBank);
   const int np = min(max(a.n_pend[b], 0), kBlock);
   const int kk = min(kBank, nb + np);
   const size_t sg = static_cast<size_t>(b) * kGroups + g;
 
-  // 1. keys
-  uint64_t mine[5];
+  // 1. keys: thread t holds candidates t + 256 r (r < 5; 1280 = 5 x 256)
+  uint64_t mine[kCand / kCommitThreads];
 #pragma unroll
-  for (int r = 0; r < kSortN / kGroupThreads; ++r) {
-    const int i = t + kGroupThreads * r;
+  for (int r = 0; r < kCand / kCommitThreads; ++r) {
+    const int i = t + kCommitThreads * r;
     uint64_t k = 0;
     if (i < kBank) {
       if (i < nb) k = cand_key(a.bank_score[sg * kBank + i], a.bank_src[sg * kBank + i]);
-    } else if (i < kCand) {
+    } else {
       const int tt = i - kBank;
       if (tt < np)
         k = cand_key(a.pend_score[(static_cast<size_t>(b) * kBlock + tt) * kGroups + g],
                      a.pend_src[static_cast<size_t>(b) * kBlock + tt]);
     }
-    keys[g][i] = k;
-    if (r < 5) mine[r] = k;
+    mine[r] = k;
   }
 
-  // 2. bitonic sort, descending
-  for (int k2 = 2; k2 <= kSortN; k2 <<= 1) {
-    for (int j = k2 >> 1; j > 0; j >>= 1) {
+  // 2. threshold: the kk-th largest key (counting equal keys), by radix selection
+  // from the most significant byte down.  Each pass counts, per byte value, the keys
+  // that match the bytes chosen so far, picks the byte under which the kk-th largest
+  // falls, and carries the rank left inside it; once that byte holds a single key,
+  // that key is the threshold.  Absent candidates are 0, below every real key.
+  uint64_t thr = 0;
+  if (kk > 0) {
+    uint64_t prefix = 0, pmask = 0;
+    int rank = kk;
+    for (int shift = 56; shift >= 0; shift -= 8) {
+      hist[t] = 0;
       __syncthreads();
 #pragma unroll
-      for (int q = 0; q < kSortN / 2 / kGroupThreads; ++q) {
-        const int idx = t + kGroupThreads * q;
-        const int i = 2 * j * (idx / j) + (idx % j);
-        const int ixj = i + j;
-        const uint64_t x = keys[g][i], y = keys[g][ixj];
-        const bool desc = (i & k2) == 0;
-        if (desc ? (x < y) : (x > y)) {
-          keys[g][i] = y;
-          keys[g][ixj] = x;
+      for (int r = 0; r < kCand / kCommitThreads; ++r)
+        if ((mine[r] & pmask) == prefix)
+          atomicAdd(&hist[static_cast<int>(mine[r] >> shift) & 255], 1u);
+      __syncthreads();
+      // thread t takes byte value 255 - t: the exclusive sum counts the larger ones
+      const int c = static_cast<int>(hist[255 - t]);
+      int total;
+      const int above = exclusive_scan(c, wave_tot, wave, lane, total);
+      if (above < rank && above + c >= rank) {
+        sel_digit = 255 - t;
+        sel_rank = rank - above;
+        sel_count = c;
+      }
+      __syncthreads();
+      prefix |= static_cast<uint64_t>(sel_digit) << shift;
+      pmask |= static_cast<uint64_t>(255) << shift;
+      rank = sel_rank;
+      if (sel_count == 1 || shift == 0) {
+        if (sel_count == 1) {
+#pragma unroll
+          for (int r = 0; r < kCand / kCommitThreads; ++r)
+            if ((mine[r] & pmask) == prefix) sel_key = mine[r];
+          __syncthreads();
+          thr = sel_key;
+        } else {
+          thr = prefix;
         }
+        break;
       }
     }
   }
-  __syncthreads();
-  const uint64_t thr = kk > 0 ? keys[g][kk - 1] : 0;
 
   // 3a. keep flags
 #pragma unroll
-  for (int r = 0; r < 5; ++r) {
-    const int i = t + kGroupThreads * r;
+  for (int r = 0; r < kCand / kCommitThreads; ++r) {
+    const int i = t + kCommitThreads * r;
     const bool valid = i < kBank ? (i < nb) : (i - kBank < np);
-    keep[g][i] = (kk > 0 && valid && mine[r] >= thr) ? 1 : 0;
+    keep[i] = (kk > 0 && valid && mine[r] >= thr) ? 1 : 0;
   }
   __syncthreads();
 
@@ -161,49 +187,49 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kernel(CommitParams a) 
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int s = 4 * t + e;
-    const bool survive = s < nb && keep[g][s];
+    const bool survive = s < nb && keep[s];
     fl[e] = survive ? 0 : 1;
     cnt += fl[e];
-    kidx[g][s] = survive ? static_cast<int16_t>(s) : static_cast<int16_t>(-1);
+    kidx[s] = survive ? static_cast<int16_t>(s) : static_cast<int16_t>(-1);
   }
   int n_free;
-  int r0 = group_exclusive_scan(cnt, wave_tot, g, gw, lane, n_free);
+  int r0 = exclusive_scan(cnt, wave_tot, wave, lane, n_free);
 #pragma unroll
   for (int e = 0; e < 4; ++e)
-    if (fl[e]) free_list[g][r0++] = static_cast<int16_t>(4 * t + e);
+    if (fl[e]) free_list[r0++] = static_cast<int16_t>(4 * t + e);
 
   // 3c. admitted pending rows, ascending (thread t owns row t)
-  const int adm = (t < np && keep[g][kBank + t]) ? 1 : 0;
+  const int adm = (t < np && keep[kBank + t]) ? 1 : 0;
   int n_adm;
-  const int arank = group_exclusive_scan(adm, wave_tot, g, gw, lane, n_adm);
+  const int arank = exclusive_scan(adm, wave_tot, wave, lane, n_adm);
   n_adm = min(n_adm, n_free);
   // (the scan's barriers order the free_list writes above before these reads)
   int16_t slot = -1;
   if (adm && arank < n_free) {
-    slot = free_list[g][arank];
-    adm_rows[g][arank] = static_cast<int16_t>(t);
+    slot = free_list[arank];
+    adm_rows[arank] = static_cast<int16_t>(t);
   }
-  adm_slot[g][t] = slot;
+  adm_slot[t] = slot;
   __syncthreads();
-  if (slot >= 0) kidx[g][slot] = static_cast<int16_t>(kBank + t);
+  if (slot >= 0) kidx[slot] = static_cast<int16_t>(kBank + t);
   __syncthreads();
 
   // 4. outputs and copies
   if (a.keep_idx) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) a.keep_idx[sg * kBank + 4 * t + e] = kidx[g][4 * t + e];
+    for (int e = 0; e < 4; ++e) a.keep_idx[sg * kBank + 4 * t + e] = kidx[4 * t + e];
   }
   // 16-byte pieces: 2 * kPieces per admitted row (K then V).  Each thread issues
-  // kCopyBatch loads before its stores, so a group waits for a handful of round
-  // trips to memory instead of one per piece.
+  // kCopyBatch loads before its stores, so the workgroup waits for a handful of
+  // round trips to memory instead of one per piece.
   const int pieces = n_adm * 2 * kPieces;
-  for (int w0 = 0; w0 < pieces; w0 += kGroupThreads * kCopyBatch) {
+  for (int w0 = 0; w0 < pieces; w0 += kCommitThreads * kCopyBatch) {
     u32x4 buf[kCopyBatch];
 #pragma unroll
     for (int u = 0; u < kCopyBatch; ++u) {
       // past the end, repeat the last piece: the same bytes go to the same place
-      const int w = min(w0 + t + u * kGroupThreads, pieces - 1);
-      const int row = adm_rows[g][w / (2 * kPieces)];
+      const int w = min(w0 + t + u * kCommitThreads, pieces - 1);
+      const int row = adm_rows[w / (2 * kPieces)];
       const int part = w % (2 * kPieces);
       const uint8_t *src = (part >= kPieces ? a.pend_v : a.pend_k) +
                            (sg * kBlock + row) * kRowBytes + (part % kPieces) * 16;
@@ -211,18 +237,18 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kernel(CommitParams a) 
     }
 #pragma unroll
     for (int u = 0; u < kCopyBatch; ++u) {
-      const int w = min(w0 + t + u * kGroupThreads, pieces - 1);
-      const int row = adm_rows[g][w / (2 * kPieces)];
+      const int w = min(w0 + t + u * kCommitThreads, pieces - 1);
+      const int row = adm_rows[w / (2 * kPieces)];
       const int part = w % (2 * kPieces);
-      const int sl = adm_slot[g][row];
+      const int sl = adm_slot[row];
       uint8_t *dst = (part >= kPieces ? a.bank_v : a.bank_k) + (sg * kBank + sl) * kRowBytes +
                      (part % kPieces) * 16;
       *reinterpret_cast<u32x4 *>(dst) = buf[u];
     }
   }
   if (t < n_adm) {
-    const int row = adm_rows[g][t];
-    const int s = adm_slot[g][row];
+    const int row = adm_rows[t];
+    const int s = adm_slot[row];
     a.bank_score[sg * kBank + s] = a.pend_score[(static_cast<size_t>(b) * kBlock + row) * kGroups + g];
     a.bank_src[sg * kBank + s] = a.pend_src[static_cast<size_t>(b) * kBlock + row];
     if constexpr (kFp8) {
@@ -230,13 +256,17 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kernel(CommitParams a) 
       a.bank_vs[sg * kBank + s] = a.pend_vs[sg * kBlock + row];
     }
   }
+}
 
-  // 5. counters, after every group has read them
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    a.n_bank[b] = kk;
-    a.n_pend[b] = 0;
-  }
+// 5. counters, after every group's workgroup has read them (a launch of its own).
+__global__ __launch_bounds__(256) void commit_counters_kernel(int32_t *n_bank, int32_t *n_pend,
+                                                              int batch) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= batch) return;
+  const int nb = min(max(n_bank[b], 0), kBank);
+  const int np = min(max(n_pend[b], 0), kBlock);
+  n_bank[b] = min(kBank, nb + np);
+  n_pend[b] = 0;
 }
 
 }  // namespace rma
@@ -255,8 +285,11 @@ static rma_status launch_commit(const CommitParams &p, int32_t batch, void *stre
   const void *al[] = {p.bank_k, p.bank_v, p.pend_k, p.pend_v};
   for (const void *ptr : al)
     if (!aligned16(ptr)) return RMA_E_ALIGN;
-  hipLaunchKernelGGL(commit_kernel<kFp8>, dim3(batch), dim3(kCommitThreads), 0,
-                     static_cast<hipStream_t>(stream), p);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(commit_kernel<kFp8>, dim3(batch * kGroups), dim3(kCommitThreads), 0, s, p);
+  if (hipPeekAtLastError() != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
+  hipLaunchKernelGGL(commit_counters_kernel, dim3((batch + 255) / 256), dim3(256), 0, s, p.n_bank,
+                     p.n_pend, batch);
   if (hipPeekAtLastError() != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
   return RMA_OK;
 }
