@@ -68,7 +68,7 @@ typedef enum {
   RMA_OK = 0,
   RMA_E_ARG = 1,       /* null pointer, batch out of range, bad stride */
   RMA_E_ALIGN = 2,     /* a row pointer or stride breaks 16-byte alignment */
-  RMA_E_WORKSPACE = 3, /* workspace smaller than rma_decode_workspace_bytes() */
+  RMA_E_WORKSPACE = 3, /* workspace missing or smaller than the entry point needs */
   RMA_E_HIP = 4        /* the HIP runtime reported an error at launch */
 } rma_status;
 
