@@ -868,7 +868,7 @@ def main() -> int:
     traffic = measured_traffic(wl.name, B)
 
     res = {
-        "metric": METRIC,
+        "metric": METRIC if B == 512 else METRIC.replace("at batch 512", f"at batch {B}"),
         "value": round(value, 1),
         "unit": "seq-steps/s",
         "n_gpus": 1,
