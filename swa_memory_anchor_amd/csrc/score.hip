@@ -47,9 +47,9 @@ struct ScoreParams {
 //
 // Tile shapes: the 4 waves are arranged WR x (4/WR); each wave owns RB row blocks
 // and CB column blocks of 32 x 32.  Large calls use 128-row tiles (WR=2, RB=2,
-// CB=4); calls with fewer row tiles than CUs use 32-row tiles (WR=1, RB=1, CB=2)
-// to spread over 4x more workgroups.  Both run the same instruction sequence per
-// output element, so results do not depend on the tile shape.
+// CB=4); calls with fewer such tiles than CUs use 64-row tiles (WR=2, RB=1, CB=4)
+// or, fewer still, 32-row tiles (WR=1, RB=1, CB=2).  All run the same instruction
+// sequence per output element, so results do not depend on the tile shape.
 template <int WR, int RB, int CB>
 __global__ __launch_bounds__(kScoreThreads, 1) void score_kernel(ScoreParams a) {
   constexpr int WC = 4 / WR;
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score_kernel(ScoreParams a) 
   constexpr int kAFloats = kRows * kStr;
   constexpr int kSF = kAFloats + kMid * kStr;
   constexpr int kTpr = kScoreThreads / kRows;  // staging threads per hidden row
-  constexpr int kKpt = kKt / kTpr;             // k values each of them stages (16 or 4)
+  constexpr int kKpt = kKt / kTpr;             // k values each of them stages (16, 8 or 4)
   __shared__ __align__(16) float smem[2 * kStageFloats];
   __shared__ float w2s[kMid * kGroups];
 
@@ -89,6 +89,10 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score_kernel(ScoreParams a) 
       }
       ha[0] = u0.x; ha[1] = u0.y; ha[2] = u0.z; ha[3] = u0.w;
       ha[4] = u1.x; ha[5] = u1.y; ha[6] = u1.z; ha[7] = u1.w;
+    } else if constexpr (kKpt == 8) {
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (arow_ok) u = *reinterpret_cast<const uint4 *>(arow + kt * kKt);
+      ha[0] = u.x; ha[1] = u.y; ha[2] = u.z; ha[3] = u.w;
     } else {
       static_assert(kKpt == 4, "staging chunk");
       uint2 u = make_uint2(0, 0);
@@ -220,12 +224,16 @@ extern "C" rma_status rma_score(const uint16_t *hidden, int64_t n_rows, int64_t 
     return RMA_E_ALIGN;
   ScoreParams p{hidden, n_rows, ld_hidden, w1, w2, scores, ld_scores};
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // 128-row tiles while they give at least one workgroup per CU (256 CUs); below
-  // that, 32-row tiles spread the same work over four times as many CUs.
+  // The largest row tile that still gives every CU (256) a workgroup: 128 rows,
+  // then 64, then 32 (a larger tile reads W1 fewer times per row).
   const int64_t big = (n_rows + 127) / 128;
+  const int64_t mid = (n_rows + 63) / 64;
   if (big >= 256) {
     if (big > 0x7fffffff) return RMA_E_ARG;
     hipLaunchKernelGGL((score_kernel<2, 2, 4>), dim3(static_cast<unsigned>(big)),
+                       dim3(kScoreThreads), 0, s, p);
+  } else if (mid >= 256) {
+    hipLaunchKernelGGL((score_kernel<2, 1, 4>), dim3(static_cast<unsigned>(mid)),
                        dim3(kScoreThreads), 0, s, p);
   } else {
     const int64_t small = (n_rows + 31) / 32;

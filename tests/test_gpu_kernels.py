@@ -272,9 +272,11 @@ def test_score_large_ragged_uses_big_tiles_and_matches_small_tiles():
     assert np.all(np.isfinite(o))
     rows = np.array([0, 1, 127, 128, 16383, 32767, 32768, 32895, 32999])
     assert_scores_close(o[rows], O.score(h[rows], w1, w2), what="large ragged")
-    # the same rows through the small-tile kernel (a 300-row call) give the same bits
-    sub = np.concatenate([rows, np.arange(291) + 100])
-    out2 = torch.empty(len(sub), 4, device=DEV)
-    R.rma_score(bf16_dev(h[sub]), len(sub), 2560, w1d, w2d, out2, 4)
-    torch.cuda.synchronize()
-    assert np.array_equal(out2.cpu().numpy(), o[sub])
+    # the same rows through the small-tile kernel (a 300-row call, 32-row tiles) and the
+    # mid-size one (a 17,000-row call, 64-row tiles) give the same bits
+    for extra in (291, 16991):
+        sub = np.concatenate([rows, np.arange(extra) + 100])
+        out2 = torch.empty(len(sub), 4, device=DEV)
+        R.rma_score(bf16_dev(h[sub]), len(sub), 2560, w1d, w2d, out2, 4)
+        torch.cuda.synchronize()
+        assert np.array_equal(out2.cpu().numpy(), o[sub]), len(sub)
