@@ -250,7 +250,8 @@ def bench_commit_burst(args):
 
 def bench_long_stream(args):
     """Batch-1 stream: per token, one step (append + attention + split merge) in all 8
-    layers; every 256 tokens the scorer and the commit in all 8 layers.
+    layers; every 256 tokens the scorer and the commit of all 8 layers (one launch
+    each for all layers).
 
     The first quarter of the stream runs eagerly (warm-up), the second quarter is timed
     eagerly (one fused-step call per layer), the second half is timed as replays of a
@@ -306,10 +307,10 @@ def bench_long_stream(args):
     wsp, wsn = ws.data_ptr(), ws.numel()
 
     def commit_block(t):
-        for l in range(L):
-            R.rma_score(hid[l, t - 255:t + 1], 256, 2560, w[l][0], w[l][1],
-                        states[l].pend_score, 4, stream)
-            R.rma_commit_topk(states[l], 1, None, stream)
+        # every layer's scores in one launch, then every layer's commit in one
+        R.rma_score_multi([(hid[l, t - 255:t + 1], w[l][0], w[l][1], states[l].pend_score)
+                           for l in range(L)], 256, 2560, 4, stream)
+        R.rma_commit_topk_multi(states, 1, None, stream)
 
     def token(t):
         for l in range(L):

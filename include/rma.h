@@ -63,6 +63,7 @@ extern "C" {
 #define RMA_HIDDEN 2560
 #define RMA_SCORER_MID 256
 #define RMA_MAX_BATCH 65536
+#define RMA_MAX_JOBS 16 /* calls one *_multi entry point takes at most */
 
 typedef enum {
   RMA_OK = 0,
@@ -194,6 +195,23 @@ rma_status swa_rma_step(const rma_layer_state *st, int32_t batch, const uint16_t
 rma_status rma_score(const uint16_t *hidden, int64_t n_rows, int64_t ld_hidden, const float *w1,
                      const float *w2, float *scores, int64_t ld_scores, void *stream);
 
+/* One call of rma_score inside rma_score_multi (device pointers, as in rma_score). */
+typedef struct rma_score_job {
+  const uint16_t *hidden;
+  const float *w1, *w2;
+  float *scores;
+} rma_score_job;
+
+/*
+ * rma_score_multi - n_jobs (1..RMA_MAX_JOBS) independent rma_score calls with the
+ * same n_rows, ld_hidden and ld_scores in one launch, e.g. every layer's scores
+ * of a block.  `jobs` is a host array; each job's results are those of rma_score
+ * with its pointers, bit for bit.  Any job failing the checks of rma_score fails
+ * the call and nothing is launched.
+ */
+rma_status rma_score_multi(const rma_score_job *jobs, int32_t n_jobs, int64_t n_rows,
+                           int64_t ld_hidden, int64_t ld_scores, void *stream);
+
 /*
  * rma_commit_topk - commit every sequence's pending block ([QB] section above:
  * each KV group keeps the best 1024 of bank + pending; [FB] section "架构…":
@@ -208,6 +226,16 @@ rma_status rma_score(const uint16_t *hidden, int64_t n_rows, int64_t ld_hidden, 
  */
 rma_status rma_commit_topk(const rma_layer_state *st, int32_t batch, int32_t *keep_idx,
                            void *stream);
+
+/*
+ * rma_commit_topk_multi - rma_commit_topk on n_states (1..RMA_MAX_JOBS) layer
+ * states of the same batch in one launch (plus one launch for the counters), e.g.
+ * every layer at a block's end.  `states` is a host array; keep_idx is NULL or a
+ * host array of n_states device pointers (each may be NULL).  Each state ends as
+ * rma_commit_topk would leave it, bit for bit.
+ */
+rma_status rma_commit_topk_multi(const rma_layer_state *states, int32_t n_states, int32_t batch,
+                                 int32_t *const *keep_idx, void *stream);
 
 /* Workspace that swa_rma_prefill needs for `n_tokens` tokens per sequence. */
 size_t rma_prefill_workspace_bytes(int32_t batch, int32_t n_tokens);

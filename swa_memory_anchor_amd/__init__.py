@@ -31,7 +31,7 @@ EXPORTS = (
     "rma_commit_topk", "rma_status_str", "rma_prefill_workspace_bytes", "swa_rma_prefill",
     "rma_layer_state_fp8_bytes", "swa_rma_append_fp8", "swa_rma_decode_attn_fp8",
     "rma_commit_topk_fp8", "gdn_layer_state_bytes", "gdn_decode_step",
-    "rma_step_workspace_bytes", "swa_rma_step",
+    "rma_step_workspace_bytes", "swa_rma_step", "rma_score_multi", "rma_commit_topk_multi",
 )
 
 _c_void_p = ctypes.c_void_p
@@ -59,6 +59,11 @@ class _StateFp8C(ctypes.Structure):
 class _NormC(ctypes.Structure):
     _fields_ = [("gq_win", _c_void_p), ("gk_win", _c_void_p), ("gq_rma", _c_void_p),
                 ("gk_rma", _c_void_p), ("eps", ctypes.c_float), ("rope_base", ctypes.c_float)]
+
+
+class _ScoreJobC(ctypes.Structure):
+    _fields_ = [("hidden", _c_void_p), ("w1", _c_void_p), ("w2", _c_void_p),
+                ("scores", _c_void_p)]
 
 
 class _GdnStateC(ctypes.Structure):
@@ -96,6 +101,10 @@ def lib() -> ctypes.CDLL:
         L.rma_score.argtypes = [vp, i64, i64, vp, vp, vp, i64, vp]
         L.rma_score.restype = ctypes.c_int
         L.rma_commit_topk.argtypes = [sp, i32, vp, vp]
+        L.rma_score_multi.argtypes = [ctypes.POINTER(_ScoreJobC), i32, i64, i64, i64, vp]
+        L.rma_score_multi.restype = ctypes.c_int
+        L.rma_commit_topk_multi.argtypes = [sp, i32, i32, ctypes.POINTER(vp), vp]
+        L.rma_commit_topk_multi.restype = ctypes.c_int
         L.rma_commit_topk.restype = ctypes.c_int
         L.rma_status_str.argtypes, L.rma_status_str.restype = [ctypes.c_int], ctypes.c_char_p
         L.rma_prefill_workspace_bytes.argtypes = [i32, i32]
@@ -327,6 +336,25 @@ def rma_commit_topk(st: LayerState, batch: int, keep_idx=None, stream=None) -> N
     s = lib().rma_commit_topk(ctypes.byref(_state_c(st)), int(batch), _ptr(keep_idx),
                               _stream(stream))
     _check(s, "rma_commit_topk")
+
+
+def rma_score_multi(jobs, n_rows: int, ld_hidden: int, ld_scores: int, stream=None) -> None:
+    """jobs: a sequence of (hidden, w1, w2, scores) tensors, one rma_score call each."""
+    arr = (_ScoreJobC * len(jobs))(*[_ScoreJobC(_ptr(h), _ptr(a), _ptr(b), _ptr(o))
+                                     for h, a, b, o in jobs])
+    s = lib().rma_score_multi(arr, len(jobs), int(n_rows), int(ld_hidden), int(ld_scores),
+                              _stream(stream))
+    _check(s, "rma_score_multi")
+
+
+def rma_commit_topk_multi(states, batch: int, keep_idx=None, stream=None) -> None:
+    """states: a sequence of LayerState; keep_idx: None or one tensor (or None) per state."""
+    arr = (_StateC * len(states))(*[_state_c(st) for st in states])
+    keeps = None
+    if keep_idx is not None:
+        keeps = (_c_void_p * len(states))(*[_ptr(k) for k in keep_idx])
+    s = lib().rma_commit_topk_multi(arr, len(states), int(batch), keeps, _stream(stream))
+    _check(s, "rma_commit_topk_multi")
 
 
 def decode_workspace(batch: int, device="cuda"):

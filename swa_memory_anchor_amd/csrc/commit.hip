@@ -87,8 +87,13 @@ __device__ __forceinline__ int exclusive_scan(int v, int *wave_tot, int wave, in
   return base + x - v;
 }
 
+// Up to RMA_MAX_JOBS layers committed by one launch (blockIdx.y picks the layer).
+struct CommitJobs {
+  CommitParams job[RMA_MAX_JOBS];
+};
+
 template <bool kFp8>
-__global__ __launch_bounds__(kCommitThreads) void commit_kernel(CommitParams a) {
+__device__ __forceinline__ void commit_group(const CommitParams &a) {
   constexpr int kRowBytes = kFp8 ? kDim : 2 * kDim;
   constexpr int kPieces = kRowBytes / 16;  // 16-byte pieces per row
   __shared__ uint32_t hist[256];
@@ -258,11 +263,29 @@ __global__ __launch_bounds__(kCommitThreads) void commit_kernel(CommitParams a) 
   }
 }
 
+// One call: the parameters stay in the kernel's own argument registers.
+template <bool kFp8>
+__global__ __launch_bounds__(kCommitThreads) void commit_kernel(CommitParams a) {
+  commit_group<kFp8>(a);
+}
+
+// Several layers in one launch (blockIdx.y picks the layer).
+template <bool kFp8>
+__global__ __launch_bounds__(kCommitThreads) void commit_multi_kernel(CommitJobs jobs) {
+  commit_group<kFp8>(jobs.job[blockIdx.y]);
+}
+
 // 5. counters, after every group's workgroup has read them (a launch of its own).
-__global__ __launch_bounds__(256) void commit_counters_kernel(int32_t *n_bank, int32_t *n_pend,
-                                                              int batch) {
+struct CounterJobs {
+  int32_t *n_bank[RMA_MAX_JOBS];
+  int32_t *n_pend[RMA_MAX_JOBS];
+};
+
+__global__ __launch_bounds__(256) void commit_counters_kernel(CounterJobs jobs, int batch) {
   const int b = blockIdx.x * 256 + threadIdx.x;
   if (b >= batch) return;
+  int32_t *n_bank = jobs.n_bank[blockIdx.y];
+  int32_t *n_pend = jobs.n_pend[blockIdx.y];
   const int nb = min(max(n_bank[b], 0), kBank);
   const int np = min(max(n_pend[b], 0), kBlock);
   n_bank[b] = min(kBank, nb + np);
@@ -276,8 +299,7 @@ using namespace rma;
 static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 template <bool kFp8>
-static rma_status launch_commit(const CommitParams &p, int32_t batch, void *stream) {
-  if (batch <= 0 || batch > RMA_MAX_BATCH) return RMA_E_ARG;
+static rma_status check_commit(const CommitParams &p) {
   if (!p.bank_k || !p.bank_v || !p.bank_score || !p.bank_src || !p.pend_k || !p.pend_v ||
       !p.pend_score || !p.pend_src || !p.n_bank || !p.n_pend)
     return RMA_E_ARG;
@@ -285,18 +307,35 @@ static rma_status launch_commit(const CommitParams &p, int32_t batch, void *stre
   const void *al[] = {p.bank_k, p.bank_v, p.pend_k, p.pend_v};
   for (const void *ptr : al)
     if (!aligned16(ptr)) return RMA_E_ALIGN;
+  return RMA_OK;
+}
+
+template <bool kFp8>
+static rma_status launch_commit(const CommitJobs &jobs, int n_jobs, int32_t batch, void *stream) {
+  if (batch <= 0 || batch > RMA_MAX_BATCH) return RMA_E_ARG;
+  CounterJobs cj{};
+  for (int j = 0; j < n_jobs; ++j) {
+    const rma_status rc = check_commit<kFp8>(jobs.job[j]);
+    if (rc != RMA_OK) return rc;
+    cj.n_bank[j] = jobs.job[j].n_bank;
+    cj.n_pend[j] = jobs.job[j].n_pend;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(commit_kernel<kFp8>, dim3(batch * kGroups), dim3(kCommitThreads), 0, s, p);
+  const unsigned nj = static_cast<unsigned>(n_jobs);
+  if (n_jobs == 1)
+    hipLaunchKernelGGL(commit_kernel<kFp8>, dim3(batch * kGroups), dim3(kCommitThreads), 0, s,
+                       jobs.job[0]);
+  else
+    hipLaunchKernelGGL(commit_multi_kernel<kFp8>, dim3(batch * kGroups, nj), dim3(kCommitThreads),
+                       0, s, jobs);
   if (hipPeekAtLastError() != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
-  hipLaunchKernelGGL(commit_counters_kernel, dim3((batch + 255) / 256), dim3(256), 0, s, p.n_bank,
-                     p.n_pend, batch);
+  hipLaunchKernelGGL(commit_counters_kernel, dim3((batch + 255) / 256, nj), dim3(256), 0, s, cj,
+                     batch);
   if (hipPeekAtLastError() != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
   return RMA_OK;
 }
 
-extern "C" rma_status rma_commit_topk(const rma_layer_state *st, int32_t batch, int32_t *keep_idx,
-                                      void *stream) {
-  if (!st) return RMA_E_ARG;
+static CommitParams commit_params(const rma_layer_state *st, int32_t *keep_idx) {
   CommitParams p{};
   p.bank_k = reinterpret_cast<uint8_t *>(st->bank_k);
   p.bank_v = reinterpret_cast<uint8_t *>(st->bank_v);
@@ -309,7 +348,25 @@ extern "C" rma_status rma_commit_topk(const rma_layer_state *st, int32_t batch, 
   p.n_bank = st->n_bank;
   p.n_pend = st->n_pend;
   p.keep_idx = keep_idx;
-  return launch_commit<false>(p, batch, stream);
+  return p;
+}
+
+extern "C" rma_status rma_commit_topk(const rma_layer_state *st, int32_t batch, int32_t *keep_idx,
+                                      void *stream) {
+  if (!st) return RMA_E_ARG;
+  CommitJobs jobs{};
+  jobs.job[0] = commit_params(st, keep_idx);
+  return launch_commit<false>(jobs, 1, batch, stream);
+}
+
+extern "C" rma_status rma_commit_topk_multi(const rma_layer_state *states, int32_t n_states,
+                                            int32_t batch, int32_t *const *keep_idx,
+                                            void *stream) {
+  if (!states || n_states < 1 || n_states > RMA_MAX_JOBS) return RMA_E_ARG;
+  CommitJobs jobs{};
+  for (int j = 0; j < n_states; ++j)
+    jobs.job[j] = commit_params(&states[j], keep_idx ? keep_idx[j] : nullptr);
+  return launch_commit<false>(jobs, n_states, batch, stream);
 }
 
 extern "C" rma_status rma_commit_topk_fp8(const rma_layer_state_fp8 *st, int32_t batch,
@@ -331,5 +388,7 @@ extern "C" rma_status rma_commit_topk_fp8(const rma_layer_state_fp8 *st, int32_t
   p.n_bank = st->n_bank;
   p.n_pend = st->n_pend;
   p.keep_idx = keep_idx;
-  return launch_commit<true>(p, batch, stream);
+  CommitJobs jobs{};
+  jobs.job[0] = p;
+  return launch_commit<true>(jobs, 1, batch, stream);
 }

@@ -50,8 +50,15 @@ struct ScoreParams {
 // CB=4); calls with fewer such tiles than CUs use 64-row tiles (WR=2, RB=1, CB=4)
 // or, fewer still, 32-row tiles (WR=1, RB=1, CB=2).  All run the same instruction
 // sequence per output element, so results do not depend on the tile shape.
+// Up to RMA_MAX_JOBS independent calls of the same row count in one launch
+// (blockIdx.y picks the call): the layers of a block, scored together.
+struct ScoreJobs {
+  ScoreParams job[RMA_MAX_JOBS];
+};
+
 template <int WR, int RB, int CB>
-__global__ __launch_bounds__(kScoreThreads, 1) void score_kernel(ScoreParams a) {
+__global__ __launch_bounds__(kScoreThreads, 1) void score_kernel(ScoreJobs jobs) {
+  const ScoreParams &a = jobs.job[blockIdx.y];
   constexpr int WC = 4 / WR;
   constexpr int kRows = 32 * RB * WR;
   constexpr int kColsW = 32 * CB;  // columns per wave
@@ -211,9 +218,10 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score_kernel(ScoreParams a) 
 
 using namespace rma;
 
-extern "C" rma_status rma_score(const uint16_t *hidden, int64_t n_rows, int64_t ld_hidden,
-                                const float *w1, const float *w2, float *scores,
-                                int64_t ld_scores, void *stream) {
+// Validate one call's arguments (shared by the single and the multi-call entry).
+static rma_status check_score(const uint16_t *hidden, int64_t n_rows, int64_t ld_hidden,
+                              const float *w1, const float *w2, const float *scores,
+                              int64_t ld_scores) {
   if (n_rows < 0 || !w1 || !w2) return RMA_E_ARG;
   if (n_rows == 0) return RMA_OK;
   if (!hidden || !scores) return RMA_E_ARG;
@@ -222,24 +230,53 @@ extern "C" rma_status rma_score(const uint16_t *hidden, int64_t n_rows, int64_t 
   if ((reinterpret_cast<uintptr_t>(hidden) & 15u) || (reinterpret_cast<uintptr_t>(w1) & 15u) ||
       (reinterpret_cast<uintptr_t>(scores) & 15u))
     return RMA_E_ALIGN;
-  ScoreParams p{hidden, n_rows, ld_hidden, w1, w2, scores, ld_scores};
+  return RMA_OK;
+}
+
+static rma_status launch_score(const ScoreJobs &jobs, int n_jobs, int64_t n_rows, void *stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   // The largest row tile that still gives every CU (256) a workgroup: 128 rows,
   // then 64, then 32 (a larger tile reads W1 fewer times per row).
   const int64_t big = (n_rows + 127) / 128;
   const int64_t mid = (n_rows + 63) / 64;
+  const unsigned nj = static_cast<unsigned>(n_jobs);
   if (big >= 256) {
     if (big > 0x7fffffff) return RMA_E_ARG;
-    hipLaunchKernelGGL((score_kernel<2, 2, 4>), dim3(static_cast<unsigned>(big)),
-                       dim3(kScoreThreads), 0, s, p);
+    hipLaunchKernelGGL((score_kernel<2, 2, 4>), dim3(static_cast<unsigned>(big), nj),
+                       dim3(kScoreThreads), 0, s, jobs);
   } else if (mid >= 256) {
-    hipLaunchKernelGGL((score_kernel<2, 1, 4>), dim3(static_cast<unsigned>(mid)),
-                       dim3(kScoreThreads), 0, s, p);
+    hipLaunchKernelGGL((score_kernel<2, 1, 4>), dim3(static_cast<unsigned>(mid), nj),
+                       dim3(kScoreThreads), 0, s, jobs);
   } else {
     const int64_t small = (n_rows + 31) / 32;
-    hipLaunchKernelGGL((score_kernel<1, 1, 2>), dim3(static_cast<unsigned>(small)),
-                       dim3(kScoreThreads), 0, s, p);
+    hipLaunchKernelGGL((score_kernel<1, 1, 2>), dim3(static_cast<unsigned>(small), nj),
+                       dim3(kScoreThreads), 0, s, jobs);
   }
   if (hipPeekAtLastError() != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
   return RMA_OK;
+}
+
+extern "C" rma_status rma_score(const uint16_t *hidden, int64_t n_rows, int64_t ld_hidden,
+                                const float *w1, const float *w2, float *scores,
+                                int64_t ld_scores, void *stream) {
+  const rma_status rc = check_score(hidden, n_rows, ld_hidden, w1, w2, scores, ld_scores);
+  if (rc != RMA_OK || n_rows == 0) return rc;
+  ScoreJobs jobs{};
+  jobs.job[0] = ScoreParams{hidden, n_rows, ld_hidden, w1, w2, scores, ld_scores};
+  return launch_score(jobs, 1, n_rows, stream);
+}
+
+extern "C" rma_status rma_score_multi(const rma_score_job *jobs, int32_t n_jobs, int64_t n_rows,
+                                      int64_t ld_hidden, int64_t ld_scores, void *stream) {
+  if (!jobs || n_jobs < 1 || n_jobs > RMA_MAX_JOBS) return RMA_E_ARG;
+  ScoreJobs sj{};
+  for (int j = 0; j < n_jobs; ++j) {
+    const rma_score_job &jb = jobs[j];
+    const rma_status rc = check_score(jb.hidden, n_rows, ld_hidden, jb.w1, jb.w2, jb.scores,
+                                      ld_scores);
+    if (rc != RMA_OK) return rc;
+    sj.job[j] = ScoreParams{jb.hidden, n_rows, ld_hidden, jb.w1, jb.w2, jb.scores, ld_scores};
+  }
+  if (n_rows == 0) return RMA_OK;
+  return launch_score(sj, n_jobs, n_rows, stream);
 }

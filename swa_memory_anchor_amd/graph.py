@@ -7,9 +7,9 @@ these launches is short, so host-side launch cost matters as much as the kernels
 the pages' single-request decoding rates (fluxbbs.com page, section "吞吐：一张
 80GB 卡跑 512 路长推理") come from a backend that replays captured graphs
 (agentlenshq.com "rockmatrix-ai/EdgeRock", section "如何尝试").  ``StreamBlockGraph``
-records one whole 256-token block for every layer (256 x L steps, then
-L x (score, commit)) into a single HIP graph through torch's graph capture, and
-replays it per block.  A step is one ``swa_rma_step`` launch (append and
+records one whole 256-token block for every layer (256 x L steps, then the
+scores of every layer in one launch and the commits of every layer in one) into a
+single HIP graph through torch's graph capture, and replays it per block.  A step is one ``swa_rma_step`` launch (append and
 attention fused; the split merge follows where the key range is split) or, with
 ``fused=False``, the separate append and decode launches.
 
@@ -27,7 +27,9 @@ from __future__ import annotations
 import ctypes
 
 from . import (BLOCK, HEAD_DIM, HIDDEN, KV_GROUPS, Q_HEADS, LayerState, Norm, _norm_c, _ptr,
-               _state_c, decode_workspace, lib, step_workspace)
+               _ScoreJobC, _state_c, _StateC, decode_workspace, lib, step_workspace)
+
+RMA_MAX_JOBS = 16  # calls one *_multi entry point takes at most (rma.h)
 
 RECORD_NAMES = ("k_win", "v_win", "k_rma", "v_rma")
 
@@ -110,17 +112,21 @@ class StreamBlockGraph:
                 if s != 0:
                     raise RuntimeError(f"swa_rma_decode_attn failed during capture (status {s})")
         if self.commit:
+            # every layer's scores in one launch, then every layer's commit in one
             hb = HIDDEN * 2 * B * T
-            for l in range(L):
-                st = ctypes.byref(self._st_c[l])
-                w1, w2 = self._scorer[l]
-                s = lb.rma_score(self.hidden.data_ptr() + l * hb, B * T, HIDDEN, _ptr(w1),
-                                 _ptr(w2), _ptr(self._states[l].pend_score), KV_GROUPS, stream)
+            for l0 in range(0, L, RMA_MAX_JOBS):
+                ls = range(l0, min(L, l0 + RMA_MAX_JOBS))
+                jobs = (_ScoreJobC * len(ls))(*[
+                    _ScoreJobC(self.hidden.data_ptr() + l * hb, _ptr(self._scorer[l][0]),
+                               _ptr(self._scorer[l][1]), _ptr(self._states[l].pend_score))
+                    for l in ls])
+                s = lb.rma_score_multi(jobs, len(ls), B * T, HIDDEN, KV_GROUPS, stream)
                 if s != 0:
-                    raise RuntimeError(f"rma_score failed during capture (status {s})")
-                s = lb.rma_commit_topk(st, B, None, stream)
+                    raise RuntimeError(f"rma_score_multi failed during capture (status {s})")
+                sts = (_StateC * len(ls))(*[self._st_c[l] for l in ls])
+                s = lb.rma_commit_topk_multi(sts, len(ls), B, None, stream)
                 if s != 0:
-                    raise RuntimeError(f"rma_commit_topk failed during capture (status {s})")
+                    raise RuntimeError(f"rma_commit_topk_multi failed during capture (status {s})")
 
     def capture(self) -> "StreamBlockGraph":
         """Record the block (nothing runs while recording)."""

@@ -129,6 +129,28 @@ def test_step_workspace_and_host_validation(lib):
     assert step(by(bad), 4, 16, need) == 1
 
 
+def test_multi_call_host_validation(lib):
+    job = R._ScoreJobC(16, 16, 16, 16)
+    jobs = (R._ScoreJobC * 17)(*([job] * 17))
+    assert lib.rma_score_multi(jobs, 0, 256, 2560, 4, None) == 1
+    assert lib.rma_score_multi(jobs, 17, 256, 2560, 4, None) == 1   # past RMA_MAX_JOBS
+    assert lib.rma_score_multi(None, 2, 256, 2560, 4, None) == 1
+    assert lib.rma_score_multi(jobs, 16, 0, 2560, 4, None) == 0     # no rows: a no-op
+    bad = (R._ScoreJobC * 2)(job, R._ScoreJobC(24, 16, 16, 16))
+    assert lib.rma_score_multi(bad, 2, 256, 2560, 4, None) == 2     # one misaligned job
+    assert lib.rma_score_multi(bad, 1, 256, 2559, 4, None) == 1
+    st = _state()
+    states = (R._StateC * 17)(*([st] * 17))
+    assert lib.rma_commit_topk_multi(states, 0, 4, None, None) == 1
+    assert lib.rma_commit_topk_multi(states, 17, 4, None, None) == 1
+    assert lib.rma_commit_topk_multi(None, 2, 4, None, None) == 1
+    assert lib.rma_commit_topk_multi(states, 2, 0, None, None) == 1
+    broken = _state()
+    broken.pend_src = None
+    mixed = (R._StateC * 2)(st, broken)
+    assert lib.rma_commit_topk_multi(mixed, 2, 4, None, None) == 1
+
+
 def test_fp8_state_size_and_host_validation(lib):
     # codes (1 B) + one FP32 scale per K and V row, plus the same metadata
     rows = 2 * 4 * (1024 + 1024 + 256)

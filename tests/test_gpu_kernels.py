@@ -280,3 +280,49 @@ def test_score_large_ragged_uses_big_tiles_and_matches_small_tiles():
         R.rma_score(bf16_dev(h[sub]), len(sub), 2560, w1d, w2d, out2, 4)
         torch.cuda.synchronize()
         assert np.array_equal(out2.cpu().numpy(), o[sub]), len(sub)
+
+
+def test_score_multi_equals_separate_calls():
+    """rma_score_multi: every job's scores are bit-identical to its own rma_score call,
+    at a small (32-row tiles) and a mid-size (64-row tiles) row count."""
+    rng = np.random.default_rng(77)
+    for n in (300, 17000):
+        print(f"case: score multi n={n}", flush=True)
+        jobs, refs = [], []
+        for j in range(3):
+            h = bf16_dev(synth.normal_bf16_np(synth.stream_key("score_multi", n, j), n * 2560)
+                         .reshape(n, 2560))
+            w1 = f32_dev((0.02 * rng.standard_normal((2560, 256))).astype(np.float32))
+            w2 = f32_dev((0.02 * rng.standard_normal((256, 4))).astype(np.float32))
+            out = torch.full((n, 4), float("nan"), device=DEV)
+            ref = torch.empty(n, 4, device=DEV)
+            R.rma_score(h, n, 2560, w1, w2, ref, 4)
+            jobs.append((h, w1, w2, out))
+            refs.append(ref)
+        R.rma_score_multi(jobs, n, 2560, 4)
+        torch.cuda.synchronize()
+        for (_, _, _, out), ref in zip(jobs, refs):
+            assert torch.equal(out.view(torch.int32), ref.view(torch.int32))
+
+
+def test_commit_multi_equals_separate_calls():
+    """rma_commit_topk_multi over three layers leaves each state and keep_idx as
+    rma_commit_topk does, bit for bit (ragged counts, ties, signed zeros, NaN)."""
+    print("case: commit multi", flush=True)
+    states = [_commit_state(f"commit_multi_{l}", COMMIT_COUNTS, special=(l != 1)) for l in range(3)]
+    B = len(COMMIT_COUNTS)
+    multi = [upload(st) for st in states]
+    single = [upload(st) for st in states]
+    k_multi = [torch.full((B, 4, 1024), -7, dtype=torch.int32, device=DEV) for _ in states]
+    k_single = [torch.full((B, 4, 1024), -7, dtype=torch.int32, device=DEV) for _ in states]
+    R.rma_commit_topk_multi(multi, B, k_multi)
+    for st, k in zip(single, k_single):
+        R.rma_commit_topk(st, B, k)
+    torch.cuda.synchronize()
+    for l in range(3):
+        assert torch.equal(k_multi[l], k_single[l]), l
+        a, b_ = download(multi[l]), download(single[l])
+        for f in ("bank_k", "bank_v", "bank_score", "bank_src", "n_bank", "n_pend", "pos"):
+            x, y = getattr(a, f), getattr(b_, f)
+            assert np.array_equal(x.view(np.uint32) if x.dtype == np.float32 else x,
+                                  y.view(np.uint32) if y.dtype == np.float32 else y), (l, f)
