@@ -142,6 +142,7 @@ def cpu_baseline(wl, budget_s: float, max_units: int):
 
 SCORER_FLOP_PER_ROW = 2 * 2560 * 256 + 2 * 256 * 4
 FP32_MATRIX_PEAK_TFLOPS = 157.3
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X's published FP32 vector figure
 
 
 def _timed(fn, reps, stream):
@@ -703,6 +704,84 @@ def cpu_baseline_long_stream(wl, budget_s: float):
                       f"the block part amortised over 256 tokens"}
 
 
+def bench_gdn_prefill(args):
+    """One 256-token chunk per sequence through the 24 Gated DeltaNet layers at batch
+    512 (24 dependent gdn_prefill launches, FP16 matrices).  Each layer has its own
+    state; the chunk inputs (2 GiB of projected inputs and the gates) are drawn once
+    and fed to every layer (values do not change the work)."""
+    import torch
+
+    import swa_memory_anchor_amd as R
+    from synth import workloads as W
+
+    wl = W.GDN_PREFILL_B512
+    B, L, C, dev = wl.batch, wl.layers, wl.extra["chunk"], "cuda"
+    stream = torch.cuda.current_stream()
+    x = torch.empty(B, C, 8192, dtype=torch.bfloat16, device=dev)
+    W.gdn_chunk_x_torch_(wl, 0, x)
+    a, b = W.gdn_chunk_gates(wl, 0, C)
+    a, b = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
+    pos = torch.full((B,), wl.position, dtype=torch.int32, device=dev)
+    o = torch.empty(B, C, 32, 128, dtype=torch.bfloat16, device=dev)
+    layers = []
+    for layer in range(L):
+        st = R.GdnState(torch.empty(B, 32, 128, 128, dtype=torch.float16, device=dev),
+                        torch.empty(B, 4, 8192, dtype=torch.bfloat16, device=dev))
+        W.gdn_state_torch_(wl, layer, st.S)
+        W.gdn_conv_torch_(wl, layer, st.conv)
+        p = W.gdn_params(wl, layer)
+        prm = R.GdnParams(*[torch.from_numpy(p[k]).to(dev) for k in ("conv_w", "a_log",
+                                                                     "dt_bias")])
+        layers.append((st, prm))
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        for l, (st, prm) in enumerate(layers):
+            if ev is not None:
+                ev[l][0].record(stream)
+            R.gdn_prefill(st, B, C, x, a, b, pos, prm, o, stream)
+            if ev is not None:
+                ev[l][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in range(L)] for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for k in range(args.steps):
+        step(evs[k])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / args.steps
+    launch_ms = sorted(e[0].elapsed_time(e[1]) for s_ in evs for e in s_)
+    avg_launch = sum(launch_ms) / len(launch_ms)
+    # per token and value head: the two column sums over the 128 x 128 matrix
+    # (2 x 2 flops per element) and the update (3 flops per element)
+    flop = B * C * 32 * 128 * 128 * 7
+    tflops = flop / (avg_launch / 1e3) / 1e12
+    return {
+        "metric": "GDN chunked prefill: tokens/s (256-token chunk per sequence, 24 layers)",
+        "value": round(B * C / (step_ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "dtype": "f16 state, f32 math",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "layers": L, "chunk": C,
+                   "positions": [wl.position, wl.position + C - 1], "state": "f16"},
+        "roofline": {"bound": "alu", "achieved": round(tflops, 2), "peak": FP32_VECTOR_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / FP32_VECTOR_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "gdn_prefill_kernel",
+                     "avg_launch_ms": round(avg_launch, 4)},
+    }
+
+
 def cpu_baseline_gdn(wl, budget_s: float):
     """The GDN oracle, untuned, on random (sequence, layer) units (all 32 heads each)."""
     import numpy as np
@@ -740,7 +819,8 @@ def main() -> int:
     ap.add_argument("--workload", default="headline_b512",
                     choices=["headline_b512", "headline_b512_fp8", "steady_b64", "batch1",
                              "commit_burst_b512", "long_stream_b1", "prefill_b512",
-                             "prefill_b64", "gdn_decode_b512", "gdn_decode_b1"])
+                             "prefill_b64", "gdn_decode_b512", "gdn_decode_b1",
+                             "gdn_prefill_b512"])
     ap.add_argument("--stream-tokens", type=int, default=16384,
                     help="long_stream_b1: tokens streamed (the second half is timed)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
@@ -778,6 +858,9 @@ def main() -> int:
         return 0
     if args.workload.startswith("prefill"):
         print(json.dumps(bench_prefill(args)))
+        return 0
+    if args.workload == "gdn_prefill_b512":
+        print(json.dumps(bench_gdn_prefill(args)))
         return 0
     if args.workload.startswith("gdn"):
         print(json.dumps(bench_gdn(args)))

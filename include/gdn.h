@@ -79,6 +79,27 @@ rma_status gdn_decode_step(const gdn_layer_state *st, int32_t batch, int32_t sta
                            const int32_t *pos, const gdn_params *prm, uint16_t *o,
                            void *stream);
 
+/* Most tokens one gdn_prefill call takes. */
+#define GDN_MAX_PREFILL 65536
+
+/*
+ * gdn_prefill - n_tokens (1..GDN_MAX_PREFILL) tokens per sequence through one GDN
+ * layer in one call: the result is that of n_tokens successive gdn_decode_step
+ * calls with positions pos[b], pos[b] + 1, ..., bit for bit (the matrices are
+ * rounded to their storage type after every token, as stored steps would be).
+ *   x       bf16 [B][n_tokens][8192]  the tokens' projected inputs;
+ *   a, b    f32  [B][n_tokens][32];
+ *   pos     i32  [B]  position of each sequence's first token of the chunk (>= 0);
+ *   o       bf16 [B][n_tokens][32][128] out.
+ * Afterwards the ring holds the inputs of the chunk's last min(n_tokens, 4) tokens
+ * (slot = position mod 4; other slots unchanged); the caller advances its
+ * positions by n_tokens.  Errors as gdn_decode_step, and RMA_E_ARG for n_tokens
+ * out of range.
+ */
+rma_status gdn_prefill(const gdn_layer_state *st, int32_t batch, int32_t n_tokens,
+                       int32_t state_dtype, const uint16_t *x, const float *a, const float *b,
+                       const int32_t *pos, const gdn_params *prm, uint16_t *o, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -32,6 +32,7 @@ EXPORTS = (
     "rma_layer_state_fp8_bytes", "swa_rma_append_fp8", "swa_rma_decode_attn_fp8",
     "rma_commit_topk_fp8", "gdn_layer_state_bytes", "gdn_decode_step",
     "rma_step_workspace_bytes", "swa_rma_step", "rma_score_multi", "rma_commit_topk_multi",
+    "gdn_prefill",
 )
 
 _c_void_p = ctypes.c_void_p
@@ -124,6 +125,9 @@ def lib() -> ctypes.CDLL:
         L.gdn_decode_step.argtypes = [ctypes.POINTER(_GdnStateC), i32, i32, vp, vp, vp, vp,
                                       ctypes.POINTER(_GdnParamsC), vp, vp]
         L.gdn_decode_step.restype = ctypes.c_int
+        L.gdn_prefill.argtypes = [ctypes.POINTER(_GdnStateC), i32, i32, i32, vp, vp, vp, vp,
+                                  ctypes.POINTER(_GdnParamsC), vp, vp]
+        L.gdn_prefill.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -474,3 +478,13 @@ def gdn_decode_step(st: GdnState, batch: int, x, a, b, pos, prm: GdnParams, o,
     s = lib().gdn_decode_step(ctypes.byref(sc), int(batch), st.dtype_code, _ptr(x), _ptr(a),
                               _ptr(b), _ptr(pos), ctypes.byref(pc), _ptr(o), _stream(stream))
     _check(s, "gdn_decode_step")
+
+
+def gdn_prefill(st: GdnState, batch: int, n_tokens: int, x, a, b, pos, prm: GdnParams, o,
+                stream=None) -> None:
+    """n_tokens successive GDN decode steps per sequence in one call (see gdn.h)."""
+    sc = _GdnStateC(_ptr(st.S), _ptr(st.conv))
+    pc = _GdnParamsC(_ptr(prm.conv_w), _ptr(prm.a_log), _ptr(prm.dt_bias))
+    s = lib().gdn_prefill(ctypes.byref(sc), int(batch), int(n_tokens), st.dtype_code, _ptr(x),
+                          _ptr(a), _ptr(b), _ptr(pos), ctypes.byref(pc), _ptr(o), _stream(stream))
+    _check(s, "gdn_prefill")

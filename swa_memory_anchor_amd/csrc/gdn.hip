@@ -266,6 +266,249 @@ __global__ __launch_bounds__(kThreads) void gdn_decode_kernel(Params pr) {
   }
 }
 
+// ---------------------------------------------------------------- chunked prefill
+// n_tokens successive decode steps of one sequence's head in one workgroup: the
+// column slice of the matrix stays in registers (as FP32 values, rounded to the
+// storage type after every token, exactly as a stored and reloaded matrix would
+// be), and each channel's convolution history (the previous three inputs) in the
+// registers of the thread that owns the channel.  Every token runs the decode
+// step's arithmetic in the same order, so the results are those of n_tokens
+// gdn_decode_step calls, bit for bit.  The ring is read here (history before the
+// chunk) and written by the launch that follows (the chunk's last inputs), so no
+// workgroup overwrites slots another still has to read.
+struct PrefillParams {
+  void *S;
+  const uint16_t *conv;
+  const uint16_t *x;       // [B][T][8192]
+  const float *a, *b;      // [B][T][32]
+  const int32_t *pos;      // [B]: position of the chunk's first token
+  const float *conv_w, *a_log, *dt_bias;
+  uint16_t *o;             // [B][T][32][128]
+  int n_tokens;
+};
+
+// The convolution history of one channel at the chunk's start: the inputs of
+// positions p0-3 .. p0-1 (ring slots), oldest first.
+__device__ __forceinline__ void history_load(const uint16_t *ring, int ch, int p0, uint16_t (&h)[3]) {
+#pragma unroll
+  for (int j = 0; j < 3; ++j) h[j] = ring[((p0 - 3 + j) & 3) * kCD + ch];
+}
+
+// SiLU of the width-4 causal convolution of one channel: taps 0..2 on the history
+// (positions p-3 .. p-1), tap 3 on the current input (the decode step's order).
+__device__ __forceinline__ float conv_silu_hist(const float4 &w, const uint16_t (&h)[3], uint16_t x) {
+  float acc = w.x * bf16f(h[0]);
+  acc = fmaf(w.y, bf16f(h[1]), acc);
+  acc = fmaf(w.z, bf16f(h[2]), acc);
+  acc = fmaf(w.w, bf16f(x), acc);
+  return acc / (1.f + expf(-acc));
+}
+
+template <bool kF32, int kCW>
+__global__ __launch_bounds__(kThreads) void gdn_prefill_kernel(PrefillParams pr) {
+  constexpr int kChunks = kCW / 8;
+  constexpr int kRG = kThreads / kChunks;
+  constexpr int kRows = kD / kRG;
+  constexpr int kSlices = kD / kCW;
+  constexpr int kWaves = kThreads / 64;
+  __shared__ float q_s[kD], k_s[kD], v_s[kD];
+  __shared__ float red[kWaves][2][kCW];
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int slice = blockIdx.x % kSlices;
+  const int bh = blockIdx.x / kSlices;
+  const int b = bh / kVH, h = bh % kVH, kh = h / (kVH / kKH);
+  const int c = t % kChunks, rg = t / kChunks;
+  const int col = slice * kCW + 8 * c;
+  const size_t head = static_cast<size_t>(bh) * kD * kD;
+  const int T = pr.n_tokens;
+
+  // the matrix slice, as FP32 values of the stored elements
+  float sv[kRows][8];
+#pragma unroll
+  for (int i = 0; i < kRows; ++i) {
+    const size_t e = head + static_cast<size_t>(rg + kRG * i) * kD + col;
+    if constexpr (kF32) {
+      const f32x4_t *src = reinterpret_cast<const f32x4_t *>(static_cast<const float *>(pr.S) + e);
+      const f32x4_t lo = __builtin_nontemporal_load(src), hi = __builtin_nontemporal_load(src + 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sv[i][j] = lo[j];
+        sv[i][4 + j] = hi[j];
+      }
+    } else {
+      const f16x8 hv = __builtin_bit_cast(
+          f16x8, __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(
+                     static_cast<const _Float16 *>(pr.S) + e)));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sv[i][j] = static_cast<float>(hv[j]);
+    }
+  }
+
+  // channels: threads t < 128 own q channel t of the key head and v channel t of
+  // the value head; threads t >= 128 own k channel t - 128
+  const int p0 = pr.pos[b];
+  const uint16_t *ring = pr.conv + static_cast<size_t>(b) * kConv * kCD;
+  const int ch0 = t < kD ? kh * kD + t : kKeyDim + kh * kD + (t - kD);
+  const int cv = kValOff + h * kD + (t & (kD - 1));
+  const float4 w0 = *reinterpret_cast<const float4 *>(pr.conv_w + 4 * ch0);
+  const float4 w1 = *reinterpret_cast<const float4 *>(pr.conv_w + 4 * cv);
+  uint16_t h0[3], h1[3];
+  history_load(ring, ch0, p0, h0);
+  history_load(ring, cv, p0, h1);
+  const float a_log = pr.a_log[h], dtb = pr.dt_bias[h];
+
+  // the token's inputs are fetched one token ahead, so their latency overlaps the
+  // previous token's work
+  auto fetch = [&](int i, uint16_t &x0, uint16_t &x1, float &ra, float &rb) {
+    const size_t tok = static_cast<size_t>(b) * T + i;
+    const uint16_t *xb = pr.x + tok * kCD;
+    x0 = xb[ch0];
+    x1 = t < kD ? xb[cv] : uint16_t(0);
+    ra = pr.a[tok * kVH + h];
+    rb = pr.b[tok * kVH + h];
+  };
+  uint16_t nx0, nx1;
+  float na, nb;
+  fetch(0, nx0, nx1, na, nb);
+  for (int i = 0; i < T; ++i) {
+    const size_t tok = static_cast<size_t>(b) * T + i;
+    const uint16_t x0 = nx0, x1 = nx1;
+    const float za = na + dtb;
+    const float zb = nb;
+    if (i + 1 < T) fetch(i + 1, nx0, nx1, na, nb);
+    const float y0 = conv_silu_hist(w0, h0, x0);
+    if (t < kD) {
+      q_s[t] = y0;
+      v_s[t] = conv_silu_hist(w1, h1, x1);
+    } else {
+      k_s[t - kD] = y0;
+    }
+    h0[0] = h0[1];
+    h0[1] = h0[2];
+    h0[2] = x0;
+    h1[0] = h1[1];
+    h1[1] = h1[2];
+    h1[2] = x1;
+    __syncthreads();
+
+    const float q0 = q_s[lane], q1 = q_s[lane + 64], k0 = k_s[lane], k1 = k_s[lane + 64];
+    const float sq = rma::wave_sum(q0 * q0 + q1 * q1);
+    const float sk = rma::wave_sum(k0 * k0 + k1 * k1);
+    const float sqk = rma::wave_sum(q0 * k0 + q1 * k1);
+    const float iq = (1.f / sqrtf(sq + kL2Eps)) * 0.08838834764831845f;  // 1/sqrt(128)
+    const float ik = 1.f / sqrtf(sk + kL2Eps);
+    const float kq = sqk * iq * ik;
+    const float softplus = fmaxf(za, 0.f) + log1pf(expf(-fabsf(za)));
+    const float alpha = expf(-expf(a_log) * softplus);
+    const float eb = expf(-fabsf(zb));
+    const float beta = zb >= 0.f ? 1.f / (1.f + eb) : eb / (1.f + eb);
+
+    float pk[8], pq[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pk[j] = pq[j] = 0.f;
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      const int row = rg + kRG * r;
+      const float kr = k_s[row] * ik, qr = q_s[row] * iq;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        pk[j] = fmaf(sv[r][j], kr, pk[j]);
+        pq[j] = fmaf(sv[r][j], qr, pq[j]);
+      }
+    }
+#pragma unroll
+    for (int off = kChunks; off < 64; off <<= 1) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        pk[j] += __shfl_xor(pk[j], off, 64);
+        pq[j] += __shfl_xor(pq[j], off, 64);
+      }
+    }
+    if (lane < kChunks) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        red[wave][0][8 * c + j] = pk[j];
+        red[wave][1][8 * c + j] = pq[j];
+      }
+    }
+    __syncthreads();
+
+    float u[8], o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float tk = 0.f, tq = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        tk += red[w][0][8 * c + j];
+        tq += red[w][1][8 * c + j];
+      }
+      u[j] = beta * (v_s[col + j] - alpha * tk);
+      o[j] = fmaf(alpha, tq, u[j] * kq);
+    }
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      const float kr = k_s[rg + kRG * r] * ik;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float nv = fmaf(alpha, sv[r][j], kr * u[j]);
+        // the stored value, as the next step would read it back
+        sv[r][j] = kF32 ? nv : static_cast<float>(static_cast<_Float16>(nv));
+      }
+    }
+    if (rg == 0) {
+      uint4 ov;
+      ov.x = rma::pack_bf16x2(o[0], o[1]);
+      ov.y = rma::pack_bf16x2(o[2], o[3]);
+      ov.z = rma::pack_bf16x2(o[4], o[5]);
+      ov.w = rma::pack_bf16x2(o[6], o[7]);
+      *reinterpret_cast<uint4 *>(pr.o + (tok * kVH + h) * kD + col) = ov;
+    }
+    __syncthreads();  // q_s / k_s / v_s / red are rewritten by the next token
+  }
+
+#pragma unroll
+  for (int i = 0; i < kRows; ++i) {
+    const size_t e = head + static_cast<size_t>(rg + kRG * i) * kD + col;
+    if constexpr (kF32) {
+      f32x4_t lo, hi;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        lo[j] = sv[i][j];
+        hi[j] = sv[i][4 + j];
+      }
+      f32x4_t *dst = reinterpret_cast<f32x4_t *>(static_cast<float *>(pr.S) + e);
+      __builtin_nontemporal_store(lo, dst);
+      __builtin_nontemporal_store(hi, dst + 1);
+    } else {
+      f16x8 hv;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) hv[j] = static_cast<_Float16>(sv[i][j]);
+      __builtin_nontemporal_store(__builtin_bit_cast(f32x4_t, hv),
+                                  reinterpret_cast<f32x4_t *>(static_cast<_Float16 *>(pr.S) + e));
+    }
+  }
+}
+
+// The ring after the chunk: the inputs of its last min(T, 4) tokens, each in slot
+// (its position) mod 4; the other slots keep what they held.  One workgroup per
+// (sequence, slot); 256 threads copy the 8192 channels in 16-byte pieces.
+__global__ __launch_bounds__(256) void gdn_prefill_ring_kernel(PrefillParams pr) {
+  const int b = blockIdx.x / kConv;
+  const int slot = blockIdx.x % kConv;
+  const int T = pr.n_tokens;
+  const int p0 = pr.pos[b];
+  // the last token of the chunk that lands in this slot, if any
+  const int last = p0 + T - 1;
+  const int d = (last - slot) & 3;  // tokens back from the last one
+  if (d >= T) return;
+  const int i = T - 1 - d;
+  const uint4 *src = reinterpret_cast<const uint4 *>(pr.x + (static_cast<size_t>(b) * T + i) * kCD);
+  uint4 *dst = reinterpret_cast<uint4 *>(const_cast<uint16_t *>(pr.conv) +
+                                         (static_cast<size_t>(b) * kConv + slot) * kCD);
+  for (int e = threadIdx.x; e < kCD / 8; e += 256) dst[e] = src[e];
+}
+
 template <bool kF32, int kCW>
 static void launch(const Params &pr, int batch, hipStream_t s) {
   hipLaunchKernelGGL((gdn_decode_kernel<kF32, kCW>), dim3(batch * kVH * (kD / kCW)),
@@ -321,6 +564,56 @@ extern "C" rma_status gdn_decode_step(const gdn_layer_state *st, int32_t batch, 
     else
       gdn::launch<false, 32>(pr, batch, s);
   }
+  if (hipPeekAtLastError() != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
+  return RMA_OK;
+}
+
+extern "C" rma_status gdn_prefill(const gdn_layer_state *st, int32_t batch, int32_t n_tokens,
+                                  int32_t state_dtype, const uint16_t *x, const float *a,
+                                  const float *b, const int32_t *pos, const gdn_params *prm,
+                                  uint16_t *o, void *stream) {
+  if (!st || !prm || !x || !a || !b || !pos || !o) return RMA_E_ARG;
+  if (!st->S || !st->conv || !prm->conv_w || !prm->a_log || !prm->dt_bias) return RMA_E_ARG;
+  if (batch <= 0 || batch > RMA_MAX_BATCH) return RMA_E_ARG;
+  if (n_tokens <= 0 || n_tokens > GDN_MAX_PREFILL) return RMA_E_ARG;
+  if (state_dtype != GDN_STATE_F16 && state_dtype != GDN_STATE_F32) return RMA_E_ARG;
+  const void *al[] = {st->S, st->conv, x, o, prm->conv_w};
+  for (const void *p : al)
+    if (!aligned16(p)) return RMA_E_ALIGN;
+  gdn::PrefillParams pr;
+  pr.S = st->S;
+  pr.conv = st->conv;
+  pr.x = x;
+  pr.a = a;
+  pr.b = b;
+  pr.pos = pos;
+  pr.conv_w = prm->conv_w;
+  pr.a_log = prm->a_log;
+  pr.dt_bias = prm->dt_bias;
+  pr.o = o;
+  pr.n_tokens = n_tokens;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // the same column slices as the decode step at this batch (and so the same
+  // arithmetic per token)
+  const bool wide = batch >= 16;
+  const unsigned per_head = wide ? gdn::kD / RMA_GDN_WIDE_COLS : gdn::kD / 32;
+  const dim3 grid(static_cast<unsigned>(batch) * gdn::kVH * per_head);
+  if (state_dtype == GDN_STATE_F32) {
+    if (wide)
+      hipLaunchKernelGGL((gdn::gdn_prefill_kernel<true, RMA_GDN_WIDE_COLS>), grid,
+                         dim3(gdn::kThreads), 0, s, pr);
+    else
+      hipLaunchKernelGGL((gdn::gdn_prefill_kernel<true, 32>), grid, dim3(gdn::kThreads), 0, s, pr);
+  } else {
+    if (wide)
+      hipLaunchKernelGGL((gdn::gdn_prefill_kernel<false, RMA_GDN_WIDE_COLS>), grid,
+                         dim3(gdn::kThreads), 0, s, pr);
+    else
+      hipLaunchKernelGGL((gdn::gdn_prefill_kernel<false, 32>), grid, dim3(gdn::kThreads), 0, s, pr);
+  }
+  if (hipPeekAtLastError() != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
+  hipLaunchKernelGGL(gdn::gdn_prefill_ring_kernel, dim3(static_cast<unsigned>(batch) * GDN_CONV),
+                     dim3(256), 0, s, pr);
   if (hipPeekAtLastError() != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
   return RMA_OK;
 }

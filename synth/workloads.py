@@ -93,6 +93,9 @@ GDN_DECODE_B512 = Workload("gdn_decode_b512", batch=512, layers=24, position=655
                            extra={"state": "f16"})
 GDN_DECODE_B1 = Workload("gdn_decode_b1", batch=1, layers=24, position=65536, gains="ones",
                          extra={"state": "f32"})
+# GDN chunked prefill: one 256-token chunk per sequence at positions 65536.. (FP16 state)
+GDN_PREFILL_B512 = Workload("gdn_prefill_b512", batch=512, layers=24, position=65536,
+                            gains="ones", extra={"state": "f16", "chunk": 256})
 
 # Chunked prefill: one 256-token chunk per sequence at positions 65536..65791 on a
 # steady-state layer (full window and bank, empty pending block).
@@ -101,7 +104,7 @@ PREFILL_B64 = Workload("prefill_b64", batch=64, layers=8, position=65535, gains=
 
 WORKLOADS = {w.name: w for w in (TINY_STREAM, STEADY_B64, HEADLINE_B512, COMMIT_BURST_B512,
                                  LONG_STREAM_B1, HEADLINE_B512_FP8, GDN_DECODE_B512,
-                                 GDN_DECODE_B1, PREFILL_B512, PREFILL_B64)}
+                                 GDN_DECODE_B1, PREFILL_B512, PREFILL_B64, GDN_PREFILL_B512)}
 
 
 def key(wl: Workload | str, *names) -> StreamKey:
@@ -410,6 +413,23 @@ def gdn_x_np(wl: Workload, layer: int, b: int, step: int = 0) -> np.ndarray:
 
 def gdn_x_torch_(wl: Workload, layer: int, out, step: int = 0) -> None:
     normal_bf16_torch_(out, key(wl, layer, "x", step))
+
+
+def gdn_chunk_x_torch_(wl: Workload, layer: int, out) -> None:
+    """A chunk's projected inputs ``[B][C][8192]`` (BF16)."""
+    normal_bf16_torch_(out, key(wl, layer, "chunk_x"))
+
+
+def gdn_chunk_x_np(wl: Workload, layer: int, b: int, chunk: int) -> np.ndarray:
+    per = chunk * GDN_CONV_DIM
+    return normal_bf16_np(key(wl, layer, "chunk_x"), per, start=b * per).reshape(chunk,
+                                                                                 GDN_CONV_DIM)
+
+
+def gdn_chunk_gates(wl: Workload, layer: int, chunk: int):
+    """a, b ``[B][C][32]`` FP32 (host) of a chunk."""
+    return (normal_f32_np(key(wl, layer, "chunk_a"), (wl.batch, chunk, GDN_V_HEADS)),
+            normal_f32_np(key(wl, layer, "chunk_b"), (wl.batch, chunk, GDN_V_HEADS)))
 
 
 def gdn_gate_inputs(wl: Workload, layer: int, step: int = 0):

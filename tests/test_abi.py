@@ -197,3 +197,18 @@ def test_gdn_state_size_and_host_validation(lib):
     assert step(by(R._GdnStateC(24, 16)), 4, 0, 16, 16, 16, 16, by(pr), 16, None) == 2
     assert step(by(st), 4, 1, 16, 16, 16, 16, by(R._GdnParamsC(20, 16, 16)), 16, None) == 2
     assert step(by(st), 4, 0, 16, 16, 16, 16, by(pr), 40, None) == 2
+
+
+def test_gdn_prefill_host_validation(lib):
+    by = ctypes.byref
+    st = R._GdnStateC(16, 16)
+    pr = R._GdnParamsC(16, 16, 16)
+    pf = lib.gdn_prefill
+    assert pf(None, 4, 8, 0, 16, 16, 16, 16, by(pr), 16, None) == 1
+    assert pf(by(st), 4, 0, 0, 16, 16, 16, 16, by(pr), 16, None) == 1        # no tokens
+    assert pf(by(st), 4, 65537, 0, 16, 16, 16, 16, by(pr), 16, None) == 1    # past the maximum
+    assert pf(by(st), 4, 8, 3, 16, 16, 16, 16, by(pr), 16, None) == 1        # unknown dtype
+    assert pf(by(st), 0, 8, 0, 16, 16, 16, 16, by(pr), 16, None) == 1
+    assert pf(by(st), 4, 8, 0, 16, 16, 16, None, by(pr), 16, None) == 1      # no positions
+    assert pf(by(st), 4, 8, 0, 24, 16, 16, 16, by(pr), 16, None) == 2        # misaligned x
+    assert pf(by(st), 4, 8, 1, 16, 16, 16, 16, by(pr), 40, None) == 2        # misaligned o

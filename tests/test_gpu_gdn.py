@@ -190,3 +190,42 @@ def test_gdn_decode_b512_every_unit():
 
 def test_gdn_decode_b1_every_head():
     _full_size(W.GDN_DECODE_B1, 1)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+@pytest.mark.parametrize("B", [6, 20])  # the narrow and the wide column slices
+def test_gdn_prefill_equals_decode_steps(dtype, B):
+    """gdn_prefill(T tokens) leaves the matrices, the ring and the outputs exactly as T
+    gdn_decode_step calls do (chunks of 1, 3 and 37 tokens; positions 0 (empty ring),
+    1 and 70001); the first token's output also against the oracle."""
+    tag = f"gdn_prefill_{B}_{dtype}"
+    prm = _params(tag)
+    pd = _params_dev(prm)
+    for T in (1, 3, 37):
+        print(f"case: gdn prefill B={B} dtype={dtype} T={T}", flush=True)
+        st = _state(f"{tag}_{T}", B, dtype)
+        p0 = np.array([0, 1, 70001] * 8, np.int32)[:B]
+        x = synth.normal_bf16_np(synth.stream_key(tag, "x", T), B * T * 8192).reshape(B, T, 8192)
+        rng = synth.rng_np(synth.stream_key(tag, "ab", T))
+        a = (rng.standard_normal((B, T, 32)) * 2).astype(np.float32)
+        b = (rng.standard_normal((B, T, 32)) * 2).astype(np.float32)
+        chunk, steps = _upload(st), _upload(st)
+        o_chunk = torch.full((B, T, 32, 128), 7.0, dtype=torch.bfloat16, device=DEV)
+        R.gdn_prefill(chunk, B, T, torch.from_numpy(x.view(np.int16)).to(DEV), f32_dev(a),
+                      f32_dev(b), i32_dev(p0), pd, o_chunk)
+        o_steps = []
+        for i in range(T):
+            xi = torch.from_numpy(np.ascontiguousarray(x[:, i]).view(np.int16)).to(DEV)
+            o_steps.append(_step(steps, B, xi, f32_dev(np.ascontiguousarray(a[:, i])),
+                                 f32_dev(np.ascontiguousarray(b[:, i])), i32_dev(p0 + i), pd))
+        torch.cuda.synchronize()
+        assert torch.equal(chunk.S.view(torch.int16 if dtype == "f16" else torch.int32),
+                           steps.S.view(torch.int16 if dtype == "f16" else torch.int32)), "S"
+        assert torch.equal(chunk.conv.view(torch.int16), steps.conv.view(torch.int16)), "ring"
+        for i in range(T):
+            assert torch.equal(o_chunk[:, i].view(torch.int16), o_steps[i].view(torch.int16)), i
+        # the first token against the oracle (the state before it is known exactly)
+        ref = G.GdnState(st.S.copy(), st.conv.copy())
+        ref_o = G.decode_step(ref, x[:, 0], a[:, 0], b[:, 0], prm["conv_w"], prm["a_log"],
+                              prm["dt_bias"], p0)
+        assert_out_close(bits_host(o_chunk[:, 0]), ref_o, what=f"o T={T} token 0")
