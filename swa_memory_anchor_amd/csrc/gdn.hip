@@ -25,6 +25,11 @@
 #include "gdn.h"
 #include "rma_device.h"
 
+// No implicit fused multiply-adds in this file: every fma is written out, so the
+// decode step and the chunked prefill, which repeat the same per-token arithmetic
+// in different code, round identically.
+#pragma clang fp contract(off)
+
 namespace gdn {
 
 constexpr int kKH = GDN_K_HEADS;
@@ -56,6 +61,15 @@ struct Params {
 };
 
 __device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// An FP32 result rounded to FP16 (nearest even).  The empty asm hides where x came
+// from, so the compiler cannot merge the conversion into the fma that produced it
+// (v_fma_mix*_f16 round the exact product-sum once, not the FP32 result): every
+// matrix element is rounded to FP32 by its fma and then to FP16, in both kernels.
+__device__ __forceinline__ _Float16 to_f16(float x) {
+  asm("" : "+v"(x));
+  return static_cast<_Float16>(x);
+}
 
 // The inputs of one channel: all four ring slots (loaded without waiting for the
 // position, which only selects among them), the current input and the taps.
@@ -251,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void gdn_decode_kernel(Params pr) {
     } else {
       f16x8 hv;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) hv[j] = static_cast<_Float16>(fmaf(alpha, sv[j], kr * u[j]));
+      for (int j = 0; j < 8; ++j) hv[j] = to_f16(fmaf(alpha, sv[j], kr * u[j]));
       __builtin_nontemporal_store(__builtin_bit_cast(f32x4_t, hv),
                                   reinterpret_cast<f32x4_t *>(static_cast<_Float16 *>(pr.S) + e));
     }
@@ -304,6 +318,11 @@ __device__ __forceinline__ float conv_silu_hist(const float4 &w, const uint16_t 
   return acc / (1.f + expf(-acc));
 }
 
+// Tokens whose inputs (convolutions, norms, gates) are prepared together before
+// the recurrence walks them: none of these depend on the matrix, so they are formed
+// in parallel over the group's tokens instead of inside the serial token loop.
+constexpr int kGroup = 16;
+
 template <bool kF32, int kCW>
 __global__ __launch_bounds__(kThreads) void gdn_prefill_kernel(PrefillParams pr) {
   constexpr int kChunks = kCW / 8;
@@ -311,10 +330,16 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_kernel(PrefillParams pr)
   constexpr int kRows = kD / kRG;
   constexpr int kSlices = kD / kCW;
   constexpr int kWaves = kThreads / 64;
-  __shared__ float q_s[kD], k_s[kD], v_s[kD];
+  constexpr int kG = kGroup;
+  // per token of the group: q and k scaled by their inverse norms (q also by
+  // 1/sqrt(128)), v, and the scalars alpha, beta and k.q
+  __shared__ float qn_s[kG][kD], kn_s[kG][kD], v_s[kG][kD];
+  __shared__ float al_s[kG], be_s[kG], kq_s[kG];
   __shared__ float red[kWaves][2][kCW];
+  __shared__ float u_s[kCW];
 
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int slice = blockIdx.x % kSlices;
   const int bh = blockIdx.x / kSlices;
   const int b = bh / kVH, h = bh % kVH, kh = h / (kVH / kKH);
@@ -358,113 +383,170 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_kernel(PrefillParams pr)
   history_load(ring, cv, p0, h1);
   const float a_log = pr.a_log[h], dtb = pr.dt_bias[h];
 
-  // the token's inputs are fetched one token ahead, so their latency overlaps the
-  // previous token's work
-  auto fetch = [&](int i, uint16_t &x0, uint16_t &x1, float &ra, float &rb) {
-    const size_t tok = static_cast<size_t>(b) * T + i;
-    const uint16_t *xb = pr.x + tok * kCD;
-    x0 = xb[ch0];
-    x1 = t < kD ? xb[cv] : uint16_t(0);
-    ra = pr.a[tok * kVH + h];
-    rb = pr.b[tok * kVH + h];
-  };
-  uint16_t nx0, nx1;
-  float na, nb;
-  fetch(0, nx0, nx1, na, nb);
-  for (int i = 0; i < T; ++i) {
-    const size_t tok = static_cast<size_t>(b) * T + i;
-    const uint16_t x0 = nx0, x1 = nx1;
-    const float za = na + dtb;
-    const float zb = nb;
-    if (i + 1 < T) fetch(i + 1, nx0, nx1, na, nb);
-    const float y0 = conv_silu_hist(w0, h0, x0);
-    if (t < kD) {
-      q_s[t] = y0;
-      v_s[t] = conv_silu_hist(w1, h1, x1);
-    } else {
-      k_s[t - kD] = y0;
-    }
-    h0[0] = h0[1];
-    h0[1] = h0[2];
-    h0[2] = x0;
-    h1[0] = h1[1];
-    h1[1] = h1[2];
-    h1[2] = x1;
-    __syncthreads();
+  for (int base = 0; base < T; base += kG) {
+    const int G = min(kG, T - base);
+    const size_t tok0 = static_cast<size_t>(b) * T + base;
 
-    const float q0 = q_s[lane], q1 = q_s[lane + 64], k0 = k_s[lane], k1 = k_s[lane + 64];
-    const float sq = rma::wave_sum(q0 * q0 + q1 * q1);
-    const float sk = rma::wave_sum(k0 * k0 + k1 * k1);
-    const float sqk = rma::wave_sum(q0 * k0 + q1 * k1);
-    const float iq = (1.f / sqrtf(sq + kL2Eps)) * 0.08838834764831845f;  // 1/sqrt(128)
-    const float ik = 1.f / sqrtf(sk + kL2Eps);
-    const float kq = sqk * iq * ik;
-    const float softplus = fmaxf(za, 0.f) + log1pf(expf(-fabsf(za)));
-    const float alpha = expf(-expf(a_log) * softplus);
-    const float eb = expf(-fabsf(zb));
-    const float beta = zb >= 0.f ? 1.f / (1.f + eb) : eb / (1.f + eb);
-
-    float pk[8], pq[8];
+    // 1. the group's inputs, then each channel's convolutions in token order
+    uint16_t xa[kG], xv[kG];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) pk[j] = pq[j] = 0.f;
-#pragma unroll
-    for (int r = 0; r < kRows; ++r) {
-      const int row = rg + kRG * r;
-      const float kr = k_s[row] * ik, qr = q_s[row] * iq;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        pk[j] = fmaf(sv[r][j], kr, pk[j]);
-        pq[j] = fmaf(sv[r][j], qr, pq[j]);
+    for (int g = 0; g < kG; ++g) {
+      if (g < G) {
+        const uint16_t *xb = pr.x + (tok0 + g) * kCD;
+        xa[g] = xb[ch0];
+        xv[g] = t < kD ? xb[cv] : uint16_t(0);
       }
     }
-#pragma unroll
-    for (int off = kChunks; off < 64; off <<= 1) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        pk[j] += __shfl_xor(pk[j], off, 64);
-        pq[j] += __shfl_xor(pq[j], off, 64);
-      }
+    float ra = 0.f, rb = 0.f;  // gate inputs of token `lane`
+    if (lane < G) {
+      ra = pr.a[(tok0 + lane) * kVH + h];
+      rb = pr.b[(tok0 + lane) * kVH + h];
     }
-    if (lane < kChunks) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        red[wave][0][8 * c + j] = pk[j];
-        red[wave][1][8 * c + j] = pq[j];
+    for (int g = 0; g < kG; ++g) {
+      if (g < G) {
+        const float y0 = conv_silu_hist(w0, h0, xa[g]);
+        if (t < kD) {
+          qn_s[g][t] = y0;
+          v_s[g][t] = conv_silu_hist(w1, h1, xv[g]);
+        } else {
+          kn_s[g][t - kD] = y0;
+        }
+        h0[0] = h0[1];
+        h0[1] = h0[2];
+        h0[2] = xa[g];
+        h1[0] = h1[1];
+        h1[1] = h1[2];
+        h1[2] = xv[g];
       }
     }
     __syncthreads();
 
-    float u[8], o[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float tk = 0.f, tq = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        tk += red[w][0][8 * c + j];
-        tq += red[w][1][8 * c + j];
+    // 2. L2 norms, k.q and gates; wave w takes tokens w, w + 4, ...  The
+    // normalised q and k replace the raw ones (each lane rewrites what it read).
+    for (int g = wave; g < G; g += kWaves) {
+      const float q0 = qn_s[g][lane], q1 = qn_s[g][lane + 64];
+      const float k0 = kn_s[g][lane], k1 = kn_s[g][lane + 64];
+      const float sq = rma::wave_sum(q0 * q0 + q1 * q1);
+      const float sk = rma::wave_sum(k0 * k0 + k1 * k1);
+      const float sqk = rma::wave_sum(q0 * k0 + q1 * k1);
+      const float iq = (1.f / sqrtf(sq + kL2Eps)) * 0.08838834764831845f;  // 1/sqrt(128)
+      const float ik = 1.f / sqrtf(sk + kL2Eps);
+      const float kq = sqk * iq * ik;
+      const float za = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ra), g)) + dtb;
+      const float zb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rb), g));
+      const float softplus = fmaxf(za, 0.f) + log1pf(expf(-fabsf(za)));
+      const float alpha = expf(-expf(a_log) * softplus);
+      const float eb = expf(-fabsf(zb));
+      const float beta = zb >= 0.f ? 1.f / (1.f + eb) : eb / (1.f + eb);
+      qn_s[g][lane] = q0 * iq;
+      qn_s[g][lane + 64] = q1 * iq;
+      kn_s[g][lane] = k0 * ik;
+      kn_s[g][lane + 64] = k1 * ik;
+      if (lane == 0) {
+        al_s[g] = alpha;
+        be_s[g] = beta;
+        kq_s[g] = kq;
       }
-      u[j] = beta * (v_s[col + j] - alpha * tk);
-      o[j] = fmaf(alpha, tq, u[j] * kq);
     }
+    __syncthreads();
+
+    // 3. the recurrence over the group's tokens
+    for (int g = 0; g < G; ++g) {
+      const size_t tok = tok0 + g;
+      float kr[kRows];
+      float pk[8], pq[8];
 #pragma unroll
-    for (int r = 0; r < kRows; ++r) {
-      const float kr = k_s[rg + kRG * r] * ik;
+      for (int j = 0; j < 8; ++j) pk[j] = pq[j] = 0.f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float nv = fmaf(alpha, sv[r][j], kr * u[j]);
-        // the stored value, as the next step would read it back
-        sv[r][j] = kF32 ? nv : static_cast<float>(static_cast<_Float16>(nv));
+      for (int r = 0; r < kRows; ++r) {
+        const int row = rg + kRG * r;
+        kr[r] = kn_s[g][row];
+        const float qr = qn_s[g][row];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          pk[j] = fmaf(sv[r][j], kr[r], pk[j]);
+          pq[j] = fmaf(sv[r][j], qr, pq[j]);
+        }
+      }
+      if constexpr (kChunks == 16) {
+        // the lanes of one column chunk differ by 16 and 32: pair sums across
+        // 16-lane rows (v_permlane16_swap), then across halves (v_permlane32_swap),
+        // two values per swap.  Each sum adds the same pairs, in the same tree, as
+        // a butterfly over lane offsets 16 then 32.
+        float pv[16], r1[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          pv[j] = pk[j];
+          pv[8 + j] = pq[j];
+        }
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+          const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(pv[2 * n]),
+                                                          __float_as_uint(pv[2 * n + 1]), false,
+                                                          false);
+          r1[n] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        }
+        // lane l of sum n: value 4n + l / 16 (S^T k for 0..7, then S^T q), chunk l % 16
+        const int cl = lane & 15, sub = lane >> 4;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(r1[2 * n]),
+                                                          __float_as_uint(r1[2 * n + 1]), false,
+                                                          false);
+          const int m = 4 * n + sub;
+          red[wave][m >> 3][8 * cl + (m & 7)] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        }
+      } else {
+#pragma unroll
+        for (int off = kChunks; off < 64; off <<= 1) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            pk[j] += __shfl_xor(pk[j], off, 64);
+            pq[j] += __shfl_xor(pq[j], off, 64);
+          }
+        }
+        if (lane < kChunks) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            red[wave][0][8 * c + j] = pk[j];
+            red[wave][1][8 * c + j] = pq[j];
+          }
+        }
+      }
+      __syncthreads();
+
+      // u and the output, one column per thread
+      if (t < kCW) {
+        const float alpha = al_s[g], beta = be_s[g], kq = kq_s[g];
+        float tk = 0.f, tq = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          tk += red[w][0][t];
+          tq += red[w][1][t];
+        }
+        const int cc = slice * kCW + t;
+        const float u = beta * (v_s[g][cc] - alpha * tk);
+        const float o = fmaf(alpha, tq, u * kq);
+        u_s[t] = u;
+        pr.o[(tok * kVH + h) * kD + cc] = static_cast<uint16_t>(rma::f32_to_bf16(o));
+      }
+      __syncthreads();
+
+      const float alpha = al_s[g];
+      float u[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) u[j] = u_s[8 * c + j];
+#pragma unroll
+      for (int r = 0; r < kRows; ++r) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float nv = fmaf(alpha, sv[r][j], kr[r] * u[j]);
+          // the stored value, as the next step would read it back
+          sv[r][j] = kF32 ? nv : static_cast<float>(to_f16(nv));
+        }
       }
     }
-    if (rg == 0) {
-      uint4 ov;
-      ov.x = rma::pack_bf16x2(o[0], o[1]);
-      ov.y = rma::pack_bf16x2(o[2], o[3]);
-      ov.z = rma::pack_bf16x2(o[4], o[5]);
-      ov.w = rma::pack_bf16x2(o[6], o[7]);
-      *reinterpret_cast<uint4 *>(pr.o + (tok * kVH + h) * kD + col) = ov;
-    }
-    __syncthreads();  // q_s / k_s / v_s / red are rewritten by the next token
   }
 
 #pragma unroll

@@ -192,16 +192,26 @@ def test_gdn_decode_b1_every_head():
     _full_size(W.GDN_DECODE_B1, 1)
 
 
+def _same_bits(x, y, what):
+    """Bit equality with a short message: count of differing elements and the first."""
+    ne = (x != y).reshape(-1)
+    n = int(ne.sum())
+    if n:
+        i = int(torch.nonzero(ne)[0])
+        raise AssertionError(f"{what}: {n} of {ne.numel()} elements differ; first at flat index "
+                             f"{i}: {int(x.reshape(-1)[i])} vs {int(y.reshape(-1)[i])}")
+
+
 @pytest.mark.parametrize("dtype", ["f16", "f32"])
 @pytest.mark.parametrize("B", [6, 20])  # the narrow and the wide column slices
 def test_gdn_prefill_equals_decode_steps(dtype, B):
     """gdn_prefill(T tokens) leaves the matrices, the ring and the outputs exactly as T
-    gdn_decode_step calls do (chunks of 1, 3 and 37 tokens; positions 0 (empty ring),
+    gdn_decode_step calls do (chunks of 1, 3, 16 and 37 tokens; positions 0 (empty ring),
     1 and 70001); the first token's output also against the oracle."""
     tag = f"gdn_prefill_{B}_{dtype}"
     prm = _params(tag)
     pd = _params_dev(prm)
-    for T in (1, 3, 37):
+    for T in (1, 3, 16, 37):
         print(f"case: gdn prefill B={B} dtype={dtype} T={T}", flush=True)
         st = _state(f"{tag}_{T}", B, dtype)
         p0 = np.array([0, 1, 70001] * 8, np.int32)[:B]
@@ -219,11 +229,11 @@ def test_gdn_prefill_equals_decode_steps(dtype, B):
             o_steps.append(_step(steps, B, xi, f32_dev(np.ascontiguousarray(a[:, i])),
                                  f32_dev(np.ascontiguousarray(b[:, i])), i32_dev(p0 + i), pd))
         torch.cuda.synchronize()
-        assert torch.equal(chunk.S.view(torch.int16 if dtype == "f16" else torch.int32),
-                           steps.S.view(torch.int16 if dtype == "f16" else torch.int32)), "S"
-        assert torch.equal(chunk.conv.view(torch.int16), steps.conv.view(torch.int16)), "ring"
+        ib = torch.int16 if dtype == "f16" else torch.int32
+        _same_bits(chunk.S.view(ib), steps.S.view(ib), "S")
+        _same_bits(chunk.conv.view(torch.int16), steps.conv.view(torch.int16), "ring")
         for i in range(T):
-            assert torch.equal(o_chunk[:, i].view(torch.int16), o_steps[i].view(torch.int16)), i
+            _same_bits(o_chunk[:, i].view(torch.int16), o_steps[i].view(torch.int16), f"o[{i}]")
         # the first token against the oracle (the state before it is known exactly)
         ref = G.GdnState(st.S.copy(), st.conv.copy())
         ref_o = G.decode_step(ref, x[:, 0], a[:, 0], b[:, 0], prm["conv_w"], prm["a_log"],
