@@ -318,6 +318,30 @@ __device__ __forceinline__ float conv_silu_hist(const float4 &w, const uint16_t 
   return acc / (1.f + expf(-acc));
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// fmaf(a, h, c) for the FP16 value h held in the low (kHi false) or high half of
+// the packed register p, as one v_fma_mix_f32: the instruction widens h exactly
+// and rounds the fma to FP32 once, as fmaf does.  
+template <bool kHi>
+__device__ __forceinline__ float fma_f16(float a, uint32_t p, float c) {
+  float d;
+  if constexpr (kHi)
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,1,0] op_sel_hi:[0,1,0]"
+        : "=v"(d)
+        : "v"(a), "v"(p), "v"(c));
+  else
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[0,1,0]" : "=v"(d) : "v"(a), "v"(p), "v"(c));
+  return d;
+}
+
+// Two FP32 values rounded to FP16 (nearest even) and packed, lo in the low half.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  uint32_t d;
+  asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(d) : "v"(lo), "v"(hi));
+  return d;
+}
+
 // Tokens whose inputs (convolutions, norms, gates) are prepared together before
 // the recurrence walks them: none of these depend on the matrix, so they are formed
 // in parallel over the group's tokens instead of inside the serial token loop.
@@ -348,8 +372,11 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_kernel(PrefillParams pr)
   const size_t head = static_cast<size_t>(bh) * kD * kD;
   const int T = pr.n_tokens;
 
-  // the matrix slice, as FP32 values of the stored elements
-  float sv[kRows][8];
+  // the matrix slice in its storage type: FP32 values, or FP16 pairs packed in
+  // 32-bit words (columns 2k and 2k+1 of a row in word k), which feed the FP32
+  // arithmetic through v_fma_mix_f32 with no separate widening
+  float sf[kF32 ? kRows : 1][8];
+  uint32_t sw[kF32 ? 1 : kRows][4];
 #pragma unroll
   for (int i = 0; i < kRows; ++i) {
     const size_t e = head + static_cast<size_t>(rg + kRG * i) * kD + col;
@@ -358,15 +385,15 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_kernel(PrefillParams pr)
       const f32x4_t lo = __builtin_nontemporal_load(src), hi = __builtin_nontemporal_load(src + 1);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        sv[i][j] = lo[j];
-        sv[i][4 + j] = hi[j];
+        sf[i][j] = lo[j];
+        sf[i][4 + j] = hi[j];
       }
     } else {
-      const f16x8 hv = __builtin_bit_cast(
-          f16x8, __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(
+      const u32x4 w = __builtin_bit_cast(
+          u32x4, __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(
                      static_cast<const _Float16 *>(pr.S) + e)));
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sv[i][j] = static_cast<float>(hv[j]);
+      for (int k = 0; k < 4; ++k) sw[i][k] = w[k];
     }
   }
 
@@ -463,10 +490,20 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_kernel(PrefillParams pr)
         const int row = rg + kRG * r;
         kr[r] = kn_s[g][row];
         const float qr = qn_s[g][row];
+        if constexpr (kF32) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          pk[j] = fmaf(sv[r][j], kr[r], pk[j]);
-          pq[j] = fmaf(sv[r][j], qr, pq[j]);
+          for (int j = 0; j < 8; ++j) {
+            pk[j] = fmaf(sf[r][j], kr[r], pk[j]);
+            pq[j] = fmaf(sf[r][j], qr, pq[j]);
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            pk[2 * k] = fma_f16<false>(kr[r], sw[r][k], pk[2 * k]);
+            pk[2 * k + 1] = fma_f16<true>(kr[r], sw[r][k], pk[2 * k + 1]);
+            pq[2 * k] = fma_f16<false>(qr, sw[r][k], pq[2 * k]);
+            pq[2 * k + 1] = fma_f16<true>(qr, sw[r][k], pq[2 * k + 1]);
+          }
         }
       }
       if constexpr (kChunks == 16) {
@@ -537,13 +574,17 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_kernel(PrefillParams pr)
       float u[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) u[j] = u_s[8 * c + j];
+      // the new elements, rounded as stored (the next step reads them back)
 #pragma unroll
       for (int r = 0; r < kRows; ++r) {
+        if constexpr (kF32) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float nv = fmaf(alpha, sv[r][j], kr[r] * u[j]);
-          // the stored value, as the next step would read it back
-          sv[r][j] = kF32 ? nv : static_cast<float>(to_f16(nv));
+          for (int j = 0; j < 8; ++j) sf[r][j] = fmaf(alpha, sf[r][j], kr[r] * u[j]);
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            sw[r][k] = pack_f16x2(fma_f16<false>(alpha, sw[r][k], kr[r] * u[2 * k]),
+                                  fma_f16<true>(alpha, sw[r][k], kr[r] * u[2 * k + 1]));
         }
       }
     }
@@ -556,17 +597,15 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_kernel(PrefillParams pr)
       f32x4_t lo, hi;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        lo[j] = sv[i][j];
-        hi[j] = sv[i][4 + j];
+        lo[j] = sf[i][j];
+        hi[j] = sf[i][4 + j];
       }
       f32x4_t *dst = reinterpret_cast<f32x4_t *>(static_cast<float *>(pr.S) + e);
       __builtin_nontemporal_store(lo, dst);
       __builtin_nontemporal_store(hi, dst + 1);
     } else {
-      f16x8 hv;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) hv[j] = static_cast<_Float16>(sv[i][j]);
-      __builtin_nontemporal_store(__builtin_bit_cast(f32x4_t, hv),
+      const u32x4 w = {sw[i][0], sw[i][1], sw[i][2], sw[i][3]};
+      __builtin_nontemporal_store(__builtin_bit_cast(f32x4_t, w),
                                   reinterpret_cast<f32x4_t *>(static_cast<_Float16 *>(pr.S) + e));
     }
   }
