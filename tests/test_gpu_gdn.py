@@ -239,3 +239,72 @@ def test_gdn_prefill_equals_decode_steps(dtype, B):
         ref_o = G.decode_step(ref, x[:, 0], a[:, 0], b[:, 0], prm["conv_w"], prm["a_log"],
                               prm["dt_bias"], p0)
         assert_out_close(bits_host(o_chunk[:, 0]), ref_o, what=f"o T={T} token 0")
+
+
+def test_gdn_prefill_b512_full_size():
+    """gdn_prefill in the benchmark's call (gdn_prefill_b512, layer 0: 512 sequences x
+    256 tokens, FP16 matrices, one 128-column slice per head): the matrices, the ring
+    and all 512 x 256 outputs equal those of 256 gdn_decode_step calls bit for bit.
+    Three sampled sequences are then checked against the oracle: one-step checks at
+    tokens 0, 128 and 255 (the oracle starts from the GPU's state before the token),
+    and the whole 256-token trajectory from the same initial state, whose distance
+    per head is at most 256 times the norm of a step's bound (the step map is
+    non-expansive; see test_gdn_stream_from_zero_state)."""
+    wl = W.GDN_PREFILL_B512
+    B, T, layer = wl.batch, wl.extra["chunk"], 0
+    print(f"case: {wl.name} full size B={B} T={T}", flush=True)
+    chunk = R.GdnState(torch.empty(B, 32, 128, 128, dtype=torch.float16, device=DEV),
+                       torch.empty(B, 4, 8192, dtype=torch.bfloat16, device=DEV))
+    W.gdn_state_torch_(wl, layer, chunk.S)
+    W.gdn_conv_torch_(wl, layer, chunk.conv)
+    steps = R.GdnState(chunk.S.clone(), chunk.conv.clone())
+    x = torch.empty(B, T, 8192, dtype=torch.bfloat16, device=DEV)
+    W.gdn_chunk_x_torch_(wl, layer, x)
+    a_h, b_h = W.gdn_chunk_gates(wl, layer, T)
+    a, b = f32_dev(a_h), f32_dev(b_h)
+    prm = W.gdn_params(wl, layer)
+    pd = _params_dev(prm)
+    pos = torch.full((B,), wl.position, dtype=torch.int32, device=DEV)
+    o_chunk = torch.full((B, T, 32, 128), 7.0, dtype=torch.bfloat16, device=DEV)
+    R.gdn_prefill(chunk, B, T, x, a, b, pos, pd, o_chunk)
+
+    samples = [0, 257, 511]
+    checks = (0, 128, T - 1)
+    snap = {}
+    o_i = torch.empty(B, 32, 128, dtype=torch.bfloat16, device=DEV)
+    for i in range(T):
+        if i in checks:
+            snap[i] = (steps.S[samples].cpu().numpy(), bits_host(steps.conv[samples]).copy())
+        R.gdn_decode_step(steps, B, x[:, i].contiguous(), a[:, i].contiguous(),
+                          b[:, i].contiguous(), pos + i, pd, o_i)
+        _same_bits(o_chunk[:, i].view(torch.int16), o_i.view(torch.int16), f"o[{i}]")
+    _same_bits(chunk.S.view(torch.int16), steps.S.view(torch.int16), "S")
+    _same_bits(chunk.conv.view(torch.int16), steps.conv.view(torch.int16), "ring")
+    print("chunk equals 256 decode steps bit for bit; oracle on sampled sequences", flush=True)
+
+    got_S = chunk.S[samples].cpu().numpy()
+    for k, s in enumerate(samples):
+        xs = W.gdn_chunk_x_np(wl, layer, s, T)
+        for i in checks:
+            S0, conv0 = snap[i]
+            st = G.GdnState(S0[k:k + 1].copy(), conv0[k:k + 1].copy())
+            ref_o = G.decode_step(st, xs[i][None], a_h[s:s + 1, i], b_h[s:s + 1, i],
+                                  prm["conv_w"], prm["a_log"], prm["dt_bias"],
+                                  np.array([wl.position + i], np.int32))
+            assert_out_close(bits_host(o_chunk[s, i])[None], ref_o, what=f"seq {s} o[{i}]")
+            if i == T - 1:
+                assert_state_close(got_S[k:k + 1], st.S, what=f"seq {s} S after token {i}")
+        # the trajectory from the initial state
+        S0, conv0 = snap[0]
+        ref = G.GdnState(S0[k:k + 1].copy(), conv0[k:k + 1].copy())
+        for i in range(T):
+            G.decode_step(ref, xs[i][None], a_h[s:s + 1, i], b_h[s:s + 1, i], prm["conv_w"],
+                          prm["a_log"], prm["dt_bias"], np.array([wl.position + i], np.int32))
+        worst = 0.0
+        for h in range(32):
+            r = ref.S[0, h]
+            d = np.linalg.norm(got_S[k, h].astype(np.float64) - r.astype(np.float64))
+            lim = T * np.linalg.norm(np.broadcast_to(state_bound(r, whole=True), (128, 128)))
+            worst = max(worst, d / lim)
+        print(f"seq {s}: 256-token trajectory, max head distance / bound {worst:.2e}", flush=True)
+        assert worst <= 1.0, s
