@@ -40,10 +40,13 @@ TRAFFIC_FILES = {
     "headline_b512_fp8": os.path.join(ROOT, "profiles",
                                       "decode_attn_fp8_headline_b512_fp8_traffic.txt"),
     "gdn_decode_b512": os.path.join(ROOT, "profiles", "gdn_decode_gdn_decode_b512_traffic.txt"),
+    "gdn_prefill_b512": os.path.join(ROOT, "profiles", "gdn_prefill_gdn_prefill_b512_traffic.txt"),
+    "commit_burst_b512": os.path.join(ROOT, "profiles", "score_commit_burst_b512_traffic.txt"),
 }
 KERNEL_SOURCES = ("swa_memory_anchor_amd/csrc/decode_attn.hip",
                   "swa_memory_anchor_amd/csrc/rma_device.h")
 GDN_SOURCES = ("swa_memory_anchor_amd/csrc/gdn.hip", "swa_memory_anchor_amd/csrc/rma_device.h")
+SCORE_SOURCES = ("swa_memory_anchor_amd/csrc/score.hip", "swa_memory_anchor_amd/csrc/rma_device.h")
 
 
 def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
@@ -64,7 +67,8 @@ def measured_traffic(workload: str, units_per_launch: int):
         if "=" in line and not line.lstrip().startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    sources = GDN_SOURCES if workload.startswith("gdn") else KERNEL_SOURCES
+    sources = (GDN_SOURCES if workload.startswith("gdn") else
+               SCORE_SOURCES if workload.startswith("commit") else KERNEL_SOURCES)
     if kv.get("kernel_source_sha256") != kernel_source_hash(sources):
         return None
     if int(kv.get("units_per_launch", -1)) != units_per_launch:
@@ -239,7 +243,8 @@ def bench_commit_burst(args):
         "config": {"workload": wl.name, "batch": B, "layers": L, "rows_per_layer": rows},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
                      "peak": FP32_MATRIX_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / FP32_MATRIX_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(tflops / FP32_MATRIX_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(wl.name, B),
                      "kernel": "score_kernel", "avg_launch_ms": round(s_avg / L, 4)},
         "commit": {"avg_launch_us": round(c_avg * 1e3, 1),
                    "admitted_rows_per_layer": admitted // L,
@@ -777,7 +782,7 @@ def bench_gdn_prefill(args):
                    "positions": [wl.position, wl.position + C - 1], "state": "f16"},
         "roofline": {"bound": "alu", "achieved": round(tflops, 2), "peak": FP32_VECTOR_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / FP32_VECTOR_PEAK_TFLOPS, 4),
-                     "traffic": None, "kernel": "gdn_prefill_kernel",
+                     "traffic": measured_traffic(wl.name, B), "kernel": "gdn_prefill_kernel",
                      "avg_launch_ms": round(avg_launch, 4)},
     }
 
