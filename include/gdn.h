@@ -70,7 +70,9 @@ size_t gdn_layer_state_bytes(int32_t batch, int32_t state_dtype);
  *   pos     i32  [B]        the token's position (>= 0; selects the ring slot);
  *   o       bf16 [B][32][128] output, o = S^T q per value head (before the model's
  *                           gated output norm).
- * Updates st->S in place and stores x into ring slot pos mod 4.  Errors:
+ * Updates st->S in place and stores x into ring slot pos mod 4.  Each new matrix
+ * element is one FP32 fused multiply-add; FP16 state stores that FP32 value rounded
+ * to nearest even.  Errors:
  * RMA_E_ARG (null pointer, batch outside 1..RMA_MAX_BATCH, unknown dtype),
  * RMA_E_ALIGN (S, conv, x, o or conv_w not 16-byte aligned), RMA_E_HIP.
  */
