@@ -308,3 +308,33 @@ def test_gdn_prefill_b512_full_size():
             worst = max(worst, d / lim)
         print(f"seq {s}: 256-token trajectory, max head distance / bound {worst:.2e}", flush=True)
         assert worst <= 1.0, s
+
+
+@pytest.mark.parametrize("B,dtype,T", [(1, "f32", 4096), (16, "f16", 1024)])
+def test_gdn_prefill_long_chunks(B, dtype, T):
+    """Long chunks (256 and 64 groups of 16 tokens) at the batch-1 configuration (FP32,
+    32-column slices) and the smallest wide batch (FP16, one slice per head): matrices,
+    ring and every output equal T gdn_decode_step calls bit for bit."""
+    tag = f"gdn_prefill_long_{B}_{dtype}"
+    print(f"case: gdn prefill long chunk B={B} dtype={dtype} T={T}", flush=True)
+    prm = _params(tag)
+    pd = _params_dev(prm)
+    st = _state(tag, B, dtype)
+    p0 = np.array([5, 70001, 0, 3] * 4, np.int32)[:B]
+    x = torch.empty(B, T, 8192, dtype=torch.bfloat16, device=DEV)
+    C.normal_bf16_torch_(x, synth.stream_key(tag, "x"))
+    rng = synth.rng_np(synth.stream_key(tag, "ab"))
+    a = f32_dev((rng.standard_normal((B, T, 32)) * 2).astype(np.float32))
+    b = f32_dev((rng.standard_normal((B, T, 32)) * 2).astype(np.float32))
+    pos = i32_dev(p0)
+    chunk, steps = _upload(st), _upload(st)
+    o_chunk = torch.full((B, T, 32, 128), 7.0, dtype=torch.bfloat16, device=DEV)
+    R.gdn_prefill(chunk, B, T, x, a, b, pos, pd, o_chunk)
+    o_i = torch.empty(B, 32, 128, dtype=torch.bfloat16, device=DEV)
+    for i in range(T):
+        R.gdn_decode_step(steps, B, x[:, i].contiguous(), a[:, i].contiguous(),
+                          b[:, i].contiguous(), pos + i, pd, o_i)
+        _same_bits(o_chunk[:, i].view(torch.int16), o_i.view(torch.int16), f"o[{i}]")
+    ib = torch.int16 if dtype == "f16" else torch.int32
+    _same_bits(chunk.S.view(ib), steps.S.view(ib), "S")
+    _same_bits(chunk.conv.view(torch.int16), steps.conv.view(torch.int16), "ring")
