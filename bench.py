@@ -710,17 +710,19 @@ def cpu_baseline_long_stream(wl, budget_s: float):
 
 
 def bench_gdn_prefill(args):
-    """One 256-token chunk per sequence through the 24 Gated DeltaNet layers at batch
-    512 (24 dependent gdn_prefill launches, FP16 matrices).  Each layer has its own
-    state; the chunk inputs (2 GiB of projected inputs and the gates) are drawn once
-    and fed to every layer (values do not change the work)."""
+    """One 256-token chunk per sequence through the 24 Gated DeltaNet layers (24
+    dependent gdn_prefill launches): batch 512 with FP16 matrices, or batch 1 with
+    FP32 ones.  Each layer has its own state; the chunk inputs (2 GiB of projected
+    inputs and the gates at batch 512) are drawn once and fed to every layer (values
+    do not change the work)."""
     import torch
 
     import swa_memory_anchor_amd as R
     from synth import workloads as W
 
-    wl = W.GDN_PREFILL_B512
+    wl = W.WORKLOADS[args.workload]
     B, L, C, dev = wl.batch, wl.layers, wl.extra["chunk"], "cuda"
+    sdt = torch.float16 if wl.extra["state"] == "f16" else torch.float32
     stream = torch.cuda.current_stream()
     x = torch.empty(B, C, 8192, dtype=torch.bfloat16, device=dev)
     W.gdn_chunk_x_torch_(wl, 0, x)
@@ -730,7 +732,7 @@ def bench_gdn_prefill(args):
     o = torch.empty(B, C, 32, 128, dtype=torch.bfloat16, device=dev)
     layers = []
     for layer in range(L):
-        st = R.GdnState(torch.empty(B, 32, 128, 128, dtype=torch.float16, device=dev),
+        st = R.GdnState(torch.empty(B, 32, 128, 128, dtype=sdt, device=dev),
                         torch.empty(B, 4, 8192, dtype=torch.bfloat16, device=dev))
         W.gdn_state_torch_(wl, layer, st.S)
         W.gdn_conv_torch_(wl, layer, st.conv)
@@ -776,10 +778,10 @@ def bench_gdn_prefill(args):
         "warmup": args.warmup,
         "ms_per_step": round(step_ms, 4),
         "higher_is_better": True,
-        "dtype": "f16 state, f32 math",
+        "dtype": "f16 state, f32 math" if wl.extra["state"] == "f16" else "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "layers": L, "chunk": C,
-                   "positions": [wl.position, wl.position + C - 1], "state": "f16"},
+                   "positions": [wl.position, wl.position + C - 1], "state": wl.extra["state"]},
         "roofline": {"bound": "alu", "achieved": round(tflops, 2), "peak": FP32_VECTOR_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / FP32_VECTOR_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic(wl.name, B), "kernel": "gdn_prefill_kernel",
@@ -825,7 +827,7 @@ def main() -> int:
                     choices=["headline_b512", "headline_b512_fp8", "steady_b64", "batch1",
                              "commit_burst_b512", "long_stream_b1", "prefill_b512",
                              "prefill_b64", "gdn_decode_b512", "gdn_decode_b1",
-                             "gdn_prefill_b512"])
+                             "gdn_prefill_b512", "gdn_prefill_b1"])
     ap.add_argument("--stream-tokens", type=int, default=16384,
                     help="long_stream_b1: tokens streamed (the second half is timed)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
@@ -864,7 +866,7 @@ def main() -> int:
     if args.workload.startswith("prefill"):
         print(json.dumps(bench_prefill(args)))
         return 0
-    if args.workload == "gdn_prefill_b512":
+    if args.workload.startswith("gdn_prefill"):
         print(json.dumps(bench_gdn_prefill(args)))
         return 0
     if args.workload.startswith("gdn"):

@@ -71,6 +71,80 @@ __device__ __forceinline__ _Float16 to_f16(float x) {
   return static_cast<_Float16>(x);
 }
 
+// Lane moves for the reductions below: a DPP move within 16-lane rows (kCtrl is the
+// DPP control: 0xB1 and 0x4E exchange lanes 1 and 2 apart inside groups of four,
+// 0x141 mirrors each half row, 0x140 each row, 0x12n rotates a row by n lanes),
+// and the two gfx950 swaps between 16-lane rows and between 32-lane halves.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+
+// The sum over the wave, the same value in every lane: lanes 1 and 2 apart inside
+// groups of four, then the other four of each eight, the other eight of each row
+// (the row mirrors), then across rows and halves (lane swaps).  No LDS round trips.
+__device__ __forceinline__ float wave_total(float v) {
+  v += dpp_mov<0xB1>(v);
+  v += dpp_mov<0x4E>(v);
+  v += dpp_mov<0x141>(v);
+  v += dpp_mov<0x140>(v);
+  {
+    const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                     false);
+    v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                   false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+// One wave's column sums: the partials pk[j] (S^T k) and pq[j] (S^T q) of columns
+// 8c..8c+7 are added over the lanes that share the chunk c (lanes kChunks apart),
+// and the totals go to red[0][8c + j] and red[1][8c + j].  The pairs are those of
+// a butterfly over lane offsets kChunks, 2 kChunks, ... (smallest first): offsets 4
+// and 8 by rotating 16-lane rows (with 4 chunks; the sum is complete in the lanes
+// whose row position is 12..15), 16 and 32 by v_permlane16_swap and
+// v_permlane32_swap, two values per swap.
+template <int kChunks, int kCW>
+__device__ __forceinline__ void column_sums(float (&pk)[8], float (&pq)[8], float (*red)[kCW],
+                                            int lane) {
+  static_assert(kChunks == 4 || kChunks == 16, "column chunks per slice");
+  if constexpr (kChunks == 4) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      pk[j] += dpp_mov<0x124>(pk[j]);
+      pq[j] += dpp_mov<0x124>(pq[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      pk[j] += dpp_mov<0x128>(pk[j]);
+      pq[j] += dpp_mov<0x128>(pq[j]);
+    }
+  }
+  float pv[16], r1[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    pv[j] = pk[j];
+    pv[8 + j] = pq[j];
+  }
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(pv[2 * n]),
+                                                     __float_as_uint(pv[2 * n + 1]), false, false);
+    r1[n] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
+  // lane l of sum n: value 4n + l / 16 (S^T k for 0..7, then S^T q) of chunk l % kChunks
+  const int cl = lane & (kChunks - 1), sub = lane >> 4;
+  const bool writer = kChunks == 16 || ((lane >> 2) & 3) == 3;
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(r1[2 * n]),
+                                                     __float_as_uint(r1[2 * n + 1]), false, false);
+    const int m = 4 * n + sub;
+    if (writer) red[m >> 3][8 * cl + (m & 7)] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
+}
+
 // The inputs of one channel: all four ring slots (loaded without waiting for the
 // position, which only selects among them), the current input and the taps.
 struct ConvIn {
@@ -184,9 +258,9 @@ __global__ __launch_bounds__(kThreads) void gdn_decode_kernel(Params pr) {
 
   // L2 norms and k.q (every wave forms them for itself), gates
   const float q0 = q_s[lane], q1 = q_s[lane + 64], k0 = k_s[lane], k1 = k_s[lane + 64];
-  const float sq = rma::wave_sum(q0 * q0 + q1 * q1);
-  const float sk = rma::wave_sum(k0 * k0 + k1 * k1);
-  const float sqk = rma::wave_sum(q0 * k0 + q1 * k1);
+  const float sq = wave_total(q0 * q0 + q1 * q1);
+  const float sk = wave_total(k0 * k0 + k1 * k1);
+  const float sqk = wave_total(q0 * k0 + q1 * k1);
   const float iq = (1.f / sqrtf(sq + kL2Eps)) * 0.08838834764831845f;  // 1/sqrt(128)
   const float ik = 1.f / sqrtf(sk + kL2Eps);
   const float kq = sqk * iq * ik;
@@ -214,22 +288,7 @@ __global__ __launch_bounds__(kThreads) void gdn_decode_kernel(Params pr) {
       pq[j] = fmaf(e[j], qr, pq[j]);
     }
   }
-  // lanes that share a column chunk differ by multiples of kChunks
-#pragma unroll
-  for (int off = kChunks; off < 64; off <<= 1) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      pk[j] += __shfl_xor(pk[j], off, 64);
-      pq[j] += __shfl_xor(pq[j], off, 64);
-    }
-  }
-  if (lane < kChunks) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      red[wave][0][8 * c + j] = pk[j];
-      red[wave][1][8 * c + j] = pq[j];
-    }
-  }
+  column_sums<kChunks, kCW>(pk, pq, red[wave], lane);
   __syncthreads();
 
   // 4. u, the output, and the new matrix
@@ -454,9 +513,9 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_kernel(PrefillParams pr)
     for (int g = wave; g < G; g += kWaves) {
       const float q0 = qn_s[g][lane], q1 = qn_s[g][lane + 64];
       const float k0 = kn_s[g][lane], k1 = kn_s[g][lane + 64];
-      const float sq = rma::wave_sum(q0 * q0 + q1 * q1);
-      const float sk = rma::wave_sum(k0 * k0 + k1 * k1);
-      const float sqk = rma::wave_sum(q0 * k0 + q1 * k1);
+      const float sq = wave_total(q0 * q0 + q1 * q1);
+      const float sk = wave_total(k0 * k0 + k1 * k1);
+      const float sqk = wave_total(q0 * k0 + q1 * k1);
       const float iq = (1.f / sqrtf(sq + kL2Eps)) * 0.08838834764831845f;  // 1/sqrt(128)
       const float ik = 1.f / sqrtf(sk + kL2Eps);
       const float kq = sqk * iq * ik;
@@ -506,51 +565,7 @@ __global__ __launch_bounds__(kThreads) void gdn_prefill_kernel(PrefillParams pr)
           }
         }
       }
-      if constexpr (kChunks == 16) {
-        // the lanes of one column chunk differ by 16 and 32: pair sums across
-        // 16-lane rows (v_permlane16_swap), then across halves (v_permlane32_swap),
-        // two values per swap.  Each sum adds the same pairs, in the same tree, as
-        // a butterfly over lane offsets 16 then 32.
-        float pv[16], r1[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          pv[j] = pk[j];
-          pv[8 + j] = pq[j];
-        }
-#pragma unroll
-        for (int n = 0; n < 8; ++n) {
-          const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(pv[2 * n]),
-                                                          __float_as_uint(pv[2 * n + 1]), false,
-                                                          false);
-          r1[n] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-        }
-        // lane l of sum n: value 4n + l / 16 (S^T k for 0..7, then S^T q), chunk l % 16
-        const int cl = lane & 15, sub = lane >> 4;
-#pragma unroll
-        for (int n = 0; n < 4; ++n) {
-          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(r1[2 * n]),
-                                                          __float_as_uint(r1[2 * n + 1]), false,
-                                                          false);
-          const int m = 4 * n + sub;
-          red[wave][m >> 3][8 * cl + (m & 7)] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-        }
-      } else {
-#pragma unroll
-        for (int off = kChunks; off < 64; off <<= 1) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            pk[j] += __shfl_xor(pk[j], off, 64);
-            pq[j] += __shfl_xor(pq[j], off, 64);
-          }
-        }
-        if (lane < kChunks) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            red[wave][0][8 * c + j] = pk[j];
-            red[wave][1][8 * c + j] = pq[j];
-          }
-        }
-      }
+      column_sums<kChunks, kCW>(pk, pq, red[wave], lane);
       __syncthreads();
 
       // u and the output, one column per thread

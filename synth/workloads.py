@@ -96,6 +96,9 @@ GDN_DECODE_B1 = Workload("gdn_decode_b1", batch=1, layers=24, position=65536, ga
 # GDN chunked prefill: one 256-token chunk per sequence at positions 65536.. (FP16 state)
 GDN_PREFILL_B512 = Workload("gdn_prefill_b512", batch=512, layers=24, position=65536,
                             gains="ones", extra={"state": "f16", "chunk": 256})
+# The same at batch 1 (FP32 state): the input phase of one long request
+GDN_PREFILL_B1 = Workload("gdn_prefill_b1", batch=1, layers=24, position=65536,
+                          gains="ones", extra={"state": "f32", "chunk": 256})
 
 # Chunked prefill: one 256-token chunk per sequence at positions 65536..65791 on a
 # steady-state layer (full window and bank, empty pending block).
@@ -104,7 +107,8 @@ PREFILL_B64 = Workload("prefill_b64", batch=64, layers=8, position=65535, gains=
 
 WORKLOADS = {w.name: w for w in (TINY_STREAM, STEADY_B64, HEADLINE_B512, COMMIT_BURST_B512,
                                  LONG_STREAM_B1, HEADLINE_B512_FP8, GDN_DECODE_B512,
-                                 GDN_DECODE_B1, PREFILL_B512, PREFILL_B64, GDN_PREFILL_B512)}
+                                 GDN_DECODE_B1, PREFILL_B512, PREFILL_B64, GDN_PREFILL_B512,
+                                 GDN_PREFILL_B1)}
 
 
 def key(wl: Workload | str, *names) -> StreamKey:
