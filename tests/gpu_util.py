@@ -8,7 +8,7 @@ import torch
 
 import oracle as O
 import swa_memory_anchor_amd as R
-from attn_check import attn_errors, key_err_ratio  # noqa: F401  (attn_errors re-exported)
+from attn_check import attn_errors, key_err_stats  # noqa: F401  (attn_errors re-exported)
 
 DEV = "cuda"
 ATTN_TOL = 2e-2  # row-relative, BF16 I/O with FP32 accumulation
@@ -87,21 +87,13 @@ def assert_scores_close(s_gpu, s_ref, tol=SCORE_TOL, what=""):
 
 
 def assert_keys_close(got_bits, ref_bits, what=""):
-    """Stored keys against the oracle's within attn_check.key_err_ratio's bound (one
+    """Stored keys against the oracle's within attn_check.key_err_stats's bound (one
     BF16 ulp of the reference element plus 2^-20 of the row's largest magnitude)."""
-    ratio = key_err_ratio(got_bits, ref_bits)
-    ndiff = int((np.asarray(got_bits) != np.asarray(ref_bits)).sum())
-    print(f"{what}: {ndiff} of {np.asarray(got_bits).size} elements differ; max err/bound "
-          f"{ratio:.3f}")
+    ratio, ndiff, nbeyond, excess = key_err_stats(got_bits, ref_bits)
+    print(f"{what}: {ndiff} of {np.asarray(got_bits).size} elements differ, {nbeyond} by more "
+          f"than one BF16 ulp (largest excess {excess:.2f} x 2^-24 of the row maximum); "
+          f"max err/bound {ratio:.3f}")
     assert ratio <= 1.0, f"{what}: out of bound ({ratio:.3f})"
-
-
-def bf16_ulp_diff(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
-    """|a - b| in BF16 units in the last place (same-sign finite values)."""
-    def ordinal(x):
-        x = x.astype(np.int32)
-        return np.where(x & 0x8000, -(x & 0x7FFF), x)
-    return np.abs(ordinal(a_bits) - ordinal(b_bits))
 
 
 # ---------------------------------------------------------------- FP8 state
