@@ -30,7 +30,8 @@
  *
  * Conventions (all entry points):
  *   - Every pointer is caller-owned device memory unless stated otherwise.
- *     The library allocates nothing and keeps no mutable global state.
+ *     The library allocates nothing.  Its only mutable global state is the
+ *     per-GPU array of swa_rma_decode_attn_noalloc (see there).
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the null
  *     stream) and never synchronises the host.
  *   - The return value reports host-detectable errors only: bad arguments,
@@ -157,6 +158,27 @@ rma_status swa_rma_decode_attn(const rma_layer_state *st, int32_t batch, const u
                                const uint16_t *q_rma, const rma_norm *norm, uint16_t *o_win,
                                float *lse_win, uint16_t *o_rma, float *lse_rma, void *workspace,
                                size_t workspace_bytes, void *stream);
+
+/*
+ * swa_rma_decode_attn_noalloc - swa_rma_decode_attn for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments (minus the workspace) and the
+ * same results, bit for bit.  The split partials go to a device array of the
+ * library instead, RMA_NOALLOC_SCRATCH_BYTES per GPU, held until the process
+ * ends; that covers every batch (the largest need, at batch 63, is 4,193,280
+ * bytes; batches of 64 and more need none).  Nothing is allocated: the first call
+ * on a device only looks up the array's device address (hipGetSymbolAddress, with
+ * that device made current), so make the first call outside graph capture.
+ * All calls on one GPU share the array and nothing in it must start at zero;
+ * calls that overlap on one GPU (on different streams or host threads) race and
+ * give undefined results.  Returns RMA_E_WORKSPACE if a batch would need more
+ * than the array holds, RMA_E_HIP if the address lookup fails.
+ */
+#define RMA_NOALLOC_SCRATCH_BYTES (4u << 20)
+rma_status swa_rma_decode_attn_noalloc(const rma_layer_state *st, int32_t batch,
+                                       const uint16_t *q_win, const uint16_t *q_rma,
+                                       const rma_norm *norm, uint16_t *o_win, float *lse_win,
+                                       uint16_t *o_rma, float *lse_rma, void *stream);
 
 /* Workspace that swa_rma_step needs at this batch: the decode's split partials,
  * then one 32-bit counter per sequence at a 256-byte aligned offset. */

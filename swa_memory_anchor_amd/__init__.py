@@ -32,7 +32,7 @@ EXPORTS = (
     "rma_layer_state_fp8_bytes", "swa_rma_append_fp8", "swa_rma_decode_attn_fp8",
     "rma_commit_topk_fp8", "gdn_layer_state_bytes", "gdn_decode_step",
     "rma_step_workspace_bytes", "swa_rma_step", "rma_score_multi", "rma_commit_topk_multi",
-    "gdn_prefill",
+    "gdn_prefill", "swa_rma_decode_attn_noalloc",
 )
 
 _c_void_p = ctypes.c_void_p
@@ -96,6 +96,8 @@ def lib() -> ctypes.CDLL:
         L.swa_rma_append.restype = ctypes.c_int
         L.swa_rma_decode_attn.argtypes = [sp, i32, vp, vp, npp, vp, vp, vp, vp, vp, sz, vp]
         L.swa_rma_decode_attn.restype = ctypes.c_int
+        L.swa_rma_decode_attn_noalloc.argtypes = [sp, i32, vp, vp, npp, vp, vp, vp, vp, vp]
+        L.swa_rma_decode_attn_noalloc.restype = ctypes.c_int
         L.swa_rma_step.argtypes = [sp, i32, vp, vp, vp, vp, vp, vp, vp, npp, vp, vp, vp, vp, vp,
                                    sz, vp]
         L.swa_rma_step.restype = ctypes.c_int
@@ -313,6 +315,15 @@ def swa_rma_decode_attn(st: LayerState, batch: int, q_win, q_rma, norm: Norm, o_
                                   _ptr(lse_win), _ptr(o_rma), _ptr(lse_rma), _ptr(workspace),
                                   ws_bytes, _stream(stream))
     _check(s, "swa_rma_decode_attn")
+
+
+def swa_rma_decode_attn_noalloc(st: LayerState, batch: int, q_win, q_rma, norm: Norm, o_win,
+                                lse_win, o_rma, lse_rma, stream=None) -> None:
+    s = lib().swa_rma_decode_attn_noalloc(ctypes.byref(_state_c(st)), int(batch), _ptr(q_win),
+                                          _ptr(q_rma), ctypes.byref(_norm_c(norm)), _ptr(o_win),
+                                          _ptr(lse_win), _ptr(o_rma), _ptr(lse_rma),
+                                          _stream(stream))
+    _check(s, "swa_rma_decode_attn_noalloc")
 
 
 def rma_step_workspace_bytes(batch: int) -> int:

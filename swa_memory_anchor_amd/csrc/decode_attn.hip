@@ -34,6 +34,9 @@
 // hardware conversion and fed to the same MFMAs (the 32 keys form one 32-long
 // contraction for P x V, read back with transposed LDS reads); the K scale
 // multiplies each score and the V scale each probability weight.
+#include <atomic>
+#include <mutex>
+
 #include "rma_device.h"
 
 namespace rma {
@@ -1029,4 +1032,69 @@ extern "C" rma_status swa_rma_step(const rma_layer_state *st, int32_t batch, con
   hipLaunchKernelGGL(decode_step_kernel, dim3(units * p.splits), dim3(kThreads), 0, s, sp);
   if (hipPeekAtLastError() != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
   return launch_merge(p, s);
+}
+
+// ---------------------------------------------------------------- no-alloc decode
+// swa_rma_decode_attn for callers that cannot allocate: the split partials go to
+// `scratch`, a device array of this library (each GPU holds its own copy until the
+// process ends), instead of a caller workspace.  4 MiB covers every batch: only
+// batches below 64 split, and the largest of them needs 1008 (unit, split) pairs of
+// 4 heads x 260 floats, 4,193,280 bytes (batch 63).
+constexpr size_t kScratchBytes = static_cast<size_t>(RMA_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+
+// The device address of `scratch` on the device that runs `stream`, resolved once per
+// device with that device current.  In host code the array's name is only a host-side
+// stand-in; kernels must be given this address.
+rma_status scratch_for_stream(hipStream_t stream, void **out) {
+  int dev = -1;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return RMA_E_ARG;
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      int cur = -1;
+      if (hipGetDevice(&cur) != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
+      if (cur != dev && hipSetDevice(dev) != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
+      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (cur != dev) (void)hipSetDevice(cur);
+      if (e != hipSuccess || !p) return (void)hipGetLastError(), RMA_E_HIP;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return RMA_OK;
+}
+}  // namespace
+
+extern "C" rma_status swa_rma_decode_attn_noalloc(const rma_layer_state *st, int32_t batch,
+                                                  const uint16_t *q_win, const uint16_t *q_rma,
+                                                  const rma_norm *norm, uint16_t *o_win,
+                                                  float *lse_win, uint16_t *o_rma, float *lse_rma,
+                                                  void *stream) {
+  if (!st) return RMA_E_ARG;
+  if (batch <= 0 || batch > RMA_MAX_BATCH) return RMA_E_ARG;
+  if (rma_decode_workspace_bytes(batch) > kScratchBytes) return RMA_E_WORKSPACE;
+  void *ws = nullptr;
+  const rma_status rc = scratch_for_stream(static_cast<hipStream_t>(stream), &ws);
+  if (rc != RMA_OK) return rc;
+  DecodeParams p{};
+  p.win_k = reinterpret_cast<const uint8_t *>(st->win_k);
+  p.win_v = reinterpret_cast<const uint8_t *>(st->win_v);
+  p.bank_k = reinterpret_cast<const uint8_t *>(st->bank_k);
+  p.bank_v = reinterpret_cast<const uint8_t *>(st->bank_v);
+  p.pend_k = reinterpret_cast<const uint8_t *>(st->pend_k);
+  p.pend_v = reinterpret_cast<const uint8_t *>(st->pend_v);
+  p.n_bank = st->n_bank;
+  p.n_pend = st->n_pend;
+  p.pos = st->pos;
+  return launch_decode<false>(p, batch, q_win, q_rma, norm, o_win, lse_win, o_rma, lse_rma, ws,
+                              kScratchBytes, stream);
 }
