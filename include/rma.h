@@ -291,8 +291,9 @@ rma_status swa_rma_prefill(const rma_layer_state *st, int32_t batch, int32_t n_t
  * ([FB] section "架构…"; [QB] section "开源到哪一步") but no format for the
  * attention state; this variant is a reading of this library:
  *   - every stored K and V row (256 values) is 256 OCP FP8 E4M3 codes plus one
- *     FP32 scale = amax / 448 (amax = max |x| over the row, FP32; an all-zero
- *     row has scale 0 and zero codes);
+ *     FP32 scale = amax / 448 (amax = max |x| over the row, FP32; a row with
+ *     amax below 448 * 2^-126, the all-zero row included, has scale 0 and zero
+ *     codes);
  *   - code = E4M3(x * (448 / amax)), products and quotient in FP32, E4M3
  *     rounding to nearest, ties to even; the row means code value * scale;
  *   - keys are quantised from their FP32 normalised and rotated value, values

@@ -12,7 +12,9 @@ reading of this build:
   * every stored K and V row (the 256 values of one sequence, KV group and slot) is
     held as 256 OCP FP8 E4M3 codes and one FP32 scale;
   * scale = amax / 448 with amax = max_i |x_i| (448 is the largest finite E4M3
-    value), computed in FP32; an all-zero row has scale 0 and all codes 0;
+    value), computed in FP32; a row whose amax is below 448 * 2^-126 (where
+    448 / amax would pass 2^126 and the scale would leave the normal FP32 range),
+    the all-zero row included, has scale 0 and all codes 0;
   * code_i = E4M3(fp32(x_i * inv)), inv = fp32(448 / amax), rounding to nearest,
     ties to even;
   * the stored row means code_value_i * scale.
@@ -88,11 +90,14 @@ def e4m3_step(value) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- per-row quantisation
+TINY_ROW = np.float32(E4M3_MAX * 2.0**-126)  # rows below this amax are stored as zero
+
+
 def quantize_rows(x_f32):
     """Rows [..., 256] of FP32 values -> (codes uint8 [..., 256], scale f32 [...])."""
     x = np.asarray(x_f32, np.float32)
     amax = np.max(np.abs(x), axis=-1)
-    zero = amax == 0
+    zero = amax < TINY_ROW
     safe = np.where(zero, np.float32(1.0), amax)
     inv = np.float32(E4M3_MAX) / safe  # FP32 division, correctly rounded
     scale = np.where(zero, np.float32(0.0), amax / np.float32(E4M3_MAX)).astype(np.float32)

@@ -61,8 +61,10 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams a) {
 // ---------------------------------------------------------------- FP8 state variant
 // Each written row becomes 256 E4M3 codes and one FP32 scale: amax = max |x| over
 // the row (a wave reduction), code = E4M3(x * (448 / amax)) with round to nearest
-// even (v_cvt_pk_fp8_f32), scale = amax / 448; an all-zero row gets zero codes and
-// scale.  Keys are quantised from their FP32 normalised and rotated value.
+// even (v_cvt_pk_fp8_f32), scale = amax / 448; a row whose amax is below
+// 448 * 2^-126 (where 448 / amax would pass 2^126 and the scale would leave the
+// normal FP32 range), the all-zero row included, gets zero codes and scale 0.  Keys
+// are quantised from their FP32 normalised and rotated value.
 struct AppendFp8Params {
   uint8_t *win_k, *win_v, *pend_k, *pend_v;
   float *win_ks, *win_vs, *pend_ks, *pend_vs;
@@ -86,12 +88,14 @@ __device__ __forceinline__ float wave_max(float v) {
 __device__ __forceinline__ uint32_t quantize_row_e4m3(const float x[4], float &scale) {
   const float amax =
       wave_max(fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))));
-  const float inv = amax > 0.f ? 448.0f / amax : 0.f;
-  scale = amax / 448.0f;
+  constexpr float kTinyRow = 448.0f * 0x1p-126f;
+  const bool tiny = amax < kTinyRow;
+  const float inv = tiny ? 0.f : 448.0f / amax;
+  scale = tiny ? 0.f : amax / 448.0f;
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] * inv, x[1] * inv, 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] * inv, x[3] * inv, w, true);
-  // an all-zero row stores +0 codes, also where its elements are -0
-  return amax > 0.f ? static_cast<uint32_t>(w) : 0u;
+  // a tiny or all-zero row stores +0 codes, also where its elements are -0
+  return tiny ? 0u : static_cast<uint32_t>(w);
 }
 
 __global__ __launch_bounds__(256) void append_fp8_kernel(AppendFp8Params a) {

@@ -106,6 +106,9 @@ def test_fp8_append_codes_and_scales():
     recs[1][2, 1] = 0
     recs[1][2, 1, ::2] = 0x8000
     recs[2][1, 3] = 0
+    # a value row of BF16 subnormals (amax below 448 * 2^-126): stored as a zero row
+    recs[3][3, 2] = (np.arange(256) % 127 + 1).astype(np.uint16) | np.where(
+        np.arange(256) % 3 == 0, 0x8000, 0).astype(np.uint16)
     score = synth.normal_f32_np(synth.stream_key("fp8_app", "score"), (B, 4))
     dst = upload_fp8(st)
     nm = norm_dev(g)
@@ -122,6 +125,7 @@ def test_fp8_append_codes_and_scales():
                               getattr(st, k + "s"), what=k)
     assert got.pend_ks[1, 3, 255] == 0.0 and np.all(got.pend_k[1, 3, 255] == 0)
     assert got.win_vs[2, 1, 0] == 0.0 and np.all(got.win_v[2, 1, 0] == 0)
+    assert got.pend_vs[3, 2, 7] == 0.0 and np.all(got.pend_v[3, 2, 7] == 0)
     # a full pending block is left untouched
     st2 = _rand_state("fp8_app_full", [(1024, 256, 9000)])
     d2 = upload_fp8(st2)

@@ -51,6 +51,27 @@ def test_encode_decode_round_trip():
     assert np.array_equal(F.e4m3_encode(F.e4m3_decode(c)), c)
 
 
+def test_quantize_rows_tiny_rows_are_stored_as_zero():
+    """A row whose largest magnitude is below 448 * 2^-126 (for example a row of BF16
+    subnormals) would need 448 / amax beyond 2^126 and a scale below the normal FP32
+    range; it is stored as a zero row.  At the threshold the row is quantised as usual,
+    its largest element going to +-448, and every code stays finite."""
+    sub = (np.arange(1, 257, dtype=np.float64) * 2.0**-133).astype(np.float32)  # BF16 subnormals
+    sub[::3] *= -1
+    thr = np.float32(448.0 * 2.0**-126)
+    at = np.full(256, thr / 2, np.float32)
+    at[17] = -thr
+    just_below = np.full(256, np.nextafter(thr, np.float32(0)), np.float32)
+    codes, scale = F.quantize_rows(np.stack([sub, at, just_below]))
+    assert np.all(codes[0] == 0) and scale[0] == 0
+    assert np.all(codes[2] == 0) and scale[2] == 0
+    assert scale[1] == np.float32(2.0**-126)
+    dec = F.e4m3_decode(codes[1])
+    assert not np.any(np.isnan(dec)) and dec[17] == -448.0 and np.all(dec[:17] == 224.0)
+    # the stored zero row is within the threshold of the input
+    assert np.all(np.abs(F.dequantize(codes[0], scale[0]) - sub) < float(thr))
+
+
 def test_quantize_rows_matches_a_torch_implementation():
     rng = synth.rng_np(synth.stream_key("fp8", "rows"))
     x = (rng.standard_normal((64, 256)) * np.exp2(rng.uniform(-8, 8, (64, 1)))).astype(np.float32)
