@@ -303,6 +303,53 @@ def burst_scores(wl: Workload, layer: int) -> dict:
     }
 
 
+
+def plant_burst_ties(wl: Workload, layer: int, pend_score) -> dict:
+    """Commit inputs built around given pending scores (e.g. the scorer's output on
+    the burst's hidden rows, whose duplicated rows already give equal score rows).
+
+    pend_score is FP32 [B][256][4].  Per (sequence, group): bank scores are drawn
+    N(0, s^2) with s the standard deviation of the given scores; 2.5% of them copy
+    a pending score of the same group; then the 1280 values are ranked and the
+    eight around the 1024th place are set equal to the 1024th, so the cut falls
+    inside a run of ties; in every fourth segment the 1024th value is subtracted
+    from all 1280 (an order-preserving FP32 shift) and the run is written as four
+    -0.0 and four +0.0.  Only values change, never ranks outside the run.
+    Returns the same fields as burst_scores.
+    """
+    B, G = wl.batch, KV_GROUPS
+    ps = np.array(pend_score, np.float32, copy=True).reshape(B, BLOCK, G)
+    rng = rng_np(key(wl, layer, "planted_ties"))
+    std = float(ps.astype(np.float64).std())
+    bank_score = (rng.standard_normal((B, G, BANK)) * std).astype(np.float32)
+    nb = int(round(0.025 * BANK))
+    for b in range(B):
+        for g in range(G):
+            dst = rng.choice(BANK, size=nb, replace=False)
+            src = rng.integers(0, BLOCK, size=nb)
+            bank_score[b, g, dst] = ps[b, src, g]
+    for b in range(B):
+        for g in range(G):
+            v = np.concatenate([bank_score[b, g], ps[b, :, g]])
+            order = np.argsort(-v.astype(np.float64), kind="stable")
+            run = order[BANK - 4:BANK + 4]
+            v[run] = v[order[BANK - 1]]
+            if (b * G + g) % 4 == 3:
+                v = (v - v[order[BANK - 1]]).astype(np.float32)
+                v[run[:4]] = -0.0
+                v[run[4:]] = 0.0
+            bank_score[b, g] = v[:BANK]
+            ps[b, :, g] = v[BANK:]
+    return {
+        "bank_score": bank_score,
+        "pend_score": ps,
+        "bank_src": bank_src_all(wl, layer),
+        "pend_src": np.broadcast_to(pend_src(wl), (B, BLOCK)).copy(),
+        "n_bank": np.full(B, BANK, np.int32),
+        "n_pend": np.full(B, BLOCK, np.int32),
+        "pos": np.full(B, wl.position, np.int32),
+    }
+
 # ------------------------------------------------------------------ token streams
 RECORD_NAMES = ("k_win", "v_win", "k_rma", "v_rma")
 

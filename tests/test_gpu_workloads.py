@@ -221,8 +221,12 @@ def test_commit_burst_b512_layer():
         for d, s in dups[b]:
             assert np.array_equal(s_gpu[b, d], s_gpu[b, s])
     del Hd
-    # commit of every sequence with generator-supplied scores (planted ties)
-    sc = W.burst_scores(wl, layer)
+    # commit of every sequence on the scorer's own output, with exact ties planted
+    # into it (bank/pending copies, a tie run across the cut, signed zeros there)
+    sc = W.plant_burst_ties(wl, layer, s_gpu)
+    changed = int((sc["pend_score"].view(np.uint32) != s_gpu.view(np.uint32)).sum())
+    print(f"commit input: the scorer's {s_gpu.size} scores, {changed} of them replaced by "
+          f"planted ties", flush=True)
     dst = R.alloc_layer_state(B, zero_kv=False)
     for nm in ("bank_k", "bank_v", "pend_k", "pend_v"):
         W.kv_torch_(wl, layer, nm, getattr(dst, nm))

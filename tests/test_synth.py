@@ -113,3 +113,32 @@ def test_prefill_chunk_slices_equal_the_device_fill():
                               W.prefill_record_np(wl, 2, "v_rma", b, C))
         assert np.array_equal(q[b].view(torch.int16).numpy().view(np.uint16),
                               W.prefill_q_np(wl, 2, b, C))
+
+
+def test_planted_ties_on_given_scores():
+    """plant_burst_ties keeps the given pending scores except where it plants ties,
+    and puts an exact tie run across the 1024th place of every segment."""
+    wl = W.Workload("burst_small", batch=8, layers=1, position=32767, gains="ones", src_hi=32512)
+    rng = np.random.default_rng(3)
+    given = (rng.standard_normal((8, 256, 4)) * 0.32).astype(np.float32)
+    given[2, 7] = given[2, 9]  # an equal score row, as a duplicated hidden row gives
+    d = W.plant_burst_ties(wl, 0, given)
+    bs, ps = d["bank_score"], d["pend_score"]
+    assert bs.shape == (8, 4, 1024) and ps.shape == (8, 256, 4)
+    zero_seg = 0
+    for b in range(8):
+        for g in range(4):
+            v = np.concatenate([bs[b, g], ps[b, :, g]]).astype(np.float64)
+            s = np.sort(v)[::-1]
+            assert np.all(s[1020:1028] == s[1023])  # the cut sits inside a run of 8 ties
+            if s[1023] == 0.0:
+                zero_seg += 1
+                z = np.concatenate([bs[b, g], ps[b, :, g]])
+                z = z[z == 0]
+                assert np.signbit(z).sum() >= 4 and (~np.signbit(z)).sum() >= 4
+            else:
+                # outside the run, pending scores are the given ones
+                keep = ps[b, :, g] != s[1023]
+                assert np.array_equal(ps[b, keep, g], given[b, keep, g])
+    assert zero_seg == 8  # every fourth segment
+    assert np.array_equal(ps[2, 7], ps[2, 9]) or (ps[2, 7] == ps[2, 9]).sum() >= 3
