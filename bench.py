@@ -86,6 +86,45 @@ def _blas_threads() -> int:
         return 1
 
 
+def _host_cores() -> int:
+    """CPU cores this process may run on."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def with_single_thread(fn, wl, budget_s: float, *extra):
+    """Run one oracle baseline twice: with the BLAS pool as wide as the cores this
+    process may use (two thirds of the budget; the reported value), then with one
+    thread (the rest).  Adds the thread count, the host's cores and CPU model."""
+    from threadpoolctl import threadpool_limits
+
+    n = _host_cores()
+    with threadpool_limits(limits=n):
+        used = _blas_threads()
+        res = fn(wl, budget_s * 2.0 / 3.0, *extra)
+    with threadpool_limits(limits=1):
+        one = fn(wl, budget_s / 3.0, *extra)
+    res["cores"] = int(used)
+    res["host_cores"] = n
+    res["cpu_model"] = _cpu_model()
+    res["value_1thread"] = one["value"]
+    res["sample_1thread"] = one["sample"]
+    return res
+
+
 def cpu_baseline(wl, budget_s: float, max_units: int):
     """The oracle, untuned, on a bounded sample of (sequence, layer) units."""
     import numpy as np
@@ -225,7 +264,8 @@ def bench_commit_burst(args):
                 c_ms.append(a.elapsed_time(b))
     admitted = int(sum(int((k >= 1024).sum()) for k in keeps))
     c_avg = sum(c_ms) / len(c_ms)
-    cpu = None if args.no_cpu_baseline else cpu_baseline_commit_burst(wl, min(args.cpu_budget, 20.0))
+    cpu = (None if args.no_cpu_baseline else
+           with_single_thread(cpu_baseline_commit_burst, wl, min(args.cpu_budget, 20.0)))
     key_bytes = B * 4 * 1280 * 8  # score + source of every candidate
     copy_bytes = admitted / L * 2 * 2 * 512  # K and V rows, read and written
     out_bytes = B * 4 * 1024 * 4  # keep_idx
@@ -393,7 +433,8 @@ def bench_long_stream(args):
         torch.cuda.synchronize()
         lat.append(a.elapsed_time(b) * 1e3)
     lat_sorted = sorted(lat)
-    cpu = None if args.no_cpu_baseline else cpu_baseline_long_stream(wl, min(args.cpu_budget, 20.0))
+    cpu = (None if args.no_cpu_baseline else
+           with_single_thread(cpu_baseline_long_stream, wl, min(args.cpu_budget, 20.0)))
     state_bytes = sum(x.numel() * x.element_size() for x in states[0].__dict__.values())
     return {
         "metric": "batch-1 stream: microseconds per token (8 layers append + decode, "
@@ -606,7 +647,7 @@ def bench_gdn(args):
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline_gdn(wl, min(args.cpu_budget, 10.0))
+        res["cpu_baseline"] = with_single_thread(cpu_baseline_gdn, wl, min(args.cpu_budget, 10.0))
     return res
 
 
@@ -997,7 +1038,8 @@ def main() -> int:
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget, args.cpu_max_units)
+        res["cpu_baseline"] = with_single_thread(cpu_baseline, wl, args.cpu_budget,
+                                                 args.cpu_max_units)
     print(json.dumps(res))
     return 0
 
