@@ -31,8 +31,9 @@
 //
 // FP8 variant (rows of 256 E4M3 codes plus one FP32 scale): 32-key tiles keep
 // the same bytes in flight per wave; codes are widened to BF16 exactly with the
-// hardware conversion and fed to the same MFMAs (the 32 keys form one 32-long
-// contraction for P x V, read back with transposed LDS reads); the K scale
+// hardware conversion and fed to the same MFMAs: K codes as they arrive, V codes
+// after an 8-bit transposing LDS read (V stays E4M3 in LDS, half the bytes of a
+// widened tile), the 32 keys forming one 32-long contraction for P x V; the K scale
 // multiplies each score and the V scale each probability weight.
 #include <atomic>
 #include <mutex>
@@ -553,9 +554,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepParams sp)
 // widened to BF16 (exactly) for the same MFMAs; the K scale multiplies the score
 // and the V scale the probability weight of its key.
 constexpr int kTile8 = 32;
-// LDS row stride of a staged (widened) V tile, in elements: 544 bytes, so rows
-// start 8 banks apart and a transposed read of 8 rows x 32 bytes hits 64 banks.
-constexpr int kVStride8 = kDim + 16;
 
 // Eight E4M3 codes (two words) -> eight BF16 values.
 __device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
@@ -603,13 +601,18 @@ __device__ __forceinline__ void load_v_fp8(const Segment &sg, int key0, int lane
         __builtin_amdgcn_raw_buffer_load_b128(sg.vs, 4 * (16 * u + 4 * kg), key0 * 4, kStream));
 }
 
-// Stage the widened V rows of a tile in the wave's LDS rows (consumes V).
-__device__ __forceinline__ void stage_v_fp8(int lane, const uint4 (&V)[8], uint16_t *vl) {
-  uint16_t *vrow = vl + (lane >> 4) * kVStride8 + 16 * (lane & 15);
+// V codes stay E4M3 in LDS: 32 rows of 256 bytes, the 16-byte chunk c of row r at
+// chunk position c ^ vswz8(r), so that the 16 rows one half-wave's transposed reads
+// touch (rows 4kg..4kg+3 and 16+4kg..16+4kg+3 of two lane groups) hit 16 distinct
+// 4-bank positions.
+__device__ __forceinline__ int vswz8(int r) { return (r & 7) | (((r >> 4) & 1) << 3); }
+
+// Stage the tile's V codes in the wave's LDS rows (consumes V).
+__device__ __forceinline__ void stage_v_fp8(int lane, const uint4 (&V)[8], uint8_t *vl) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    *reinterpret_cast<uint4 *>(vrow + 4 * i * kVStride8) = e4m3x8_to_bf16x8(V[i].x, V[i].y);
-    *reinterpret_cast<uint4 *>(vrow + 4 * i * kVStride8 + 8) = e4m3x8_to_bf16x8(V[i].z, V[i].w);
+    const int r = 4 * i + (lane >> 4);
+    *reinterpret_cast<uint4 *>(vl + r * kDim + (((lane & 15) ^ vswz8(r)) << 4)) = V[i];
   }
 }
 
@@ -652,7 +655,7 @@ __device__ __forceinline__ void scores_tile_fp8(int nvalid, int lane, const uint
 // rounded probability times its V scale; the denominator sums the rounded
 // probabilities.  A key past the end has probability 0 and scale 0.
 __device__ __forceinline__ void accumulate_tile_fp8(const f32x4 (&sc)[2], int lane,
-                                                    const uint16_t *vl, const f32x4 (&vsc)[2],
+                                                    const uint8_t *vl, const f32x4 (&vsc)[2],
                                                     SoftmaxState &st) {
   const int kg = lane >> 4, r = lane & 15;
   float mt = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
@@ -684,23 +687,27 @@ __device__ __forceinline__ void accumulate_tile_fp8(const f32x4 (&sc)[2], int la
   st.l = st.l * alpha + psum;
   st.m = m_new;
   const bf16x8 pb = bitcast<bf16x8>(make_uint4(pw[0], pw[1], pw[2], pw[3]));
-  // Transposed read: lane r of group kg supplies row 4kg + r/4, dims 4(r%4) .. +4 of
-  // a 16-dim block, and receives dim r of rows 4kg .. 4kg+3 (16 rows further on
-  // for the second half).
-  const uint16_t *src = vl + (4 * kg + (r >> 2)) * kVStride8 + 4 * (r & 3);
+  // Transposed 8-bit read: within a 16-lane group, lanes 2j and 2j+1 supply the two
+  // 8-byte halves of a 16-byte chunk of row K_j, and lane i receives byte i of the
+  // eight rows K_0..K_7 -- here the keys 4kg .. 4kg+3, 16 + 4kg .. 16 + 4kg+3, in the
+  // order of the P operand -- i.e. dim 16 db + i of those keys, widened to BF16.
+  const int j = r >> 1;
+  const int key = j < 4 ? 4 * kg + j : 16 + 4 * kg + (j - 4);
+  const uint8_t *src = vl + key * kDim + 8 * (r & 1);
+  const int sw = vswz8(key);
 #pragma unroll
   for (int db = 0; db < 16; ++db) {
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src + 16 * db));
-    const s16x4 hi =
-        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src + 16 * kVStride8 + 16 * db));
-    const bf16x8 va = bitcast<bf16x8>(make_uint4(bitcast<uint2>(lo).x, bitcast<uint2>(lo).y,
-                                                 bitcast<uint2>(hi).x, bitcast<uint2>(hi).y));
+    typedef int v2i __attribute__((ext_vector_type(2)));
+    typedef __attribute__((address_space(3))) v2i lds_v2i;
+    const v2i c = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i *)(src + ((db ^ sw) << 4)));
+    const bf16x8 va = bitcast<bf16x8>(e4m3x8_to_bf16x8(static_cast<uint32_t>(c[0]),
+                                                       static_cast<uint32_t>(c[1])));
     st.acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, st.acc[db], 0, 0, 0);
   }
 }
 
 __global__ __launch_bounds__(kThreads, 2) void decode_attn_fp8_kernel(DecodeParams a) {
-  __shared__ __align__(16) uint16_t v_lds[kWaves][kTile8 * kVStride8];
+  __shared__ __align__(16) uint8_t v_lds[kWaves][kTile8 * kDim];
   __shared__ __align__(16) uint16_t q_lds[16][kQStride];  // rows 4..15 stay zero
   __shared__ float red_m[kWaves][kHeadsPerGroup], red_l[kWaves][kHeadsPerGroup];
 
@@ -727,7 +734,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_fp8_kernel(DecodePara
 #pragma unroll
   for (int d = 0; d < 16; ++d) st.acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  uint16_t *vl = v_lds[wave];
+  uint8_t *vl = v_lds[wave];
   uint4 K[8], V[8];
   f32x4 ks[2], vs[2];
   int t = tb + wave;
