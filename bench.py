@@ -42,11 +42,14 @@ TRAFFIC_FILES = {
     "gdn_decode_b512": os.path.join(ROOT, "profiles", "gdn_decode_gdn_decode_b512_traffic.txt"),
     "gdn_prefill_b512": os.path.join(ROOT, "profiles", "gdn_prefill_gdn_prefill_b512_traffic.txt"),
     "commit_burst_b512": os.path.join(ROOT, "profiles", "score_commit_burst_b512_traffic.txt"),
+    "commit_burst_b512:commit": os.path.join(ROOT, "profiles",
+                                             "commit_commit_burst_b512_traffic.txt"),
 }
 KERNEL_SOURCES = ("swa_memory_anchor_amd/csrc/decode_attn.hip",
                   "swa_memory_anchor_amd/csrc/rma_device.h")
 GDN_SOURCES = ("swa_memory_anchor_amd/csrc/gdn.hip", "swa_memory_anchor_amd/csrc/rma_device.h")
 SCORE_SOURCES = ("swa_memory_anchor_amd/csrc/score.hip", "swa_memory_anchor_amd/csrc/rma_device.h")
+COMMIT_SOURCES = ("swa_memory_anchor_amd/csrc/commit.hip", "swa_memory_anchor_amd/csrc/rma_device.h")
 
 
 def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
@@ -68,6 +71,7 @@ def measured_traffic(workload: str, units_per_launch: int):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
     sources = (GDN_SOURCES if workload.startswith("gdn") else
+               COMMIT_SOURCES if workload.endswith(":commit") else
                SCORE_SOURCES if workload.startswith("commit") else KERNEL_SOURCES)
     if kv.get("kernel_source_sha256") != kernel_source_hash(sources):
         return None
@@ -264,6 +268,20 @@ def bench_commit_burst(args):
                 c_ms.append(a.elapsed_time(b))
     admitted = int(sum(int((k >= 1024).sum()) for k in keeps))
     c_avg = sum(c_ms) / len(c_ms)
+    # the same 8 commits as one launch (rma_commit_topk_multi), as a block end runs them
+    m_ms = []
+    for rep in range(args.warmup + args.steps):
+        for l in range(L):
+            restore(l)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        R.rma_commit_topk_multi(states, B, keeps, stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        if rep >= args.warmup:
+            m_ms.append(a.elapsed_time(b) / L)
+    m_avg = sum(m_ms) / len(m_ms)
     cpu = (None if args.no_cpu_baseline else
            with_single_thread(cpu_baseline_commit_burst, wl, min(args.cpu_budget, 20.0)))
     key_bytes = B * 4 * 1280 * 8  # score + source of every candidate
@@ -289,7 +307,13 @@ def bench_commit_burst(args):
         "commit": {"avg_launch_us": round(c_avg * 1e3, 1),
                    "admitted_rows_per_layer": admitted // L,
                    "algorithmic_bytes_per_launch": int(key_bytes + copy_bytes + out_bytes),
-                   "gbps": round((key_bytes + copy_bytes + out_bytes) / (c_avg / 1e3) / 1e9, 1)},
+                   "gbps": round((key_bytes + copy_bytes + out_bytes) / (c_avg / 1e3) / 1e9, 1),
+                   "frac": round((key_bytes + copy_bytes + out_bytes) / (c_avg / 1e3) / 1e9
+                                 / HBM_PEAK_GBPS, 4),
+                   "traffic": measured_traffic(wl.name + ":commit", B),
+                   "multi_layer_us_per_layer": round(m_avg * 1e3, 1),
+                   "multi_layer_gbps": round((key_bytes + copy_bytes + out_bytes) / (m_avg / 1e3)
+                                             / 1e9, 1)},
         "cpu_baseline": cpu,
     }
 

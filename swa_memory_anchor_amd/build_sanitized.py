@@ -2,9 +2,10 @@
 UndefinedBehaviorSanitizer on the host side only (argument checks, sizes, launch
 set-up).  Device code is compiled as usual; GPU sanitizers are not used.
 
-The library goes to ``_build/librma_san.so``; it needs the clang ASan runtime
-preloaded into an uninstrumented interpreter (``asan_runtime()`` gives its path).
-It is a test build: nothing in the package loads it.
+The library goes to a fresh temporary directory (``build_sanitized()`` returns its
+path; the caller removes it); it needs the clang ASan runtime preloaded into an
+uninstrumented interpreter (``asan_runtime()`` gives its path).  It is a test
+build: nothing in the package loads it, and none of it stays in the tree.
 """
 
 from __future__ import annotations
@@ -12,10 +13,9 @@ from __future__ import annotations
 import concurrent.futures as cf
 import os
 import subprocess
+import tempfile
 
-from .build import ARCH, CSRC, INCLUDE, OBJ_DIR, _hipcc, sources
-
-SAN_LIB = os.path.join(OBJ_DIR, "librma_san.so")
+from .build import ARCH, CSRC, INCLUDE, _hipcc, sources
 SAN_FLAGS = [
     f"--offload-arch={ARCH}", "-O1", "-g", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -44,8 +44,8 @@ def asan_runtime() -> str:
     return r.stdout.strip()
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ_DIR, "san_" + os.path.basename(src) + ".o")
+def _compile(src: str, out_dir: str) -> str:
+    obj = os.path.join(out_dir, os.path.basename(src) + ".o")
     cmd = [_hipcc(), *SAN_FLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -54,15 +54,17 @@ def _compile(src: str) -> str:
 
 
 def build_sanitized() -> str:
-    os.makedirs(OBJ_DIR, exist_ok=True)
+    """Build into a new temporary directory; returns the library's path."""
+    out_dir = tempfile.mkdtemp(prefix="librma_san_")
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    cmd = [_hipcc(), *SAN_LINK, *objs, "-o", SAN_LIB]
+        objs = list(ex.map(lambda s: _compile(s, out_dir), srcs))
+    lib = os.path.join(out_dir, "librma_san.so")
+    cmd = [_hipcc(), *SAN_LINK, *objs, "-o", lib]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    return SAN_LIB
+    return lib
 
 
 if __name__ == "__main__":

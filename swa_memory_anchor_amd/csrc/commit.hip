@@ -14,17 +14,23 @@
 // total whenever sources are distinct within a group.
 //
 // One workgroup (256 threads) per (sequence, KV group), so that a CU holds several
-// and one's sort overlaps another's copies:
+// and one's selection overlaps another's copies:
 //   1. build the 1280 candidate keys, five per thread, in registers;
-//   2. the admission threshold is the min(1024, n_bank + n_pend)-th largest key,
-//      found by radix selection (byte by byte from the top, LDS histograms);
+//   2. the admission threshold is the min(1024, n_bank + n_pend)-th largest key
+//      (equal keys counted): a first pass sorts the candidates into buckets by
+//      score, linearly between the segment's smallest and largest score (a
+//      monotone map), and finds the bucket holding that rank; its few keys are
+//      then ranked against each other directly, or, for a bucket too full (all
+//      scores equal, heavy ties), radix selection continues among them byte by
+//      byte from the top;
 //   3. a bank record survives in place; free slots (evicted slots, then slots
 //      >= n_bank) are listed in ascending order by a prefix sum; admitted
 //      pending rows, in ascending row order, take the free slots in order;
-//   4. only admitted rows move: K and V rows (512 bytes in BF16, 256 bytes of
-//      E4M3 codes in the FP8 variant) are copied in 16-byte pieces (8 in flight
-//      per thread), plus their score, source and, in the FP8 variant, the two
-//      row scales;
+//   4. only admitted rows move: each wave moves whole rows -- K and V (512 bytes
+//      each in BF16, 256 bytes of E4M3 codes in the FP8 variant) one 16-byte piece
+//      per lane, 8 rows in flight per lane, with non-temporal loads and stores
+//      (the rows are read once and not read again by this launch) -- plus their
+//      score, source and, in the FP8 variant, the two row scales;
 //   5. a second launch sets n_bank = min(1024, n_bank + n_pend), n_pend = 0, once
 //      every group's workgroup has read them.
 #include "rma_device.h"
@@ -33,7 +39,7 @@ namespace rma {
 
 constexpr int kCand = kBank + kBlock;  // 1280
 constexpr int kCommitThreads = 256;
-constexpr int kCopyBatch = 8;  // 16-byte copies in flight per thread
+constexpr int kCopyBatch = 8;  // rows in flight per lane of the copy loop
 
 // K/V rows are BF16 (512 bytes) or, in the FP8 variant, E4M3 codes (256 bytes)
 // with one FP32 scale per row (*_ks, *_vs), which moves with the row.
@@ -105,6 +111,9 @@ __device__ __forceinline__ void commit_group(const CommitParams &a) {
   __shared__ int16_t adm_slot[kBlock];
   __shared__ int16_t adm_rows[kBlock];
   __shared__ int wave_tot[4];
+  __shared__ float red_lo[4], red_hi[4];
+  __shared__ uint64_t gather[kCommitThreads];
+  __shared__ int gather_n;
 
   const int b = blockIdx.x / kGroups;
   const int g = blockIdx.x % kGroups;
@@ -117,40 +126,84 @@ __device__ __forceinline__ void commit_group(const CommitParams &a) {
   const size_t sg = static_cast<size_t>(b) * kGroups + g;
 
   // 1. keys: thread t holds candidates t + 256 r (r < 5; 1280 = 5 x 256)
-  uint64_t mine[kCand / kCommitThreads];
+  constexpr int kPer = kCand / kCommitThreads;
+  uint64_t mine[kPer];
+  float msc[kPer];
+  bool act[kPer];  // a valid candidate still in the running for the threshold
 #pragma unroll
-  for (int r = 0; r < kCand / kCommitThreads; ++r) {
+  for (int r = 0; r < kPer; ++r) {
     const int i = t + kCommitThreads * r;
     uint64_t k = 0;
+    float sc = 0.f;
+    bool v = false;
     if (i < kBank) {
-      if (i < nb) k = cand_key(a.bank_score[sg * kBank + i], a.bank_src[sg * kBank + i]);
+      if (i < nb) {
+        sc = a.bank_score[sg * kBank + i];
+        k = cand_key(sc, a.bank_src[sg * kBank + i]);
+        v = true;
+      }
     } else {
       const int tt = i - kBank;
-      if (tt < np)
-        k = cand_key(a.pend_score[(static_cast<size_t>(b) * kBlock + tt) * kGroups + g],
-                     a.pend_src[static_cast<size_t>(b) * kBlock + tt]);
+      if (tt < np) {
+        sc = a.pend_score[(static_cast<size_t>(b) * kBlock + tt) * kGroups + g];
+        k = cand_key(sc, a.pend_src[static_cast<size_t>(b) * kBlock + tt]);
+        v = true;
+      }
     }
     mine[r] = k;
+    msc[r] = sc;
+    act[r] = v;
   }
 
-  // 2. threshold: the kk-th largest key (counting equal keys), by radix selection
-  // from the most significant byte down.  Each pass counts, per byte value, the keys
-  // that match the bytes chosen so far, picks the byte under which the kk-th largest
-  // falls, and carries the rank left inside it; once that byte holds a single key,
-  // that key is the threshold.  Absent candidates are 0, below every real key.
+  // 2. threshold: the kk-th largest key (counting equal keys).
+  //  a. A first pass sorts the valid candidates into 255 buckets by score, linearly
+  //     between the segment's smallest and largest number (NaN scores form a bucket
+  //     of their own below them).  The map is monotone, so every key of a higher
+  //     bucket is larger than every key of a lower one; the pass picks the bucket
+  //     holding rank kk and the rank left inside it.
+  //  b. If that bucket holds at most 256 keys, they are gathered and each is ranked
+  //     against the others directly.  Otherwise (scores all equal, heavy ties) radix
+  //     selection continues among the bucket's keys, byte by byte from the top: each
+  //     pass counts, per byte value, the keys that match the bytes chosen so far,
+  //     picks the byte under which the target rank falls and carries the rank left
+  //     inside it; once that byte holds a single key, that key is the threshold.
   uint64_t thr = 0;
   if (kk > 0) {
-    uint64_t prefix = 0, pmask = 0;
-    int rank = kk;
-    for (int shift = 56; shift >= 0; shift -= 8) {
-      hist[t] = 0;
-      __syncthreads();
+    float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < kCand / kCommitThreads; ++r)
-        if ((mine[r] & pmask) == prefix)
-          atomicAdd(&hist[static_cast<int>(mine[r] >> shift) & 255], 1u);
+    for (int r = 0; r < kPer; ++r)
+      if (act[r] && !__builtin_isnan(msc[r])) {
+        lo = fminf(lo, msc[r]);
+        hi = fmaxf(hi, msc[r]);
+      }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      lo = fminf(lo, __shfl_xor(lo, off, 64));
+      hi = fmaxf(hi, __shfl_xor(hi, off, 64));
+    }
+    if (lane == 0) {
+      red_lo[wave] = lo;
+      red_hi[wave] = hi;
+    }
+    hist[t] = 0;
+    if (t == 0) gather_n = 0;
+    __syncthreads();
+    lo = fminf(fminf(red_lo[0], red_lo[1]), fminf(red_lo[2], red_lo[3]));
+    hi = fmaxf(fmaxf(red_hi[0], red_hi[1]), fmaxf(red_hi[2], red_hi[3]));
+    const float scale = 254.0f / (hi - lo);
+    const bool spread = hi > lo && scale < INFINITY;
+    int rank = kk;
+    int count = 0x7fffffff;
+    if (spread) {
+      int bin[kPer];
+#pragma unroll
+      for (int r = 0; r < kPer; ++r) {
+        const float x = (msc[r] - lo) * scale;  // in [0, 254] (NaN for a NaN score)
+        bin[r] = __builtin_isnan(msc[r]) ? 0 : 1 + min(253, static_cast<int>(x));
+        if (act[r]) atomicAdd(&hist[bin[r]], 1u);
+      }
       __syncthreads();
-      // thread t takes byte value 255 - t: the exclusive sum counts the larger ones
+      // thread t takes bucket 255 - t: the exclusive sum counts the larger ones
       const int c = static_cast<int>(hist[255 - t]);
       int total;
       const int above = exclusive_scan(c, wave_tot, wave, lane, total);
@@ -160,27 +213,70 @@ __device__ __forceinline__ void commit_group(const CommitParams &a) {
         sel_count = c;
       }
       __syncthreads();
-      prefix |= static_cast<uint64_t>(sel_digit) << shift;
-      pmask |= static_cast<uint64_t>(255) << shift;
       rank = sel_rank;
-      if (sel_count == 1 || shift == 0) {
-        if (sel_count == 1) {
+      count = sel_count;
 #pragma unroll
-          for (int r = 0; r < kCand / kCommitThreads; ++r)
-            if ((mine[r] & pmask) == prefix) sel_key = mine[r];
-          __syncthreads();
-          thr = sel_key;
-        } else {
-          thr = prefix;
+      for (int r = 0; r < kPer; ++r) act[r] = act[r] && bin[r] == sel_digit;
+    }
+    if (count <= kCommitThreads) {
+      // b. rank the bucket's keys against each other
+#pragma unroll
+      for (int r = 0; r < kPer; ++r)
+        if (act[r]) gather[atomicAdd(&gather_n, 1)] = mine[r];
+      __syncthreads();
+      if (t < count) {
+        const uint64_t k = gather[t];
+        int gt = 0, ge = 0;
+        for (int j = 0; j < count; ++j) {
+          const uint64_t o = gather[j];
+          gt += o > k;
+          ge += o >= k;
         }
-        break;
+        if (gt < rank && rank <= ge) sel_key = k;
+      }
+      __syncthreads();
+      thr = sel_key;
+    } else {
+      uint64_t prefix = 0, pmask = 0;
+      for (int shift = 56; shift >= 0; shift -= 8) {
+        hist[t] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < kPer; ++r)
+          if (act[r] && (mine[r] & pmask) == prefix)
+            atomicAdd(&hist[static_cast<int>(mine[r] >> shift) & 255], 1u);
+        __syncthreads();
+        const int c = static_cast<int>(hist[255 - t]);
+        int total;
+        const int above = exclusive_scan(c, wave_tot, wave, lane, total);
+        if (above < rank && above + c >= rank) {
+          sel_digit = 255 - t;
+          sel_rank = rank - above;
+          sel_count = c;
+        }
+        __syncthreads();
+        prefix |= static_cast<uint64_t>(sel_digit) << shift;
+        pmask |= static_cast<uint64_t>(255) << shift;
+        rank = sel_rank;
+        if (sel_count == 1 || shift == 0) {
+          if (sel_count == 1) {
+#pragma unroll
+            for (int r = 0; r < kPer; ++r)
+              if (act[r] && (mine[r] & pmask) == prefix) sel_key = mine[r];
+            __syncthreads();
+            thr = sel_key;
+          } else {
+            thr = prefix;
+          }
+          break;
+        }
       }
     }
   }
 
   // 3a. keep flags
 #pragma unroll
-  for (int r = 0; r < kCand / kCommitThreads; ++r) {
+  for (int r = 0; r < kPer; ++r) {
     const int i = t + kCommitThreads * r;
     const bool valid = i < kBank ? (i < nb) : (i - kBank < np);
     keep[i] = (kk > 0 && valid && mine[r] >= thr) ? 1 : 0;
@@ -224,31 +320,39 @@ __device__ __forceinline__ void commit_group(const CommitParams &a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) a.keep_idx[sg * kBank + 4 * t + e] = kidx[4 * t + e];
   }
-  // 16-byte pieces: 2 * kPieces per admitted row (K then V).  Each thread issues
-  // kCopyBatch loads before its stores, so the workgroup waits for a handful of
-  // round trips to memory instead of one per piece.
-  const int pieces = n_adm * 2 * kPieces;
-  for (int w0 = 0; w0 < pieces; w0 += kCommitThreads * kCopyBatch) {
-    u32x4 buf[kCopyBatch];
+  // Whole rows per wave: an admitted row's K and V are 2 * kPieces 16-byte pieces,
+  // one per lane (lanes [0, kPieces): K, [kPieces, 2 kPieces): V), so a wave moves
+  // 64 / (2 kPieces) rows per instruction.  Wave w takes rows w, w + 4, ... of the
+  // admitted list; each lane keeps kCopyBatch loads in flight before its stores.
+  {
+    constexpr int kLanesPerRow = 2 * kPieces;             // 64 (BF16) or 32 (FP8)
+    constexpr int kRowsPerInst = 64 / kLanesPerRow;       // 1 or 2
+    constexpr int kRowsPerPass = 4 * kRowsPerInst;        // rows the 4 waves move per instruction
+    const int sub = lane / kLanesPerRow;
+    const int piece = lane % kLanesPerRow;
+    const bool is_v = piece >= kPieces;
+    const size_t off = static_cast<size_t>(piece % kPieces) * 16;
+    const uint8_t *src_base = (is_v ? a.pend_v : a.pend_k) + sg * kBlock * kRowBytes + off;
+    uint8_t *dst_base = (is_v ? a.bank_v : a.bank_k) + sg * kBank * kRowBytes + off;
+    const int first = wave * kRowsPerInst + sub;
+    for (int i0 = first; i0 < n_adm; i0 += kRowsPerPass * kCopyBatch) {
+      u32x4 buf[kCopyBatch];
 #pragma unroll
-    for (int u = 0; u < kCopyBatch; ++u) {
-      // past the end, repeat the last piece: the same bytes go to the same place
-      const int w = min(w0 + t + u * kCommitThreads, pieces - 1);
-      const int row = adm_rows[w / (2 * kPieces)];
-      const int part = w % (2 * kPieces);
-      const uint8_t *src = (part >= kPieces ? a.pend_v : a.pend_k) +
-                           (sg * kBlock + row) * kRowBytes + (part % kPieces) * 16;
-      buf[u] = *reinterpret_cast<const u32x4 *>(src);
-    }
+      for (int u = 0; u < kCopyBatch; ++u) {
+        const int i = i0 + u * kRowsPerPass;
+        if (i < n_adm) {
+          const uint8_t *src = src_base + static_cast<size_t>(adm_rows[i]) * kRowBytes;
+          buf[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src));
+        }
+      }
 #pragma unroll
-    for (int u = 0; u < kCopyBatch; ++u) {
-      const int w = min(w0 + t + u * kCommitThreads, pieces - 1);
-      const int row = adm_rows[w / (2 * kPieces)];
-      const int part = w % (2 * kPieces);
-      const int sl = adm_slot[row];
-      uint8_t *dst = (part >= kPieces ? a.bank_v : a.bank_k) + (sg * kBank + sl) * kRowBytes +
-                     (part % kPieces) * 16;
-      *reinterpret_cast<u32x4 *>(dst) = buf[u];
+      for (int u = 0; u < kCopyBatch; ++u) {
+        const int i = i0 + u * kRowsPerPass;
+        if (i < n_adm) {
+          uint8_t *dst = dst_base + static_cast<size_t>(adm_slot[adm_rows[i]]) * kRowBytes;
+          __builtin_nontemporal_store(buf[u], reinterpret_cast<u32x4 *>(dst));
+        }
+      }
     }
   }
   if (t < n_adm) {

@@ -8,15 +8,18 @@
 //
 // Design.  Stage 1 is a dense FP32 contraction (256 flop per input byte), so it
 // runs on v_mfma_f32_32x32x2f32:
-//  * one workgroup (4 waves) per 128-row tile and all 256 columns; each wave owns
-//    a 64 x 128 block = 2 x 4 accumulators of 32 x 32 (32-row tiles for calls too
-//    small to give every CU a 128-row tile);
+//  * one workgroup (4 waves) per 256-row tile and all 256 columns; each wave owns
+//    a 128 x 128 block = 4 x 4 accumulators of 32 x 32 (256 accumulator registers
+//    per lane), so W1 is read once per 256 rows and each staged slice feeds 256
+//    MFMAs per wave; calls too small to give every CU a 256-row tile use 128-, 64-
+//    or 32-row tiles;
 //  * K is walked in slices of 32: BF16 rows are widened (exactly) to FP32 while
 //    being staged in LDS row-major (m-major), W1 is staged column-major (n-major);
 //    each lane's 16 operands of a slice are then contiguous, so a slice's operands
-//    come in with 24 16-byte LDS reads and its 128 MFMAs issue back to back; two
-//    LDS buffers, the next slice's global loads in flight meanwhile;
-//  * stage 2 (x W2, 256 -> 4) is fused: the 128 x 256 block of stage-1 results is
+//    come in with 16-byte LDS reads (32 per slice on 256-row tiles) and its MFMAs
+//    issue back to back; two LDS buffers, the next slice's global loads in flight
+//    meanwhile;
+//  * stage 2 (x W2, 256 -> 4) is fused: the rows x 256 block of stage-1 results is
 //    passed through LDS in two column halves and every output row is summed over
 //    its 256 columns in the same fixed order, so identical input rows give
 //    bit-identical scores wherever they sit.
@@ -28,8 +31,6 @@ constexpr int kKt = 32;             // contraction depth of one staged slice
 constexpr int kStr = kKt + 4;       // LDS row stride (floats) of the m-major / n-major slices
 constexpr int kZStr = 129;          // stage-1 block: [row][col], floats (one column half)
 constexpr int kScoreThreads = 256;
-constexpr int kMaxRowsWG = 128;
-constexpr int kStageFloats = kMaxRowsWG * kStr + kMid * kStr;
 
 struct ScoreParams {
   const uint16_t *hidden;
@@ -46,10 +47,11 @@ struct ScoreParams {
 // 16-byte reads.  The same k order is used for A and B, so the products pair up.
 //
 // Tile shapes: the 4 waves are arranged WR x (4/WR); each wave owns RB row blocks
-// and CB column blocks of 32 x 32.  Large calls use 128-row tiles (WR=2, RB=2,
-// CB=4); calls with fewer such tiles than CUs use 64-row tiles (WR=2, RB=1, CB=4)
-// or, fewer still, 32-row tiles (WR=1, RB=1, CB=2).  All run the same instruction
-// sequence per output element, so results do not depend on the tile shape.
+// and CB column blocks of 32 x 32.  Large calls use 256-row tiles (WR=2, RB=4,
+// CB=4); calls with fewer such tiles than CUs use 128-row tiles (WR=2, RB=2, CB=4),
+// 64-row tiles (WR=2, RB=1, CB=4) or, fewer still, 32-row tiles (WR=1, RB=1,
+// CB=2).  All run the same instruction sequence per output element, so results do
+// not depend on the tile shape.
 // Up to RMA_MAX_JOBS independent calls of the same row count in one launch
 // (blockIdx.y picks the call): the layers of a block, scored together.
 struct ScoreJobs {
@@ -66,8 +68,9 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score_kernel(ScoreJobs jobs)
   constexpr int kAFloats = kRows * kStr;
   constexpr int kSF = kAFloats + kMid * kStr;
   constexpr int kTpr = kScoreThreads / kRows;  // staging threads per hidden row
-  constexpr int kKpt = kKt / kTpr;             // k values each of them stages (16, 8 or 4)
-  __shared__ __align__(16) float smem[2 * kStageFloats];
+  constexpr int kKpt = kKt / kTpr;             // k values each of them stages (32, 16, 8 or 4)
+  static_assert(kRows * kZStr <= 2 * kSF, "the stage-1 block fits in the staging buffers");
+  __shared__ __align__(16) float smem[2 * kSF];
   __shared__ float w2s[kMid * kGroups];
 
   const int tid = threadIdx.x;
@@ -88,7 +91,18 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score_kernel(ScoreJobs jobs)
   uint32_t ha[kKpt / 2];
   float wb[kKt];
   auto load_stage = [&](int kt) {
-    if constexpr (kKpt == 16) {
+    if constexpr (kKpt == 32) {
+      uint4 u[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0),
+                    make_uint4(0, 0, 0, 0)};
+      if (arow_ok) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) u[q] = *reinterpret_cast<const uint4 *>(arow + kt * kKt + 8 * q);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        ha[4 * q] = u[q].x; ha[4 * q + 1] = u[q].y; ha[4 * q + 2] = u[q].z; ha[4 * q + 3] = u[q].w;
+      }
+    } else if constexpr (kKpt == 16) {
       uint4 u0 = make_uint4(0, 0, 0, 0), u1 = u0;
       if (arow_ok) {
         u0 = *reinterpret_cast<const uint4 *>(arow + kt * kKt);
@@ -235,12 +249,17 @@ static rma_status check_score(const uint16_t *hidden, int64_t n_rows, int64_t ld
 
 static rma_status launch_score(const ScoreJobs &jobs, int n_jobs, int64_t n_rows, void *stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // The largest row tile that still gives every CU (256) a workgroup: 128 rows,
-  // then 64, then 32 (a larger tile reads W1 fewer times per row).
+  // The largest row tile that still gives every CU (256) a workgroup: 256 rows,
+  // then 128, 64, 32 (a larger tile reads W1 fewer times per row).
+  const int64_t huge = (n_rows + 255) / 256;
   const int64_t big = (n_rows + 127) / 128;
   const int64_t mid = (n_rows + 63) / 64;
   const unsigned nj = static_cast<unsigned>(n_jobs);
-  if (big >= 256) {
+  if (huge >= 256) {
+    if (huge > 0x7fffffff) return RMA_E_ARG;
+    hipLaunchKernelGGL((score_kernel<2, 4, 4>), dim3(static_cast<unsigned>(huge), nj),
+                       dim3(kScoreThreads), 0, s, jobs);
+  } else if (big >= 256) {
     if (big > 0x7fffffff) return RMA_E_ARG;
     hipLaunchKernelGGL((score_kernel<2, 2, 4>), dim3(static_cast<unsigned>(big), nj),
                        dim3(kScoreThreads), 0, s, jobs);

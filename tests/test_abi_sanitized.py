@@ -4,6 +4,7 @@ UndefinedBehaviorSanitizer: the ABI tests run again, in a child interpreter with
 the ASan runtime preloaded, against a sanitized build.  CPU only."""
 
 import os
+import shutil
 import subprocess
 import sys
 
@@ -29,8 +30,11 @@ def test_abi_checks_under_host_sanitizers():
             "import pytest\n"
             "sys.exit(pytest.main(['-q', '-p', 'no:cacheprovider', %r]))\n"
             % (ROOT, lib, os.path.join(ROOT, "tests", "test_abi.py")))
-    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
-                       timeout=600, cwd=ROOT)
+    try:
+        r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                           timeout=600, cwd=ROOT)
+    finally:
+        shutil.rmtree(os.path.dirname(lib), ignore_errors=True)
     print(r.stdout[-2000:], r.stderr[-2000:])
     assert r.returncode == 0, r.stdout[-4000:] + r.stderr[-4000:]
     assert "passed" in r.stdout and "failed" not in r.stdout
