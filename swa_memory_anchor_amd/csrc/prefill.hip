@@ -15,25 +15,29 @@
 //     straight into pending rows n_pend .. n_pend + C - 1, the window keys into the
 //     workspace (the ring cannot be overwritten yet: earlier tokens of the chunk
 //     still read the positions the chunk will replace).
-//  2. prefill_attn: one workgroup per (branch, sequence, group, 32-token tile): 128
-//     query rows (32 tokens x 4 heads), 32 per wave, held in AGPRs in the operand
-//     layout of v_mfma_f32_32x32x16_bf16 after norm + rotary.  Key tiles of 32
-//     reach LDS through buffer loads straight into LDS, four stages deep (three
-//     tiles in flight while one is computed); rows are XOR-swizzled against bank
-//     conflicts.  S^T = K Q^T reads K rows; O^T += V^T P^T reads V^T with
-//     transposing LDS reads, in the key order of the score accumulator, so P goes
-//     from registers straight into the second product.  Keys are masked by
-//     position (ring age, causal order in the chunk).  The softmax reference
-//     maximum moves only when a row's maximum grows by more than 2^8, so the 128
-//     accumulators are rarely rescaled.  The tiles of one unit are numbered onto
-//     one XCD so they share its L2.
+//  2. prefill_attn: one workgroup per (branch, sequence, group, 64-token tile): 256
+//     query rows (64 tokens x 4 heads), 32 per wave, eight waves (two per SIMD),
+//     held in VGPRs in the operand layout of v_mfma_f32_32x32x16_bf16 after norm +
+//     rotary.  Every K/V tile brought into LDS serves 256 rows: the L2-to-LDS
+//     traffic per flop is half that of 128-row workgroups, and that traffic ran
+//     close to the MFMA time.  Key tiles of 32 reach LDS through buffer loads
+//     straight into LDS, four stages deep (three tiles in flight while one is
+//     computed); rows are XOR-swizzled against bank conflicts.  S^T = K Q^T reads
+//     K rows; O^T += V^T P^T reads V^T with transposing LDS reads, in the key
+//     order of the score accumulator, so P goes from registers straight into the
+//     second product.  Keys are masked by position (ring age, causal order in the
+//     chunk).  The softmax reference maximum moves only when a row's maximum grows
+//     by more than 2^8, so the 128 accumulators are rarely rescaled.  The rotary
+//     (cos, sin) of each (token, pair) is formed once per wave and shared across
+//     the token's four heads.  The tiles of one unit are numbered onto one XCD so
+//     they share its L2.
 //  3. prefill_ring: copy the chunk's window K/V into ring slots, then advance
 //     n_pend and pos.
 #include "rma_device.h"
 
 namespace rma {
 
-constexpr int kPWaves = 4;                         // waves per attention workgroup
+constexpr int kPWaves = 8;                         // waves per attention workgroup (2 per SIMD)
 constexpr int kPThreads = 64 * kPWaves;
 constexpr int kPRowsWave = 32;                     // query rows per wave (8 tokens x 4 heads)
 constexpr int kPTok = kPWaves * kPRowsWave / kHeadsPerGroup;  // 64 tokens per workgroup
@@ -165,6 +169,13 @@ __shared__ __align__(16) uint16_t pf_v1[kTileElems];
 __shared__ __align__(16) uint16_t pf_v2[kTileElems];
 __shared__ __align__(16) uint16_t pf_v3[kTileElems];
 static_assert(kStages == 4, "the tile loop below is written out for four stages");
+// Per-thread LDS offsets, read back per tile (keeping them in registers across the
+// tile loop would cost registers the loop needs): the lane's K and V chunk offsets
+// of its two loads, and its four V^T read offsets.
+typedef int pf_i32x4 __attribute__((ext_vector_type(4)));
+typedef volatile __attribute__((address_space(3))) pf_i32x4 lds_vi32x4;
+__shared__ pf_i32x4 pf_dma_tab[kPThreads];
+__shared__ pf_i32x4 pf_vrd_tab[kPThreads];
 
 template <int N>
 __device__ __forceinline__ void wait_vm_barrier() {
@@ -225,33 +236,39 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(PrefillParams a
   const PSeg &sg_ = si_##sg_ == 0 ? seg0 : (si_##sg_ == 1 ? seg1 : seg2);                    \
   const int k0_ = ((t_) - (si_##sg_ == 0 ? 0 : (si_##sg_ == 1 ? tl0 : tl0 + tl1))) * kPKeys;
 
-  // Load-to-LDS of tile t into stage st: each wave moves 4 KB of K and 4 KB of V,
+  // Load-to-LDS of tile t into stage st: each wave moves 2 KB of K and 2 KB of V,
   // 1 KB (two rows) per instruction; lane L fills chunk position L % 32 of row
   // 2i + L / 32, i.e. fetches the chunk that the swizzle puts there.  Rows past
   // the segment's end read as zero.
   // The tile's first row and the wave's row pair go into the scalar offset; the
-  // lane's part (odd row of the pair, swizzled chunk) is fixed per load and is
-  // formed once here.
-  const int dma_row_lo = lane >> 5, dma_pos = lane & 31;
+  // lane's part (odd row of the pair, swizzled chunk) is fixed per load, formed
+  // once here and kept in an LDS table that each tile reads back.
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-  int dma_kc[4], dma_vc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 2 * (4 * wave_s + i) + dma_row_lo;
-    dma_kc[i] = (dma_pos ^ k_swz(row)) << 4;
-    dma_vc[i] = (dma_pos ^ v_swz(row)) << 4;
+  constexpr int kPairs = kPKeys / 2 / kPWaves;  // row pairs each wave moves per tile: 2
+  static_assert(kPairs == 2, "the offset table holds two K and two V chunk offsets");
+  {
+    const int rlo = lane >> 5, cpos = lane & 31;
+    pf_i32x4 t;
+    const int row0 = 2 * (kPairs * wave_s) + rlo, row1 = row0 + 2;
+    t.x = (cpos ^ k_swz(row0)) << 4;
+    t.y = (cpos ^ k_swz(row1)) << 4;
+    t.z = (cpos ^ v_swz(row0)) << 4;
+    t.w = (cpos ^ v_swz(row1)) << 4;
+    pf_dma_tab[threadIdx.x] = t;
   }
 #define PREFILL_ISSUE_TILE(t_, kdst_, vdst_)                                                 \
   {                                                                                          \
     PREFILL_TILE_SEG(t_, isg, ik0)                                                           \
-    const int lo_off = dma_row_lo * isg.stride;                                              \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                          \
-      const int pr = 4 * wave_s + i;                                                         \
+    const pf_i32x4 dt = ((lds_vi32x4 *)pf_dma_tab)[threadIdx.x];                             \
+    const int lo_off = (lane >> 5) * isg.stride;                                             \
+    const int kc[2] = {dt.x, dt.y}, vc[2] = {dt.z, dt.w};                                    \
+    _Pragma("unroll") for (int i = 0; i < kPairs; ++i) {                                     \
+      const int pr = kPairs * wave_s + i;                                                    \
       const int soff = (ik0 + 2 * pr) * isg.stride;                                          \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(isg.k, (lds_void *)&kdst_[pr * 2 * kDim], 16, \
-                                               lo_off + dma_kc[i], soff, 0, 0);              \
+                                               lo_off + kc[i], soff, 0, 0);                  \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(isg.v, (lds_void *)&vdst_[pr * 2 * kDim], 16, \
-                                               lo_off + dma_vc[i], soff, 0, 0);              \
+                                               lo_off + vc[i], soff, 0, 0);                  \
     }                                                                                        \
   }
   // Start the first tiles' loads before the query prologue.
@@ -266,7 +283,6 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(PrefillParams a
   const int my_tl = wave * (kPRowsWave / kHeadsPerGroup) + rl / kHeadsPerGroup;
   const int my_head = rl % kHeadsPerGroup;
   const int my_tok = tok0 + my_tl;
-  const int my_pos = p0 + 1 + my_tok;
   const bool my_row_ok = my_tl < ntok && fits;
   bf16x8 qb[16];
   {
@@ -276,18 +292,39 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(PrefillParams a
          g * kHeadsPerGroup + my_head) * kDim + 8 * hh;
     const float *gam = (anchor ? a.gq_rma : a.gq_win) + 8 * hh;
     u32x4 raw[16];
-    float ss = 0.f;
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      raw[s] = *reinterpret_cast<const u32x4 *>(qrow + 16 * s);
+    for (int s = 0; s < 16; ++s) raw[s] = *reinterpret_cast<const u32x4 *>(qrow + 16 * s);
+    // (cos, sin) of the wave's 8 tokens x 32 rotary pairs, each formed once: lane L
+    // takes token L / 8 and pairs 4 (L % 8) .. +3 (theta_i = r^i by binary powering
+    // for the first pair, then repeated multiplication)
+    float rc[4], rsn[4];
+    {
+      const int tpos = p0 + 1 + tok0 + wave * (kPRowsWave / kHeadsPerGroup) + (lane >> 3);
+      const int i0 = 4 * (lane & 7);
+      double theta = 1.0, sq = a.rope_ratio;
+#pragma unroll
+      for (int k = 0; k < 5; ++k) {
+        if ((i0 >> k) & 1) theta *= sq;
+        sq *= sq;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        rope_cos_sin_theta(theta, tpos, rc[j], rsn[j]);
+        theta *= a.rope_ratio;
+      }
+    }
+    float ssp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float lo = bf16_lo(raw[s][e]), hi = bf16_hi(raw[s][e]);
-        ss += lo * lo + hi * hi;
+        ssp[e] = fmaf(lo, lo, fmaf(hi, hi, ssp[e]));
       }
-    }
+    float ss = (ssp[0] + ssp[1]) + (ssp[2] + ssp[3]);
     ss += __shfl_xor(ss, 32, 64);
     const float inv = 1.0f / sqrtf(ss * (1.0f / kDim) + a.eps);
+    const float inv_sc = my_row_ok ? inv * kPQScale : 0.f;  // rows not stored get zeros
     // dims past the rotary part: scale and pack in place
 #pragma unroll
     for (int s = 4; s < 16; ++s) {
@@ -296,17 +333,13 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(PrefillParams a
       const float gm[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
       u32x4 w;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float lo = bf16_lo(raw[s][e]) * inv * gm[2 * e];
-        const float hi = bf16_hi(raw[s][e]) * inv * gm[2 * e + 1];
-        w[e] = my_row_ok ? pack_bf16x2(lo * kPQScale, hi * kPQScale) : 0u;
-      }
+      for (int e = 0; e < 4; ++e)
+        w[e] = pack_bf16x2_hw(bf16_lo(raw[s][e]) * inv_sc * gm[2 * e],
+                              bf16_hi(raw[s][e]) * inv_sc * gm[2 * e + 1]);
       qb[s] = pbitcast<bf16x8>(w);
     }
     // rotary dims i = 16s + 8hh + e (s = 0, 1) pair with i + 32 (chunk s + 2, same
-    // lane); theta_i = r^i, formed from r^(16s + 8hh) by repeated multiplication
-    const double r8 = a.rope_ratio * a.rope_ratio * a.rope_ratio * a.rope_ratio *
-                      a.rope_ratio * a.rope_ratio * a.rope_ratio * a.rope_ratio;
+    // lane); their (cos, sin) sit in lane 8 (rl / 4) + i / 4, slot i % 4
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const float4 ga0 = *reinterpret_cast<const float4 *>(gam + 16 * s);
@@ -315,36 +348,35 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(PrefillParams a
       const float4 gb1 = *reinterpret_cast<const float4 *>(gam + 16 * (s + 2) + 4);
       const float gma[8] = {ga0.x, ga0.y, ga0.z, ga0.w, ga1.x, ga1.y, ga1.z, ga1.w};
       const float gmb[8] = {gb0.x, gb0.y, gb0.z, gb0.w, gb1.x, gb1.y, gb1.z, gb1.w};
-      double theta = (s ? r8 * r8 : 1.0) * (hh ? r8 : 1.0);
-      u32x4 wa, wb;
+      float y1[8], y2[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float c, sn;
-        rope_cos_sin_theta(theta, my_pos, c, sn);
-        theta *= a.rope_ratio;
+        const int src = 8 * (rl >> 2) + 4 * s + 2 * hh + (e >> 2);
+        const float c = __shfl(rc[e & 3], src, 64);
+        const float sn = __shfl(rsn[e & 3], src, 64);
         const uint32_t ra = raw[s][e >> 1], rb = raw[s + 2][e >> 1];
         const float x1 = ((e & 1) ? bf16_hi(ra) : bf16_lo(ra)) * inv * gma[e];
         const float x2 = ((e & 1) ? bf16_hi(rb) : bf16_lo(rb)) * inv * gmb[e];
-        const float y1 = (x1 * c - x2 * sn) * kPQScale;
-        const float y2 = (x2 * c + x1 * sn) * kPQScale;
-        const uint32_t b1 = my_row_ok ? f32_to_bf16(y1) : 0u;
-        const uint32_t b2 = my_row_ok ? f32_to_bf16(y2) : 0u;
-        if (e & 1) {
-          wa[e >> 1] |= b1 << 16;
-          wb[e >> 1] |= b2 << 16;
-        } else {
-          wa[e >> 1] = b1;
-          wb[e >> 1] = b2;
-        }
+        const float k = my_row_ok ? kPQScale : 0.f;
+        y1[e] = (x1 * c - x2 * sn) * k;
+        y2[e] = (x2 * c + x1 * sn) * k;
+      }
+      u32x4 wa, wb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        wa[e] = pack_bf16x2_hw(y1[2 * e], y1[2 * e + 1]);
+        wb[e] = pack_bf16x2_hw(y2[2 * e], y2[2 * e + 1]);
       }
       qb[s] = pbitcast<bf16x8>(wa);
       qb[s + 2] = pbitcast<bf16x8>(wb);
     }
   }
-  // keep the query operands in AGPRs (read-only MFMA B operands), leaving the VGPRs
-  // to the accumulators and the LDS operand reads
+  // The query operands stay in VGPRs: with two waves per SIMD a wave has 256
+  // registers, and any AGPR use would split them evenly between the two files,
+  // while the tile loop needs about 250 arch VGPRs (128 accumulators, 64 query
+  // operands, scores, operand reads and LDS offsets).
 #pragma unroll
-  for (int s = 0; s < 16; ++s) asm volatile("" : "+a"(qb[s]));
+  for (int s = 0; s < 16; ++s) asm volatile("" : "+v"(qb[s]));
 
   float m_ref = -INFINITY, l_run = 0.f;  // reference maximum (log2 units) and row sum
   f32x16 acc[kDim / 32];
@@ -362,71 +394,48 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(PrefillParams a
   const int age_max = min(p0, kWindow - 2 - my_tok);
   const int wave_age_max = min(p0, kWindow - 2 - wave_last_tok);
 
-  // LDS operand addresses (elements).  K (A of S^T = K Q^T): key rl, chunk 2s + hh.
+  // LDS operand offsets (bytes).  K (A of S^T = K Q^T): key rl, chunk 2s + hh.
   // V^T (A of O^T = V^T P^T) by transposed reads: lane i of 16-lane group G points
   // at key 16j + 8r + 4(G/2) + i/4, dims 32d + 16(G%2) + 4(i%4) .. +3; the read
   // hands lane i dim 32d + 16(G%2) + i of the four keys 16j + 8r + 4(G/2) + 0..3.
   // chunk 2s + hh of key rl sits at 16 (s / 8) + ((2 (s % 8) + hh) ^ (rl & 15))
   int k_addr[8];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) k_addr[c] = rl * kDim + (((2 * c + hh) ^ k_swz(rl)) << 3);
+  for (int c = 0; c < 8; ++c) k_addr[c] = 2 * (rl * kDim + (((2 * c + hh) ^ k_swz(rl)) << 3));
   const int vg = lane >> 4, vi = lane & 15;
   const int v_key = 4 * (vg >> 1) + (vi >> 2);  // + 16j + 8r (keeps key & 3)
   const int v_dim = 16 * (vg & 1) + 4 * (vi & 3);  // + 32d
   // chunk 4d + x (x = v_dim / 8) sits at 4 (d ^ q) + x with q = key & 3, i.e. at the
   // lane's base for d % 4 plus 16 chunks (128 elements) per d / 4
-  int v_addr[4];
+  int v_addr[4];  // bytes
 #pragma unroll
   for (int c = 0; c < 4; ++c)
-    v_addr[c] = v_key * kDim + ((4 * (c ^ (v_key & 3)) + (v_dim >> 3)) << 3) + (v_dim & 7);
+    v_addr[c] = 2 * (v_key * kDim + ((4 * (c ^ (v_key & 3)) + (v_dim >> 3)) << 3) + (v_dim & 7));
+  pf_vrd_tab[threadIdx.x] = pf_i32x4{v_addr[0], v_addr[1], v_addr[2], v_addr[3]};
 
-  // One key tile on this wave's 32 rows.  S^T = K Q^T in two independent MFMA
-  // chains (even / odd dim steps); mask; online softmax against a reference
-  // maximum that moves only when a row's maximum grows by more than kPTau (so P
-  // <= 2^kPTau and the 128 accumulators are rarely rescaled); O^T += V^T P^T.
+  // One key tile on this wave's 32 rows: S^T = K Q^T (one MFMA chain over the 16
+  // dim steps), mask, online softmax against a reference maximum that moves only
+  // when a row's maximum grows by more than kPTau, O^T += V^T P^T.  The K offsets
+  // pass through an opaque move per tile and the V^T offsets come from an LDS
+  // table: hoisted out of the loop, each stage's base would occupy registers of
+  // its own instead of folding into the LDS instructions' offsets.
 #define PREFILL_COMPUTE_TILE(t, kt, vt)                                                      \
   {                                                                                          \
     PREFILL_TILE_SEG(t, csg, k0)                                                             \
     const int kind = csg.kind;                                                               \
     const int n = csg.n;                                                                     \
-    /* chunk tiles that start after this wave's last token are invisible to it */            \
     if (wave_live && !(kind == 2 && k0 > wave_last_tok)) {                                   \
-      /* K operands read eight dim steps ahead of their MFMAs (the scheduler would */       \
-      /* otherwise issue each read just before its use and wait on every one) */             \
-      u32x4 kf[8];                                                                           \
-      _Pragma("unroll") for (int s = 0; s < 8; ++s) kf[s] =                                  \
-          *reinterpret_cast<const u32x4 *>(kt + k_addr[s & 7] + 128 * (s >> 3));              \
-      __builtin_amdgcn_sched_barrier(0);                                                     \
-      f32x16 sc, sc1;                                                                        \
-      _Pragma("unroll") for (int s = 0; s < 8; s += 2) {                                     \
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pbitcast<bf16x8>(kf[s]), qb[s],         \
-                                                     s ? sc : f32x16{}, 0, 0, 0);            \
-        kf[s] = *reinterpret_cast<const u32x4 *>(kt + k_addr[s & 7] + 128 * ((s + 8) >> 3));  \
-        sc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pbitcast<bf16x8>(kf[s + 1]), qb[s + 1], \
-                                                      s ? sc1 : f32x16{}, 0, 0, 0);          \
-        kf[s + 1] = *reinterpret_cast<const u32x4 *>(kt + k_addr[(s + 1) & 7] +              \
-                                                     128 * ((s + 9) >> 3));                   \
+      _Pragma("unroll") for (int c = 0; c < 8; ++c) asm volatile("" : "+v"(k_addr[c]));     \
+      f32x16 sc = {};                                                                        \
+      _Pragma("unroll") for (int s = 0; s < 16; ++s) {                                       \
+        const u32x4 kv = *reinterpret_cast<const u32x4 *>(                                   \
+            reinterpret_cast<const char *>(kt) + k_addr[s & 7] + 256 * (s >> 3));                \
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pbitcast<bf16x8>(kv), qb[s], sc, 0, 0,  \
+                                                     0);                                     \
       }                                                                                      \
-      __builtin_amdgcn_sched_barrier(0);                                                     \
-      _Pragma("unroll") for (int s = 8; s < 16; s += 2) {                                    \
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pbitcast<bf16x8>(kf[s - 8]), qb[s], sc, \
-                                                     0, 0, 0);                               \
-        sc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pbitcast<bf16x8>(kf[s - 7]),           \
-                                                      qb[s + 1], sc1, 0, 0, 0);              \
-      }                                                                                      \
-      /* first half of the V^T operands: independent of the softmax, read now */            \
-      s16x4_t vf[2 * (kDim / 32)];                                                           \
-      _Pragma("unroll") for (int d = 0; d < kDim / 32; ++d) {                                \
-        const int vb = v_addr[d & 3] + 128 * (d >> 2);                     \
-        vf[2 * d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + vb));         \
-        vf[2 * d + 1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + vb + 8 * kDim)); \
-      }                                                                                      \
-      _Pragma("unroll") for (int r = 0; r < 16; ++r) sc[r] += sc1[r];                        \
       /* key of register r: kl + 8(r/4) + r%4 */                                             \
       const int kl = k0 + 4 * hh;                                                            \
       if (kind == 1) {                                                                       \
-        /* ring ages in this tile run down from A (no wrap when A >= 31); every row of */    \
-        /* the wave sees ages up to wave_age_max */                                          \
         const int A = (p0 - k0) & (kWindow - 1);                                             \
         if (A < kPKeys - 1 || A > wave_age_max) {                                            \
           const int age0 = p0 - kl;                                                          \
@@ -437,14 +446,16 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(PrefillParams a
         }                                                                                    \
       } else if (kind == 2) {                                                                \
         if (k0 + kPKeys - 1 > wave_first_tok) {                                              \
+          /* the lane index from mbcnt: nothing kept live across the loop */                \
+          const int ln_ = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); \
+          const int tok_ = wave_first_tok + ((ln_ & 31) >> 2);                               \
           _Pragma("unroll") for (int r = 0; r < 16; ++r) sc[r] =                             \
-              kl + 8 * (r >> 2) + (r & 3) <= my_tok ? sc[r] : -INFINITY;                     \
+              kl + 8 * (r >> 2) + (r & 3) <= tok_ ? sc[r] : -INFINITY;                       \
         }                                                                                    \
       } else if (k0 + kPKeys > n) {                                                          \
         _Pragma("unroll") for (int r = 0; r < 16; ++r) sc[r] =                               \
             kl + 8 * (r >> 2) + (r & 3) < n ? sc[r] : -INFINITY;                             \
       }                                                                                      \
-      /* row maximum: a tree over the lane's 16 keys, then across the lane pair */          \
       float m8[8];                                                                           \
       _Pragma("unroll") for (int r = 0; r < 8; ++r) m8[r] = fmaxf(sc[r], sc[r + 8]);          \
       _Pragma("unroll") for (int r = 0; r < 4; ++r) m8[r] = fmaxf(m8[r], m8[r + 4]);          \
@@ -454,10 +465,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(PrefillParams a
                                                          __float_as_uint(mt), false, false); \
         mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));                          \
       }                                                                                      \
-      /* move the reference only past kPTau (covers m_ref = -inf, mt finite) */             \
       const bool move = mt > m_ref + kPTau;                                                  \
       const float m_use = move ? mt : m_ref;                                                 \
-      /* rows with nothing accumulated yet need no rescale */                                \
       const float alpha =                                                                    \
           (move && m_ref != -INFINITY) ? __builtin_amdgcn_exp2f(m_ref - m_use) : 1.f;        \
       if (__any(alpha != 1.f)) {                                                             \
@@ -466,36 +475,28 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(PrefillParams a
         l_run *= alpha;                                                                      \
       }                                                                                      \
       m_ref = m_use;                                                                         \
-      /* masked scores are -inf: exp2 gives 0; a row with no reference yet has no */        \
-      /* visible key in this tile either */                                                  \
       const float m_sub = m_use == -INFINITY ? 0.f : m_use;                                  \
       u32x4 pw[2];                                                                           \
       _Pragma("unroll") for (int r = 0; r < 16; r += 2) pw[r >> 3][(r & 7) >> 1] =           \
           pack_bf16x2_hw(__builtin_amdgcn_exp2f(sc[r] - m_sub),                              \
                          __builtin_amdgcn_exp2f(sc[r + 1] - m_sub));                         \
-      /* O^T += V^T P^T: lane holds dims 32d + 8(r/4) + 4hh + r%4 of row rl */               \
+      const pf_i32x4 vt4 = ((lds_vi32x4 *)pf_vrd_tab)[threadIdx.x];                            \
+      const int va[4] = {vt4.x, vt4.y, vt4.z, vt4.w};                                        \
       _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                        \
         const bf16x8 pb = pbitcast<bf16x8>(pw[j]);                                           \
-        if (j == 1) {                                                                        \
-          _Pragma("unroll") for (int d = 0; d < kDim / 32; ++d) {                            \
-            const int vb = v_addr[d & 3] + 128 * (d >> 2) + 16 * kDim;   \
-            vf[2 * d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + vb));     \
-            vf[2 * d + 1] =                                                                  \
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + vb + 8 * kDim));  \
-          }                                                                                  \
-        }                                                                                    \
-        __builtin_amdgcn_sched_barrier(0);                                                   \
         _Pragma("unroll") for (int d = 0; d < kDim / 32; ++d) {                              \
-          const s16x4_t lohi[2] = {vf[2 * d], vf[2 * d + 1]};                                \
+          const int vb = va[d & 3] + 2 * (128 * (d >> 2) + 16 * kDim * j);                   \
+          const char *vp = reinterpret_cast<const char *>(vt) + vb;                          \
+          const s16x4_t lohi[2] = {                                                          \
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vp)),                    \
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vp + 16 * kDim))};       \
           acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pbitcast<bf16x8>(lohi), pb,       \
                                                            acc[d], 0, 0, 0);                 \
         }                                                                                    \
-        __builtin_amdgcn_sched_barrier(0);                                                   \
       }                                                                                      \
-      /* row sums (lane-partial) of the rounded probabilities, off the MFMA path */         \
-      _Pragma("unroll") for (int q = 0; q < 8; ++q)                                          \
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(pbitcast<bf16x2_t>(pw[q >> 2][q & 3]),      \
-                                                  kOnesBf16x2, l_run, false);                \
+      _Pragma("unroll") for (int q = 0; q < 8; ++q) l_run =                                  \
+          __builtin_amdgcn_fdot2_f32_bf16(pbitcast<bf16x2_t>(pw[q >> 2][q & 3]), kOnesBf16x2, \
+                                          l_run, false);                                     \
     }                                                                                        \
   }
 
