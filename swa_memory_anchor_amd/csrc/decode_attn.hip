@@ -310,14 +310,12 @@ __device__ __forceinline__ void accumulate_tile(f32x4 sc, int lane, const uint16
   float psum = 0.f;
   if (m_new != -INFINITY) {
     alpha = __builtin_amdgcn_exp2f(st.m - m_new);
-    const uint32_t p0 = f32_to_bf16(__builtin_amdgcn_exp2f(sc[0] - m_new));
-    const uint32_t p1 = f32_to_bf16(__builtin_amdgcn_exp2f(sc[1] - m_new));
-    const uint32_t p2 = f32_to_bf16(__builtin_amdgcn_exp2f(sc[2] - m_new));
-    const uint32_t p3 = f32_to_bf16(__builtin_amdgcn_exp2f(sc[3] - m_new));
+    pw0 = pack_bf16x2_cvt(__builtin_amdgcn_exp2f(sc[0] - m_new),
+                          __builtin_amdgcn_exp2f(sc[1] - m_new));
+    pw1 = pack_bf16x2_cvt(__builtin_amdgcn_exp2f(sc[2] - m_new),
+                          __builtin_amdgcn_exp2f(sc[3] - m_new));
     // the denominator uses the same rounded weights as the numerator
-    psum = (bf16_to_f32(p0) + bf16_to_f32(p1)) + (bf16_to_f32(p2) + bf16_to_f32(p3));
-    pw0 = p0 | (p1 << 16);
-    pw1 = p2 | (p3 << 16);
+    psum = (bf16_lo(pw0) + bf16_hi(pw0)) + (bf16_lo(pw1) + bf16_hi(pw1));
   }
   // rescale the accumulators only when some head's running maximum moved (alpha
   // is exactly 1 otherwise)
@@ -672,12 +670,14 @@ __device__ __forceinline__ void accumulate_tile_fp8(const f32x4 (&sc)[2], int la
     for (int u = 0; u < 2; ++u) {
       float e[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        e[i] = __builtin_amdgcn_exp2f(sc[u][i] - m_new);
-        psum += bf16_to_f32(static_cast<uint16_t>(f32_to_bf16(e[i])));
-      }
-      pw[2 * u] = pack_bf16x2(e[0] * vsc[u][0], e[1] * vsc[u][1]);
-      pw[2 * u + 1] = pack_bf16x2(e[2] * vsc[u][2], e[3] * vsc[u][3]);
+      for (int i = 0; i < 4; ++i) e[i] = __builtin_amdgcn_exp2f(sc[u][i] - m_new);
+      const uint32_t r0 = pack_bf16x2_cvt(e[0], e[1]), r1 = pack_bf16x2_cvt(e[2], e[3]);
+      psum += bf16_lo(r0);
+      psum += bf16_hi(r0);
+      psum += bf16_lo(r1);
+      psum += bf16_hi(r1);
+      pw[2 * u] = pack_bf16x2_cvt(e[0] * vsc[u][0], e[1] * vsc[u][1]);
+      pw[2 * u + 1] = pack_bf16x2_cvt(e[2] * vsc[u][2], e[3] * vsc[u][3]);
     }
   }
   if (__any(m_new != st.m)) {
