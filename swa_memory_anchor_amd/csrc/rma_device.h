@@ -43,15 +43,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }
 
-// The same pair packed by the hardware conversion (v_cvt_pk_bf16_f32, round to
-// nearest even): the same bits as pack_bf16x2 for every input but NaN, in one
-// instruction instead of about ten.
-__device__ __forceinline__ uint32_t pack_bf16x2_cvt(float lo, float hi) {
-  typedef __bf16 bf16x2_cvt_t __attribute__((ext_vector_type(2)));
-  const bf16x2_cvt_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
-  return __builtin_bit_cast(uint32_t, v);
-}
-
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
