@@ -159,9 +159,12 @@ def new_layer_state_fp8(batch: int, window: int = R.WINDOW, bank: int = R.BANK,
 
 
 def append(st: LayerStateFP8, k_win, v_win, k_rma, v_rma, gk_win, gk_rma, eps: float,
-           base: float, score=None) -> None:
+           base: float, score=None, quant=None) -> None:
     """``rma_ref.append`` with each written row quantised (keys from their FP32
-    normalised and rotated value, values from their BF16 input)."""
+    normalised and rotated value, values from their BF16 input).  ``quant`` is the
+    row codec (FP32 rows -> codes, scales); E4M3 unless another 8-bit format's is
+    given (``oracle.int8_ref``)."""
+    quantize_rows_ = quant or quantize_rows
     B = st.pos.shape[0]
     window, block = st.win_k.shape[2], st.pend_k.shape[2]
     for b in range(B):
@@ -172,11 +175,11 @@ def append(st: LayerStateFP8, k_win, v_win, k_rma, v_rma, gk_win, gk_rma, eps: f
         for g in range(st.win_k.shape[1]):
             kw = R.rope(R.rms_norm(R.bf16_to_f64(k_win[b, g]), gk_win, eps), p, base)
             kr = R.rope(R.rms_norm(R.bf16_to_f64(k_rma[b, g]), gk_rma, eps), p, base)
-            st.win_k[b, g, slot], st.win_ks[b, g, slot] = quantize_rows(kw.astype(np.float32))
-            st.win_v[b, g, slot], st.win_vs[b, g, slot] = quantize_rows(
+            st.win_k[b, g, slot], st.win_ks[b, g, slot] = quantize_rows_(kw.astype(np.float32))
+            st.win_v[b, g, slot], st.win_vs[b, g, slot] = quantize_rows_(
                 R.bf16_to_f64(v_win[b, g]).astype(np.float32))
-            st.pend_k[b, g, t], st.pend_ks[b, g, t] = quantize_rows(kr.astype(np.float32))
-            st.pend_v[b, g, t], st.pend_vs[b, g, t] = quantize_rows(
+            st.pend_k[b, g, t], st.pend_ks[b, g, t] = quantize_rows_(kr.astype(np.float32))
+            st.pend_v[b, g, t], st.pend_vs[b, g, t] = quantize_rows_(
                 R.bf16_to_f64(v_rma[b, g]).astype(np.float32))
         st.pend_src[b, t] = p
         if score is not None:
@@ -185,7 +188,7 @@ def append(st: LayerStateFP8, k_win, v_win, k_rma, v_rma, gk_win, gk_rma, eps: f
         st.pos[b] = p
 
 
-def _branch_rows(st: LayerStateFP8, b: int, g: int, branch: str):
+def _branch_rows(st: LayerStateFP8, b: int, g: int, branch: str, dequantize=dequantize):
     if branch == "win":
         n = min(int(st.pos[b]) + 1, st.win_k.shape[2])
         return dequantize(st.win_k[b, g, :n], st.win_ks[b, g, :n]), dequantize(
@@ -214,8 +217,11 @@ def decode_one(keys_by_group, vals_by_group, q_bits, gamma_q, pos: int, eps: flo
     return o, lse
 
 
-def decode(st: LayerStateFP8, q_win, q_rma, gq_win, gq_rma, eps: float, base: float):
-    """Both branches for every sequence, as ``rma_ref.decode`` (float64 results)."""
+def decode(st: LayerStateFP8, q_win, q_rma, gq_win, gq_rma, eps: float, base: float,
+           deq=None):
+    """Both branches for every sequence, as ``rma_ref.decode`` (float64 results).
+    ``deq`` is the row decoder (codes, scales -> float64); E4M3 unless given."""
+    deq = deq or dequantize
     B = st.pos.shape[0]
     G = st.win_k.shape[1]
     out = {}
@@ -223,7 +229,7 @@ def decode(st: LayerStateFP8, q_win, q_rma, gq_win, gq_rma, eps: float, base: fl
         o = np.zeros((B, R.Q_HEADS, R.HEAD_DIM))
         lse = np.zeros((B, R.Q_HEADS))
         for b in range(B):
-            kv = [_branch_rows(st, b, g, branch) for g in range(G)]
+            kv = [_branch_rows(st, b, g, branch, deq) for g in range(G)]
             o[b], lse[b] = decode_one([k for k, _ in kv], [v for _, v in kv], q[b], gq,
                                       int(st.pos[b]), eps, base)
         out[branch] = (o, lse)
