@@ -39,6 +39,8 @@ TRAFFIC_FILES = {
     "headline_b512": os.path.join(ROOT, "profiles", "decode_attn_headline_b512_traffic.txt"),
     "headline_b512_fp8": os.path.join(ROOT, "profiles",
                                       "decode_attn_fp8_headline_b512_fp8_traffic.txt"),
+    "headline_b512_i8": os.path.join(ROOT, "profiles",
+                                     "decode_attn_i8_headline_b512_i8_traffic.txt"),
     "gdn_decode_b512": os.path.join(ROOT, "profiles", "gdn_decode_gdn_decode_b512_traffic.txt"),
     "gdn_prefill_b512": os.path.join(ROOT, "profiles", "gdn_prefill_gdn_prefill_b512_traffic.txt"),
     "commit_burst_b512": os.path.join(ROOT, "profiles", "score_commit_burst_b512_traffic.txt"),
@@ -137,7 +139,12 @@ def cpu_baseline(wl, budget_s: float, max_units: int):
     from oracle import fp8_ref as F
     from synth import workloads as W
 
-    fp8 = wl.extra.get("kv") == "e4m3"
+    fp8 = wl.extra.get("kv") in ("e4m3", "int8")
+    if wl.extra.get("kv") == "int8":
+        from oracle import int8_ref as I
+        kv_np, deq = W.kv_i8_np, I.dequantize
+    else:
+        kv_np, deq = W.kv_fp8_np, F.dequantize
 
     cores = _blas_threads()
     rng = np.random.default_rng(7)
@@ -156,9 +163,9 @@ def cpu_baseline(wl, budget_s: float, max_units: int):
         q = W.q_np(wl, layer, b)
         g = gains.setdefault(layer, W.gains(wl, layer))
         if fp8:
-            s = {nm: W.kv_fp8_np(wl, layer, nm, b) for nm in W.KV_NAMES}
+            s = {nm: kv_np(wl, layer, nm, b) for nm in W.KV_NAMES}
             t0 = time.perf_counter()
-            rows = {nm: F.dequantize(*s[nm]) for nm in W.KV_NAMES}
+            rows = {nm: deq(*s[nm]) for nm in W.KV_NAMES}
             F.decode_one(list(rows["win_k"]), list(rows["win_v"]), q, g["gq_win"], wl.position,
                          wl.eps, wl.rope_base)
             keys = [np.concatenate([rows["bank_k"][i], rows["pend_k"][i]]) for i in range(4)]
@@ -889,7 +896,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="headline_b512",
-                    choices=["headline_b512", "headline_b512_fp8", "steady_b64", "batch1",
+                    choices=["headline_b512", "headline_b512_fp8", "headline_b512_i8",
+                             "steady_b64", "batch1",
                              "commit_burst_b512", "long_stream_b1", "prefill_b512",
                              "prefill_b64", "gdn_decode_b512", "gdn_decode_b1",
                              "gdn_prefill_b512", "gdn_prefill_b1"])
@@ -941,6 +949,8 @@ def main() -> int:
         wl = W.HEADLINE_B512
     elif args.workload == "headline_b512_fp8":
         wl = W.HEADLINE_B512_FP8
+    elif args.workload == "headline_b512_i8":
+        wl = W.HEADLINE_B512_I8
     elif args.workload == "steady_b64":
         wl = W.STEADY_B64
     else:
@@ -948,15 +958,18 @@ def main() -> int:
     B, L = wl.batch, wl.layers
     dev = "cuda"
 
-    fp8 = wl.extra.get("kv") == "e4m3"
-    attn = R.swa_rma_decode_attn_fp8 if fp8 else R.swa_rma_decode_attn
+    i8 = wl.extra.get("kv") == "int8"
+    fp8 = wl.extra.get("kv") == "e4m3" or i8  # an 8-bit state: codes + row scales
+    attn = (R.swa_rma_decode_attn_i8 if i8 else R.swa_rma_decode_attn_fp8) if fp8 else \
+        R.swa_rma_decode_attn
     state_bytes = STATE_BYTES_PER_UNIT_FP8 if fp8 else STATE_BYTES_PER_UNIT
     states, qs, norms, outs = [], [], [], []
     for layer in range(L):
         if fp8:
             st = R.alloc_layer_state_fp8(B, dev)
+            fill = W.kv_i8_torch_ if i8 else W.kv_fp8_torch_
             for nm in W.KV_NAMES:
-                W.kv_fp8_torch_(wl, layer, nm, getattr(st, nm), getattr(st, nm + "s"))
+                fill(wl, layer, nm, getattr(st, nm), getattr(st, nm + "s"))
         else:
             st = R.alloc_layer_state(B, dev, zero_kv=False)
             for nm in W.KV_NAMES:
@@ -1034,14 +1047,15 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3+bf16" if fp8 else "bf16",
+        "dtype": ("int8+bf16" if i8 else "fp8e4m3+bf16") if fp8 else "bf16",
         "data": "synthetic",
         "config": {
             "workload": wl.name,
             "batch": B,
             "layers": L,
             "position": wl.position,
-            "kv_format": "e4m3 codes + fp32 row scale" if fp8 else "bf16",
+            "kv_format": (("int8" if i8 else "e4m3") + " codes + fp32 row scale") if fp8
+                         else "bf16",
             "state_bytes_per_step": B * L * state_bytes,
             "decode_splits": R.rma_decode_splits(B),
             "hbm_gbps_step": round(B * L * (state_bytes + IO_BYTES_PER_UNIT)
@@ -1054,7 +1068,8 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": "decode_attn_fp8_kernel" if fp8 else "decode_attn_kernel",
+            "kernel": ("decode_attn_q8_kernel<int8>" if i8 else "decode_attn_q8_kernel<e4m3>")
+                      if fp8 else "decode_attn_kernel",
             "avg_launch_ms": round(avg_launch_ms, 4),
             "median_launch_ms": round(launch_ms[len(launch_ms) // 2], 4),
             "bytes_per_launch": bytes_per_launch,

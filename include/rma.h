@@ -340,9 +340,39 @@ rma_status swa_rma_decode_attn_fp8(const rma_layer_state_fp8 *st, int32_t batch,
                                    size_t workspace_bytes, void *stream);
 
 /* rma_commit_topk for the FP8 state: the same selection and slot rule; an
- * admitted row moves with its codes and its K and V scales. */
+ * admitted row moves with its codes and its K and V scales.  The codes are moved
+ * as bytes, so the same call commits an INT8 state (below). */
 rma_status rma_commit_topk_fp8(const rma_layer_state_fp8 *st, int32_t batch, int32_t *keep_idx,
                                void *stream);
+
+/*
+ * INT8 state variant (the pages list INT8 releases beside FP8 ones, [FB] section
+ * "架构…", [QB] section "开源到哪一步"; the format is, as for FP8, a reading of this
+ * library).  The layout is rma_layer_state_fp8's, and rma_layer_state_fp8_bytes
+ * and rma_commit_topk_fp8 serve it as they are; only the meaning of a code
+ * differs:
+ *   - every stored K and V row is 256 signed 8-bit codes (two's complement) plus
+ *     one FP32 scale = amax / 127 (a row with amax below 127 * 2^-126, the
+ *     all-zero row included, has scale 0 and zero codes);
+ *   - code = round-half-even(x * (127 / amax)), quotient and product in FP32, so
+ *     |code| <= 127; the row means code * scale;
+ *   - keys are quantised from their FP32 normalised and rotated value, values
+ *     from their BF16 input.
+ */
+
+/* swa_rma_append for the INT8 state: the same rows, quantised as described above.
+ * Arguments, alignment and error behaviour as swa_rma_append_fp8. */
+rma_status swa_rma_append_i8(const rma_layer_state_fp8 *st, int32_t batch, const uint16_t *k_win,
+                             const uint16_t *v_win, const uint16_t *k_rma, const uint16_t *v_rma,
+                             const float *score, const rma_norm *norm, void *stream);
+
+/* swa_rma_decode_attn over the INT8 state: the attention of the dequantised rows.
+ * Arguments, outputs, workspace and error behaviour as swa_rma_decode_attn_fp8. */
+rma_status swa_rma_decode_attn_i8(const rma_layer_state_fp8 *st, int32_t batch,
+                                  const uint16_t *q_win, const uint16_t *q_rma,
+                                  const rma_norm *norm, uint16_t *o_win, float *lse_win,
+                                  uint16_t *o_rma, float *lse_rma, void *workspace,
+                                  size_t workspace_bytes, void *stream);
 
 /* Human-readable name of a status code (static string). */
 const char *rma_status_str(rma_status s);

@@ -8,7 +8,9 @@ raises: there is no fallback.
 
 Entry points: ``swa_rma_append``, ``swa_rma_decode_attn``, ``rma_score``,
 ``rma_commit_topk``, ``swa_rma_prefill``, the FP8-state variants ``swa_rma_append_fp8``,
-``swa_rma_decode_attn_fp8`` and ``rma_commit_topk_fp8``, plus the size helpers
+``swa_rma_decode_attn_fp8`` and ``rma_commit_topk_fp8`` (which also commits the INT8
+state), the INT8-state variants ``swa_rma_append_i8`` and ``swa_rma_decode_attn_i8``,
+plus the size helpers
 ``rma_layer_state_bytes``, ``rma_layer_state_fp8_bytes``, ``rma_layer_kv_bytes``,
 ``rma_decode_workspace_bytes``, ``rma_decode_splits``, ``rma_prefill_workspace_bytes`` and
 ``rma_status_str``.
@@ -32,7 +34,7 @@ EXPORTS = (
     "rma_layer_state_fp8_bytes", "swa_rma_append_fp8", "swa_rma_decode_attn_fp8",
     "rma_commit_topk_fp8", "gdn_layer_state_bytes", "gdn_decode_step",
     "rma_step_workspace_bytes", "swa_rma_step", "rma_score_multi", "rma_commit_topk_multi",
-    "gdn_prefill", "swa_rma_decode_attn_noalloc",
+    "gdn_prefill", "swa_rma_decode_attn_noalloc", "swa_rma_append_i8", "swa_rma_decode_attn_i8",
 )
 
 _c_void_p = ctypes.c_void_p
@@ -123,6 +125,10 @@ def lib() -> ctypes.CDLL:
         L.swa_rma_decode_attn_fp8.restype = ctypes.c_int
         L.rma_commit_topk_fp8.argtypes = [s8, i32, vp, vp]
         L.rma_commit_topk_fp8.restype = ctypes.c_int
+        L.swa_rma_append_i8.argtypes = [s8, i32, vp, vp, vp, vp, vp, npp, vp]
+        L.swa_rma_append_i8.restype = ctypes.c_int
+        L.swa_rma_decode_attn_i8.argtypes = [s8, i32, vp, vp, npp, vp, vp, vp, vp, vp, sz, vp]
+        L.swa_rma_decode_attn_i8.restype = ctypes.c_int
         L.gdn_layer_state_bytes.argtypes, L.gdn_layer_state_bytes.restype = [i32, i32], sz
         L.gdn_decode_step.argtypes = [ctypes.POINTER(_GdnStateC), i32, i32, vp, vp, vp, vp,
                                       ctypes.POINTER(_GdnParamsC), vp, vp]
@@ -438,6 +444,27 @@ def rma_commit_topk_fp8(st: LayerStateFP8, batch: int, keep_idx=None, stream=Non
     s = lib().rma_commit_topk_fp8(ctypes.byref(_state_fp8_c(st)), int(batch), _ptr(keep_idx),
                                   _stream(stream))
     _check(s, "rma_commit_topk_fp8")
+
+
+# ---------------------------------------------------------------- INT8 state variant
+# The FP8 state's layout with signed 8-bit codes: LayerStateFP8 / alloc_layer_state_fp8
+# hold it, rma_commit_topk_fp8 commits it.
+def swa_rma_append_i8(st: LayerStateFP8, batch: int, k_win, v_win, k_rma, v_rma, score,
+                      norm: Norm, stream=None) -> None:
+    s = lib().swa_rma_append_i8(ctypes.byref(_state_fp8_c(st)), int(batch), _ptr(k_win),
+                                _ptr(v_win), _ptr(k_rma), _ptr(v_rma), _ptr(score),
+                                ctypes.byref(_norm_c(norm)), _stream(stream))
+    _check(s, "swa_rma_append_i8")
+
+
+def swa_rma_decode_attn_i8(st: LayerStateFP8, batch: int, q_win, q_rma, norm: Norm, o_win,
+                           lse_win, o_rma, lse_rma, workspace=None, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    s = lib().swa_rma_decode_attn_i8(ctypes.byref(_state_fp8_c(st)), int(batch), _ptr(q_win),
+                                     _ptr(q_rma), ctypes.byref(_norm_c(norm)), _ptr(o_win),
+                                     _ptr(lse_win), _ptr(o_rma), _ptr(lse_rma), _ptr(workspace),
+                                     ws_bytes, _stream(stream))
+    _check(s, "swa_rma_decode_attn_i8")
 
 
 # ---------------------------------------------------------------- GDN decode step (gdn.h)

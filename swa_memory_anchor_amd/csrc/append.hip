@@ -98,7 +98,29 @@ __device__ __forceinline__ uint32_t quantize_row_e4m3(const float x[4], float &s
   return tiny ? 0u : static_cast<uint32_t>(w);
 }
 
-__global__ __launch_bounds__(256) void append_fp8_kernel(AppendFp8Params a) {
+// INT8 rows (the same layout): code = round-half-even(x * (127 / amax)) as a signed
+// byte, scale = amax / 127; a row whose amax is below 127 * 2^-126 gets zero codes
+// and scale 0.  |x * inv| <= 127 up to the rounding of inv and of the product, which
+// cannot carry it past 127.5, so no code leaves [-127, 127].
+__device__ __forceinline__ uint32_t quantize_row_i8(const float x[4], float &scale) {
+  const float amax =
+      wave_max(fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))));
+  constexpr float kTinyRow = 127.0f * 0x1p-126f;
+  const bool tiny = amax < kTinyRow;
+  const float inv = tiny ? 0.f : 127.0f / amax;
+  scale = tiny ? 0.f : amax / 127.0f;
+  uint32_t w = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int q = static_cast<int>(__builtin_rintf(x[e] * inv));  // ties to even
+    w |= (static_cast<uint32_t>(q) & 0xffu) << (8 * e);
+  }
+  return tiny ? 0u : w;
+}
+
+// The 8-bit append for either row codec (E4M3 or INT8).
+template <bool kInt8>
+__global__ __launch_bounds__(256) void append_q8_kernel(AppendFp8Params a) {
   const int b = blockIdx.x;
   const int g = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -123,10 +145,10 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(AppendFp8Params a) {
   norm_rope_head(xw, a.gk_win, a.eps, c, sn, lane);
   norm_rope_head(xr, a.gk_rma, a.eps, c, sn, lane);
   float s0, s1, s2, s3;
-  const uint32_t c0 = quantize_row_e4m3(xw, s0);
-  const uint32_t c1 = quantize_row_e4m3(yw, s1);
-  const uint32_t c2 = quantize_row_e4m3(xr, s2);
-  const uint32_t c3 = quantize_row_e4m3(yr, s3);
+  const uint32_t c0 = kInt8 ? quantize_row_i8(xw, s0) : quantize_row_e4m3(xw, s0);
+  const uint32_t c1 = kInt8 ? quantize_row_i8(yw, s1) : quantize_row_e4m3(yw, s1);
+  const uint32_t c2 = kInt8 ? quantize_row_i8(xr, s2) : quantize_row_e4m3(xr, s2);
+  const uint32_t c3 = kInt8 ? quantize_row_i8(yr, s3) : quantize_row_e4m3(yr, s3);
   *reinterpret_cast<uint32_t *>(a.win_k + w_row * kDim + 4 * lane) = c0;
   *reinterpret_cast<uint32_t *>(a.win_v + w_row * kDim + 4 * lane) = c1;
   *reinterpret_cast<uint32_t *>(a.pend_k + p_row * kDim + 4 * lane) = c2;
@@ -192,10 +214,11 @@ extern "C" rma_status swa_rma_append(const rma_layer_state *st, int32_t batch,
   return RMA_OK;
 }
 
-extern "C" rma_status swa_rma_append_fp8(const rma_layer_state_fp8 *st, int32_t batch,
-                                         const uint16_t *k_win, const uint16_t *v_win,
-                                         const uint16_t *k_rma, const uint16_t *v_rma,
-                                         const float *score, const rma_norm *norm, void *stream) {
+template <bool kInt8>
+static rma_status append_q8(const rma_layer_state_fp8 *st, int32_t batch,
+                            const uint16_t *k_win, const uint16_t *v_win,
+                            const uint16_t *k_rma, const uint16_t *v_rma, const float *score,
+                            const rma_norm *norm, void *stream) {
   if (!st || !norm || !k_win || !v_win || !k_rma || !v_rma) return RMA_E_ARG;
   if (batch <= 0 || batch > RMA_MAX_BATCH) return RMA_E_ARG;
   if (!st->win_k || !st->win_v || !st->pend_k || !st->pend_v || !st->win_ks || !st->win_vs ||
@@ -231,8 +254,22 @@ extern "C" rma_status swa_rma_append_fp8(const rma_layer_state_fp8 *st, int32_t 
   p.gk_rma = norm->gk_rma;
   p.eps = norm->eps;
   p.rope_ratio = rope_ratio(norm->rope_base);
-  hipLaunchKernelGGL(append_fp8_kernel, dim3(batch), dim3(256), 0,
+  hipLaunchKernelGGL(append_q8_kernel<kInt8>, dim3(batch), dim3(256), 0,
                      static_cast<hipStream_t>(stream), p);
   if (hipPeekAtLastError() != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
   return RMA_OK;
+}
+
+extern "C" rma_status swa_rma_append_fp8(const rma_layer_state_fp8 *st, int32_t batch,
+                                         const uint16_t *k_win, const uint16_t *v_win,
+                                         const uint16_t *k_rma, const uint16_t *v_rma,
+                                         const float *score, const rma_norm *norm, void *stream) {
+  return append_q8<false>(st, batch, k_win, v_win, k_rma, v_rma, score, norm, stream);
+}
+
+extern "C" rma_status swa_rma_append_i8(const rma_layer_state_fp8 *st, int32_t batch,
+                                        const uint16_t *k_win, const uint16_t *v_win,
+                                        const uint16_t *k_rma, const uint16_t *v_rma,
+                                        const float *score, const rma_norm *norm, void *stream) {
+  return append_q8<true>(st, batch, k_win, v_win, k_rma, v_rma, score, norm, stream);
 }

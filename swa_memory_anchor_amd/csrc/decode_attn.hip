@@ -570,6 +570,28 @@ __device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
                     bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true)));
 }
 
+// Eight signed 8-bit codes (two words, byte i = code i) -> eight BF16 values: each
+// code converts exactly (|code| <= 127 has at most 7 significant bits).
+__device__ __forceinline__ uint4 i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[i] = static_cast<float>(static_cast<int8_t>(lo >> (8 * i)));
+    f[4 + i] = static_cast<float>(static_cast<int8_t>(hi >> (8 * i)));
+  }
+  return make_uint4(pack_bf16x2_cvt(f[0], f[1]), pack_bf16x2_cvt(f[2], f[3]),
+                    pack_bf16x2_cvt(f[4], f[5]), pack_bf16x2_cvt(f[6], f[7]));
+}
+
+// The widening of the 8-bit variant in use: E4M3 codes or INT8 codes.
+template <bool kInt8>
+__device__ __forceinline__ uint4 q8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  if constexpr (kInt8)
+    return i8x8_to_bf16x8(lo, hi);
+  else
+    return e4m3x8_to_bf16x8(lo, hi);
+}
+
 // Loads of one 32-key tile at row key0 of a segment (16-byte loads throughout):
 //  K[4u + s]: key key0 + 16u + lane%16, codes of dims 64s + 16(lane/16) .. +16;
 //  V[i]:      row key0 + 4i + lane/16, codes of dims 16(lane%16) .. +16;
@@ -627,6 +649,7 @@ __device__ __forceinline__ void stage_v_fp8(int lane, const uint4 (&V)[8], uint8
 // head dimension runs in a permuted order that the K loads and the query reads
 // share: MFMA (s, h) covers, for lane group kg, dims 64s + 16kg + 8h .. +8.  Lane
 // holds, in sc[u], keys 16u + 4kg .. +4 of head hh.
+template <bool kInt8>
 __device__ __forceinline__ void scores_tile_fp8(int nvalid, int lane, const uint4 (&K)[8],
                                                 const f32x4 (&ks)[2], const bf16x8 (&qv)[8],
                                                 f32x4 (&sc)[2]) {
@@ -640,7 +663,7 @@ __device__ __forceinline__ void scores_tile_fp8(int nvalid, int lane, const uint
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const uint4 &kw = K[4 * u + s];
-        const uint4 kb = h ? e4m3x8_to_bf16x8(kw.z, kw.w) : e4m3x8_to_bf16x8(kw.x, kw.y);
+        const uint4 kb = h ? q8x8_to_bf16x8<kInt8>(kw.z, kw.w) : q8x8_to_bf16x8<kInt8>(kw.x, kw.y);
         sc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(kb), qv[2 * s + h], sc[u],
                                                         0, 0, 0);
       }
@@ -661,6 +684,7 @@ __device__ __forceinline__ void scores_tile_fp8(int nvalid, int lane, const uint
 // operand from two transposed 8-byte LDS reads.  A key's numerator weight is its
 // rounded probability times its V scale; the denominator sums the rounded
 // probabilities.  A key past the end has probability 0 and scale 0.
+template <bool kInt8>
 __device__ __forceinline__ void accumulate_tile_fp8(const f32x4 (&sc)[2], int lane,
                                                     const uint8_t *vl, const f32x4 (&vsc)[2],
                                                     SoftmaxState &st) {
@@ -709,13 +733,15 @@ __device__ __forceinline__ void accumulate_tile_fp8(const f32x4 (&sc)[2], int la
     typedef int v2i __attribute__((ext_vector_type(2)));
     typedef __attribute__((address_space(3))) v2i lds_v2i;
     const v2i c = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i *)(src + ((db ^ sw) << 4)));
-    const bf16x8 va = bitcast<bf16x8>(e4m3x8_to_bf16x8(static_cast<uint32_t>(c[0]),
-                                                       static_cast<uint32_t>(c[1])));
+    const bf16x8 va = bitcast<bf16x8>(q8x8_to_bf16x8<kInt8>(static_cast<uint32_t>(c[0]),
+                                                            static_cast<uint32_t>(c[1])));
     st.acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, st.acc[db], 0, 0, 0);
   }
 }
 
-__global__ __launch_bounds__(kThreads, 2) void decode_attn_fp8_kernel(DecodeParams a) {
+// The 8-bit state decode for either code format (E4M3 or INT8).
+template <bool kInt8>
+__global__ __launch_bounds__(kThreads, 2) void decode_attn_q8_kernel(DecodeParams a) {
   __shared__ __align__(16) uint8_t v_lds[kWaves][kTile8 * kDim];
   __shared__ __align__(16) uint16_t q_lds[16][kQStride];  // rows 4..15 stay zero
   __shared__ float red_m[kWaves][kHeadsPerGroup], red_l[kWaves][kHeadsPerGroup];
@@ -776,9 +802,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_fp8_kernel(DecodePara
     const f32x4 vsc[2] = {vs[0], vs[1]};  // this tile's, before the next tile's loads
     if (tn < te) load_v_fp8(nsg, nkey0, lane, V, vs);
     f32x4 sc[2];
-    scores_tile_fp8(nvalid, lane, K, ks, qv, sc);
+    scores_tile_fp8<kInt8>(nvalid, lane, K, ks, qv, sc);
     if (tn < te) load_k_fp8(nsg, nkey0, lane, K, ks);
-    accumulate_tile_fp8(sc, lane, vl, vsc, st);
+    accumulate_tile_fp8<kInt8>(sc, lane, vl, vsc, st);
   }
 
   __syncthreads();
@@ -920,7 +946,8 @@ static rma_status launch_merge(const DecodeParams &p, hipStream_t s) {
 }
 
 // Validate, then launch the decode and the split merge.
-template <bool kFp8>
+// kFp8: an 8-bit state (codes + row scales); kInt8 picks INT8 codes over E4M3.
+template <bool kFp8, bool kInt8 = false>
 static rma_status launch_decode(DecodeParams &p, int32_t batch, const uint16_t *q_win,
                                 const uint16_t *q_rma, const rma_norm *norm, uint16_t *o_win,
                                 float *lse_win, uint16_t *o_rma, float *lse_rma, void *workspace,
@@ -931,7 +958,8 @@ static rma_status launch_decode(DecodeParams &p, int32_t batch, const uint16_t *
   hipStream_t s = static_cast<hipStream_t>(stream);
   const unsigned units = static_cast<unsigned>(batch) * kGroups * 2;
   if constexpr (kFp8)
-    hipLaunchKernelGGL(decode_attn_fp8_kernel, dim3(units * p.splits), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(decode_attn_q8_kernel<kInt8>, dim3(units * p.splits), dim3(kThreads), 0, s,
+                       p);
   else
     hipLaunchKernelGGL(decode_attn_kernel, dim3(units * p.splits), dim3(kThreads), 0, s, p);
   if (hipPeekAtLastError() != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
@@ -958,12 +986,11 @@ extern "C" rma_status swa_rma_decode_attn(const rma_layer_state *st, int32_t bat
                               workspace, workspace_bytes, stream);
 }
 
-extern "C" rma_status swa_rma_decode_attn_fp8(const rma_layer_state_fp8 *st, int32_t batch,
-                                              const uint16_t *q_win, const uint16_t *q_rma,
-                                              const rma_norm *norm, uint16_t *o_win,
-                                              float *lse_win, uint16_t *o_rma, float *lse_rma,
-                                              void *workspace, size_t workspace_bytes,
-                                              void *stream) {
+template <bool kInt8>
+static rma_status decode_q8(const rma_layer_state_fp8 *st, int32_t batch, const uint16_t *q_win,
+                            const uint16_t *q_rma, const rma_norm *norm, uint16_t *o_win,
+                            float *lse_win, uint16_t *o_rma, float *lse_rma, void *workspace,
+                            size_t workspace_bytes, void *stream) {
   if (!st) return RMA_E_ARG;
   DecodeParams p{};
   p.win_k = st->win_k;
@@ -981,8 +1008,28 @@ extern "C" rma_status swa_rma_decode_attn_fp8(const rma_layer_state_fp8 *st, int
   p.n_bank = st->n_bank;
   p.n_pend = st->n_pend;
   p.pos = st->pos;
-  return launch_decode<true>(p, batch, q_win, q_rma, norm, o_win, lse_win, o_rma, lse_rma,
+  return launch_decode<true, kInt8>(p, batch, q_win, q_rma, norm, o_win, lse_win, o_rma, lse_rma,
                              workspace, workspace_bytes, stream);
+}
+
+extern "C" rma_status swa_rma_decode_attn_fp8(const rma_layer_state_fp8 *st, int32_t batch,
+                                              const uint16_t *q_win, const uint16_t *q_rma,
+                                              const rma_norm *norm, uint16_t *o_win,
+                                              float *lse_win, uint16_t *o_rma, float *lse_rma,
+                                              void *workspace, size_t workspace_bytes,
+                                              void *stream) {
+  return decode_q8<false>(st, batch, q_win, q_rma, norm, o_win, lse_win, o_rma, lse_rma,
+                          workspace, workspace_bytes, stream);
+}
+
+extern "C" rma_status swa_rma_decode_attn_i8(const rma_layer_state_fp8 *st, int32_t batch,
+                                             const uint16_t *q_win, const uint16_t *q_rma,
+                                             const rma_norm *norm, uint16_t *o_win,
+                                             float *lse_win, uint16_t *o_rma, float *lse_rma,
+                                             void *workspace, size_t workspace_bytes,
+                                             void *stream) {
+  return decode_q8<true>(st, batch, q_win, q_rma, norm, o_win, lse_win, o_rma, lse_rma,
+                         workspace, workspace_bytes, stream);
 }
 
 // ---------------------------------------------------------------- fused step host

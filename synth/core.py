@@ -201,29 +201,74 @@ def normal_e4m3_torch_(out, key: StreamKey, start: int = 0, chunk: int = 1 << 26
         del idx
 
 
-def row_scale_np(key: StreamKey, count: int, start: int = 0) -> np.ndarray:
-    """FP32 row scales in [3/512, 4/512): (3 + u) / 512 with u = (hash >> 10) / 2^22,
-    every operation exact in FP32 (so host and device streams agree bit for bit)."""
-    assert 0 <= start and start + count <= (1 << 32)
+def row_scale_np(key: StreamKey, count: int, start: int = 0, denom: int = 512) -> np.ndarray:
+    """FP32 row scales in [3/denom, 4/denom) (denom a power of two): (3 + u) / denom with
+    u = (hash >> 10) / 2^22, every operation exact in FP32 (so host and device streams
+    agree bit for bit)."""
+    assert 0 <= start and start + count <= (1 << 32) and denom & (denom - 1) == 0
     idx = np.arange(start, start + count, dtype=np.uint64)
     u = (_hash_np(key, idx) >> np.uint64(10)).astype(np.float32) * np.float32(2.0 ** -22)
-    return ((np.float32(3.0) + u) * np.float32(1.0 / 512.0)).astype(np.float32)
+    return ((np.float32(3.0) + u) * np.float32(1.0 / denom)).astype(np.float32)
 
 
-def row_scale_torch_(out, key: StreamKey, start: int = 0, chunk: int = 1 << 24) -> None:
+def row_scale_torch_(out, key: StreamKey, start: int = 0, chunk: int = 1 << 24,
+                     denom: int = 512) -> None:
     """Fill the contiguous FP32 tensor ``out`` with the same scale stream."""
     import torch
 
     n = out.numel()
     assert out.is_contiguous() and out.dtype == torch.float32
-    assert 0 <= start and start + n <= (1 << 32)
+    assert 0 <= start and start + n <= (1 << 32) and denom & (denom - 1) == 0
     flat = out.view(-1)
     for c0 in range(0, n, chunk):
         c1 = min(n, c0 + chunk)
         idx = torch.arange(start + c0, start + c1, dtype=torch.int64, device=out.device)
         u = (_hash_t(key, idx) >> 10).to(torch.float32) * (2.0 ** -22)
-        flat[c0:c1] = (u + 3.0) * (1.0 / 512.0)
+        flat[c0:c1] = (u + 3.0) * (1.0 / denom)
         del idx, u
+
+
+# ---------------------------------------------------------------- INT8 code streams
+I8_SPREAD = 36.0  # codes ~ N(0, 36^2), clipped at 127 (3.5 sigma)
+_I8_TABLE = None
+
+
+def normal_i8_table() -> np.ndarray:
+    """Signed 8-bit codes (as uint8 bytes) of the 65536 standard-normal quantiles times
+    36, rounded to nearest and clipped to [-127, 127].  With a row scale near 1/36 (the
+    scale stream with denom 128) a code stands for about N(0,1)."""
+    global _I8_TABLE
+    if _I8_TABLE is None:
+        from scipy.special import ndtri
+
+        j = np.arange(65536, dtype=np.float64)
+        q = np.clip(np.rint(ndtri((j + 0.5) / 65536.0) * I8_SPREAD), -127, 127)
+        _I8_TABLE = q.astype(np.int8).view(np.uint8).copy()
+        _I8_TABLE.setflags(write=False)
+    return _I8_TABLE
+
+
+def normal_i8_np(key: StreamKey, count: int, start: int = 0) -> np.ndarray:
+    """Elements ``start .. start+count-1`` of an INT8 code stream (uint8 bytes)."""
+    assert 0 <= start and start + count <= (1 << 32)
+    idx = np.arange(start, start + count, dtype=np.uint64)
+    return normal_i8_table()[(_hash_np(key, idx) >> np.uint64(16)).astype(np.int64)]
+
+
+def normal_i8_torch_(out, key: StreamKey, start: int = 0, chunk: int = 1 << 26) -> None:
+    """Fill the contiguous 8-bit tensor ``out`` with the same code stream."""
+    import torch
+
+    n = out.numel()
+    assert out.is_contiguous() and out.element_size() == 1
+    assert 0 <= start and start + n <= (1 << 32)
+    flat = out.view(torch.uint8).view(-1)
+    table = torch.from_numpy(normal_i8_table().copy()).to(out.device)
+    for c0 in range(0, n, chunk):
+        c1 = min(n, c0 + chunk)
+        idx = torch.arange(start + c0, start + c1, dtype=torch.int64, device=out.device)
+        flat[c0:c1] = table[_hash_t(key, idx) >> 16]
+        del idx
 
 
 # ---------------------------------------------------------------- FP16 / FP32 state streams

@@ -23,6 +23,10 @@ group, 8 SWA||RMA layers, hidden width 2560 feeding a 2560->256->4 scorer.
                         E4M3 codes and one FP32 scale: codes of N(0,1) quantiles
                         times 128 with scales in [3/512, 4/512), so a row decodes
                         to about N(0, 1) as in the BF16 state.
+* ``headline_b512_i8``  ``headline_b512`` with every stored K/V row held as 256
+                        signed 8-bit codes and one FP32 scale: N(0,1) quantiles
+                        times 36, rounded and clipped to [-127, 127], with scales
+                        in [3/128, 4/128), so a row again decodes to about N(0, 1).
 
 Every large BF16 tensor is a counter-based stream (see ``synth.core``), so the
 host can regenerate any slice of what the device drew.
@@ -43,6 +47,8 @@ from .core import (
     normal_e4m3_np,
     normal_e4m3_torch_,
     normal_f32_np,
+    normal_i8_np,
+    normal_i8_torch_,
     rng_np,
     row_scale_np,
     row_scale_torch_,
@@ -88,6 +94,8 @@ COMMIT_BURST_B512 = Workload("commit_burst_b512", batch=512, layers=8, position=
 LONG_STREAM_B1 = Workload("long_stream_b1", batch=1, layers=8, position=262144, gains="normal")
 HEADLINE_B512_FP8 = Workload("headline_b512_fp8", batch=512, layers=8, position=65536,
                              gains="normal", extra={"kv": "e4m3"})
+HEADLINE_B512_I8 = Workload("headline_b512_i8", batch=512, layers=8, position=65536,
+                            gains="normal", extra={"kv": "int8"})
 
 GDN_DECODE_B512 = Workload("gdn_decode_b512", batch=512, layers=24, position=65536, gains="ones",
                            extra={"state": "f16"})
@@ -106,7 +114,7 @@ PREFILL_B512 = Workload("prefill_b512", batch=512, layers=8, position=65535, gai
 PREFILL_B64 = Workload("prefill_b64", batch=64, layers=8, position=65535, gains="normal")
 
 WORKLOADS = {w.name: w for w in (TINY_STREAM, STEADY_B64, HEADLINE_B512, COMMIT_BURST_B512,
-                                 LONG_STREAM_B1, HEADLINE_B512_FP8, GDN_DECODE_B512,
+                                 LONG_STREAM_B1, HEADLINE_B512_FP8, HEADLINE_B512_I8, GDN_DECODE_B512,
                                  GDN_DECODE_B1, PREFILL_B512, PREFILL_B64, GDN_PREFILL_B512,
                                  GDN_PREFILL_B1)}
 
@@ -171,6 +179,25 @@ def kv_fp8_torch_(wl: Workload, layer: int, name: str, codes, scales) -> None:
     assert scales.shape == codes.shape[:3]
     normal_e4m3_torch_(codes, key(wl, layer, name, "e4m3"))
     row_scale_torch_(scales, key(wl, layer, name, "scale"))
+
+
+def kv_i8_np(wl: Workload, layer: int, name: str, b: int):
+    """One sequence's INT8 slice: codes ``[4][slots][256]`` (uint8 bytes of int8) and
+    scales ``[4][slots]`` in [3/128, 4/128)."""
+    slots = kv_slots(name)
+    per_seq = KV_GROUPS * slots
+    codes = normal_i8_np(key(wl, layer, name, "int8"), per_seq * HEAD_DIM,
+                         start=b * per_seq * HEAD_DIM)
+    scales = row_scale_np(key(wl, layer, name, "scale"), per_seq, start=b * per_seq, denom=128)
+    return codes.reshape(KV_GROUPS, slots, HEAD_DIM), scales.reshape(KV_GROUPS, slots)
+
+
+def kv_i8_torch_(wl: Workload, layer: int, name: str, codes, scales) -> None:
+    """Fill device tensors codes ``[B][4][slots][256]`` (uint8) and scales ``[B][4][slots]``."""
+    assert codes.shape[1:] == (KV_GROUPS, kv_slots(name), HEAD_DIM)
+    assert scales.shape == codes.shape[:3]
+    normal_i8_torch_(codes, key(wl, layer, name, "int8"))
+    row_scale_torch_(scales, key(wl, layer, name, "scale"), denom=128)
 
 
 def q_np(wl: Workload, layer: int, b: int, step: int = 0) -> np.ndarray:

@@ -130,6 +130,43 @@ def decode_gpu_fp8(st: R.LayerStateFP8, q_win, q_rma, norm: R.Norm):
     return o_w, l_w, o_r, l_r
 
 
+def decode_gpu_i8(st: R.LayerStateFP8, q_win, q_rma, norm: R.Norm):
+    B = st.pos.shape[0]
+    o_w = torch.empty(B, 16, 256, dtype=torch.bfloat16, device=DEV)
+    o_r = torch.empty_like(o_w)
+    l_w = torch.empty(B, 16, dtype=torch.float32, device=DEV)
+    l_r = torch.empty_like(l_w)
+    R.swa_rma_decode_attn_i8(st, B, q_win, q_rma, norm, o_w, l_w, o_r, l_r,
+                             R.decode_workspace(B))
+    return o_w, l_w, o_r, l_r
+
+
+def assert_i8_keys_close(got_codes, got_scale, ref_codes, ref_scale, what=""):
+    """Stored INT8 key rows against the oracle's.
+
+    As for FP8, the GPU's FP32 normalised and rotated key differs from the oracle's
+    (float64 rounded to FP32) by a few units of 2^-24 of the row's largest magnitude,
+    and the scale with it; a scaled element near a half-integer can then take the
+    neighbouring code.  Each dequantised element must lie within one step of the
+    row's grid (its scale) of the reference, plus 2^-16 of the row's largest
+    magnitude; the scales must agree to 2^-18 relative.
+    """
+    from oracle import int8_ref as I
+
+    gs = np.asarray(got_scale, np.float64)
+    rs = np.asarray(ref_scale, np.float64)
+    assert np.all(np.abs(gs - rs) <= 2.0 ** -18 * rs), f"{what}: scales differ"
+    g = I.dequantize(got_codes, got_scale)
+    r = I.dequantize(ref_codes, ref_scale)
+    row = np.abs(r).max(axis=-1, keepdims=True)
+    err = np.abs(g - r)
+    bound = rs[..., None] + 2.0 ** -16 * row
+    ndiff = int((np.asarray(got_codes) != np.asarray(ref_codes)).sum())
+    print(f"{what}: {ndiff} of {g.size} codes differ; max err/bound "
+          f"{float((err / np.maximum(bound, 1e-300)).max()):.3f}")
+    assert np.all(err <= bound), f"{what}: {int((err > bound).sum())} elements out of bound"
+
+
 def assert_fp8_keys_close(got_codes, got_scale, ref_codes, ref_scale, what=""):
     """Stored FP8 key rows against the oracle's.
 

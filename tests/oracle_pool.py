@@ -3,8 +3,8 @@ over worker processes.
 
 Each worker regenerates the unit's inputs on the host from the seeded generators
 (state, query, gains: the same counter streams the device copies were drawn from),
-runs the float64 oracle for both branches (the FP8 oracle on the dequantised rows
-for an E4M3 state), and compares with the GPU's outputs for
+runs the float64 oracle for both branches (on the dequantised rows for an E4M3 or
+INT8 state), and compares with the GPU's outputs for
 that unit, which the parent passes in.  Workers import NumPy, the oracle and the
 generators only: no torch, no GPU.  They are started with "spawn" (never forked
 from a process that holds a GPU context).
@@ -45,6 +45,12 @@ def unit_errors(task):
         from oracle import fp8_ref as F
 
         rows = {nm: F.dequantize(*W.kv_fp8_np(wl, layer, nm, b)) for nm in W.KV_NAMES}
+        dec, pos = F.decode_one, wl.position
+    elif wl.extra.get("kv") == "int8":  # codes + row scales, dequantised by the INT8 oracle
+        from oracle import fp8_ref as F
+        from oracle import int8_ref as I
+
+        rows = {nm: I.dequantize(*W.kv_i8_np(wl, layer, nm, b)) for nm in W.KV_NAMES}
         dec, pos = F.decode_one, wl.position
     else:
         rows = W.decode_state_np(wl, layer, b)

@@ -177,6 +177,29 @@ def test_fp8_state_size_and_host_validation(lib):
     assert lib.rma_commit_topk_fp8(None, 2, None, None) == 1
 
 
+def test_int8_entry_points_validate_like_the_fp8_ones(lib):
+    st8 = R._StateFp8C(*([16] * 19))
+    nm = _norm()
+    by = ctypes.byref
+    dec = lambda st_, b, ws=None, wsb=0: lib.swa_rma_decode_attn_i8(  # noqa: E731
+        st_, b, 16, 16, by(nm), 16, 16, 16, 16, ws, wsb, None)
+    assert dec(None, 4) == 1
+    bad = R._StateFp8C(*([16] * 19))
+    bad.win_vs = None
+    assert dec(by(bad), 512) == 1
+    mis = R._StateFp8C(*([16] * 19))
+    mis.pend_ks = 20
+    assert dec(by(mis), 512) == 2
+    assert dec(by(st8), 4) == 3          # split batch without a workspace
+    assert dec(by(st8), 0) == 1
+    app = lambda st_, b, k=16: lib.swa_rma_append_i8(  # noqa: E731
+        st_, b, k, 16, 16, 16, None, by(nm), None)
+    assert app(by(bad), 2) == 1
+    assert app(by(st8), 0) == 1
+    assert app(by(st8), 2, k=None) == 1
+    assert app(by(st8), 2, k=20) == 2    # raw key rows are read 8 bytes at a time
+
+
 def test_gdn_state_size_and_host_validation(lib):
     # 32 heads x 128 x 128 matrix entries + 4 convolution inputs of 8192 BF16 channels
     assert R.gdn_layer_state_bytes(3, 0) == 3 * (32 * 128 * 128 * 2 + 4 * 8192 * 2)
