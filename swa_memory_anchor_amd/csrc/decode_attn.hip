@@ -135,8 +135,9 @@ __device__ __forceinline__ void unit_segments_at(const DecodeParams &a, int b, i
   constexpr int rb = kFp8 ? kDim : 2 * kDim;
   const size_t sgi = static_cast<size_t>(b) * kGroups + g;
   if (anchor) {
-    const int nb = min(max(n_bank, 0), kBank);
-    const int np = min(max(n_pend, 0), kBlock);
+    // uniform values, kept scalar so that the buffer resources stay in scalar registers
+    const int nb = __builtin_amdgcn_readfirstlane(min(max(n_bank, 0), kBank));
+    const int np = __builtin_amdgcn_readfirstlane(min(max(n_pend, 0), kBlock));
     seg0.k = make_rsrc(a.bank_k + sgi * kBank * rb, nb * rb);
     seg0.v = make_rsrc(a.bank_v + sgi * kBank * rb, nb * rb);
     seg0.n = nb;
@@ -150,7 +151,7 @@ __device__ __forceinline__ void unit_segments_at(const DecodeParams &a, int b, i
       seg1.vs = make_rsrc(a.pend_vs + sgi * kBlock, np * 4);
     }
   } else {
-    const int nw = min(max(p + 1, 0), kWindow);
+    const int nw = __builtin_amdgcn_readfirstlane(min(max(p + 1, 0), kWindow));
     seg0.k = make_rsrc(a.win_k + sgi * kWindow * rb, nw * rb);
     seg0.v = make_rsrc(a.win_v + sgi * kWindow * rb, nw * rb);
     seg0.n = nw;
@@ -598,8 +599,7 @@ __device__ __forceinline__ uint4 q8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 //  ks[u], vs[u]: scales of keys key0 + 16u + 4(lane/16) .. +4 (the lane's score keys).
 // The K and V halves are issued separately: each half's next loads go out as soon
 // as its registers are consumed.
-__device__ __forceinline__ void load_k_fp8(const Segment &sg, int key0, int lane, uint4 (&K)[8],
-                                           f32x4 (&ks)[2]) {
+__device__ __forceinline__ void load_k_fp8(const Segment &sg, int key0, int lane, uint4 (&K)[8]) {
   const int hh = lane & 15, kg = lane >> 4;
   const int soff = key0 * kDim;
   const int koff = hh * kDim + 16 * kg;
@@ -609,25 +609,41 @@ __device__ __forceinline__ void load_k_fp8(const Segment &sg, int key0, int lane
     for (int s = 0; s < 4; ++s)
       K[4 * u + s] = bitcast<uint4>(__builtin_amdgcn_raw_buffer_load_b128(
           sg.k, koff + 16 * u * kDim + 64 * s, soff, kStream));
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-    ks[u] = bitcast<f32x4>(
-        __builtin_amdgcn_raw_buffer_load_b128(sg.ks, 4 * (16 * u + 4 * kg), key0 * 4, kStream));
 }
 
-__device__ __forceinline__ void load_v_fp8(const Segment &sg, int key0, int lane, uint4 (&V)[8],
-                                           f32x4 (&vs)[2]) {
-  const int kg = lane >> 4;
+__device__ __forceinline__ void load_v_fp8(const Segment &sg, int key0, int lane, uint4 (&V)[8]) {
   const int soff = key0 * kDim;
   const int voff = (lane >> 4) * kDim + 16 * (lane & 15);
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     V[i] = bitcast<uint4>(
         __builtin_amdgcn_raw_buffer_load_b128(sg.v, voff + 4 * i * kDim, soff, kStream));
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-    vs[u] = bitcast<f32x4>(
-        __builtin_amdgcn_raw_buffer_load_b128(sg.vs, 4 * (16 * u + 4 * kg), key0 * 4, kStream));
+}
+
+// The K and V scales of a workgroup's tiles [tb, te) go to LDS once, before the key
+// loop, as two contiguous runs read by the whole workgroup (16 bytes a thread):
+// per-tile loads of 128 bytes each from the two scale arrays cost more than their
+// share of the bytes.  Entry 32(t - tb) + i holds key i of tile t; keys past a
+// segment's end read as zero.
+constexpr int kMaxScaleKeys = (kBank + kBlock) / kTile8 * kTile8;  // a whole anchor unit
+__device__ __forceinline__ void load_scale_run(const Segment &sg, int row0, int n4, float *ks_l,
+                                               float *vs_l) {
+  for (int i = threadIdx.x; i < n4; i += kThreads) {
+    const f32x4 k4 = bitcast<f32x4>(__builtin_amdgcn_raw_buffer_load_b128(sg.ks, 16 * i, row0 * 4, kStream));
+    const f32x4 v4 = bitcast<f32x4>(__builtin_amdgcn_raw_buffer_load_b128(sg.vs, 16 * i, row0 * 4, kStream));
+    *reinterpret_cast<f32x4 *>(ks_l + 4 * i) = k4;
+    *reinterpret_cast<f32x4 *>(vs_l + 4 * i) = v4;
+  }
+}
+
+__device__ __forceinline__ void load_scales_fp8(const Segment &seg0, const Segment &seg1, int T0,
+                                                int tb, int te, float *ks_l, float *vs_l) {
+  // tiles [tb, min(te, T0)) of segment 0, then [max(tb, T0), te) of segment 1
+  const int e0 = min(te, T0), b1 = max(tb, T0);
+  if (tb < e0) load_scale_run(seg0, tb * kTile8, (e0 - tb) * (kTile8 / 4), ks_l, vs_l);
+  if (b1 < te)
+    load_scale_run(seg1, (b1 - T0) * kTile8, (te - b1) * (kTile8 / 4), ks_l + (b1 - tb) * kTile8,
+                   vs_l + (b1 - tb) * kTile8);
 }
 
 // V codes stay E4M3 in LDS: 32 rows of 256 bytes, the 16-byte chunk c of row r at
@@ -651,7 +667,7 @@ __device__ __forceinline__ void stage_v_fp8(int lane, const uint4 (&V)[8], uint8
 // holds, in sc[u], keys 16u + 4kg .. +4 of head hh.
 template <bool kInt8>
 __device__ __forceinline__ void scores_tile_fp8(int nvalid, int lane, const uint4 (&K)[8],
-                                                const f32x4 (&ks)[2], const bf16x8 (&qv)[8],
+                                                const float *ks_t, const bf16x8 (&qv)[8],
                                                 f32x4 (&sc)[2]) {
   const int kg = lane >> 4;
   sc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -671,7 +687,7 @@ __device__ __forceinline__ void scores_tile_fp8(int nvalid, int lane, const uint
   }
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    sc[u] *= ks[u];
+    sc[u] *= *reinterpret_cast<const f32x4 *>(ks_t + 16 * u + 4 * kg);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (16 * u + 4 * kg + i >= nvalid) sc[u][i] = -INFINITY;
@@ -686,9 +702,11 @@ __device__ __forceinline__ void scores_tile_fp8(int nvalid, int lane, const uint
 // probabilities.  A key past the end has probability 0 and scale 0.
 template <bool kInt8>
 __device__ __forceinline__ void accumulate_tile_fp8(const f32x4 (&sc)[2], int lane,
-                                                    const uint8_t *vl, const f32x4 (&vsc)[2],
+                                                    const uint8_t *vl, const float *vs_t,
                                                     SoftmaxState &st) {
   const int kg = lane >> 4, r = lane & 15;
+  const f32x4 vsc[2] = {*reinterpret_cast<const f32x4 *>(vs_t + 4 * kg),
+                        *reinterpret_cast<const f32x4 *>(vs_t + 16 + 4 * kg)};
   float mt = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
                    fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
   mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
@@ -745,6 +763,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_q8_kernel(DecodeParam
   __shared__ __align__(16) uint8_t v_lds[kWaves][kTile8 * kDim];
   __shared__ __align__(16) uint16_t q_lds[16][kQStride];  // rows 4..15 stay zero
   __shared__ float red_m[kWaves][kHeadsPerGroup], red_l[kWaves][kHeadsPerGroup];
+  __shared__ __align__(16) float ks_lds[kMaxScaleKeys], vs_lds[kMaxScaleKeys];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps tile selection scalar
@@ -762,6 +781,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_q8_kernel(DecodeParam
   const int per = (T + a.splits - 1) / a.splits;
   const int tb = split * per;
   const int te = min(T, tb + per);
+  // the scales first (the query prologue's barrier publishes them)
+  load_scales_fp8(seg0, seg1, T0, tb, te, ks_lds, vs_lds);
 
   SoftmaxState st;
   st.m = -INFINITY;
@@ -771,13 +792,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_q8_kernel(DecodeParam
 
   uint8_t *vl = v_lds[wave];
   uint4 K[8], V[8];
-  f32x4 ks[2], vs[2];
   int t = tb + wave;
   if (t < te) {
     const Segment &sg = t < T0 ? seg0 : seg1;
     const int key0 = (t < T0 ? t : t - T0) * kTile8;
-    load_v_fp8(sg, key0, lane, V, vs);
-    load_k_fp8(sg, key0, lane, K, ks);
+    load_v_fp8(sg, key0, lane, V);
+    load_k_fp8(sg, key0, lane, K);
   }
   stage_query(a, b, g, anchor, a.pos[b], wave, lane, q_lds);
   // Query operands in registers: qv[2s + h] holds, for lane (hh, kg), dims
@@ -799,12 +819,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_q8_kernel(DecodeParam
     const Segment &nsg = tn < T0 ? seg0 : seg1;
     const int nkey0 = (tn < T0 ? tn : tn - T0) * kTile8;
     stage_v_fp8(lane, V, vl);
-    const f32x4 vsc[2] = {vs[0], vs[1]};  // this tile's, before the next tile's loads
-    if (tn < te) load_v_fp8(nsg, nkey0, lane, V, vs);
+    if (tn < te) load_v_fp8(nsg, nkey0, lane, V);
     f32x4 sc[2];
-    scores_tile_fp8<kInt8>(nvalid, lane, K, ks, qv, sc);
-    if (tn < te) load_k_fp8(nsg, nkey0, lane, K, ks);
-    accumulate_tile_fp8<kInt8>(sc, lane, vl, vsc, st);
+    scores_tile_fp8<kInt8>(nvalid, lane, K, ks_lds + (t - tb) * kTile8, qv, sc);
+    if (tn < te) load_k_fp8(nsg, nkey0, lane, K);
+    accumulate_tile_fp8<kInt8>(sc, lane, vl, vs_lds + (t - tb) * kTile8, st);
   }
 
   __syncthreads();
