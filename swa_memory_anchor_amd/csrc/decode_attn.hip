@@ -73,6 +73,10 @@ constexpr int kMaxSplits = 20;
 constexpr int kMinWorkgroups = RMA_DECODE_MIN_WGS;
 constexpr float kQScale = 1.4426950408889634f / 16.0f;  // log2(e) / sqrt(256)
 constexpr float kLn2 = 0.69314718055994531f;
+// Row offset of a load that must go out without touching memory (past every
+// segment, so the range check returns zeros): a load issued on every path keeps the
+// compiler's wait counts exact.
+constexpr int kNoRows = 1 << 20;
 // Cache policy of the K/V loads: non-temporal (every byte is read exactly once per
 // step, so it should not displace anything in the caches).
 constexpr int kStream = 2;
@@ -174,19 +178,38 @@ __device__ __forceinline__ void unit_segments(const DecodeParams &a, int b, int 
     unit_segments_at<kFp8>(a, b, g, false, a.pos[b], 0, 0, seg0, seg1);
 }
 
-// Query prep at position p: wave w < 4 normalises, rotates and scales head 4g + w
-// into q_lds row w; the other rows are zeroed.  Ends with a workgroup barrier.
-__device__ __forceinline__ void stage_query(const DecodeParams &a, int b, int g, bool anchor,
-                                            int p, int wave, int lane,
-                                            uint16_t (*q_lds)[kQStride]) {
-  if (wave < kHeadsPerGroup) {
-    const uint16_t *q = (anchor ? a.q_rma : a.q_win) +
-                        (static_cast<size_t>(b) * kHeads + g * kHeadsPerGroup + wave) * kDim;
-    const uint2 raw = *reinterpret_cast<const uint2 *>(q + 4 * lane);
-    float x[4] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y)};
+// The raw query elements of wave w (head 4g + w, dims 4*lane..4*lane+3) and the
+// lane's four query gains.  Issued first in a kernel, their wait does not cover the
+// key loads issued after them.
+static_assert(kWaves == kHeadsPerGroup, "one wave per head of the group");
+struct QueryRaw {
+  uint2 q;
+  float4 gain;
+};
+
+__device__ __forceinline__ QueryRaw load_query(const DecodeParams &a, int b, int g, bool anchor,
+                                               int wave, int lane) {
+  const uint16_t *q = (anchor ? a.q_rma : a.q_win) +
+                      (static_cast<size_t>(b) * kHeads + g * kHeadsPerGroup + wave) * kDim;
+  QueryRaw r;
+  r.q = *reinterpret_cast<const uint2 *>(q + 4 * lane);
+  r.gain = *reinterpret_cast<const float4 *>((anchor ? a.gq_rma : a.gq_win) + 4 * lane);
+  return r;
+}
+
+// Query prep at position p from the raw elements: wave w normalises, rotates and
+// scales head 4g + w into q_lds row w; the other rows are zeroed.  The gains go
+// through the wave's own LDS row (g_row, kDim floats), so the norm reads them there
+// rather than from memory.  Ends with a workgroup barrier.
+__device__ __forceinline__ void stage_query_raw(const DecodeParams &a, const QueryRaw &raw,
+                                                int p, int wave, int lane,
+                                                uint16_t (*q_lds)[kQStride], float *g_row) {
+  {
+    *reinterpret_cast<float4 *>(g_row + 4 * lane) = raw.gain;
+    float x[4] = {bf16_lo(raw.q.x), bf16_hi(raw.q.x), bf16_lo(raw.q.y), bf16_hi(raw.q.y)};
     float c, sn;
     rope_cos_sin(a.rope_ratio, p, lane, c, sn);
-    norm_rope_head(x, anchor ? a.gq_rma : a.gq_win, a.eps, c, sn, lane);
+    norm_rope_head(x, g_row, a.eps, c, sn, lane);
     uint2 o;
     o.x = pack_bf16x2(x[0] * kQScale, x[1] * kQScale);
     o.y = pack_bf16x2(x[2] * kQScale, x[3] * kQScale);
@@ -195,6 +218,12 @@ __device__ __forceinline__ void stage_query(const DecodeParams &a, int b, int g,
   for (int i = threadIdx.x; i < 12 * kQStride / 4; i += kThreads)
     reinterpret_cast<uint2 *>(&q_lds[kHeadsPerGroup][0])[i] = make_uint2(0, 0);
   __syncthreads();
+}
+
+__device__ __forceinline__ void stage_query(const DecodeParams &a, int b, int g, bool anchor,
+                                            int p, int wave, int lane,
+                                            uint16_t (*q_lds)[kQStride], float *g_row) {
+  stage_query_raw(a, load_query(a, b, g, anchor, wave, lane), p, wave, lane, q_lds, g_row);
 }
 
 // Merge the four waves' partial softmax states through LDS (macc: 16 KiB that no
@@ -352,6 +381,7 @@ __device__ __forceinline__ void accumulate_tile(f32x4 sc, int lane, const uint16
 __global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(DecodeParams a) {
   __shared__ __align__(16) uint16_t v_lds[kWaves][kTile * kVStride];
   __shared__ __align__(16) uint16_t q_lds[16][kQStride];  // rows 4..15 stay zero
+  __shared__ __align__(16) float g_lds[kWaves][kDim];
   __shared__ float red_m[kWaves][kHeadsPerGroup], red_l[kWaves][kHeadsPerGroup];
 
   const int lane = threadIdx.x & 63;
@@ -382,10 +412,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(DecodeParams a
   uint16_t *vl = v_lds[wave];
   uint4 K[8], V[8];
   int t = tb + wave;
-  // The first tile's loads do not depend on the query: issue them before the
-  // query prologue so its latency overlaps the norm and rotary work.
-  if (t < te) load_tile(t < T0 ? seg0 : seg1, (t < T0 ? t : t - T0) * kTile, lane, K, V);
-  stage_query(a, b, g, anchor, a.pos[b], wave, lane, q_lds);
+  // The query's loads go first and the first tile's right after them (on every
+  // path): the prologue waits for the query alone, and its norm and rotary work
+  // overlaps the tile's loads.
+  const QueryRaw qraw = load_query(a, b, g, anchor, wave, lane);
+  load_tile(t < T0 ? seg0 : seg1, t < te ? (t < T0 ? t : t - T0) * kTile : kNoRows, lane, K, V);
+  stage_query_raw(a, qraw, a.pos[b], wave, lane, q_lds, g_lds[wave]);
   // The query operands stay in registers for the whole key loop: lane (hh, kg) holds
   // dims 32s + 8kg .. +8 of head hh (rows >= 4 are zero).
   bf16x8 qv[8];
@@ -441,6 +473,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepParams sp)
   __shared__ __align__(16) uint16_t v_lds[kWaves][kTile * kVStride];
   __shared__ __align__(16) uint16_t q_lds[16][kQStride];
   __shared__ __align__(16) uint16_t patch[2][kDim];  // the new K and V rows
+  __shared__ __align__(16) float g_lds[kWaves + 1][kDim];  // query gains per wave, key gains
   __shared__ float red_m[kWaves][kHeadsPerGroup], red_l[kWaves][kHeadsPerGroup];
 
   const int lane = threadIdx.x & 63;
@@ -451,6 +484,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepParams sp)
   const bool anchor = unit < per_branch;
   const int bg = anchor ? unit : unit - per_branch;
   const int b = bg / kGroups, g = bg % kGroups;
+
+  // The query and the token's records do not depend on the state: their loads go
+  // first, so that waiting for them does not wait for the key loads, and the norm
+  // and rotary work overlaps those loads.
+  const QueryRaw qraw = load_query(a, b, g, anchor, wave, lane);
+  const size_t rec_in = (static_cast<size_t>(b) * kGroups + g) * kDim + 4 * lane;
+  const uint2 krec_raw = *reinterpret_cast<const uint2 *>((anchor ? sp.k_rma : sp.k_win) + rec_in);
+  const uint2 vrec_raw = *reinterpret_cast<const uint2 *>((anchor ? sp.v_rma : sp.v_win) + rec_in);
+  const float4 kgain = *reinterpret_cast<const float4 *>((anchor ? sp.gk_rma : sp.gk_win) + 4 * lane);
 
   // the state before the token; a full pending block takes no token (as in append)
   const int p_old = a.pos[b];
@@ -481,18 +523,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepParams sp)
   uint16_t *vl = v_lds[wave];
   uint4 K[8], V[8];
   int t = tb + wave;
-  if (t < te) load_tile(t < T0 ? seg0 : seg1, (t < T0 ? t : t - T0) * kTile, lane, K, V);
+  load_tile(t < T0 ? seg0 : seg1, t < te ? (t < T0 ? t : t - T0) * kTile : kNoRows, lane, K, V);
   // the owner's wave 0 forms the new rows; stage_query's barrier publishes the patch
   if (owner && wave == 0) {
-    const size_t in = (static_cast<size_t>(b) * kGroups + g) * kDim + 4 * lane;
-    const uint16_t *krec = anchor ? sp.k_rma : sp.k_win;
-    const uint16_t *vrec = anchor ? sp.v_rma : sp.v_win;
-    const uint2 kr = *reinterpret_cast<const uint2 *>(krec + in);
-    const uint2 vr = *reinterpret_cast<const uint2 *>(vrec + in);
+    const uint2 kr = krec_raw;
+    const uint2 vr = vrec_raw;
     float x[4] = {bf16_lo(kr.x), bf16_hi(kr.x), bf16_lo(kr.y), bf16_hi(kr.y)};
     float c, sn;
     rope_cos_sin(a.rope_ratio, p, lane, c, sn);
-    norm_rope_head(x, anchor ? sp.gk_rma : sp.gk_win, a.eps, c, sn, lane);
+    *reinterpret_cast<float4 *>(&g_lds[kWaves][4 * lane]) = kgain;
+    norm_rope_head(x, &g_lds[kWaves][0], a.eps, c, sn, lane);
     const uint2 kw = make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
     *reinterpret_cast<uint2 *>(&patch[0][4 * lane]) = kw;
     *reinterpret_cast<uint2 *>(&patch[1][4 * lane]) = vr;
@@ -501,7 +541,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepParams sp)
     *reinterpret_cast<uint2 *>((anchor ? sp.pend_k : sp.win_k) + row + 4 * lane) = kw;
     *reinterpret_cast<uint2 *>((anchor ? sp.pend_v : sp.win_v) + row + 4 * lane) = vr;
   }
-  stage_query(a, b, g, anchor, p, wave, lane, q_lds);
+  stage_query_raw(a, qraw, p, wave, lane, q_lds, g_lds[wave]);
   bf16x8 qv[8];
   {
     const uint16_t *qrow = &q_lds[0][0] + (lane & 15) * kQStride + 8 * (lane >> 4);
@@ -764,6 +804,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_q8_kernel(DecodeParam
   __shared__ __align__(16) uint16_t q_lds[16][kQStride];  // rows 4..15 stay zero
   __shared__ float red_m[kWaves][kHeadsPerGroup], red_l[kWaves][kHeadsPerGroup];
   __shared__ __align__(16) float ks_lds[kMaxScaleKeys], vs_lds[kMaxScaleKeys];
+  __shared__ __align__(16) float g_lds[kWaves][kDim];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps tile selection scalar
@@ -793,13 +834,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_q8_kernel(DecodeParam
   uint8_t *vl = v_lds[wave];
   uint4 K[8], V[8];
   int t = tb + wave;
-  if (t < te) {
+  // the query's loads first, then the first tile's (on every path): the prologue
+  // waits for the query alone
+  const QueryRaw qraw = load_query(a, b, g, anchor, wave, lane);
+  {
     const Segment &sg = t < T0 ? seg0 : seg1;
-    const int key0 = (t < T0 ? t : t - T0) * kTile8;
+    const int key0 = t < te ? (t < T0 ? t : t - T0) * kTile8 : kNoRows;
     load_v_fp8(sg, key0, lane, V);
     load_k_fp8(sg, key0, lane, K);
   }
-  stage_query(a, b, g, anchor, a.pos[b], wave, lane, q_lds);
+  stage_query_raw(a, qraw, a.pos[b], wave, lane, q_lds, g_lds[wave]);
   // Query operands in registers: qv[2s + h] holds, for lane (hh, kg), dims
   // 64s + 16kg + 8h .. +8 of head hh (the permuted contraction order).
   bf16x8 qv[8];
