@@ -130,6 +130,18 @@ struct SoftmaxState {
 };
 
 // ---------------------------------------------------------------- setup and epilogue
+// Workgroup -> (unit, split).  Workgroups are handed to the 8 XCDs in turn, so the
+// splits of one unit are numbered 8 apart: they all run on one XCD, whose L2 then
+// still holds their partials when the merge workgroup of that unit (number = unit,
+// the same XCD) reads them.  Units come in multiples of 8 (2 branches x 4 groups per
+// sequence), so the map is a bijection; without splits it is the identity.
+constexpr int kXcds = 8;
+static_assert(2 * kGroups % kXcds == 0, "units per sequence are a multiple of the XCD count");
+__device__ __forceinline__ void unit_split_of(int wg, int splits, int &unit, int &split) {
+  const int xcd = wg % kXcds, slot = wg / kXcds;
+  unit = (slot / splits) * kXcds + xcd;
+  split = slot % splits;
+}
 // The key segments of one (branch, sequence, group) for position p and the given
 // bank and pending counts; rb = bytes per row.
 template <bool kFp8>
@@ -386,8 +398,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_kernel(DecodeParams a
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps tile selection scalar
-  const int split = blockIdx.x % a.splits;
-  const int unit = blockIdx.x / a.splits;
+  int unit, split;
+  unit_split_of(blockIdx.x, a.splits, unit, split);
   const int per_branch = a.batch * kGroups;
   const bool anchor = unit < per_branch;  // anchor units first: they are the longer ones
   const int bg = anchor ? unit : unit - per_branch;
@@ -478,8 +490,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepParams sp)
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int split = blockIdx.x % a.splits;
-  const int unit = blockIdx.x / a.splits;
+  int unit, split;
+  unit_split_of(blockIdx.x, a.splits, unit, split);
   const int per_branch = a.batch * kGroups;
   const bool anchor = unit < per_branch;
   const int bg = anchor ? unit : unit - per_branch;
@@ -808,8 +820,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_q8_kernel(DecodeParam
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps tile selection scalar
-  const int split = blockIdx.x % a.splits;
-  const int unit = blockIdx.x / a.splits;
+  int unit, split;
+  unit_split_of(blockIdx.x, a.splits, unit, split);
   const int per_branch = a.batch * kGroups;
   const bool anchor = unit < per_branch;
   const int bg = anchor ? unit : unit - per_branch;
