@@ -63,7 +63,7 @@ static_assert(kWaves >= kHeadsPerGroup, "one wave per head in the query prologue
 // apart and a transposed read of 8 rows x 32 bytes hits 64 distinct banks.
 constexpr int kVStride = kDim + 16;
 constexpr int kPartStride = 4 + kDim;
-constexpr int kMaxSplits = 20;
+constexpr int kMaxSplits = 16;  // batch 1: 8 units x 16 = 128 workgroups, 16 per XCD
 #ifndef RMA_DECODE_MIN_WGS
 #define RMA_DECODE_MIN_WGS 512
 #endif

@@ -48,7 +48,7 @@ def test_split_policy_and_workspace(lib):
     assert R.rma_decode_splits(512) == 1 and R.rma_decode_workspace_bytes(512) == 0
     assert R.rma_decode_splits(64) == 1 and R.rma_decode_workspace_bytes(64) == 0
     assert R.rma_decode_splits(16) == 4
-    assert R.rma_decode_splits(1) == 20
+    assert R.rma_decode_splits(1) == 16
     assert R.rma_decode_workspace_bytes(16) == 16 * 8 * 4 * 4 * 260 * 4
 
 

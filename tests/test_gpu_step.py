@@ -150,7 +150,7 @@ def test_step_matches_append_then_decode_unsplit_batch():
 
 
 def test_step_batch_one_stream_wraps_the_window():
-    # pos + 1 = 1024 puts the new key in slot 0; 20 splits at batch 1
+    # pos + 1 = 1024 puts the new key in slot 0; 16 splits at batch 1
     got = _run_both("step_b1", [(700, 250, 1021)], 4, False)
     assert got.pos[0] == 1025 and got.n_pend[0] == 254
 
