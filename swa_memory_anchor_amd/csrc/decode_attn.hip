@@ -698,6 +698,51 @@ __device__ __forceinline__ void load_scales_fp8(const Segment &seg0, const Segme
                    vs_l + (b1 - tb) * kTile8);
 }
 
+// The same runs through registers: this thread's 16-byte piece of each run (a run
+// is at most 1024 keys, 256 pieces), loaded after the first tile's loads and stored
+// after the query prologue.  The INT8 decode, with more vector work per tile, gains
+// from not waiting for the scales before its first tile goes out; the E4M3 decode
+// does not (measured both ways).
+struct ScalePieces {
+  f32x4 k0, v0, k1, v1;
+  int i0, i1;  // LDS float index of each piece, -1 if none
+};
+static_assert(kBank / 4 <= kThreads && kBlock / 4 <= kThreads && kWindow / 4 <= kThreads,
+              "one 16-byte piece of each scale run per thread");
+
+__device__ __forceinline__ ScalePieces load_scale_pieces(const Segment &seg0, const Segment &seg1,
+                                                         int T0, int tb, int te) {
+  ScalePieces sp;
+  const int e0 = min(te, T0), b1 = max(tb, T0);
+  const int i = threadIdx.x;
+  sp.i0 = -1;
+  sp.i1 = -1;
+  sp.k0 = sp.v0 = sp.k1 = sp.v1 = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (tb < e0 && i < (e0 - tb) * (kTile8 / 4)) {
+    sp.k0 = bitcast<f32x4>(__builtin_amdgcn_raw_buffer_load_b128(seg0.ks, 16 * i, tb * kTile8 * 4, kStream));
+    sp.v0 = bitcast<f32x4>(__builtin_amdgcn_raw_buffer_load_b128(seg0.vs, 16 * i, tb * kTile8 * 4, kStream));
+    sp.i0 = 4 * i;
+  }
+  if (b1 < te && i < (te - b1) * (kTile8 / 4)) {
+    const int row0 = (b1 - T0) * kTile8;
+    sp.k1 = bitcast<f32x4>(__builtin_amdgcn_raw_buffer_load_b128(seg1.ks, 16 * i, row0 * 4, kStream));
+    sp.v1 = bitcast<f32x4>(__builtin_amdgcn_raw_buffer_load_b128(seg1.vs, 16 * i, row0 * 4, kStream));
+    sp.i1 = (b1 - tb) * kTile8 + 4 * i;
+  }
+  return sp;
+}
+
+__device__ __forceinline__ void store_scale_pieces(const ScalePieces &sp, float *ks_l, float *vs_l) {
+  if (sp.i0 >= 0) {
+    *reinterpret_cast<f32x4 *>(ks_l + sp.i0) = sp.k0;
+    *reinterpret_cast<f32x4 *>(vs_l + sp.i0) = sp.v0;
+  }
+  if (sp.i1 >= 0) {
+    *reinterpret_cast<f32x4 *>(ks_l + sp.i1) = sp.k1;
+    *reinterpret_cast<f32x4 *>(vs_l + sp.i1) = sp.v1;
+  }
+}
+
 // V codes stay E4M3 in LDS: 32 rows of 256 bytes, the 16-byte chunk c of row r at
 // chunk position c ^ vswz8(r), so that the 16 rows one half-wave's transposed reads
 // touch (rows 4kg..4kg+3 and 16+4kg..16+4kg+3 of two lane groups) hit 16 distinct
@@ -834,8 +879,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_q8_kernel(DecodeParam
   const int per = (T + a.splits - 1) / a.splits;
   const int tb = split * per;
   const int te = min(T, tb + per);
-  // the scales first (the query prologue's barrier publishes them)
-  load_scales_fp8(seg0, seg1, T0, tb, te, ks_lds, vs_lds);
+  // E4M3: the scales first (the query prologue's barrier publishes them)
+  if constexpr (!kInt8) load_scales_fp8(seg0, seg1, T0, tb, te, ks_lds, vs_lds);
 
   SoftmaxState st;
   st.m = -INFINITY;
@@ -855,7 +900,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attn_q8_kernel(DecodeParam
     load_v_fp8(sg, key0, lane, V);
     load_k_fp8(sg, key0, lane, K);
   }
-  stage_query_raw(a, qraw, a.pos[b], wave, lane, q_lds, g_lds[wave]);
+  if constexpr (kInt8) {
+    // INT8: the scales after the first tile, stored once the query is staged
+    const ScalePieces spc = load_scale_pieces(seg0, seg1, T0, tb, te);
+    stage_query_raw(a, qraw, a.pos[b], wave, lane, q_lds, g_lds[wave]);
+    store_scale_pieces(spc, ks_lds, vs_lds);
+    __syncthreads();
+  } else {
+    stage_query_raw(a, qraw, a.pos[b], wave, lane, q_lds, g_lds[wave]);
+  }
   // Query operands in registers: qv[2s + h] holds, for lane (hh, kg), dims
   // 64s + 16kg + 8h .. +8 of head hh (the permuted contraction order).
   bf16x8 qv[8];
