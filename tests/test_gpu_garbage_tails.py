@@ -18,18 +18,20 @@ import torch
 
 import oracle as O
 from oracle import fp8_ref as F
+from oracle import int8_ref as I
 import swa_memory_anchor_amd as R
 import synth
 from synth import core as C
 
 from gpu_util import (DEV, KV, assert_attn_close, assert_keys_close, bf16_dev, bits_host,
-                      decode_gpu, decode_gpu_fp8, download, download_fp8, f32_dev, norm_dev,
-                      upload, upload_fp8)
+                      decode_gpu, decode_gpu_fp8, decode_gpu_i8, download, download_fp8, f32_dev,
+                      norm_dev, upload, upload_fp8)
 
 pytestmark = pytest.mark.gpu
 
 BF16_BAD = np.array([0x7FC0, 0x7F80, 0xFF80, 0xFFFF, 0x7FFF], np.uint16)  # NaN, +-inf, NaNs
 E4M3_BAD = np.array([0x7F, 0xFF], np.uint8)  # the two E4M3 NaN codes
+I8_BAD = np.array([0x80, 0x7F, 0x81], np.uint8)  # -128 (never written), +127, -127
 F32_BAD = np.array([np.nan, np.inf, -np.inf], np.float32)
 
 # (n_bank, n_pend, pos): partial 16- and 32-key tiles in every segment, empty
@@ -262,3 +264,40 @@ def test_fp8_decode_ignores_poisoned_tails(batch_rep):
             if a.dtype == np.float32:
                 a, r = a.view(np.uint32), r.view(np.uint32)
             assert np.array_equal(a, r), (b, k)
+
+
+def _i8_state(tag, counts):
+    """INT8 state whose invalid slots hold extreme codes (-128 included, which the
+    quantiser never writes) and NaN/infinite row scales, so any such row that took part
+    in a dot product or the probability x value sum would make the output non-finite."""
+    st = I.new_layer_state_i8(len(counts))
+    for nm in KV:
+        a = getattr(st, nm)
+        a[...] = C.normal_i8_np(synth.stream_key(tag, nm), a.size).reshape(a.shape)
+        s = getattr(st, nm + "s")
+        s[...] = C.row_scale_np(synth.stream_key(tag, nm, "s"), s.size, denom=128).reshape(s.shape)
+    for b, (nb, npd, pos) in enumerate(counts):
+        st.n_bank[b], st.n_pend[b], st.pos[b] = nb, npd, pos
+    win, bank, pend = _valid_masks(st)
+    for nm, m in (("win_k", win), ("win_v", win), ("bank_k", bank), ("bank_v", bank),
+                  ("pend_k", pend), ("pend_v", pend)):
+        a = getattr(st, nm)
+        a[...] = np.where(~m[:, None, :, None], _bad_fill(a.shape, I8_BAD), a)
+        s = getattr(st, nm + "s")
+        s[...] = np.where(~m[:, None, :], _bad_fill(s.shape, F32_BAD), s)
+    return st
+
+
+@pytest.mark.parametrize("batch_rep", [1, 8])
+def test_int8_decode_ignores_poisoned_tails(batch_rep):
+    counts = COUNTS * batch_rep
+    B = len(counts)
+    print(f"case: poisoned int8 decode B={B}", flush=True)
+    st = _i8_state("poison_i8", counts)
+    g = _gains("poison_i8")
+    q = synth.normal_bf16_np(synth.stream_key("poison_i8", "q"), B * 4096).reshape(B, 16, 256)
+    qd = bf16_dev(q)
+    outs = decode_gpu_i8(upload_fp8(st), qd, qd, norm_dev(g))
+    torch.cuda.synchronize()
+    ref = I.decode(st, q, q, g["gq_win"], g["gq_rma"], 1e-6, 1e7)
+    _check_outputs(outs, ref, f"poisoned int8 decode B={B}")
