@@ -235,6 +235,37 @@ rma_status rma_score_multi(const rma_score_job *jobs, int32_t n_jobs, int64_t n_
                            int64_t ld_hidden, int64_t ld_scores, void *stream);
 
 /*
+ * rma_score_workspace_bytes - workspace rma_score_multi_ws needs for n_jobs
+ * calls of n_rows rows each: n_jobs * n_rows * 1024 bytes (the 256 stage-1
+ * results of every row, FP32) when the calls are small enough for its split
+ * path (n_jobs * ceil(n_rows / 32) <= 256), else 0.  0 for n_jobs outside
+ * 1..RMA_MAX_JOBS.
+ */
+size_t rma_score_workspace_bytes(int32_t n_jobs, int64_t n_rows);
+
+/*
+ * rma_score_multi_ws - rma_score_multi for calls too small to give every CU a
+ * row tile (the scores of a 256-token block at batch 1, [QB] section "三段记忆…":
+ * candidates are scored once per 256-token block).  Arguments and results as
+ * rma_score_multi, bit for bit; in addition
+ *   workspace  device memory of rma_score_workspace_bytes(n_jobs, n_rows) bytes,
+ *              16-byte aligned, owned by the caller; may be NULL when that size
+ *              is 0.  Its contents need no initial value and are scratch after
+ *              the call (stage-1 results).  Calls sharing a workspace must not
+ *              overlap.
+ * Small calls run as two launches: one wave per 32 x 32 block of stage-1 results
+ * (the 256 columns of a row tile spread over 8 CUs), then the fixed-order sum of
+ * each row over its 256 columns.  Larger calls run rma_score_multi's launch and
+ * leave the workspace untouched.
+ * Errors: those of rma_score_multi; RMA_E_WORKSPACE when the workspace is NULL or
+ * smaller than required, RMA_E_ALIGN when it is not 16-byte aligned (nothing is
+ * launched in either case).
+ */
+rma_status rma_score_multi_ws(const rma_score_job *jobs, int32_t n_jobs, int64_t n_rows,
+                              int64_t ld_hidden, int64_t ld_scores, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/*
  * rma_commit_topk - commit every sequence's pending block ([QB] section above:
  * each KV group keeps the best 1024 of bank + pending; [FB] section "架构…":
  * groups choose independently and may keep the same positions).

@@ -33,7 +33,8 @@ EXPORTS = (
     "rma_commit_topk", "rma_status_str", "rma_prefill_workspace_bytes", "swa_rma_prefill",
     "rma_layer_state_fp8_bytes", "swa_rma_append_fp8", "swa_rma_decode_attn_fp8",
     "rma_commit_topk_fp8", "gdn_layer_state_bytes", "gdn_decode_step",
-    "rma_step_workspace_bytes", "swa_rma_step", "rma_score_multi", "rma_commit_topk_multi",
+    "rma_step_workspace_bytes", "swa_rma_step", "rma_score_multi", "rma_score_workspace_bytes",
+    "rma_score_multi_ws", "rma_commit_topk_multi",
     "gdn_prefill", "swa_rma_decode_attn_noalloc", "swa_rma_append_i8", "swa_rma_decode_attn_i8",
 )
 
@@ -108,6 +109,11 @@ def lib() -> ctypes.CDLL:
         L.rma_commit_topk.argtypes = [sp, i32, vp, vp]
         L.rma_score_multi.argtypes = [ctypes.POINTER(_ScoreJobC), i32, i64, i64, i64, vp]
         L.rma_score_multi.restype = ctypes.c_int
+        L.rma_score_workspace_bytes.argtypes = [i32, i64]
+        L.rma_score_workspace_bytes.restype = sz
+        L.rma_score_multi_ws.argtypes = [ctypes.POINTER(_ScoreJobC), i32, i64, i64, i64, vp, sz,
+                                         vp]
+        L.rma_score_multi_ws.restype = ctypes.c_int
         L.rma_commit_topk_multi.argtypes = [sp, i32, i32, ctypes.POINTER(vp), vp]
         L.rma_commit_topk_multi.restype = ctypes.c_int
         L.rma_commit_topk.restype = ctypes.c_int
@@ -366,6 +372,29 @@ def rma_score_multi(jobs, n_rows: int, ld_hidden: int, ld_scores: int, stream=No
     s = lib().rma_score_multi(arr, len(jobs), int(n_rows), int(ld_hidden), int(ld_scores),
                               _stream(stream))
     _check(s, "rma_score_multi")
+
+
+def rma_score_workspace_bytes(n_jobs: int, n_rows: int) -> int:
+    return int(lib().rma_score_workspace_bytes(int(n_jobs), int(n_rows)))
+
+
+def score_workspace(n_jobs: int, n_rows: int, device="cuda"):
+    """A workspace of the size rma_score_multi_ws needs for these calls (or None)."""
+    import torch
+
+    n = rma_score_workspace_bytes(n_jobs, n_rows)
+    return None if n == 0 else torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def rma_score_multi_ws(jobs, n_rows: int, ld_hidden: int, ld_scores: int, workspace,
+                       stream=None) -> None:
+    """rma_score_multi with a workspace (``score_workspace``) for its small-call path."""
+    arr = (_ScoreJobC * len(jobs))(*[_ScoreJobC(_ptr(h), _ptr(a), _ptr(b), _ptr(o))
+                                     for h, a, b, o in jobs])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    s = lib().rma_score_multi_ws(arr, len(jobs), int(n_rows), int(ld_hidden), int(ld_scores),
+                                 _ptr(workspace), ws_bytes, _stream(stream))
+    _check(s, "rma_score_multi_ws")
 
 
 def rma_commit_topk_multi(states, batch: int, keep_idx=None, stream=None) -> None:

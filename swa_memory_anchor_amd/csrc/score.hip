@@ -23,6 +23,14 @@
 //    passed through LDS in two column halves and every output row is summed over
 //    its 256 columns in the same fixed order, so identical input rows give
 //    bit-identical scores wherever they sit.
+// Calls too small to give every CU a tile even at 32 rows (a 256-token block of
+// a batch-1 stream: 8 tiles per layer) are bound by one CU's MFMA rate per tile.
+// With a workspace they take a split path instead: one wave per 32 x 32 block of
+// stage-1 results, its operands loaded straight from global memory (four slices
+// in flight, no LDS, no barrier), the block written to the workspace; a second
+// launch then sums each row over its 256 columns in the same order as above.
+// Every stage-1 element is the same MFMA chain in both paths, so the scores are
+// bit-identical to those of the one-launch path.
 #include "rma_device.h"
 
 namespace rma {
@@ -228,9 +236,145 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score_kernel(ScoreJobs jobs)
   }
 }
 
+// Split path, stage 1: workgroup b takes call b % n_jobs (with 8 calls, every
+// wave of a call runs on one XCD); its wave w takes task t = (b / n_jobs) *
+// waves + w of that call: 32-row tile t / 8, 32-column block t % 8.  Lane l supplies A[m = l%32][k] and B[k][n = l%32]
+// for k = 16h .. 16h+15 of each 32-deep slice (h = l/32), exactly the operand
+// order of score_kernel, so every element sees the same MFMA sequence.  Rows past
+// n_rows load the last row (they are never stored); each slice's loads are
+// unconditional, the last ones re-reading the final slice, so the wait for a
+// slice covers only that slice.
+#ifndef RMA_SCORE_SPLIT_WAVES
+#define RMA_SCORE_SPLIT_WAVES 1
+#endif
+#ifndef RMA_SCORE_SPLIT_DEPTH
+#define RMA_SCORE_SPLIT_DEPTH 4
+#endif
+constexpr int kSplitDepth = RMA_SCORE_SPLIT_DEPTH;  // slices in flight per wave (18 loads each)
+constexpr int kColBlocks = kMid / 32;
+constexpr int kSplitWaves = RMA_SCORE_SPLIT_WAVES;  // waves (column blocks) per workgroup
+static_assert(kColBlocks % kSplitWaves == 0, "a workgroup's waves share one row tile");
+
+__global__ __launch_bounds__(64 * kSplitWaves, 1) void score_split_kernel(ScoreJobs jobs, float *z,
+                                                                          int n_jobs) {
+  const int job = blockIdx.x % n_jobs;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int task = (blockIdx.x / n_jobs) * kSplitWaves + wave;
+  const ScoreParams &a = jobs.job[job];
+  const int cb = task % kColBlocks, rt = task / kColBlocks;
+  const int lane = threadIdx.x & 63, ml = lane & 31, kh = lane >> 5;
+  const int64_t row = min(static_cast<int64_t>(rt) * 32 + ml, a.n_rows - 1);
+  const uint16_t *hp = a.hidden + row * a.ld_hidden + 16 * kh;
+  const float *wp = a.w1 + static_cast<size_t>(16 * kh) * kMid + 32 * cb + ml;
+  constexpr int nkt = kHidden / kKt;
+  static_assert(nkt % kSplitDepth == 0, "whole rounds of the slice ring");
+
+  uint4 ra[kSplitDepth][2];
+  float rb[kSplitDepth][16];
+  auto load = [&](int d, int kt) {
+    const uint16_t *h = hp + kt * kKt;
+    ra[d][0] = *reinterpret_cast<const uint4 *>(h);
+    ra[d][1] = *reinterpret_cast<const uint4 *>(h + 8);
+    const float *wk = wp + static_cast<size_t>(kt * kKt) * kMid;
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) rb[d][kk] = wk[static_cast<size_t>(kk) * kMid];
+  };
+
+  f32x16 acc;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+#pragma unroll
+  for (int d = 0; d < kSplitDepth; ++d) load(d, d);
+  for (int kt0 = 0; kt0 < nkt; kt0 += kSplitDepth) {
+#pragma unroll
+    for (int d = 0; d < kSplitDepth; ++d) {
+      float av[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t u0 = j == 0 ? ra[d][0].x : j == 1 ? ra[d][0].y : j == 2 ? ra[d][0].z : ra[d][0].w;
+        const uint32_t u1 = j == 0 ? ra[d][1].x : j == 1 ? ra[d][1].y : j == 2 ? ra[d][1].z : ra[d][1].w;
+        av[2 * j] = bf16_lo(u0);
+        av[2 * j + 1] = bf16_hi(u0);
+        av[8 + 2 * j] = bf16_lo(u1);
+        av[8 + 2 * j + 1] = bf16_hi(u1);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk)
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[kk], rb[d][kk], acc, 0, 0, 0);
+      // the scheduler would otherwise sink each refill next to its use
+      __builtin_amdgcn_sched_barrier(0);
+      load(d, min(kt0 + d + kSplitDepth, nkt - 1));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // acc[q] is Z[32 rt + 8 (q/4) + 4 h + q%4][32 cb + l%32]
+  float *zc = z + static_cast<size_t>(job) * a.n_rows * kMid + 32 * cb + ml;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int64_t r = static_cast<int64_t>(rt) * 32 + 8 * (q >> 2) + 4 * kh + (q & 3);
+    if (r < a.n_rows) zc[r * kMid] = acc[q];
+  }
+}
+
+// Split path, stage 2: one thread per row of call blockIdx.y; s[row][g] =
+// sum_{n=0..255} Z[row][n] * W2[n][g], n ascending, the chain of score_kernel.
+// The tile's 64 rows come into LDS with coalesced loads (load i of every lane
+// reads row i, all 64 in flight: the rows were written by other XCDs), then each
+// thread walks its row in a short loop.
+constexpr int kZRow = kMid + 4;  // padded LDS row (floats): 16-byte reads down a column hit distinct banks
+
+__global__ __launch_bounds__(64) void score_split_sum_kernel(ScoreJobs jobs, const float *z) {
+  const ScoreParams &a = jobs.job[blockIdx.y];
+  __shared__ __align__(16) float zs[64 * kZRow];
+  __shared__ __align__(16) float w2s[kMid * kGroups];
+  const int t = threadIdx.x;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int nr = static_cast<int>(min(static_cast<int64_t>(64), a.n_rows - r0));
+  // a buffer resource over the tile's rows: rows past n_rows read as zeros
+  const __amdgpu_buffer_rsrc_t zr_all = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float *>(z + (static_cast<size_t>(blockIdx.y) * a.n_rows + r0) * kMid), 0,
+      nr * kMid * static_cast<int>(sizeof(float)), 0x00020000);
+  using u32x4 = decltype(__builtin_amdgcn_raw_buffer_load_b128(zr_all, 0, 0, 0));
+  u32x4 v[64];
+#pragma unroll
+  for (int i = 0; i < 64; ++i)
+    v[i] = __builtin_amdgcn_raw_buffer_load_b128(zr_all, 16 * t, i * kMid * 4, 0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < kMid * kGroups / 64; ++i) w2s[i * 64 + t] = a.w2[i * 64 + t];
+#pragma unroll
+  for (int i = 0; i < 64; ++i)
+    *reinterpret_cast<u32x4 *>(zs + i * kZRow + 4 * t) = v[i];
+  __syncthreads();
+  if (t >= nr) return;
+  const float *zr = zs + t * kZRow;
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  static_assert(kGroups == 4, "four scores per row");
+#pragma unroll 2
+  for (int n4 = 0; n4 < kMid / 4; ++n4) {
+    const float4 zz = *reinterpret_cast<const float4 *>(zr + 4 * n4);
+    const float e4[4] = {zz.x, zz.y, zz.z, zz.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float4 w = *reinterpret_cast<const float4 *>(w2s + (4 * n4 + e) * kGroups);
+      s0 = fmaf(e4[e], w.x, s0);
+      s1 = fmaf(e4[e], w.y, s1);
+      s2 = fmaf(e4[e], w.z, s2);
+      s3 = fmaf(e4[e], w.w, s3);
+    }
+  }
+  *reinterpret_cast<float4 *>(a.scores + (r0 + t) * a.ld_scores) = make_float4(s0, s1, s2, s3);
+}
+
 }  // namespace rma
 
 using namespace rma;
+
+// The split path serves calls whose 32-row tiles, over all calls, number at most
+// one per CU; it needs n_jobs * n_rows stage-1 rows of workspace.
+static bool score_takes_split(int64_t n_jobs, int64_t n_rows) {
+  return n_rows > 0 && n_jobs * ((n_rows + 31) / 32) <= 256;
+}
 
 // Validate one call's arguments (shared by the single and the multi-call entry).
 static rma_status check_score(const uint16_t *hidden, int64_t n_rows, int64_t ld_hidden,
@@ -285,10 +429,9 @@ extern "C" rma_status rma_score(const uint16_t *hidden, int64_t n_rows, int64_t 
   return launch_score(jobs, 1, n_rows, stream);
 }
 
-extern "C" rma_status rma_score_multi(const rma_score_job *jobs, int32_t n_jobs, int64_t n_rows,
-                                      int64_t ld_hidden, int64_t ld_scores, void *stream) {
+static rma_status collect_jobs(const rma_score_job *jobs, int32_t n_jobs, int64_t n_rows,
+                               int64_t ld_hidden, int64_t ld_scores, ScoreJobs &sj) {
   if (!jobs || n_jobs < 1 || n_jobs > RMA_MAX_JOBS) return RMA_E_ARG;
-  ScoreJobs sj{};
   for (int j = 0; j < n_jobs; ++j) {
     const rma_score_job &jb = jobs[j];
     const rma_status rc = check_score(jb.hidden, n_rows, ld_hidden, jb.w1, jb.w2, jb.scores,
@@ -296,6 +439,41 @@ extern "C" rma_status rma_score_multi(const rma_score_job *jobs, int32_t n_jobs,
     if (rc != RMA_OK) return rc;
     sj.job[j] = ScoreParams{jb.hidden, n_rows, ld_hidden, jb.w1, jb.w2, jb.scores, ld_scores};
   }
-  if (n_rows == 0) return RMA_OK;
+  return RMA_OK;
+}
+
+extern "C" rma_status rma_score_multi(const rma_score_job *jobs, int32_t n_jobs, int64_t n_rows,
+                                      int64_t ld_hidden, int64_t ld_scores, void *stream) {
+  ScoreJobs sj{};
+  const rma_status rc = collect_jobs(jobs, n_jobs, n_rows, ld_hidden, ld_scores, sj);
+  if (rc != RMA_OK || n_rows == 0) return rc;
   return launch_score(sj, n_jobs, n_rows, stream);
+}
+
+extern "C" size_t rma_score_workspace_bytes(int32_t n_jobs, int64_t n_rows) {
+  if (n_jobs < 1 || n_jobs > RMA_MAX_JOBS || !score_takes_split(n_jobs, n_rows)) return 0;
+  return static_cast<size_t>(n_jobs) * static_cast<size_t>(n_rows) * kMid * sizeof(float);
+}
+
+extern "C" rma_status rma_score_multi_ws(const rma_score_job *jobs, int32_t n_jobs, int64_t n_rows,
+                                         int64_t ld_hidden, int64_t ld_scores, void *workspace,
+                                         size_t workspace_bytes, void *stream) {
+  ScoreJobs sj{};
+  const rma_status rc = collect_jobs(jobs, n_jobs, n_rows, ld_hidden, ld_scores, sj);
+  if (rc != RMA_OK || n_rows == 0) return rc;
+  if (!score_takes_split(n_jobs, n_rows)) return launch_score(sj, n_jobs, n_rows, stream);
+  if (!workspace || workspace_bytes < rma_score_workspace_bytes(n_jobs, n_rows))
+    return RMA_E_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) & 15u) return RMA_E_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float *z = static_cast<float *>(workspace);
+  const unsigned tiles = static_cast<unsigned>((n_rows + 31) / 32);
+  hipLaunchKernelGGL(score_split_kernel,
+                     dim3(static_cast<unsigned>(n_jobs) * tiles * (kColBlocks / kSplitWaves)),
+                     dim3(64 * kSplitWaves), 0, s, sj, z, static_cast<int>(n_jobs));
+  hipLaunchKernelGGL(score_split_sum_kernel,
+                     dim3(static_cast<unsigned>((n_rows + 63) / 64), static_cast<unsigned>(n_jobs)),
+                     dim3(64), 0, s, sj, static_cast<const float *>(z));
+  if (hipPeekAtLastError() != hipSuccess) return (void)hipGetLastError(), RMA_E_HIP;
+  return RMA_OK;
 }

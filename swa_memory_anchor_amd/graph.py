@@ -8,7 +8,8 @@ the pages' single-request decoding rates (fluxbbs.com page, section "ÂêûÂêêÔºö‰∏
 80GB Âç°Ë∑ë 512 Ë∑ØÈïøÊé®ÁêÜ") come from a backend that replays captured graphs
 (agentlenshq.com "rockmatrix-ai/EdgeRock", section "Â¶Ç‰ΩïÂ∞ùËØï").  ``StreamBlockGraph``
 records one whole 256-token block for every layer (256 x L steps, then the
-scores of every layer in one launch and the commits of every layer in one) into a
+scores of every layer (one launch, or two for small blocks) and the commits of every
+layer in one launch) into a
 single HIP graph through torch's graph capture, and replays it per block.  A step is one ``swa_rma_step`` launch (append and
 attention fused; the split merge follows where the key range is split) or, with
 ``fused=False``, the separate append and decode launches.
@@ -27,7 +28,8 @@ from __future__ import annotations
 import ctypes
 
 from . import (BLOCK, HEAD_DIM, HIDDEN, KV_GROUPS, Q_HEADS, LayerState, Norm, _norm_c, _ptr,
-               _ScoreJobC, _state_c, _StateC, decode_workspace, lib, step_workspace)
+               _ScoreJobC, _state_c, _StateC, decode_workspace, lib, score_workspace,
+               step_workspace)
 
 RMA_MAX_JOBS = 16  # calls one *_multi entry point takes at most (rma.h)
 
@@ -41,18 +43,19 @@ class StreamBlockGraph:
     Static inputs (device tensors, filled by the caller before ``replay``):
       rec[name]  [L][tokens][B][4][256] BF16 (raw window / candidate records)
       q_win, q_rma  [L][tokens][B][16][256] BF16
-      hidden     [L][B][tokens][2560] BF16 (scorer input; used when ``commit``)
+      hidden     [L][B][256][2560] BF16 (the block's scorer input; used when ``commit``)
     Outputs: o_win, o_rma [L][tokens][B][16][256] BF16; lse_win, lse_rma [L][tokens][B][16].
-    With commit=True the block must end on a commit boundary (the pending block is
-    full after the last token), as in a stream that starts on one.
+    With commit=True the last token must end a block (the pending block is full after
+    it), as in a stream that starts on a block boundary: a whole block of 256 tokens,
+    or fewer tokens that finish one (a single block-end token, say).
     """
 
     def __init__(self, states: list[LayerState], norms: list[Norm], scorer, batch: int,
                  tokens: int = BLOCK, commit: bool = True, fused: bool = True, device="cuda"):
         import torch
 
-        if commit and tokens != BLOCK:
-            raise ValueError("a block that commits holds exactly one pending block of tokens")
+        if commit and not 1 <= tokens <= BLOCK:
+            raise ValueError("a graph that commits ends one pending block: 1..256 tokens")
         L = len(states)
         self.L, self.B, self.T, self.commit = L, batch, tokens, commit
         bf = torch.bfloat16
@@ -60,7 +63,7 @@ class StreamBlockGraph:
                     for nm in RECORD_NAMES}
         self.q_win = torch.zeros(L, tokens, batch, Q_HEADS, HEAD_DIM, dtype=bf, device=device)
         self.q_rma = torch.zeros_like(self.q_win)
-        self.hidden = (torch.zeros(L, batch, tokens, HIDDEN, dtype=bf, device=device)
+        self.hidden = (torch.zeros(L, batch, BLOCK, HIDDEN, dtype=bf, device=device)
                        if commit else None)
         self.o_win = torch.zeros(L, tokens, batch, Q_HEADS, HEAD_DIM, dtype=bf, device=device)
         self.o_rma = torch.zeros_like(self.o_win)
@@ -70,6 +73,10 @@ class StreamBlockGraph:
         # the fused step's workspace holds counters that start at zero and are back
         # at zero after every step, so one zero fill serves every replay
         self.workspace = step_workspace(batch, device) if fused else decode_workspace(batch, device)
+        # stage-1 scorer results of every layer's block (small calls spread the 256
+        # columns of a row tile over 8 CUs and sum them in a second launch)
+        self.score_ws = (score_workspace(min(L, RMA_MAX_JOBS), batch * BLOCK, device)
+                         if commit else None)
         self._states, self._norms, self._scorer = states, norms, scorer
         # the ctypes structs must outlive the graph: kernels read them at launch only,
         # but keep them with the object for the record
@@ -113,16 +120,19 @@ class StreamBlockGraph:
                     raise RuntimeError(f"swa_rma_decode_attn failed during capture (status {s})")
         if self.commit:
             # every layer's scores in one launch, then every layer's commit in one
-            hb = HIDDEN * 2 * B * T
+            hb = HIDDEN * 2 * B * BLOCK
             for l0 in range(0, L, RMA_MAX_JOBS):
                 ls = range(l0, min(L, l0 + RMA_MAX_JOBS))
                 jobs = (_ScoreJobC * len(ls))(*[
                     _ScoreJobC(self.hidden.data_ptr() + l * hb, _ptr(self._scorer[l][0]),
                                _ptr(self._scorer[l][1]), _ptr(self._states[l].pend_score))
                     for l in ls])
-                s = lb.rma_score_multi(jobs, len(ls), B * T, HIDDEN, KV_GROUPS, stream)
+                sws = _ptr(self.score_ws)
+                swn = 0 if self.score_ws is None else self.score_ws.numel()
+                s = lb.rma_score_multi_ws(jobs, len(ls), B * BLOCK, HIDDEN, KV_GROUPS, sws,
+                                          swn, stream)
                 if s != 0:
-                    raise RuntimeError(f"rma_score_multi failed during capture (status {s})")
+                    raise RuntimeError(f"rma_score_multi_ws failed during capture (status {s})")
                 sts = (_StateC * len(ls))(*[self._st_c[l] for l in ls])
                 s = lb.rma_commit_topk_multi(sts, len(ls), B, None, stream)
                 if s != 0:

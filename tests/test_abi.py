@@ -139,6 +139,23 @@ def test_multi_call_host_validation(lib):
     bad = (R._ScoreJobC * 2)(job, R._ScoreJobC(24, 16, 16, 16))
     assert lib.rma_score_multi(bad, 2, 256, 2560, 4, None) == 2     # one misaligned job
     assert lib.rma_score_multi(bad, 1, 256, 2559, 4, None) == 1
+    # the split scorer path: workspace sizes and the checks made before any launch
+    assert lib.rma_score_workspace_bytes(8, 256) == 8 * 256 * 1024
+    assert lib.rma_score_workspace_bytes(1, 8192) == 8192 * 1024      # 256 row tiles
+    assert lib.rma_score_workspace_bytes(1, 8193) == 0                # 257: one-launch path
+    assert lib.rma_score_workspace_bytes(16, 512) == 16 * 512 * 1024
+    assert lib.rma_score_workspace_bytes(16, 513) == 0
+    assert lib.rma_score_workspace_bytes(0, 256) == 0
+    assert lib.rma_score_workspace_bytes(17, 256) == 0
+    assert lib.rma_score_workspace_bytes(1, 0) == 0
+    need = 2 * 256 * 1024
+    assert lib.rma_score_multi_ws(jobs, 0, 256, 2560, 4, 64, need, None) == 1
+    assert lib.rma_score_multi_ws(jobs, 17, 256, 2560, 4, 64, need, None) == 1
+    assert lib.rma_score_multi_ws(bad, 2, 256, 2560, 4, 64, need, None) == 2
+    assert lib.rma_score_multi_ws(jobs, 2, 0, 2560, 4, None, 0, None) == 0   # no rows
+    assert lib.rma_score_multi_ws(jobs, 2, 256, 2560, 4, None, need, None) == 3
+    assert lib.rma_score_multi_ws(jobs, 2, 256, 2560, 4, 64, need - 1, None) == 3
+    assert lib.rma_score_multi_ws(jobs, 2, 256, 2560, 4, 72, need, None) == 2  # misaligned
     st = _state()
     states = (R._StateC * 17)(*([st] * 17))
     assert lib.rma_commit_topk_multi(states, 0, 4, None, None) == 1

@@ -129,3 +129,76 @@ def test_block_graph_replays_match_eager(B, fused):
         # the replay advanced every sequence by one block and committed it
         assert live[0].pos.cpu().tolist() == [p + T for _, p in counts]
         assert live[0].n_pend.cpu().tolist() == [0] * B
+
+
+def test_block_end_token_graph_matches_eager():
+    """A one-token graph that ends a block (step, then the block's scores from its 256
+    hidden rows per sequence, then the commit) replays bit for bit as the same calls
+    made eagerly with the one-launch scorer."""
+    B, L = 2, 2
+    tag = "graph_end"
+    print(f"case: block-end token graph B={B}", flush=True)
+    counts = [(1024, 65790), (300, 766)]  # 255 pending rows each: the next token ends a block
+    init = []
+    for l in range(L):
+        st = R.alloc_layer_state(B, DEV)
+        _fill_state(st, (tag, l), counts)
+        for b, (_, pos) in enumerate(counts):
+            st.n_pend[b] = T - 1
+            st.pend_src[b] = torch.arange(pos - (T - 2), pos + 2, dtype=torch.int32)
+        init.append(st)
+    norms, scorer = [], []
+    for l in range(L):
+        gs = [torch.from_numpy(synth.normal_f32_np(synth.stream_key(tag, l, nm), (256,), 1.0, 0.1))
+              .to(DEV) for nm in ("gq_win", "gk_win", "gq_rma", "gk_rma")]
+        norms.append(R.Norm(*gs))
+        w1 = synth.normal_f32_np(synth.stream_key(tag, l, "w1"), (R.HIDDEN, R.SCORER_MID), 0, 0.02)
+        w2 = synth.normal_f32_np(synth.stream_key(tag, l, "w2"), (R.SCORER_MID, 4), 0, 0.02)
+        scorer.append((torch.from_numpy(w1).to(DEV), torch.from_numpy(w2).to(DEV)))
+    live = [_clone(s) for s in init]
+    eager_states = [_clone(s) for s in init]
+    g = StreamBlockGraph(live, norms, scorer, B, tokens=1, commit=True)
+    for nm in RECORD_NAMES:
+        normal_bf16_torch_(g.rec[nm], synth.stream_key(tag, "rec", nm))
+    normal_bf16_torch_(g.q_win, synth.stream_key(tag, "qw"))
+    normal_bf16_torch_(g.q_rma, synth.stream_key(tag, "qr"))
+    normal_bf16_torch_(g.hidden, synth.stream_key(tag, "hid"))
+
+    ref = [torch.empty_like(x) for x in (g.o_win, g.lse_win, g.o_rma, g.lse_rma)]
+    ws = R.step_workspace(B)
+    for l in range(L):
+        R.swa_rma_step(eager_states[l], B, *[g.rec[nm][l, 0] for nm in RECORD_NAMES], None,
+                       g.q_win[l, 0], g.q_rma[l, 0], norms[l], ref[0][l, 0], ref[1][l, 0],
+                       ref[2][l, 0], ref[3][l, 0], ws)
+    for l in range(L):
+        R.rma_score(g.hidden[l], B * T, R.HIDDEN, scorer[l][0], scorer[l][1],
+                    eager_states[l].pend_score, R.KV_GROUPS)
+        R.rma_commit_topk(eager_states[l], B)
+    R.rma_score_multi_ws([(g.hidden[0], scorer[0][0], scorer[0][1], torch.empty(B * T, 4, device=DEV))],
+                         B * T, R.HIDDEN, R.KV_GROUPS, R.score_workspace(1, B * T, DEV))
+    torch.cuda.synchronize()
+    g.capture()
+    ref_bits = [bits_host(ref[0]), ref[1].cpu().numpy(), bits_host(ref[2]), ref[3].cpu().numpy()]
+    for rep in range(3):
+        for l in range(L):
+            _assign(live[l], init[l])
+        for x in (g.o_win, g.o_rma, g.lse_win, g.lse_rma):
+            x.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [bits_host(g.o_win), g.lse_win.cpu().numpy(), bits_host(g.o_rma),
+               g.lse_rma.cpu().numpy()]
+        for a, b_, nm in zip(got, ref_bits, ("o_win", "lse_win", "o_rma", "lse_rma")):
+            assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                                  b_.view(np.uint32) if b_.dtype == np.float32 else b_), (rep, nm)
+        for l in range(L):
+            for k, v in live[l].__dict__.items():
+                e = eager_states[l].__dict__[k]
+                if v.dtype == torch.bfloat16:
+                    v, e = v.view(torch.int16), e.view(torch.int16)
+                elif v.dtype == torch.float32:
+                    v, e = v.view(torch.int32), e.view(torch.int32)
+                assert torch.equal(v, e), (rep, l, k)
+        assert live[0].n_pend.cpu().tolist() == [0] * B
+        assert live[0].pos.cpu().tolist() == [p + 1 for _, p in counts]

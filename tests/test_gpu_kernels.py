@@ -305,6 +305,58 @@ def test_score_multi_equals_separate_calls():
             assert torch.equal(out.view(torch.int32), ref.view(torch.int32))
 
 
+@pytest.mark.parametrize("n_jobs,n,ld_h,ld_s", [(8, 256, 2560, 4), (8, 1, 2560, 4),
+                                                 (3, 33, 2568, 8), (8, 1000, 2560, 4),
+                                                 (1, 8192, 2560, 4), (1, 8193, 2560, 4)])
+def test_score_multi_ws_equals_single_calls(n_jobs, n, ld_h, ld_s):
+    """rma_score_multi_ws: every job's scores are bit-identical to its own rma_score
+    call, on the split path (up to 256 row tiles in all, ragged last tile, strided
+    input and output) and past it (8193 rows: the one-launch path).  The workspace
+    starts out holding NaNs, and a second call reuses it."""
+    rng = np.random.default_rng(78 + n)
+    need = R.rma_score_workspace_bytes(n_jobs, n)
+    assert need == (n_jobs * n * 1024 if n_jobs * ((n + 31) // 32) <= 256 else 0)
+    print(f"case: score multi ws jobs={n_jobs} n={n} ld={ld_h},{ld_s} ws={need}", flush=True)
+    ws = None if need == 0 else torch.full((need // 4,), float("nan"), device=DEV)
+    for rep in range(2):
+        jobs, refs = [], []
+        for j in range(n_jobs):
+            h = bf16_dev(synth.normal_bf16_np(synth.stream_key("score_ws", n, j, rep), n * ld_h)
+                         .reshape(n, ld_h))
+            w1 = f32_dev((0.02 * rng.standard_normal((2560, 256))).astype(np.float32))
+            w2 = f32_dev((0.02 * rng.standard_normal((256, 4))).astype(np.float32))
+            out = torch.full((n, ld_s), float("nan"), device=DEV)
+            ref = torch.full((n, ld_s), float("nan"), device=DEV)
+            R.rma_score(h, n, ld_h, w1, w2, ref, ld_s)
+            jobs.append((h, w1, w2, out))
+            refs.append(ref)
+        R.rma_score_multi_ws(jobs, n, ld_h, ld_s, ws)
+        torch.cuda.synchronize()
+        for (_, _, _, out), ref in zip(jobs, refs):
+            assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), rep
+            if ld_s > 4:
+                assert torch.isnan(out[:, 4:]).all()  # columns past the 4 scores untouched
+
+
+def test_score_multi_ws_duplicate_rows_and_oracle():
+    """Split path: identical rows give identical scores wherever they sit, and the
+    scores match the float64 oracle within the scorer's bar."""
+    print("case: score multi ws duplicates", flush=True)
+    n = 256
+    base = synth.normal_bf16_np(synth.stream_key("score_ws_dup"), n * 2560).reshape(n, 2560)
+    base[200:] = base[:56]
+    rng = np.random.default_rng(5)
+    w1 = (0.02 * rng.standard_normal((2560, 256))).astype(np.float32)
+    w2 = (0.02 * rng.standard_normal((256, 4))).astype(np.float32)
+    out = torch.empty(n, 4, device=DEV)
+    ws = R.score_workspace(1, n, DEV)
+    R.rma_score_multi_ws([(bf16_dev(base), f32_dev(w1), f32_dev(w2), out)], n, 2560, 4, ws)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.array_equal(o[200:].view(np.uint32), o[:56].view(np.uint32))
+    assert_scores_close(o, O.score(base, w1, w2), what="score multi ws")
+
+
 def test_commit_multi_equals_separate_calls():
     """rma_commit_topk_multi over three layers leaves each state and keep_idx as
     rma_commit_topk does, bit for bit (ragged counts, ties, signed zeros, NaN)."""

@@ -3,7 +3,7 @@
 The stream runs as the benchmark's does: per token and layer one fused step
 (swa_rma_step: append to window + pending, then decode); at every block end the
 scorer writes all 8 layers' pending scores from the block's hidden rows
-(rma_score_multi, straight into pend_score) and all 8 layers commit
+(rma_score_multi_ws, straight into pend_score) and all 8 layers commit
 (rma_commit_topk_multi), 1024 commits per layer.
 
 Checked against the oracle (worker processes):
@@ -90,6 +90,7 @@ def test_long_stream_b1():
     hid = torch.empty(L, CHUNK, 2560, dtype=torch.bfloat16, device=DEV)
     ws = R.step_workspace(1)
     ws_p, ws_n = ws.data_ptr(), ws.numel()
+    score_ws = R.score_workspace(L, O.BLOCK, DEV)
     rec_stride, q_stride = 4 * 256 * 2, 16 * 256 * 2
     o_stride, l_stride = 16 * 256 * 2, 16 * 4
     print(f"stream: {T} positions x {L} layers, {ncheck} checked positions per layer",
@@ -118,9 +119,9 @@ def test_long_stream_b1():
             if (p + 1) % O.BLOCK == 0:
                 c = p // O.BLOCK
                 t0 = t - (O.BLOCK - 1)
-                R.rma_score_multi([(hid[l, t0:t0 + O.BLOCK], w[l][0], w[l][1],
-                                    states[l].pend_score) for l in range(L)],
-                                  O.BLOCK, 2560, 4, stream)
+                R.rma_score_multi_ws([(hid[l, t0:t0 + O.BLOCK], w[l][0], w[l][1],
+                                       states[l].pend_score) for l in range(L)],
+                                     O.BLOCK, 2560, 4, score_ws, stream)
                 for l in range(L):
                     stash[c, l].copy_(states[l].pend_score[0])
                 R.rma_commit_topk_multi(states, 1, [keeps[c, l] for l in range(L)], stream)
