@@ -252,3 +252,13 @@ def test_gdn_prefill_host_validation(lib):
     assert pf(by(st), 4, 8, 0, 16, 16, 16, None, by(pr), 16, None) == 1      # no positions
     assert pf(by(st), 4, 8, 0, 24, 16, 16, 16, by(pr), 16, None) == 2        # misaligned x
     assert pf(by(st), 4, 8, 1, 16, 16, 16, 16, by(pr), 40, None) == 2        # misaligned o
+
+
+def test_block_graph_rejects_token_counts_that_cannot_end_a_block():
+    """A graph that commits ends one pending block: 1..256 tokens (checked before any
+    device memory is touched)."""
+    from swa_memory_anchor_amd.graph import StreamBlockGraph
+
+    for tokens in (0, 257, 512):
+        with pytest.raises(ValueError):
+            StreamBlockGraph([], [], [], 1, tokens=tokens, commit=True, device="cpu")
