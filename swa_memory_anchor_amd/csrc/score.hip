@@ -271,18 +271,32 @@ __global__ __launch_bounds__(64 * kSplitWaves, 1) void score_split_kernel(ScoreJ
 
   uint4 ra[kSplitDepth][2];
   float rb[kSplitDepth][16];
+  // every load fenced: the ring's prologue and its refills then issue the 18 loads
+  // of a slice in one order (the order of use), which is what lets the waits at the
+  // loop head count only the slice being used
   auto load = [&](int d, int kt) {
     const uint16_t *h = hp + kt * kKt;
-    ra[d][0] = *reinterpret_cast<const uint4 *>(h);
-    ra[d][1] = *reinterpret_cast<const uint4 *>(h + 8);
     const float *wk = wp + static_cast<size_t>(kt * kKt) * kMid;
+    ra[d][0] = *reinterpret_cast<const uint4 *>(h);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) rb[d][kk] = wk[static_cast<size_t>(kk) * kMid];
+    for (int kk = 0; kk < 8; ++kk) {
+      rb[d][kk] = wk[static_cast<size_t>(kk) * kMid];
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    ra[d][1] = *reinterpret_cast<const uint4 *>(h + 8);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 8; kk < 16; ++kk) {
+      rb[d][kk] = wk[static_cast<size_t>(kk) * kMid];
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   f32x16 acc;
 #pragma unroll
   for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int d = 0; d < kSplitDepth; ++d) load(d, d);
   for (int kt0 = 0; kt0 < nkt; kt0 += kSplitDepth) {
@@ -298,6 +312,9 @@ __global__ __launch_bounds__(64 * kSplitWaves, 1) void score_split_kernel(ScoreJ
         av[8 + 2 * j] = bf16_lo(u1);
         av[8 + 2 * j + 1] = bf16_hi(u1);
       }
+      // all 16 operands widened first, then the slice's MFMAs back to back: a VALU
+      // or load instruction between two MFMAs of the chain costs more than it hides
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kk = 0; kk < 16; ++kk)
         acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[kk], rb[d][kk], acc, 0, 0, 0);
