@@ -307,11 +307,13 @@ def test_score_multi_equals_separate_calls():
 
 @pytest.mark.parametrize("n_jobs,n,ld_h,ld_s", [(8, 256, 2560, 4), (8, 1, 2560, 4),
                                                  (3, 33, 2568, 8), (8, 1000, 2560, 4),
-                                                 (1, 8192, 2560, 4), (1, 8193, 2560, 4)])
+                                                 (1, 8192, 2560, 4), (1, 8193, 2560, 4),
+                                                 (16, 512, 2560, 4), (16, 513, 2560, 4)])
 def test_score_multi_ws_equals_single_calls(n_jobs, n, ld_h, ld_s):
     """rma_score_multi_ws: every job's scores are bit-identical to its own rma_score
-    call, on the split path (up to 256 row tiles in all, ragged last tile, strided
-    input and output) and past it (8193 rows: the one-launch path).  The workspace
+    call, on the split path (up to 256 row tiles in all, the most jobs included,
+    ragged last tile, strided input and output) and past it (8193 rows, or 16 jobs
+    of 513: the one-launch path).  The workspace
     starts out holding NaNs, and a second call reuses it."""
     rng = np.random.default_rng(78 + n)
     need = R.rma_score_workspace_bytes(n_jobs, n)
