@@ -1,0 +1,178 @@
+"""GPU parity at a batch whose state offsets pass 2^31 and 2^32 elements.
+
+One layer at B = 4100: a K array is 4100 x 4 x 1024 x 256 BF16 elements (8.6 GB), so
+the element offset of sequence b passes 2^31 from b = 2048 and 2^32 from b = 4096; byte
+offsets pass 2^31 from b = 1024.  Decode, append, commit and the FP8 decode run over the
+whole batch.  Eight sequences on both sides of those boundaries hold seeded contents and
+are compared with the oracle; every other sequence holds zero K/V under full, consistent
+counts, so the launches have the shape of a full batch.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from oracle import fp8_ref as F
+import swa_memory_anchor_amd as R
+import synth
+from synth import core as C
+
+from gpu_util import (DEV, KV, KV_SCALES, META, assert_attn_close, assert_keys_close, bf16_dev,
+                      bits_host, decode_gpu, decode_gpu_fp8, f32_dev, i32_dev, norm_dev)
+
+pytestmark = pytest.mark.gpu
+
+B = 4100
+SAMPLE = [0, 1, 1023, 1024, 2047, 2048, 4095, 4099]
+# (n_bank, n_pend, pos) of the sampled sequences: partial tiles, empty and full segments
+COUNTS = [(1024, 255, 70000), (37, 5, 600), (513, 129, 100), (1024, 0, 262142), (0, 1, 0),
+          (16, 16, 15), (700, 200, 5000), (1000, 255, 1023)]
+
+
+def _gains(tag):
+    return {nm: synth.normal_f32_np(synth.stream_key(tag, nm), (256,), 1.0, 0.1)
+            for nm in ("gq_win", "gk_win", "gq_rma", "gk_rma")}
+
+
+def _fill_rest(big):
+    """Every sequence outside the sample: full window, bank and pending block, distinct
+    sources, zero scores (zero K/V from the allocation)."""
+    big.n_bank.fill_(1024)
+    big.n_pend.fill_(200)
+    big.pos.fill_(70000)
+    big.bank_src.copy_(torch.arange(1024, dtype=torch.int32, device=DEV).expand(B, 4, 1024))
+    big.pend_src.copy_(torch.arange(100000, 100256, dtype=torch.int32, device=DEV).expand(B, 256))
+
+
+def _place(big, st, names):
+    """Copy the oracle state's rows into the sampled sequences of the device state."""
+    idx = torch.tensor(SAMPLE, device=DEV)
+    for nm in names:
+        a = getattr(st, nm)
+        if nm in KV:
+            src = bf16_dev(a) if a.dtype == np.uint16 else torch.from_numpy(a).to(DEV)
+        else:
+            src = f32_dev(a) if a.dtype == np.float32 else i32_dev(a)
+        getattr(big, nm)[idx] = src
+
+
+def _rows(big, nm):
+    t = getattr(big, nm)[torch.tensor(SAMPLE, device=DEV)]
+    return bits_host(t) if t.dtype == torch.bfloat16 else t.cpu().numpy()
+
+
+@pytest.fixture(autouse=True)
+def _free_device_memory():
+    """Each test holds about 39 GB of state; hand it back once the test's frame is gone."""
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def test_large_batch_decode_then_append():
+    print(f"case: decode + append at B={B}, sequences {SAMPLE}", flush=True)
+    n = len(SAMPLE)
+    st = O.new_layer_state(n)
+    for nm in KV:
+        a = getattr(st, nm)
+        a[...] = synth.normal_bf16_np(synth.stream_key("big", nm), a.size).reshape(a.shape)
+    for i, (nb, npd, pos) in enumerate(COUNTS):
+        st.n_bank[i], st.n_pend[i], st.pos[i] = nb, npd, pos
+    g = _gains("big")
+    q = synth.normal_bf16_np(synth.stream_key("big", "q"), n * 4096).reshape(n, 16, 256)
+    big = R.alloc_layer_state(B, DEV)
+    _fill_rest(big)
+    _place(big, st, KV + META)
+    idx = torch.tensor(SAMPLE, device=DEV)
+    qd = torch.zeros(B, 16, 256, dtype=torch.bfloat16, device=DEV)
+    qd[idx] = bf16_dev(q)
+    nm = norm_dev(g)
+    o_w, l_w, o_r, l_r = decode_gpu(big, qd, qd, nm)
+    torch.cuda.synchronize()
+    ref = O.decode(st, q, q, g["gq_win"], g["gq_rma"], 1e-6, 1e7)
+    assert_attn_close(bits_host(o_w[idx]), l_w[idx].cpu().numpy(), ref[0], ref[1],
+                      what=f"window B={B}")
+    assert_attn_close(bits_host(o_r[idx]), l_r[idx].cpu().numpy(), ref[2], ref[3],
+                      what=f"anchor B={B}")
+    # the sequences around them are untouched (zero K/V: uniform softmax over zero rows)
+    assert torch.all(o_w[2049:4095].view(torch.int16) == 0)
+
+    recs = [synth.normal_bf16_np(synth.stream_key("big", r), n * 1024).reshape(n, 4, 256)
+            for r in ("kw", "vw", "kr", "vr")]
+    score = synth.normal_f32_np(synth.stream_key("big", "score"), (n, 4))
+    rd = []
+    for r in recs:
+        t = torch.zeros(B, 4, 256, dtype=torch.bfloat16, device=DEV)
+        t[idx] = bf16_dev(r)
+        rd.append(t)
+    sd = torch.zeros(B, 4, device=DEV)
+    sd[idx] = f32_dev(score)
+    R.swa_rma_append(big, B, *rd, sd, nm)
+    torch.cuda.synchronize()
+    O.append(st, *recs, g["gk_win"], g["gk_rma"], 1e-6, 1e7, score=score)
+    for nmk in ("win_v", "pend_v", "pend_score", "pend_src", "n_pend", "pos", "bank_k"):
+        assert np.array_equal(_rows(big, nmk), getattr(st, nmk)), nmk
+    for nmk in ("win_k", "pend_k"):
+        assert_keys_close(_rows(big, nmk), getattr(st, nmk), what=f"{nmk} B={B}")
+
+
+def test_large_batch_commit():
+    print(f"case: commit at B={B}, sequences {SAMPLE}", flush=True)
+    n = len(SAMPLE)
+    st = O.new_layer_state(n)
+    rng = synth.rng_np(synth.stream_key("big_commit"))
+    for nm in ("bank_k", "bank_v", "pend_k", "pend_v"):
+        a = getattr(st, nm)
+        a[...] = synth.normal_bf16_np(synth.stream_key("big_commit", nm), a.size).reshape(a.shape)
+    for i, (nb, npd, _) in enumerate(COUNTS):
+        st.n_bank[i], st.n_pend[i], st.pos[i] = nb, npd, 60000
+        for g in range(4):
+            st.bank_src[i, g] = rng.permutation(40000)[:1024]
+            st.bank_score[i, g] = rng.standard_normal(1024).astype(np.float32) * 0.3
+        st.pend_src[i] = np.arange(40000, 40256)
+        st.pend_score[i] = rng.standard_normal((256, 4)).astype(np.float32) * 0.3
+        st.pend_score[i, 5] = st.bank_score[i, :, 3]  # ties across the two parts
+    big = R.alloc_layer_state(B, DEV)
+    _fill_rest(big)
+    _place(big, st, KV + META)
+    keep = torch.full((B, 4, 1024), -9, dtype=torch.int32, device=DEV)
+    R.rma_commit_topk(big, B, keep)
+    torch.cuda.synchronize()
+    ref_keep = O.commit(st)
+    assert np.array_equal(keep[torch.tensor(SAMPLE, device=DEV)].cpu().numpy(), ref_keep)
+    for nmk in ("bank_k", "bank_v", "bank_src", "n_bank", "n_pend"):
+        assert np.array_equal(_rows(big, nmk), getattr(st, nmk)), nmk
+    assert np.array_equal(_rows(big, "bank_score").view(np.uint32), st.bank_score.view(np.uint32))
+    # a sequence outside the sample: 1024 + 200 equal scores keep the 1024 lowest sources
+    # (the bank's own 0..1023) and the counters advance
+    assert torch.equal(keep[3000, 0].cpu(), torch.arange(1024, dtype=torch.int32))
+    assert int(big.n_bank[3000]) == 1024 and int(big.n_pend[3000]) == 0
+
+
+def test_large_batch_fp8_decode():
+    print(f"case: fp8 decode at B={B}, sequences {SAMPLE}", flush=True)
+    n = len(SAMPLE)
+    st = F.new_layer_state_fp8(n)
+    for nm in KV:
+        a = getattr(st, nm)
+        a[...] = C.normal_e4m3_np(synth.stream_key("big8", nm), a.size).reshape(a.shape)
+        s = getattr(st, nm + "s")
+        s[...] = C.row_scale_np(synth.stream_key("big8", nm, "s"), s.size).reshape(s.shape)
+    for i, (nb, npd, pos) in enumerate(COUNTS):
+        st.n_bank[i], st.n_pend[i], st.pos[i] = nb, npd, pos
+    g = _gains("big8")
+    q = synth.normal_bf16_np(synth.stream_key("big8", "q"), n * 4096).reshape(n, 16, 256)
+    big = R.alloc_layer_state_fp8(B, DEV)
+    _fill_rest(big)
+    _place(big, st, KV + KV_SCALES + ("n_bank", "n_pend", "pos"))
+    idx = torch.tensor(SAMPLE, device=DEV)
+    qd = torch.zeros(B, 16, 256, dtype=torch.bfloat16, device=DEV)
+    qd[idx] = bf16_dev(q)
+    o_w, l_w, o_r, l_r = decode_gpu_fp8(big, qd, qd, norm_dev(g))
+    torch.cuda.synchronize()
+    ref = F.decode(st, q, q, g["gq_win"], g["gq_rma"], 1e-6, 1e7)
+    assert_attn_close(bits_host(o_w[idx]), l_w[idx].cpu().numpy(), ref[0], ref[1],
+                      what=f"fp8 window B={B}")
+    assert_attn_close(bits_host(o_r[idx]), l_r[idx].cpu().numpy(), ref[2], ref[3],
+                      what=f"fp8 anchor B={B}")
