@@ -176,3 +176,49 @@ def test_large_batch_fp8_decode():
                       what=f"fp8 window B={B}")
     assert_attn_close(bits_host(o_r[idx]), l_r[idx].cpu().numpy(), ref[2], ref[3],
                       what=f"fp8 anchor B={B}")
+
+
+def test_large_batch_gdn_step():
+    """The GDN step at B = 4100 (FP16 matrices, 4.3 GB: element offsets pass 2^31 from
+    sequence 4096) against the oracle on the sampled sequences."""
+    from oracle import gdn_ref as G
+    from gdn_check import O_TOL, out_rel, state_err_ratio
+
+    print(f"case: gdn step at B={B}, sequences {SAMPLE}", flush=True)
+    n = len(SAMPLE)
+    st = G.new_state(n, "f16")
+    st.S[...] = C.scaled_normal_np(synth.stream_key("big_gdn", "S"), st.S.size,
+                                   dtype=np.float16).reshape(st.S.shape)
+    st.conv[...] = synth.normal_bf16_np(synth.stream_key("big_gdn", "conv"),
+                                        st.conv.size).reshape(st.conv.shape)
+    rng = synth.rng_np(synth.stream_key("big_gdn", "params"))
+    conv_w = (rng.standard_normal((8192, 4)) * 0.5).astype(np.float32)
+    a_log = np.log(rng.uniform(1, 16, 32)).astype(np.float32)
+    dt_bias = rng.standard_normal(32).astype(np.float32)
+    x = synth.normal_bf16_np(synth.stream_key("big_gdn", "x"), n * 8192).reshape(n, 8192)
+    a = (rng.standard_normal((n, 32)) * 2).astype(np.float32)
+    bb = (rng.standard_normal((n, 32)) * 2).astype(np.float32)
+    pos = np.array([0, 1, 2, 3, 70001, 5, 1023, 262143], np.int32)
+    idx = torch.tensor(SAMPLE, device=DEV)
+    dev = R.alloc_gdn_state(B, "f16", DEV)
+    dev.S[idx] = torch.from_numpy(st.S.copy()).to(DEV)
+    dev.conv[idx] = bf16_dev(st.conv)
+    xd = torch.zeros(B, 8192, dtype=torch.bfloat16, device=DEV)
+    xd[idx] = bf16_dev(x)
+    ad = torch.zeros(B, 32, device=DEV)
+    ad[idx] = f32_dev(a)
+    bd = torch.zeros(B, 32, device=DEV)
+    bd[idx] = f32_dev(bb)
+    pd = torch.full((B,), 7, dtype=torch.int32, device=DEV)
+    pd[idx] = i32_dev(pos)
+    o = torch.full((B, 32, 128), 7.0, dtype=torch.bfloat16, device=DEV)
+    R.gdn_decode_step(dev, B, xd, ad, bd, pd,
+                      R.GdnParams(f32_dev(conv_w), f32_dev(a_log), f32_dev(dt_bias)), o)
+    torch.cuda.synchronize()
+    ref_o = G.decode_step(st, x, a, bb, conv_w, a_log, dt_bias, pos)
+    assert np.array_equal(bits_host(dev.conv[idx]), st.conv), "convolution ring"
+    ratio = state_err_ratio(dev.S[idx].cpu().numpy(), st.S)
+    assert ratio <= 1.0, f"S out of bound ({ratio:.3f})"
+    rel = out_rel(synth.bf16_bits_to_f32_np(bits_host(o[idx])), ref_o)
+    print(f"gdn B={B}: state err/bound {ratio:.3f}, out max {rel.max():.3e}")
+    assert np.all(np.isfinite(rel)) and rel.max() <= O_TOL
