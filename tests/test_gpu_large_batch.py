@@ -222,3 +222,76 @@ def test_large_batch_gdn_step():
     rel = out_rel(synth.bf16_bits_to_f32_np(bits_host(o[idx])), ref_o)
     print(f"gdn B={B}: state err/bound {ratio:.3f}, out max {rel.max():.3e}")
     assert np.all(np.isfinite(rel)) and rel.max() <= O_TOL
+
+
+def test_large_batch_prefill():
+    """An 8-token chunk for every sequence at B = 4100; the sampled sequences replayed
+    token by token by the oracle (those whose pending block has no room are left as
+    they were, with empty outputs)."""
+    Cn = 8
+    print(f"case: prefill C={Cn} at B={B}, sequences {SAMPLE}", flush=True)
+    n = len(SAMPLE)
+    st = O.new_layer_state(n)
+    for nm in KV:
+        a = getattr(st, nm)
+        a[...] = synth.normal_bf16_np(synth.stream_key("big_pf", nm), a.size).reshape(a.shape)
+    # as COUNTS, with the chunk kept inside the 262,144 positions
+    counts = [(nb, npd, min(pos, 262144 - 1 - Cn)) for nb, npd, pos in COUNTS]
+    for i, (nb, npd, pos) in enumerate(counts):
+        st.n_bank[i], st.n_pend[i], st.pos[i] = nb, npd, pos
+        for g in range(4):
+            st.bank_src[i, g] = synth.distinct_ints_np(synth.stream_key("big_pf", "src", i, g),
+                                                       1024, 10**6, 10**6 + 4096)
+        st.pend_src[i] = np.arange(256) + 2 * 10**6
+    g = _gains("big_pf")
+    recs = [synth.normal_bf16_np(synth.stream_key("big_pf", "rec", r), n * Cn * 1024)
+            .reshape(n, Cn, 4, 256) for r in range(4)]
+    q = synth.normal_bf16_np(synth.stream_key("big_pf", "q"), n * Cn * 4096).reshape(n, Cn, 16, 256)
+    score = synth.normal_f32_np(synth.stream_key("big_pf", "score"), (n, Cn, 4))
+    big = R.alloc_layer_state(B, DEV)
+    _fill_rest(big)
+    _place(big, st, KV + META)
+    idx = torch.tensor(SAMPLE, device=DEV)
+
+    def spread(x, shape, dtype):
+        t = torch.zeros(*shape, dtype=dtype, device=DEV)
+        t[idx] = bf16_dev(x) if dtype == torch.bfloat16 else f32_dev(x)
+        return t
+
+    rd = [spread(r, (B, Cn, 4, 256), torch.bfloat16) for r in recs]
+    qd = spread(q, (B, Cn, 16, 256), torch.bfloat16)
+    sd = spread(score, (B, Cn, 4), torch.float32)
+    o_w = torch.full((B, Cn, 16, 256), 3.0, dtype=torch.bfloat16, device=DEV)
+    o_r = torch.full_like(o_w, 3.0)
+    l_w = torch.full((B, Cn, 16), 3.0, device=DEV)
+    l_r = torch.full_like(l_w, 3.0)
+    R.swa_rma_prefill(big, B, Cn, *rd, sd, qd, qd, norm_dev(g), o_w, l_w, o_r, l_r,
+                      R.prefill_workspace(B, Cn))
+    torch.cuda.synchronize()
+    ow, lw = bits_host(o_w[idx]), l_w[idx].cpu().numpy()
+    orr, lr = bits_host(o_r[idx]), l_r[idx].cpu().numpy()
+    got = {k: _rows(big, k) for k in KV + META}
+    for i, (nb, npd, pos) in enumerate(counts):
+        if npd + Cn > 256:
+            for k in ("win_k", "win_v", "pend_k", "pend_v", "n_pend", "pos", "pend_src"):
+                assert np.array_equal(got[k][i], getattr(st, k)[i]), (i, k)
+            assert np.all(ow[i] == 0) and np.all(np.isneginf(lw[i]))
+            continue
+        one = O.new_layer_state(1)
+        for k in one.__dict__:
+            getattr(one, k)[...] = getattr(st, k)[i:i + 1]
+        ref = [[], [], [], []]
+        for t in range(Cn):
+            O.append(one, *[r[i:i + 1, t] for r in recs], g["gk_win"], g["gk_rma"], 1e-6, 1e7,
+                     score=score[i:i + 1, t])
+            d = O.decode(one, q[i:i + 1, t], q[i:i + 1, t], g["gq_win"], g["gq_rma"], 1e-6, 1e7)
+            for j in range(4):
+                ref[j].append(d[j][0])
+        assert_attn_close(ow[i], lw[i], np.stack(ref[0]), np.stack(ref[1]), what=f"seq {i} win")
+        assert_attn_close(orr[i], lr[i], np.stack(ref[2]), np.stack(ref[3]), what=f"seq {i} rma")
+        for k in ("win_v", "pend_v", "pend_src", "n_pend", "pos", "bank_k", "n_bank"):
+            assert np.array_equal(got[k][i], getattr(one, k)[0]), (i, k)
+        assert np.array_equal(got["pend_score"][i].view(np.uint32),
+                              one.pend_score[0].view(np.uint32))
+        for k in ("win_k", "pend_k"):
+            assert_keys_close(got[k][i], getattr(one, k)[0], what=f"seq {i} {k}")
