@@ -295,3 +295,27 @@ def test_large_batch_prefill():
                               one.pend_score[0].view(np.uint32))
         for k in ("win_k", "pend_k"):
             assert_keys_close(got[k][i], getattr(one, k)[0], what=f"seq {i} {k}")
+
+
+def test_large_scorer_call():
+    """rma_score over 900,000 rows (4.6 GB of hidden state: row offsets pass 2^31 elements
+    from row 838,861) on the 256-row tiles; seeded rows on both sides of that row and at
+    the end against the oracle, zero rows scoring exactly zero."""
+    from gpu_util import assert_scores_close
+
+    N = 900_000
+    rows = [0, 1, 838_860, 838_861, 838_862, 899_743, N - 1]
+    print(f"case: scorer N={N}, rows {rows}", flush=True)
+    h = synth.normal_bf16_np(synth.stream_key("big_score", "h"), len(rows) * 2560)
+    h = h.reshape(len(rows), 2560)
+    w1 = synth.normal_f32_np(synth.stream_key("big_score", "w1"), (2560, 256), 0.0, 0.02)
+    w2 = synth.normal_f32_np(synth.stream_key("big_score", "w2"), (256, 4), 0.0, 0.02)
+    ridx = torch.tensor(rows, device=DEV)
+    hd = torch.zeros(N, 2560, dtype=torch.bfloat16, device=DEV)
+    hd[ridx] = bf16_dev(h)
+    out = torch.full((N, 4), float("nan"), device=DEV)
+    R.rma_score(hd, N, 2560, f32_dev(w1), f32_dev(w2), out, 4)
+    torch.cuda.synchronize()
+    assert_scores_close(out[ridx].cpu().numpy(), O.score(h, w1, w2), what=f"scorer N={N}")
+    zero_rows = torch.tensor([2, 838_859, 899_999 - 1], device=DEV)
+    assert torch.all(out[zero_rows] == 0)
