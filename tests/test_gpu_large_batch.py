@@ -319,3 +319,53 @@ def test_large_scorer_call():
     assert_scores_close(out[ridx].cpu().numpy(), O.score(h, w1, w2), what=f"scorer N={N}")
     zero_rows = torch.tensor([2, 838_859, 899_999 - 1], device=DEV)
     assert torch.all(out[zero_rows] == 0)
+
+
+def test_large_batch_step_equals_append_then_decode():
+    """The fused step at B = 4100 gives the bits of append followed by decode: every
+    output of the batch, and the appended rows and counters of the sampled sequences."""
+    print(f"case: fused step at B={B}", flush=True)
+    n = len(SAMPLE)
+    st = O.new_layer_state(n)
+    for nm in KV:
+        a = getattr(st, nm)
+        a[...] = synth.normal_bf16_np(synth.stream_key("big_step", nm), a.size).reshape(a.shape)
+    for i, (nb, npd, pos) in enumerate(COUNTS):
+        st.n_bank[i], st.n_pend[i], st.pos[i] = nb, min(npd, 255), pos
+    g = _gains("big_step")
+    nm = norm_dev(g)
+    idx = torch.tensor(SAMPLE, device=DEV)
+    recs = []
+    for r in ("kw", "vw", "kr", "vr"):
+        t = torch.zeros(B, 4, 256, dtype=torch.bfloat16, device=DEV)
+        t[idx] = bf16_dev(synth.normal_bf16_np(synth.stream_key("big_step", r), n * 1024)
+                          .reshape(n, 4, 256))
+        recs.append(t)
+    qd = torch.zeros(B, 16, 256, dtype=torch.bfloat16, device=DEV)
+    qd[idx] = bf16_dev(synth.normal_bf16_np(synth.stream_key("big_step", "q"), n * 4096)
+                       .reshape(n, 16, 256))
+    outs = {}
+    for fused in (True, False):
+        big = R.alloc_layer_state(B, DEV)
+        _fill_rest(big)
+        _place(big, st, KV + META)
+        o = [torch.empty(B, 16, 256, dtype=torch.bfloat16, device=DEV),
+             torch.empty(B, 16, device=DEV),
+             torch.empty(B, 16, 256, dtype=torch.bfloat16, device=DEV),
+             torch.empty(B, 16, device=DEV)]
+        if fused:
+            R.swa_rma_step(big, B, *recs, None, qd, qd, nm, *o, R.step_workspace(B))
+        else:
+            R.swa_rma_append(big, B, *recs, None, nm)
+            R.swa_rma_decode_attn(big, B, qd, qd, nm, *o, R.decode_workspace(B))
+        torch.cuda.synchronize()
+        outs[fused] = ([x.view(torch.int32) if x.dtype == torch.float32 else x.view(torch.int16)
+                        for x in o],
+                       {k: _rows(big, k) for k in ("win_k", "win_v", "pend_k", "pend_v",
+                                                   "n_pend", "pos")})
+        del big, o
+        torch.cuda.empty_cache()
+    for a, b_ in zip(outs[True][0], outs[False][0]):
+        assert torch.equal(a, b_)
+    for k, v in outs[True][1].items():
+        assert np.array_equal(v, outs[False][1][k]), k
