@@ -138,13 +138,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// LDS tiles are row-major (32 keys x 32 sixteen-byte chunks) with the chunk index
-// XOR-swizzled by the key, so that the MFMA operand reads below spread over all
+// LDS tile layouts, chosen so that the MFMA operand reads below spread over all
 // banks (gfx950 LDS serves 256 bytes per clock: 16 lanes of a 16-byte read, 32
 // lanes of an 8-byte transposed read):
-//   K chunk c of key k sits at chunk position c ^ (k & 15)
-//   V chunk c of key k sits at chunk position c ^ (4 (k & 3))
-__device__ __forceinline__ int k_swz(int key) { return key & 15; }
+//  * K: key pair j (keys j and j + 16, 512 bytes each) at byte 1040 j, the 16
+//    bytes after each pair unused.  Lanes 0..15 of a read take keys 0..15 at one
+//    chunk: 1040 j is 16 j modulo 256, so the 16 reads cover the 64 banks once.
+//    A lane's reads of a tile then differ only by immediate offsets (one address
+//    register), and one load-to-LDS instruction (64 lanes x 16 bytes) fills one
+//    pair, each half-wave reading 512 contiguous bytes of one key.
+//  * V: row-major, chunk c of key k at chunk position c ^ (4 (k & 3)).
+constexpr int kKPairBytes = 2 * kDim * 2 + 16;                  // 1040
+constexpr int kKStageElems = kPKeys / 2 * kKPairBytes / 2;      // 8320 (16,640 bytes)
 __device__ __forceinline__ int v_swz(int key) { return 4 * (key & 3); }
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -160,18 +165,18 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
 // One K and one V tile buffer per pipeline stage, as separate arrays so that the
 // compiler's wait for loads-to-LDS can tell the stage being read from the stages
 // still being filled.
-__shared__ __align__(16) uint16_t pf_k0[kTileElems];
-__shared__ __align__(16) uint16_t pf_k1[kTileElems];
-__shared__ __align__(16) uint16_t pf_k2[kTileElems];
-__shared__ __align__(16) uint16_t pf_k3[kTileElems];
+__shared__ __align__(16) uint16_t pf_k0[kKStageElems];
+__shared__ __align__(16) uint16_t pf_k1[kKStageElems];
+__shared__ __align__(16) uint16_t pf_k2[kKStageElems];
+__shared__ __align__(16) uint16_t pf_k3[kKStageElems];
 __shared__ __align__(16) uint16_t pf_v0[kTileElems];
 __shared__ __align__(16) uint16_t pf_v1[kTileElems];
 __shared__ __align__(16) uint16_t pf_v2[kTileElems];
 __shared__ __align__(16) uint16_t pf_v3[kTileElems];
 static_assert(kStages == 4, "the tile loop below is written out for four stages");
 // Per-thread LDS offsets, read back per tile (keeping them in registers across the
-// tile loop would cost registers the loop needs): the lane's K and V chunk offsets
-// of its two loads, and its four V^T read offsets.
+// tile loop would cost registers the loop needs): the lane's V chunk offsets of
+// its two V loads, and its four V^T read offsets.
 typedef int pf_i32x4 __attribute__((ext_vector_type(4)));
 typedef volatile __attribute__((address_space(3))) pf_i32x4 lds_vi32x4;
 __shared__ pf_i32x4 pf_dma_tab[kPThreads];
@@ -237,12 +242,13 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(PrefillParams a
   const int k0_ = ((t_) - (si_##sg_ == 0 ? 0 : (si_##sg_ == 1 ? tl0 : tl0 + tl1))) * kPKeys;
 
   // Load-to-LDS of tile t into stage st: each wave moves 2 KB of K and 2 KB of V,
-  // 1 KB (two rows) per instruction; lane L fills chunk position L % 32 of row
-  // 2i + L / 32, i.e. fetches the chunk that the swizzle puts there.  Rows past
-  // the segment's end read as zero.
+  // 1 KB per instruction.  K: the instruction for key pair j fills its 1040-byte
+  // slot, lane L taking chunk L % 32 of key j + 16 (L / 32).  V: lane L fills chunk
+  // position L % 32 of row 2i + L / 32, i.e. fetches the chunk that the swizzle
+  // puts there.  Rows past the segment's end read as zero.
   // The tile's first row and the wave's row pair go into the scalar offset; the
-  // lane's part (odd row of the pair, swizzled chunk) is fixed per load, formed
-  // once here and kept in an LDS table that each tile reads back.
+  // lane's part of a V load (odd row of the pair, swizzled chunk) is fixed per
+  // load, formed once here and kept in an LDS table that each tile reads back.
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   constexpr int kPairs = kPKeys / 2 / kPWaves;  // row pairs each wave moves per tile: 2
   static_assert(kPairs == 2, "the offset table holds two K and two V chunk offsets");
@@ -250,8 +256,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(PrefillParams a
     const int rlo = lane >> 5, cpos = lane & 31;
     pf_i32x4 t;
     const int row0 = 2 * (kPairs * wave_s) + rlo, row1 = row0 + 2;
-    t.x = (cpos ^ k_swz(row0)) << 4;
-    t.y = (cpos ^ k_swz(row1)) << 4;
+    t.x = 0;
+    t.y = 0;
     t.z = (cpos ^ v_swz(row0)) << 4;
     t.w = (cpos ^ v_swz(row1)) << 4;
     pf_dma_tab[threadIdx.x] = t;
@@ -261,14 +267,16 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(PrefillParams a
     PREFILL_TILE_SEG(t_, isg, ik0)                                                           \
     const pf_i32x4 dt = ((lds_vi32x4 *)pf_dma_tab)[threadIdx.x];                             \
     const int lo_off = (lane >> 5) * isg.stride;                                             \
-    const int kc[2] = {dt.x, dt.y}, vc[2] = {dt.z, dt.w};                                    \
+    const int k_off = 16 * lo_off + ((lane & 31) << 4);                                      \
+    const int vc[2] = {dt.z, dt.w};                                                          \
     _Pragma("unroll") for (int i = 0; i < kPairs; ++i) {                                     \
       const int pr = kPairs * wave_s + i;                                                    \
-      const int soff = (ik0 + 2 * pr) * isg.stride;                                          \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(isg.k, (lds_void *)&kdst_[pr * 2 * kDim], 16, \
-                                               lo_off + kc[i], soff, 0, 0);                  \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(                                              \
+          isg.k, (lds_void *)(reinterpret_cast<char *>(kdst_) + pr * kKPairBytes), 16, k_off, \
+          (ik0 + pr) * isg.stride, 0, 0);                                                    \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(isg.v, (lds_void *)&vdst_[pr * 2 * kDim], 16, \
-                                               lo_off + vc[i], soff, 0, 0);                  \
+                                               lo_off + vc[i], (ik0 + 2 * pr) * isg.stride,  \
+                                               0, 0);                                        \
     }                                                                                        \
   }
   // Start the first tiles' loads before the query prologue.
@@ -394,14 +402,12 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(PrefillParams a
   const int age_max = min(p0, kWindow - 2 - my_tok);
   const int wave_age_max = min(p0, kWindow - 2 - wave_last_tok);
 
-  // LDS operand offsets (bytes).  K (A of S^T = K Q^T): key rl, chunk 2s + hh.
+  // LDS operand offsets (bytes).  K (A of S^T = K Q^T): key rl, chunk 2s + hh, at
+  // k_base + 32 s.
   // V^T (A of O^T = V^T P^T) by transposed reads: lane i of 16-lane group G points
   // at key 16j + 8r + 4(G/2) + i/4, dims 32d + 16(G%2) + 4(i%4) .. +3; the read
   // hands lane i dim 32d + 16(G%2) + i of the four keys 16j + 8r + 4(G/2) + 0..3.
-  // chunk 2s + hh of key rl sits at 16 (s / 8) + ((2 (s % 8) + hh) ^ (rl & 15))
-  int k_addr[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) k_addr[c] = 2 * (rl * kDim + (((2 * c + hh) ^ k_swz(rl)) << 3));
+  int k_base = (rl & 15) * kKPairBytes + (rl >> 4) * (2 * kDim) + 16 * hh;
   const int vg = lane >> 4, vi = lane & 15;
   const int v_key = 4 * (vg >> 1) + (vi >> 2);  // + 16j + 8r (keeps key & 3)
   const int v_dim = 16 * (vg & 1) + 4 * (vi & 3);  // + 32d
@@ -425,11 +431,11 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(PrefillParams a
     const int kind = csg.kind;                                                               \
     const int n = csg.n;                                                                     \
     if (wave_live && !(kind == 2 && k0 > wave_last_tok)) {                                   \
-      _Pragma("unroll") for (int c = 0; c < 8; ++c) asm volatile("" : "+v"(k_addr[c]));     \
+      asm volatile("" : "+v"(k_base));                                                       \
       f32x16 sc = {};                                                                        \
       _Pragma("unroll") for (int s = 0; s < 16; ++s) {                                       \
         const u32x4 kv = *reinterpret_cast<const u32x4 *>(                                   \
-            reinterpret_cast<const char *>(kt) + k_addr[s & 7] + 256 * (s >> 3));                \
+            reinterpret_cast<const char *>(kt) + k_base + 32 * s);                           \
         sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pbitcast<bf16x8>(kv), qb[s], sc, 0, 0,  \
                                                      0);                                     \
       }                                                                                      \
@@ -444,17 +450,14 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(PrefillParams a
             sc[r] = age <= age_max ? sc[r] : -INFINITY;                                      \
           }                                                                                  \
         }                                                                                    \
-      } else if (kind == 2) {                                                                \
-        if (k0 + kPKeys - 1 > wave_first_tok) {                                              \
-          /* the lane index from mbcnt: nothing kept live across the loop */                \
-          const int ln_ = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); \
-          const int tok_ = wave_first_tok + ((ln_ & 31) >> 2);                               \
-          _Pragma("unroll") for (int r = 0; r < 16; ++r) sc[r] =                             \
-              kl + 8 * (r >> 2) + (r & 3) <= tok_ ? sc[r] : -INFINITY;                       \
-        }                                                                                    \
-      } else if (k0 + kPKeys > n) {                                                          \
+      } else if (kind == 2 ? k0 + kPKeys - 1 > wave_first_tok : k0 + kPKeys > n) {           \
+        /* keys at or past lim are masked: the segment's end, or, in the chunk, the      */ \
+        /* row's own token + 1 (the lane index from mbcnt: nothing kept live across the  */ \
+        /* loop)                                                                         */ \
+        const int ln_ = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));   \
+        const int lim = kind == 2 ? wave_first_tok + ((ln_ & 31) >> 2) + 1 : n;              \
         _Pragma("unroll") for (int r = 0; r < 16; ++r) sc[r] =                               \
-            kl + 8 * (r >> 2) + (r & 3) < n ? sc[r] : -INFINITY;                             \
+            kl + 8 * (r >> 2) + (r & 3) < lim ? sc[r] : -INFINITY;                           \
       }                                                                                      \
       float m8[8];                                                                           \
       _Pragma("unroll") for (int r = 0; r < 8; ++r) m8[r] = fmaxf(sc[r], sc[r + 8]);          \
